@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs and the workload shapes (no quantization arithmetic).
+
+The pages measure on a private video, dataset and checkpoints of a DINOv3
+ViT + EoMT segmenter (lightly-train README "DINOv3 + EoMT on RTX 5090",
+section 1). None of that is available, so every input here is a seeded
+synthetic bf16 tensor with the shapes of the ViT linear layers named in the
+README's section 4.3 (qkv, proj, fc1, fc2 per block) and these values:
+
+  activations  N(0, 1), each element independently (p = 1e-3) multiplied by
+               50 to model the "massive activations" of README section 5.5
+  fc2 input    GELU (exact erf) of such an activation
+  weights      N(0, 0.02)        bias  N(0, 0.01)        grad_out  N(0, 1e-3)
+
+(the second parameter is a standard deviation). Two generators produce the
+same recipe:
+  * ``np_*``: numpy PCG64 in float64, rounded float64 -> float32 -> bf16, each
+    step round-to-nearest-even. Used by tests, so the oracle sees exactly
+    the bits the GPU sees.
+  * ``torch_*``: torch's device generator in float32 -> bf16 (RNE). Used by
+    the benchmark to fill gigabytes of HBM quickly; same distributions,
+    different random stream.
+
+Seeds: seed = 100000 * workload_id + 100 * block + tensor_id.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+OUTLIER_P = 1e-3
+OUTLIER_GAIN = 50.0
+W_STD = 0.02
+BIAS_STD = 0.01
+GRAD_STD = 1e-3
+
+
+# ------------------------------------------------------------- bf16 bits
+
+def _f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> float32 -> bf16 bit patterns (each step RNE)."""
+    return _f32_to_bf16_bits(np.asarray(x, dtype=np.float64).astype(np.float32))
+
+
+# ------------------------------------------------------------- numpy recipe
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _activation_f64(shape, seed: int) -> np.ndarray:
+    rng = _rng(seed)
+    z = rng.standard_normal(shape)
+    hit = rng.random(shape) < OUTLIER_P
+    z[hit] *= OUTLIER_GAIN
+    return z
+
+
+def np_activation(shape, seed: int) -> np.ndarray:
+    return to_bf16_bits(_activation_f64(shape, seed))
+
+
+def np_gelu_activation(shape, seed: int) -> np.ndarray:
+    from scipy.special import erf
+    z = _activation_f64(shape, seed)
+    return to_bf16_bits(0.5 * z * (1.0 + erf(z / np.sqrt(2.0))))
+
+
+def np_normal(shape, seed: int, std: float) -> np.ndarray:
+    return to_bf16_bits(_rng(seed).standard_normal(shape) * std)
+
+
+# ------------------------------------------------------------- torch recipe
+
+def torch_activation(shape, seed: int, device="cuda", gelu=False):
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    z = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    hit = torch.rand(shape, generator=g, device=device) < OUTLIER_P
+    z = torch.where(hit, z * OUTLIER_GAIN, z)
+    if gelu:
+        z = torch.nn.functional.gelu(z)
+    return z.to(torch.bfloat16)
+
+
+def torch_normal(shape, seed: int, std: float, device="cuda"):
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+# ------------------------------------------------------------- workloads
+
+@dataclass(frozen=True)
+class Linear:
+    """One quantized GEMM C[M, N] = A[M, K] * W[N, K]^T + bias."""
+    name: str
+    n: int
+    k: int
+    a_kind: str          # "act" or "gelu"
+    a_id: int            # tensor ids for seeds
+    w_id: int
+    bias_id: int
+
+
+@dataclass(frozen=True)
+class Stack:
+    """A forward linear stack: `blocks` ViT blocks of qkv/proj/fc1/fc2."""
+    wid: int
+    name: str
+    fmt: str
+    m: int
+    hidden: int
+    mlp: int
+    blocks: int
+    linears: tuple = field(default=())
+
+    def gemm_flops(self) -> int:
+        return 2 * self.m * sum(l.n * l.k for l in self.linears) * self.blocks
+
+
+def _vit_linears(hidden: int, mlp: int):
+    return (
+        Linear("qkv", 3 * hidden, hidden, "act", 0, 1, 2),
+        Linear("proj", hidden, hidden, "act", 3, 4, 5),
+        Linear("fc1", mlp, hidden, "act", 6, 7, 8),
+        Linear("fc2", hidden, mlp, "gelu", 9, 10, 11),
+    )
+
+
+TOKENS = 1605                  # 40 x 40 patches of a 640 x 640 image + cls + 4 registers
+
+SINGLE_LAYER = Stack(1, "single_mxfp8_256x768x768", "mxfp8", 256, 768, 768, 1,
+                     (Linear("linear", 768, 768, "act", 0, 1, 2),))
+VITB_MXFP8 = Stack(2, "vitb16_mxfp8_fwd_stack", "mxfp8", 14 * TOKENS, 768, 3072, 12,
+                   _vit_linears(768, 3072))
+VITL_MXFP8 = Stack(3, "vitl16_mxfp8_fwd_stack", "mxfp8", 7 * TOKENS, 1024, 4096, 24,
+                   _vit_linears(1024, 4096))
+VITL_MXFP4 = Stack(4, "vitl16_mxfp4_fwd_stack", "mxfp4", 7 * TOKENS, 1024, 4096, 24,
+                   _vit_linears(1024, 4096))
+
+STACKS = {s.name: s for s in (SINGLE_LAYER, VITB_MXFP8, VITL_MXFP8, VITL_MXFP4)}
+
+
+@dataclass(frozen=True)
+class TrainPair:
+    """fc1/fc2 of one ViT-L block: fprop, dgrad and wgrad GEMMs in NVFP4."""
+    wid: int = 5
+    name: str = "vitl16_nvfp4_fc1fc2_train"
+    fmt: str = "nvfp4"
+    m: int = 7 * TOKENS
+    hidden: int = 1024
+    mlp: int = 4096
+    # tensor ids
+    X: int = 20
+    H: int = 21
+    DY1: int = 22
+    DY2: int = 23
+    W1: int = 24
+    W2: int = 25
+    B1: int = 26
+    B2: int = 27
+
+    def gemm_flops(self) -> int:
+        return 6 * 2 * self.m * self.hidden * self.mlp
+
+
+TRAIN_PAIR = TrainPair()
+
+
+def seed(wid: int, block: int, tensor_id: int) -> int:
+    return 100000 * wid + 100 * block + tensor_id

@@ -1,0 +1,155 @@
+"""Pins for oracle/gemm.py.
+
+* Brute force: exact Fraction dot products over values decoded here from the
+  stored bytes (packed nibbles unpacked by this test, scale buffer and NVFP4
+  trailer read back by this test) agree with the float64 reference.
+* Orientation: inputs that quantize exactly give C = A * B^T of the original
+  values, for non-square shapes (a transposed operand fails).
+* Scale shift: scaling A by 2^k scales C (without bias) by exactly 2^k.
+* Acceptance: the rule admits the correctly rounded result and rejects a
+  value one bf16 step outside the bound.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import gemm as G
+from oracle import quantize as Q
+from block_scaled_precision_mx_amd import workloads as W
+
+from test_oracle_formats import frac_bf16, frac_e2m1, frac_e4m3
+
+
+def bits_of(x):
+    return W.to_bf16_bits(np.asarray(x, dtype=np.float64))
+
+
+def frac_operand(q: Q.Quantized):
+    """Exact values [rows][length] from the stored byte images."""
+    packed = q.packed_codes()
+    sbuf = q.scale_buffer()
+    bs = Q.block_size(q.fmt)
+    nblk = q.k_pad // bs
+    s_t = None
+    if q.fmt == "nvfp4":
+        off = -(-(q.rows * nblk) // 16) * 16
+        s_t = Fraction(float(sbuf[off: off + 4].view(np.float32)[0]))
+    out = []
+    for r in range(q.rows):
+        row = []
+        for k in range(q.length):
+            if q.fmt == "mxfp8":
+                e = frac_e4m3(int(packed[r, k]))
+            else:
+                byte = int(packed[r, k // 2])
+                e = frac_e2m1(byte & 15 if k % 2 == 0 else byte >> 4)
+            sb = int(sbuf[r * nblk + k // bs])
+            if q.fmt == "nvfp4":
+                scale = frac_e4m3(sb) * s_t
+            else:
+                scale = Fraction(2) ** (sb - 127)
+            row.append(e * scale)
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("fmt", Q.FORMATS)
+@pytest.mark.parametrize("mnk", [(1, 1, 32), (3, 4, 64), (4, 2, 99), (2, 3, 11)])
+def test_brute_force_dot_products(fmt, mnk):
+    m, n, k = mnk
+    a_bits = W.np_activation((m, k), seed=31 + k)
+    b_bits = W.np_normal((n, k), seed=32 + k, std=0.02)
+    bias = W.np_normal((n,), seed=33, std=0.01)
+    qa, qb = Q.quantize(a_bits, fmt), Q.quantize(b_bits, fmt)
+    c, s = G.gemm_ref(qa, qb, bias)
+    fa, fb = frac_operand(qa), frac_operand(qb)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(x * y for x, y in zip(fa[i], fb[j])) + frac_bf16(int(bias[j]))
+            sabs = sum(abs(x * y) for x, y in zip(fa[i], fb[j])) + abs(frac_bf16(int(bias[j])))
+            assert abs(Fraction(float(c[i, j])) - exact) <= Fraction(k + 1, 2 ** 52) * sabs
+            assert abs(Fraction(float(s[i, j])) - sabs) <= Fraction(k + 1, 2 ** 52) * sabs
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "nvfp4"])
+def test_orientation_with_exact_inputs(fmt):
+    """Grid-valued inputs with unit scales quantize exactly, so C must equal
+    the plain product A @ B.T of the inputs (M=3, N=5, K=64: a transposed or
+    swapped operand cannot even be multiplied)."""
+    rng = np.random.default_rng(3)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6.0])
+    a = rng.choice(grid, (3, 64)) * rng.choice([-1, 1], (3, 64))
+    b = rng.choice(grid, (5, 64)) * rng.choice([-1, 1], (5, 64))
+    bs = Q.block_size(fmt)
+    a[:, ::bs] = 6.0         # every block max is 6: MX e = 0 for E2M1 / E4M3 grid values
+    b[:, ::bs] = 6.0
+    if fmt == "nvfp4":
+        # s_t = 2688 / 2688 = 1; the block holding 2688 gets scale 448 and
+        # holds nothing else, every other block gets scale 6 / 6 = 1.
+        for t in (a, b):
+            t[0, :bs] = 0.0
+            t[0, 0] = 2688.0
+    qa, qb = Q.quantize(bits_of(a), fmt), Q.quantize(bits_of(b), fmt)
+    assert np.array_equal(qa.dequantize(), a) and np.array_equal(qb.dequantize(), b)
+    c, _ = G.gemm_ref(qa, qb)
+    assert c.shape == (3, 5)
+    assert np.array_equal(c, a @ b.T)
+
+
+@pytest.mark.parametrize("fmt", Q.FORMATS)
+def test_scale_shift(fmt):
+    a_bits = W.np_activation((4, 96), seed=41)
+    b_bits = W.np_normal((6, 96), seed=42, std=0.02)
+    bias = W.np_normal((6,), seed=43, std=0.01)
+    qb = Q.quantize(b_bits, fmt)
+    c0, s0 = G.gemm_ref(Q.quantize(a_bits, fmt), qb)
+    for k in (-3, 4):
+        ak = bits_of(F.bf16_to_f64(a_bits) * 2.0 ** k)
+        ck, sk = G.gemm_ref(Q.quantize(ak, fmt), qb)
+        assert np.array_equal(ck, c0 * 2.0 ** k)
+        assert np.array_equal(sk, s0 * 2.0 ** k)
+    # the bias enters once, unscaled
+    cb, _ = G.gemm_ref(Q.quantize(a_bits, fmt), qb, bias)
+    assert np.array_equal(cb, c0 + F.bf16_to_f64(bias)[None, :])
+
+
+def test_accept_rule_bf16_and_f32():
+    c_ref = np.array([1.0 + 2.0 ** -10, 3.0, -7.25])
+    s = np.array([2.0 ** -4, 1.0, 0.0])          # bound 2^-16, 2^-12, 0
+    lo, hi = G.accept_bounds(c_ref, s, "bf16")
+    exact = F.f64_to_bf16_rne(c_ref)
+    assert np.all(G.accept(exact, c_ref, s, "bf16"))
+    ulp = np.ldexp(1.0, np.frexp(np.abs(exact))[1] - 8)
+    assert not np.any(G.accept(hi + ulp, c_ref, s, "bf16"))
+    assert not np.any(G.accept(lo - ulp, c_ref, s, "bf16"))
+    assert np.all(G.accept(c_ref + G.TOL * s, c_ref, s, "f32"))
+    assert not np.any(G.accept(c_ref + G.TOL * s + 1e-9, c_ref, s, "f32"))
+
+
+def test_sampled_entries_equal_full_gemm():
+    a_bits = W.np_activation((9, 200), seed=51)
+    b_bits = W.np_normal((7, 200), seed=52, std=0.02)
+    bias = W.np_normal((7,), seed=53, std=0.01)
+    for fmt in Q.FORMATS:
+        qa, qb = Q.quantize(a_bits, fmt), Q.quantize(b_bits, fmt)
+        c, s = G.gemm_ref(qa, qb, bias)
+        rows, cols = np.array([0, 8, 3]), np.array([6, 0, 2])
+        ce, se = G.gemm_ref_entries(qa, qb, rows, cols, bias)
+        assert np.allclose(ce, c[rows, cols], rtol=1e-15, atol=0)
+        assert np.allclose(se, s[rows, cols], rtol=1e-15, atol=0)
+
+
+def test_quantization_error_is_format_ordered():
+    """Plausibility, not a pin: relative L2 error of the quantized GEMM against
+    the unquantized one grows MXFP8 < NVFP4 < MXFP4, the order the README's
+    section 5.4 reports (about 0.03 / 0.11 / 0.19 on its own activations)."""
+    a_bits = W.np_activation((64, 1024), seed=61)
+    b_bits = W.np_normal((96, 1024), seed=62, std=0.02)
+    exact = F.bf16_to_f64(a_bits) @ F.bf16_to_f64(b_bits).T
+    err = {}
+    for fmt in Q.FORMATS:
+        c, _ = G.gemm_ref(Q.quantize(a_bits, fmt), Q.quantize(b_bits, fmt))
+        err[fmt] = np.linalg.norm(c - exact) / np.linalg.norm(exact)
+    assert 0.005 < err["mxfp8"] < err["nvfp4"] < err["mxfp4"] < 0.5, err
