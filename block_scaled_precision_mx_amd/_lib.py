@@ -1,0 +1,40 @@
+"""ctypes loader for libmx.so: argument types only, no logic."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmx.so")
+
+# every symbol include/mx.h declares, with (restype, argtypes)
+_c = ctypes
+SIGNATURES = {
+    "mx_version": (_c.c_int, []),
+    "mx_k_pad": (_c.c_int64, [_c.c_int64]),
+    "mx_codes_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
+    "mx_scales_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
+    "mx_quantize": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
+                               _c.c_int, _c.c_int, _c.c_void_p]),
+    "mx_gemm": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
+                           _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p]),
+    "mx_last_error": (_c.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: the HIP library must be built first "
+                "(python -m block_scaled_precision_mx_amd.build)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib

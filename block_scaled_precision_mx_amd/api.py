@@ -1,0 +1,95 @@
+"""Python binding of libmx with the C ABI's names (marshalling only).
+
+Tensors are PyTorch device tensors; every step of quantization and GEMM
+runs in the HIP library. Calls are enqueued on the current torch stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from ._lib import lib
+
+FMT = {"mxfp8": 1, "mxfp4": 2, "nvfp4": 3}
+AXIS = {"row": 0, "col": 1}
+OUT = {"bf16": 0, "f32": 1}
+STATUS = {0: "MX_OK", 1: "MX_ERR_INVALID_ARG", 2: "MX_ERR_UNSUPPORTED", 3: "MX_ERR_ALIGNMENT", 4: "MX_ERR_HIP"}
+
+
+class MxError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MxError(status, lib().mx_last_error().decode())
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+@dataclass
+class Quantized:
+    """Codes and scales of one operand: `rows` stored rows of `length` elements."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    fmt: str
+    rows: int
+    length: int
+
+
+def k_pad(length: int) -> int:
+    return lib().mx_k_pad(length)
+
+
+def codes_bytes(rows: int, cols: int, fmt: str, axis: str = "row") -> int:
+    return lib().mx_codes_bytes(rows, cols, FMT[fmt], AXIS[axis])
+
+
+def scales_bytes(rows: int, cols: int, fmt: str, axis: str = "row") -> int:
+    return lib().mx_scales_bytes(rows, cols, FMT[fmt], AXIS[axis])
+
+
+def mx_quantize(x: torch.Tensor, fmt: str, axis: str = "row", codes: torch.Tensor | None = None,
+                scales: torch.Tensor | None = None, stream=None) -> Quantized:
+    """Quantize a 2-D bf16 device tensor (unit column stride) along `axis`."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D bfloat16 device tensor")
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit stride along its last dimension")
+    rows, cols = x.shape
+    nc, ns = codes_bytes(rows, cols, fmt, axis), scales_bytes(rows, cols, fmt, axis)
+    if codes is None:
+        codes = torch.empty(nc, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(ns, dtype=torch.uint8, device=x.device)
+    if codes.numel() < nc or scales.numel() < ns:
+        raise ValueError("codes / scales buffers are too small")
+    _check(lib().mx_quantize(x.data_ptr(), rows, cols, x.stride(0), codes.data_ptr(), scales.data_ptr(),
+                             FMT[fmt], AXIS[axis], _stream(stream)))
+    stored_rows, length = (rows, cols) if axis == "row" else (cols, rows)
+    return Quantized(codes, scales, fmt, stored_rows, length)
+
+
+def mx_gemm(a: Quantized, b: Quantized, bias: torch.Tensor | None = None, out_dtype: str = "bf16",
+            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """C[M, N] = A * B^T (+ bias) from two operands quantized in one format."""
+    if a.fmt != b.fmt or a.length != b.length:
+        raise ValueError("operands must share format and K")
+    M, N, K = a.rows, b.rows, a.length
+    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=a.codes.device)
+    if out.dtype != dt or out.numel() < M * N or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of M*N elements of the output dtype")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bf16 tensor of N elements")
+    _check(lib().mx_gemm(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
+                         out.data_ptr(), M, N, K, FMT[a.fmt], None if bias is None else bias.data_ptr(),
+                         OUT[out_dtype], _stream(stream)))
+    return out

@@ -1,0 +1,124 @@
+// C ABI of libmx: argument validation on the host, then dispatch to the
+// launch wrappers. Every check happens before the first launch, so a call
+// that returns an argument error has not touched any output.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/mx.h"
+#include "mx_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mx_status fail(mx_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mx_status fail(mx_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bool valid_fmt(int f) { return f == MX_FMT_MXFP8 || f == MX_FMT_MXFP4 || f == MX_FMT_NVFP4; }
+bool valid_axis(int a) { return a == MX_AXIS_ROW || a == MX_AXIS_COL; }
+int64_t k_pad(int64_t len) { return (len + 127) / 128 * 128; }
+int64_t code_row_bytes(int64_t kpad, int fmt) { return fmt == MX_FMT_MXFP8 ? kpad : kpad / 2; }
+int block_elems(int fmt) { return fmt == MX_FMT_NVFP4 ? 16 : 32; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Buffer offsets inside the kernels are 32-bit.
+constexpr int64_t kMaxBytes = (int64_t)1 << 31;
+
+int64_t scales_total(int64_t R, int64_t kpad, int fmt) {
+  int64_t n = R * (kpad / block_elems(fmt));
+  if (fmt == MX_FMT_NVFP4) n = (n + 15) / 16 * 16 + 16;
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mx_version(void) { return 10000; }
+
+int64_t mx_k_pad(int64_t length) { return length < 1 ? 0 : k_pad(length); }
+
+size_t mx_codes_bytes(int64_t rows, int64_t cols, mx_fmt fmt, mx_axis axis) {
+  if (rows < 1 || cols < 1 || !valid_fmt(fmt) || !valid_axis(axis)) return 0;
+  const int64_t R = axis == MX_AXIS_ROW ? rows : cols, L = axis == MX_AXIS_ROW ? cols : rows;
+  return (size_t)(R * code_row_bytes(k_pad(L), fmt));
+}
+
+size_t mx_scales_bytes(int64_t rows, int64_t cols, mx_fmt fmt, mx_axis axis) {
+  if (rows < 1 || cols < 1 || !valid_fmt(fmt) || !valid_axis(axis)) return 0;
+  const int64_t R = axis == MX_AXIS_ROW ? rows : cols, L = axis == MX_AXIS_ROW ? cols : rows;
+  return (size_t)scales_total(R, k_pad(L), fmt);
+}
+
+mx_status mx_quantize(const void* src, int64_t rows, int64_t cols, int64_t ld, void* codes, void* scales,
+                      mx_fmt fmt, mx_axis axis, void* hip_stream) {
+  if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown format %d", (int)fmt);
+  if (!valid_axis(axis)) return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown axis %d", (int)axis);
+  if (rows < 1 || cols < 1) return fail(MX_ERR_INVALID_ARG, "mx_quantize: empty tensor (%lld x %lld)", (long long)rows, (long long)cols);
+  if (ld < cols) return fail(MX_ERR_INVALID_ARG, "mx_quantize: ld %lld < cols %lld", (long long)ld, (long long)cols);
+  if (!src || !codes || !scales) return fail(MX_ERR_INVALID_ARG, "mx_quantize: null pointer");
+  if (!aligned(src, 2)) return fail(MX_ERR_ALIGNMENT, "mx_quantize: src must be 2-byte aligned");
+  if (!aligned(codes, 16) || !aligned(scales, 16))
+    return fail(MX_ERR_ALIGNMENT, "mx_quantize: codes and scales must be 16-byte aligned");
+  const int64_t R = axis == MX_AXIS_ROW ? rows : cols, L = axis == MX_AXIS_ROW ? cols : rows;
+  const int64_t kpad = k_pad(L);
+  if (R * code_row_bytes(kpad, fmt) >= kMaxBytes || scales_total(R, kpad, fmt) >= kMaxBytes)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: output larger than 2 GiB");
+  if (rows > ((int64_t)1 << 40) / ld) return fail(MX_ERR_UNSUPPORTED, "mx_quantize: input too large");
+  hipError_t e = mx::launch_quantize(static_cast<const uint16_t*>(src), rows, cols, ld, static_cast<uint8_t*>(codes),
+                                     static_cast<uint8_t*>(scales), (int)fmt, (int)axis,
+                                     static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(MX_ERR_HIP, "mx_quantize: launch failed: %s", hipGetErrorString(e));
+  return MX_OK;
+}
+
+mx_status mx_gemm(const void* A, const void* As, const void* B, const void* Bs, void* C, int64_t M, int64_t N,
+                  int64_t K, mx_fmt fmt, const void* bias, mx_dtype out_dtype, void* hip_stream) {
+  if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "mx_gemm: unknown format %d", (int)fmt);
+  if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32)
+    return fail(MX_ERR_INVALID_ARG, "mx_gemm: unknown output dtype %d", (int)out_dtype);
+  if (M < 1 || N < 1 || K < 1)
+    return fail(MX_ERR_INVALID_ARG, "mx_gemm: M, N, K must be >= 1 (got %lld, %lld, %lld)", (long long)M, (long long)N,
+                (long long)K);
+  if (!A || !As || !B || !Bs || !C) return fail(MX_ERR_INVALID_ARG, "mx_gemm: null pointer");
+  if (!aligned(A, 16) || !aligned(As, 16) || !aligned(B, 16) || !aligned(Bs, 16) || !aligned(C, 16))
+    return fail(MX_ERR_ALIGNMENT, "mx_gemm: A, As, B, Bs and C must be 16-byte aligned");
+  if (bias && !aligned(bias, 2)) return fail(MX_ERR_ALIGNMENT, "mx_gemm: bias must be 2-byte aligned");
+  const int64_t kpad = k_pad(K);
+  const int64_t rb = code_row_bytes(kpad, fmt);
+  if (M * rb >= kMaxBytes || N * rb >= kMaxBytes || scales_total(M, kpad, fmt) >= kMaxBytes ||
+      scales_total(N, kpad, fmt) >= kMaxBytes)
+    return fail(MX_ERR_UNSUPPORTED, "mx_gemm: operand larger than 2 GiB");
+  if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
+    return fail(MX_ERR_UNSUPPORTED, "mx_gemm: M and N must be below 2^31");
+  hipError_t e;
+  const int out_f32 = out_dtype == MX_OUT_F32;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (fmt == MX_FMT_NVFP4) {
+    e = mx::launch_gemm_nvfp4(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(As),
+                              static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(Bs), C, M, N, K,
+                              static_cast<const uint16_t*>(bias), out_f32, s);
+  } else {
+    e = mx::launch_gemm_mx(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(As),
+                           static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(Bs), C, M, N, K, (int)fmt,
+                           static_cast<const uint16_t*>(bias), out_f32, s);
+  }
+  if (e != hipSuccess) return fail(MX_ERR_HIP, "mx_gemm: launch failed: %s", hipGetErrorString(e));
+  return MX_OK;
+}
+
+const char* mx_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

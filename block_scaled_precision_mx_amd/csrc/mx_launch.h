@@ -1,0 +1,23 @@
+// Launch wrappers called by the C ABI layer (host code, no validation here).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
+                           uint8_t* scales, int fmt, int axis, hipStream_t stream);
+
+// MXFP8 / MXFP4: scaled-MFMA GEMM. C = A * B^T (+ bias), fp32 accumulate.
+hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs,
+                          void* C, int64_t M, int64_t N, int64_t K, int fmt, const uint16_t* bias,
+                          int out_f32, hipStream_t stream);
+
+// NVFP4: E2M1 x E4M3 operands dequantized exactly to fp16 on the way into
+// LDS, fp16 MFMA with fp32 accumulate, s_tA * s_tB applied in the epilogue.
+hipError_t launch_gemm_nvfp4(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs,
+                             void* C, int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
+                             hipStream_t stream);
+
+}  // namespace mx

@@ -1,0 +1,118 @@
+/*
+ * mx.h -- C ABI of libmx, block-scaled quantize-then-GEMM for MI355X (gfx950).
+ *
+ * What the library computes (lightly-train README "DINOv3 + EoMT on RTX 5090"):
+ *   - section 2, number formats table: MXFP8 = E4M3 elements with a UE8M0
+ *     (power-of-two) scale per 1x32 block; MXFP4 = E2M1 elements with a
+ *     UE8M0 scale per 1x32; NVFP4 = E2M1 elements with an E4M3 scale per
+ *     1x16 plus one fp32 scale for the whole tensor.
+ *   - section 4.3: the quantized GEMMs of a ViT block are qkv, proj, fc1 and
+ *     fc2, each C = A * W^T (+ bias).
+ *   - section 5.5: every low-precision GEMM is "TN" (both operands K-major);
+ *     the weight-gradient GEMM needs a copy of its operands quantized along
+ *     the token axis and stored transposed (MX_AXIS_COL below).
+ *
+ * Conventions the pages leave open, fixed by this library:
+ *   - MX shared exponent e = floor(log2(block amax)) - emax, emax = 8 (E4M3)
+ *     or 2 (E2M1), clamped to [-127, 127]; an all-zero block has e = -127.
+ *     Scale byte = e + 127. Elements are x * 2^-e rounded to nearest, ties
+ *     to even, saturating at +-448 (E4M3) / +-6 (E2M1).
+ *   - NVFP4 tensor scale s_t = fp32 round-to-nearest-even(tensor amax / 2688),
+ *     2688 = 448 * 6; block byte = E4M3 RNE(block amax / (6 s_t)) of the exact
+ *     quotient; element = E2M1 RNE(x / (dec(byte) * s_t)) of the exact
+ *     quotient. If that scale is zero, the block's codes are signed zeros.
+ *   - The sign bit of a code is the sign bit of its input (-0.0 -> 0x80 / 0x8).
+ *   - Inputs must be finite; NaN / Inf inputs are outside the contract.
+ *
+ * Storage (all row-major, no swizzle):
+ *   Quantizing X [rows, cols] (bf16, leading dimension ld >= cols elements):
+ *     axis ROW: blocks run along cols.  L = cols, R = rows.
+ *     axis COL: blocks run along rows; the result is the ROW quantization of
+ *               X^T, i.e. stored as R = cols rows of L = rows elements.
+ *   K_pad = round_up(L, 128).
+ *   codes : R x K_pad bytes (MXFP8), R x K_pad/2 bytes (MXFP4, NVFP4; element
+ *           2i in the low nibble of byte i, 2i+1 in the high nibble).
+ *           Codes past L are 0.
+ *   scales: R x K_pad/bs bytes (bs = 32 for MX, 16 for NVFP4), scale bytes past
+ *           the last real block are 0. NVFP4 appends a 16-byte trailer at
+ *           byte offset round_up(R * K_pad/16, 16): {float s_t; float amax;
+ *           uint32 0; uint32 0}; bytes between the last scale and the
+ *           trailer are 0.
+ *   Use mx_codes_bytes / mx_scales_bytes for the sizes.
+ *
+ * GEMM: C[M, N] = A[M, K] * B[N, K]^T (+ bias[N]), A and B the outputs of
+ *   mx_quantize in the same format (A: M rows, B: N rows, both of length K).
+ *   fp32 accumulation; the bias (bf16) is added in fp32; NVFP4 multiplies by
+ *   s_tA * s_tB before the bias; the result is stored as bf16 (round to
+ *   nearest even) or fp32, row-major with leading dimension N.
+ *   Accuracy: |C - exact| <= 2^-12 * (sum_k |a_k b_k| + |bias|) before the
+ *   final bf16 rounding, "exact" being the sum of the dequantized values.
+ *
+ * Memory: every pointer is a device pointer owned by the caller; the library
+ *   never allocates, frees or synchronizes. Codes, scales and C must be
+ *   16-byte aligned; src and bias 2-byte aligned. Calls are asynchronous on
+ *   the given HIP stream (NULL = the default stream) and are reentrant; two
+ *   calls writing the same buffers must be ordered by the caller.
+ *
+ * Errors: invalid arguments are detected on the host before any launch and
+ *   leave every output untouched (MX_ERR_INVALID_ARG, MX_ERR_ALIGNMENT,
+ *   MX_ERR_UNSUPPORTED). A failed launch returns MX_ERR_HIP. The message of
+ *   the last non-OK status of the calling thread is in mx_last_error().
+ */
+#ifndef MX_H_
+#define MX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MX_FMT_MXFP8 = 1, MX_FMT_MXFP4 = 2, MX_FMT_NVFP4 = 3 } mx_fmt;
+typedef enum { MX_AXIS_ROW = 0, MX_AXIS_COL = 1 } mx_axis;
+typedef enum { MX_OUT_BF16 = 0, MX_OUT_F32 = 1 } mx_dtype;
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_INVALID_ARG = 1,
+  MX_ERR_UNSUPPORTED = 2,
+  MX_ERR_ALIGNMENT = 3,
+  MX_ERR_HIP = 4
+} mx_status;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mx_version(void);
+
+/* K_pad = round_up(length, 128): the stored length of a quantized row. */
+int64_t mx_k_pad(int64_t length);
+
+/* Bytes of the codes / scales buffers for X [rows, cols] quantized along
+ * axis in fmt. 0 if an argument is invalid (rows or cols < 1, unknown enum). */
+size_t mx_codes_bytes(int64_t rows, int64_t cols, mx_fmt fmt, mx_axis axis);
+size_t mx_scales_bytes(int64_t rows, int64_t cols, mx_fmt fmt, mx_axis axis);
+
+/* Quantize X [rows, cols] (bf16, row-major, leading dimension ld elements)
+ * along axis into codes / scales (layouts above). README section 2 (formats)
+ * and section 5.5 (the transposed, token-axis copy for weight gradients).
+ * NVFP4 first reduces the tensor amax (stored in the scales trailer), then
+ * quantizes; the whole call is stream-ordered. */
+mx_status mx_quantize(const void* src, int64_t rows, int64_t cols, int64_t ld,
+                      void* codes, void* scales, mx_fmt fmt, mx_axis axis,
+                      void* hip_stream);
+
+/* C = A * B^T (+ bias) from quantized operands (README section 4.3 GEMMs,
+ * section 5.5 TN layout). A / As: codes and scales of an M-row operand,
+ * B / Bs: of an N-row operand, both of logical length K. bias: bf16[N] or
+ * NULL. out_dtype selects bf16 or fp32 C. */
+mx_status mx_gemm(const void* A, const void* As, const void* B, const void* Bs,
+                  void* C, int64_t M, int64_t N, int64_t K, mx_fmt fmt,
+                  const void* bias, mx_dtype out_dtype, void* hip_stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* mx_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX_H_ */

@@ -1,0 +1,102 @@
+"""Host-side checks of the C ABI (no GPU compute): the library loads, exports
+every function include/mx.h declares, reports the buffer sizes the oracle's
+layout implies, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_precision_mx_amd import _lib
+from oracle import quantize as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mx.h")
+FMTS = {"mxfp8": 1, "mxfp4": 2, "nvfp4": 3}
+AXES = {"row": 0, "col": 1}
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = header_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_version_and_kpad(L):
+    assert L.mx_version() >= 10000
+    assert [L.mx_k_pad(n) for n in (1, 127, 128, 129, 11235)] == [128, 128, 128, 256, 11264]
+    assert L.mx_k_pad(0) == 0
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (3, 70), (256, 768), (11235, 1024), (4096, 11235)])
+def test_sizes_match_oracle_layout(L, shape):
+    for fmt, f in FMTS.items():
+        for axis, a in AXES.items():
+            assert L.mx_codes_bytes(*shape, f, a) == Q.codes_bytes(*shape, fmt, axis)
+            assert L.mx_scales_bytes(*shape, f, a) == Q.scales_bytes(*shape, fmt, axis)
+
+
+def test_size_queries_reject_bad_args(L):
+    assert L.mx_codes_bytes(0, 5, 1, 0) == 0
+    assert L.mx_codes_bytes(5, 5, 9, 0) == 0
+    assert L.mx_scales_bytes(5, 5, 1, 7) == 0
+
+
+ALIGNED = 1 << 20      # fake, never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, 7, 0), 1, "unknown format"),
+    ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, 1, 3), 1, "unknown axis"),
+    ((ALIGNED, 0, 4, 4, ALIGNED, ALIGNED, 1, 0), 1, "empty"),
+    ((ALIGNED, 4, 8, 4, ALIGNED, ALIGNED, 1, 0), 1, "ld"),
+    ((None, 4, 4, 4, ALIGNED, ALIGNED, 1, 0), 1, "null"),
+    ((ALIGNED + 1, 4, 4, 4, ALIGNED, ALIGNED, 1, 0), 3, "2-byte"),
+    ((ALIGNED, 4, 4, 4, ALIGNED + 8, ALIGNED, 1, 0), 3, "16-byte"),
+    ((ALIGNED, 1 << 20, 1 << 12, 1 << 12, ALIGNED, ALIGNED, 1, 0), 2, "2 GiB"),
+])
+def test_quantize_validation(L, args, status, msg):
+    assert L.mx_quantize(*args, None) == status
+    assert msg in L.mx_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((ALIGNED,) * 5 + (4, 4, 32, 9, None, 0), 1, "unknown format"),
+    ((ALIGNED,) * 5 + (4, 4, 32, 1, None, 5), 1, "output dtype"),
+    ((ALIGNED,) * 5 + (0, 4, 32, 1, None, 0), 1, ">= 1"),
+    ((ALIGNED,) * 5 + (4, 4, 0, 1, None, 0), 1, ">= 1"),
+    ((ALIGNED, None, ALIGNED, ALIGNED, ALIGNED, 4, 4, 32, 1, None, 0), 1, "null"),
+    ((ALIGNED, ALIGNED, ALIGNED + 4, ALIGNED, ALIGNED, 4, 4, 32, 1, None, 0), 3, "16-byte"),
+    ((ALIGNED,) * 5 + (4, 4, 32, 1, ALIGNED + 1, 0), 3, "bias"),
+    ((ALIGNED,) * 5 + (1 << 22, 4, 1024, 1, None, 0), 2, "2 GiB"),
+])
+def test_gemm_validation(L, args, status, msg):
+    assert L.mx_gemm(*args, None) == status
+    assert msg in L.mx_last_error().decode()
+
+
+def test_last_error_is_per_thread(L):
+    import threading
+    L.mx_quantize(None, 4, 4, 4, ALIGNED, ALIGNED, 1, 0, None)
+    seen = {}
+
+    def other():
+        L.mx_gemm(*((ALIGNED,) * 5 + (4, 4, 32, 9, None, 0)), None)
+        seen["msg"] = L.mx_last_error().decode()
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert "unknown format" in seen["msg"]
+    assert "null" in L.mx_last_error().decode()

@@ -1,0 +1,132 @@
+"""GPU parity of mx_quantize: codes and scale bytes (with the NVFP4 trailer)
+must equal the oracle's byte for byte, for every format and axis, on seeded
+inputs that span several tiles, ragged tails, zero blocks, subnormals,
+negative zeros, near-maximum values, the transpose identity and the full
+ViT sizes of the workloads."""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_precision_mx_amd import api
+from block_scaled_precision_mx_amd import workloads as W
+from oracle import quantize as Q
+from gpu_util import bytes_of, log, to_device_bf16
+
+pytestmark = pytest.mark.gpu
+FMTS = ["mxfp8", "mxfp4", "nvfp4"]
+
+
+def special(rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)) * 10.0 ** rng.integers(-3, 3, (rows, 1))
+    x[rng.random((rows, cols)) < 0.01] *= 50
+    x[0, : min(cols, 64)] = 0.0
+    if cols > 40:
+        x[0, 40] = -0.0
+    if rows > 2:
+        x[1, :] *= 2.0 ** -128
+        x[2, min(5, cols - 1)] = 3.0e38
+    if rows > 5:
+        x[5, :] = 0.0
+    return W.to_bf16_bits(x)
+
+
+def compare(bits, fmt, axis, src=None):
+    rows, cols = bits.shape
+    log(f"quantize fmt={fmt} axis={axis} shape={rows}x{cols}")
+    x = to_device_bf16(bits) if src is None else src
+    q = api.mx_quantize(x, fmt, axis)
+    ref = Q.quantize(bits, fmt, axis)
+    got_codes = bytes_of(q.codes).reshape(ref.rows, -1)
+    got_scales = bytes_of(q.scales)
+    exp_codes = ref.packed_codes()
+    exp_scales = ref.scale_buffer()
+    bad = np.argwhere(got_codes != exp_codes)
+    assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[:5].tolist()}"
+    assert np.array_equal(got_scales, exp_scales), np.argwhere(got_scales != exp_scales)[:10].tolist()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("shape", [(1, 1), (3, 32), (37, 300), (130, 99), (256, 768), (300, 1030)])
+def test_quantize_random(fmt, axis, shape):
+    compare(W.np_activation(shape, seed=hash(shape) % 1000), fmt, axis)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("shape", [(7, 64), (129, 257), (64, 11235)])
+def test_quantize_special_values(fmt, axis, shape):
+    compare(special(*shape, seed=sum(shape)), fmt, axis)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_gelu_and_grads(fmt):
+    compare(W.np_gelu_activation((200, 512), seed=3), fmt, "row")
+    compare(W.np_normal((300, 256), seed=4, std=1e-3), fmt, "col")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_all_zero(fmt):
+    bits = np.zeros((5, 96), dtype=np.uint16)
+    bits[2, 7] = 0x8000
+    compare(bits, fmt, "row")
+    compare(bits, fmt, "col")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_strided_source(fmt):
+    """A row-major view with ld > cols quantizes like its contiguous copy."""
+    base = W.np_activation((64, 320), seed=8)
+    x = to_device_bf16(base)[:, 16:16 + 256]
+    assert x.stride(0) == 320
+    bits = np.ascontiguousarray(base[:, 16:16 + 256])
+    compare(bits, fmt, "row", src=x)
+    compare(bits, fmt, "col", src=x)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_exact_nvfp4_ties(fmt):
+    """Elements on E2M1 midpoints of a block with scale 1.5 and s_t = 1."""
+    row = [2688.0] + [0.0] * 15 + [9.0] + [m * 1.5 for m in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)] + [0.0] * 8
+    bits = W.to_bf16_bits(np.array([row] * 4))
+    bits[1, 17:24] += 1
+    bits[2, 17:24] -= 1
+    compare(bits, fmt, "row")
+    compare(bits, fmt, "col")
+
+
+def test_transpose_identity_gpu():
+    """COL quantization of X equals ROW quantization of X^T, on the GPU alone."""
+    bits = W.np_activation((333, 200), seed=21)
+    x = to_device_bf16(bits)
+    xt = x.t().contiguous()
+    for fmt in FMTS:
+        log(f"transpose identity {fmt}")
+        a = api.mx_quantize(x, fmt, "col")
+        b = api.mx_quantize(xt, fmt, "row")
+        assert np.array_equal(bytes_of(a.codes), bytes_of(b.codes))
+        assert np.array_equal(bytes_of(a.scales), bytes_of(b.scales))
+
+
+@pytest.mark.parametrize("fmt,axis,shape,kind", [
+    ("mxfp8", "row", (11235, 1024), "act"),      # ViT-L activations
+    ("mxfp8", "row", (11235, 4096), "gelu"),     # ViT-L fc2 input
+    ("mxfp4", "row", (11235, 4096), "gelu"),
+    ("nvfp4", "row", (11235, 4096), "gelu"),     # H, fprop of fc2
+    ("nvfp4", "col", (11235, 4096), "gelu"),     # H^T, wgrad of fc2
+    ("nvfp4", "col", (11235, 1024), "grad"),     # dY2^T
+    ("nvfp4", "col", (4096, 1024), "weight"),    # W1^T, dgrad of fc1
+    ("mxfp8", "row", (3072, 1024), "weight"),
+])
+def test_quantize_full_size(fmt, axis, shape, kind):
+    seed = W.seed(9, 0, hash((fmt, axis, shape)) % 97)
+    if kind == "act":
+        bits = W.np_activation(shape, seed)
+    elif kind == "gelu":
+        bits = W.np_gelu_activation(shape, seed)
+    elif kind == "grad":
+        bits = W.np_normal(shape, seed, W.GRAD_STD)
+    else:
+        bits = W.np_normal(shape, seed, W.W_STD)
+    compare(bits, fmt, axis)
