@@ -1,0 +1,313 @@
+"""Throughput of the block-scaled quantize-then-GEMM hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: for every ViT block
+and every linear layer (qkv, proj, fc1, fc2) quantize the activation and the
+weight row-wise (mx_quantize) and run the block-scaled GEMM with its bias
+epilogue (mx_gemm). For the NVFP4 training workload a step is the fc1/fc2
+pair's fprop, dgrad and wgrad GEMMs with every operand quantized along its
+own K axis (row and transposed copies, tensor amax included).
+
+Inputs are seeded synthetic bf16 tensors (the value recipe of
+block_scaled_precision_mx_amd.workloads) generated on the device before the
+timed region; every block has its own tensors so repeated launches cannot be
+served from the 256 MB Infinity Cache. The JSON line reports whole-step
+throughput in GEMM TFLOP/s (the GEMM flops of the step over the step time,
+quantization included), the dominant GEMM kernel against the MFMA roofline
+(per-launch HIP events on the stream the kernels run on), the quantizer's
+algorithmic bandwidth, and the CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 10100.0, "fp16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+# algorithmic bytes per quantized element: 2 read + codes + scales written
+QUANT_BYTES = {"mxfp8": 2 + 1 + 1 / 32, "mxfp4": 2 + 0.5 + 1 / 32, "nvfp4": 2 + 0.5 + 1 / 16}
+NVFP4_AMAX_BYTES = 2.0
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="vitl16_mxfp8_fwd_stack",
+                   choices=["vitl16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack", "vitb16_mxfp8_fwd_stack",
+                            "vitl16_nvfp4_fc1fc2_train", "single_mxfp8_256x768x768"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ workloads
+
+class Op:
+    """One launch of the path: a quantization or a GEMM."""
+
+    def __init__(self, kind, fn, flops=0.0, nbytes=0.0, label=""):
+        self.kind, self.fn, self.flops, self.nbytes, self.label = kind, fn, flops, nbytes, label
+
+
+def build_stack(stack, dev):
+    import torch
+    from block_scaled_precision_mx_amd import api
+    from block_scaled_precision_mx_amd import workloads as W
+
+    ops = []
+    fmt = stack.fmt
+    for blk in range(stack.blocks):
+        for lin in stack.linears:
+            a = W.torch_activation((stack.m, lin.k), W.seed(stack.wid, blk, lin.a_id), dev, gelu=lin.a_kind == "gelu")
+            w = W.torch_normal((lin.n, lin.k), W.seed(stack.wid, blk, lin.w_id), W.W_STD, dev)
+            bias = W.torch_normal((lin.n,), W.seed(stack.wid, blk, lin.bias_id), W.BIAS_STD, dev)
+            qa = api.Quantized(torch.empty(api.codes_bytes(stack.m, lin.k, fmt), dtype=torch.uint8, device=dev),
+                               torch.empty(api.scales_bytes(stack.m, lin.k, fmt), dtype=torch.uint8, device=dev),
+                               fmt, stack.m, lin.k)
+            qw = api.Quantized(torch.empty(api.codes_bytes(lin.n, lin.k, fmt), dtype=torch.uint8, device=dev),
+                               torch.empty(api.scales_bytes(lin.n, lin.k, fmt), dtype=torch.uint8, device=dev),
+                               fmt, lin.n, lin.k)
+            out = torch.empty((stack.m, lin.n), dtype=torch.bfloat16, device=dev)
+            qb = QUANT_BYTES[fmt]
+            ops.append(Op("quant", lambda a=a, qa=qa: api.mx_quantize(a, fmt, "row", qa.codes, qa.scales),
+                          nbytes=qb * a.numel(), label=f"quant_{lin.name}_act"))
+            ops.append(Op("quant", lambda w=w, qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales),
+                          nbytes=qb * w.numel(), label=f"quant_{lin.name}_w"))
+            ops.append(Op("gemm", lambda qa=qa, qw=qw, bias=bias, out=out: api.mx_gemm(qa, qw, bias, "bf16", out),
+                          flops=2.0 * stack.m * lin.n * lin.k, label=f"gemm_{lin.name}"))
+    return ops
+
+
+def build_train(tp, dev):
+    import torch
+    from block_scaled_precision_mx_amd import api
+    from block_scaled_precision_mx_amd import workloads as W
+
+    fmt = "nvfp4"
+    S = lambda tid: W.seed(tp.wid, 0, tid)   # noqa: E731
+    X = W.torch_activation((tp.m, tp.hidden), S(tp.X), dev)
+    H = W.torch_activation((tp.m, tp.mlp), S(tp.H), dev, gelu=True)
+    dY1 = W.torch_normal((tp.m, tp.mlp), S(tp.DY1), W.GRAD_STD, dev)
+    dY2 = W.torch_normal((tp.m, tp.hidden), S(tp.DY2), W.GRAD_STD, dev)
+    W1 = W.torch_normal((tp.mlp, tp.hidden), S(tp.W1), W.W_STD, dev)
+    W2 = W.torch_normal((tp.hidden, tp.mlp), S(tp.W2), W.W_STD, dev)
+    b1 = W.torch_normal((tp.mlp,), S(tp.B1), W.BIAS_STD, dev)
+    b2 = W.torch_normal((tp.hidden,), S(tp.B2), W.BIAS_STD, dev)
+    ops = []
+    q = {}
+
+    def quant(name, t, axis):
+        r, c = t.shape
+        buf = api.Quantized(torch.empty(api.codes_bytes(r, c, fmt, axis), dtype=torch.uint8, device=dev),
+                            torch.empty(api.scales_bytes(r, c, fmt, axis), dtype=torch.uint8, device=dev),
+                            fmt, r if axis == "row" else c, c if axis == "row" else r)
+        q[name] = buf
+        ops.append(Op("quant", lambda: api.mx_quantize(t, fmt, axis, buf.codes, buf.scales),
+                      nbytes=(QUANT_BYTES[fmt] + NVFP4_AMAX_BYTES) * t.numel(), label=f"quant_{name}"))
+
+    def gemm(name, a, b, bias, m, n, k):
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ops.append(Op("gemm", lambda: api.mx_gemm(q[a], q[b], bias, "bf16", out), flops=2.0 * m * n * k,
+                      label=f"gemm_{name}"))
+
+    # fc1: fprop X W1^T, dgrad dY1 W1, wgrad dY1^T X
+    quant("X_row", X, "row"); quant("W1_row", W1, "row")
+    gemm("fc1_fprop", "X_row", "W1_row", b1, tp.m, tp.mlp, tp.hidden)
+    quant("dY1_row", dY1, "row"); quant("W1_col", W1, "col")
+    gemm("fc1_dgrad", "dY1_row", "W1_col", None, tp.m, tp.hidden, tp.mlp)
+    quant("dY1_col", dY1, "col"); quant("X_col", X, "col")
+    gemm("fc1_wgrad", "dY1_col", "X_col", None, tp.mlp, tp.hidden, tp.m)
+    # fc2: fprop H W2^T, dgrad dY2 W2, wgrad dY2^T H
+    quant("H_row", H, "row"); quant("W2_row", W2, "row")
+    gemm("fc2_fprop", "H_row", "W2_row", b2, tp.m, tp.hidden, tp.mlp)
+    quant("dY2_row", dY2, "row"); quant("W2_col", W2, "col")
+    gemm("fc2_dgrad", "dY2_row", "W2_col", None, tp.m, tp.mlp, tp.hidden)
+    quant("dY2_col", dY2, "col"); quant("H_col", H, "col")
+    gemm("fc2_wgrad", "dY2_col", "H_col", None, tp.hidden, tp.mlp, tp.m)
+    return ops
+
+
+# ------------------------------------------------------------------ CPU oracle
+
+def cpu_baseline(workload_name, fmt):
+    """The oracle as it stands on a bounded sample of the same workload:
+    the four linears of one block with 1024 of the M token rows (ViT-L
+    shapes) or the fc1 fprop with 1024 rows (training pair); returns GEMM
+    TFLOP/s of quantize + dequantize + float64 GEMM."""
+    import numpy as np
+    from block_scaled_precision_mx_amd import workloads as W
+    from oracle import gemm as G
+    from oracle import quantize as Q
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rows = 1024
+    if workload_name.startswith("vitl16_nvfp4"):
+        shapes = [("fc1_fprop", W.TRAIN_PAIR.mlp, W.TRAIN_PAIR.hidden, "act")]
+        wid = W.TRAIN_PAIR.wid
+    else:
+        stack = W.STACKS[workload_name]
+        shapes = [(l.name, l.n, l.k, l.a_kind) for l in stack.linears]
+        wid = stack.wid
+    gen = []
+    for i, (name, n, k, kind) in enumerate(shapes):
+        a = (W.np_gelu_activation if kind == "gelu" else W.np_activation)((rows, k), W.seed(wid, 0, 3 * i))
+        w = W.np_normal((n, k), W.seed(wid, 0, 3 * i + 1), W.W_STD)
+        b = W.np_normal((n,), W.seed(wid, 0, 3 * i + 2), W.BIAS_STD)
+        gen.append((a, w, b, n, k))
+    t0 = time.perf_counter()
+    flops = 0.0
+    for a, w, b, n, k in gen:
+        qa, qw = Q.quantize(a, fmt), Q.quantize(w, fmt)
+        G.gemm_ref(qa, qw, b)
+        flops += 2.0 * rows * n * k
+    dt = time.perf_counter() - t0
+    sample = f"{len(gen)} GEMM(s) of one block, {rows} token rows each: " + ", ".join(
+        f"{rows}x{n}x{k}" for _, _, _, n, k in gen)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the block-scaled path here runs on a single MI355X; "
+              "multi-GPU runs are not part of this build (see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from block_scaled_precision_mx_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.workload == "vitl16_nvfp4_fc1fc2_train":
+        wl = W.TRAIN_PAIR
+        fmt = "nvfp4"
+        ops = build_train(wl, dev)
+        gemm_peak_key = "fp16"
+        config = {"workload": wl.name, "M": wl.m, "hidden": wl.hidden, "mlp": wl.mlp, "tokens_per_image": W.TOKENS,
+                  "batch": wl.m // W.TOKENS, "format": "nvfp4", "gemms": "fc1/fc2 fprop+dgrad+wgrad",
+                  "quantizations": 12}
+    else:
+        wl = W.STACKS[args.workload]
+        fmt = wl.fmt
+        ops = build_stack(wl, dev)
+        gemm_peak_key = fmt
+        config = {"workload": wl.name, "M": wl.m, "hidden": wl.hidden, "mlp": wl.mlp, "blocks": wl.blocks,
+                  "tokens_per_image": W.TOKENS, "batch": wl.m // W.TOKENS, "format": fmt,
+                  "gemms_per_block": [f"{l.name} {l.n}x{l.k}" for l in wl.linears]}
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for op in ops:
+            op.fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events on the stream the kernels run on
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    # per-launch durations, same stream, same launches: one event pair per op
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+    per_op = [0.0] * len(ops)
+    for _ in range(args.steps):
+        for i, op in enumerate(ops):
+            ev[i][0].record(stream)
+            op.fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        for i in range(len(ops)):
+            per_op[i] += ev[i][0].elapsed_time(ev[i][1])
+    per_op = [t / args.steps for t in per_op]
+
+    gemm_flops = sum(op.flops for op in ops)
+    gemm_ms = sum(t for op, t in zip(ops, per_op) if op.kind == "gemm")
+    quant_bytes = sum(op.nbytes for op in ops if op.kind == "quant")
+    quant_ms = sum(t for op, t in zip(ops, per_op) if op.kind == "quant")
+    by_label = {}
+    for op, t in zip(ops, per_op):
+        d = by_label.setdefault(op.label, {"ms": 0.0, "n": 0, "flops": 0.0, "bytes": 0.0})
+        d["ms"] += t
+        d["n"] += 1
+        d["flops"] += op.flops
+        d["bytes"] += op.nbytes
+    breakdown = {}
+    for lab, d in by_label.items():
+        e = {"us_per_launch": round(1e3 * d["ms"] / d["n"], 2)}
+        if d["flops"]:
+            e["tflops"] = round(d["flops"] / (d["ms"] * 1e-3) / 1e12, 1)
+        if d["bytes"]:
+            e["gbps"] = round(d["bytes"] / (d["ms"] * 1e-3) / 1e9, 1)
+        breakdown[lab] = e
+
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[gemm_peak_key]
+    n_gemm = sum(1 for op in ops if op.kind == "gemm")
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+    result = {
+        "metric": "block-scaled GEMM TFLOP/s of the whole quantize-then-GEMM step on ViT-L shapes",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3" if fmt == "mxfp8" else ("fp4-e2m1+fp16-mfma" if fmt == "nvfp4" else "fp4-e2m1"),
+        "data": "synthetic (seeded, device-generated bf16; no dataset or weights)",
+        "config": config,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_mx_kernel" if fmt != "nvfp4" else "gemm_nv_kernel",
+            "achieved": round(achieved, 1),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "launches_per_step": n_gemm,
+            "avg_launch_us": round(1e3 * gemm_ms / n_gemm, 2),
+            "flops_per_launch_avg": gemm_flops / n_gemm,
+        },
+        "gemm_only_tflops": round(achieved, 1),
+        "quant": {"gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1), "peak_gbps": PEAK_HBM_GBS,
+                  "frac": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                  "ms_per_step": round(quant_ms, 4)},
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(config["workload"], fmt)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

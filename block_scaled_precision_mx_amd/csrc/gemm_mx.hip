@@ -6,55 +6,99 @@
 // / fc1 / fc2 are the quantized GEMMs, with their bias in the epilogue),
 // section 5.5 (TN: both operands K-major). The page's kernels target an
 // RTX 5090's block-scaled mma.sync; on gfx950 the same arithmetic is one
-// V_MFMA_SCALE_F32_16X16X128_F8F6F4 per 16 x 16 x 128 sub-tile, which takes
-// the E8M0 scale bytes of both operands directly, so no dequantization
-// happens outside the matrix core.
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 per 32 x 32 x 64 sub-tile, which takes the
+// E8M0 scale bytes of both operands directly, so no dequantization happens
+// outside the matrix core. (The 16x16x128 form runs FP4 at only the FP8 rate
+// on this chip; the 32x32x64 form runs FP4 at twice the FP8 rate.)
 //
-// Operand layout inside the instruction (measured on gfx950):
-//   FP8:  lane l holds row l%16; bytes 0-15 are K 16g..16g+15 and bytes
-//         16-31 are K 64+16g..64+16g+15, g = l/16; the scale of K-block kb
-//         of row r comes from lane r + 16 kb.
-//   FP4:  lane l holds row l%16, K 32g..32g+31 (low nibble first) in its
-//         first four registers; its scale is its own block g.
-//   Out:  lane l holds D[4g + v][l%16], v = 0..3.
-// The kernel feeds the B tile as the instruction's first operand, so each
-// lane ends up with 4 consecutive output columns of one output row (one
-// 8-byte bf16 store).
+// Operand layout inside the instruction (measured on gfx950), lane l,
+// r = l % 32, g = l / 32:
+//   FP8:  row r; bytes 0-15 are K 16g..16g+15, bytes 16-31 are K 32+16g..+15;
+//         the scale of K-block kb of row r comes from lane r + 32 kb.
+//   FP4:  row r, K 32g..32g+31 (low nibble first) in the first 4 registers;
+//         its scale is its own block g.
+//   Out:  register 4q + v holds D[8q + 4g + v][r].
+// The B tile is fed as the instruction's first operand, so each lane ends up
+// with runs of 4 consecutive output columns of one output row.
 //
-// Tiling: a workgroup computes a BM x BN tile; 128 K-elements per stage
-// (128 bytes of fp8 / 64 bytes of fp4 per row) are copied global -> LDS with
-// 16-byte loads, double-buffered, with an XOR swizzle of the 16-byte chunks
-// so that the 16 lanes reading one chunk column hit distinct banks. Scale
-// bytes go straight from global memory (L2) to registers, one dword per
-// lane per 16-row fragment per stage. Workgroups are renumbered so that each
-// XCD (own L2) gets a contiguous range of tiles, grouped 8 tile-rows deep.
+// Pipeline: a K-stage is 64 bytes of codes per row (64 fp8 / 128 fp4
+// elements) plus the aligned scale dword holding that stage's blocks (fp8:
+// the 4 blocks of stages 2j, 2j+1; fp4: the 4 blocks of the stage). NST
+// stages are in flight: each wave copies its share of a stage global -> LDS
+// with buffer_load ... lds (16 bytes of codes or one scale dword per lane,
+// rows past the tensor read as zero), waits with vmcnt for its own copies of
+// the stage about to be used, then a workgroup barrier makes every wave's
+// copies visible. The copies are issued from inline assembly so that the
+// compiler does not conservatively wait for all of them before each LDS
+// read; the kernel does its own counting. Code rows are XOR-swizzled in
+// 16-byte chunks so the 32 lanes reading one chunk column hit distinct
+// banks. Tiles are renumbered so each XCD (own L2) gets a contiguous range,
+// walked in groups of 8 tile-rows.
 #include "mx_device.h"
 #include "mx_launch.h"
 
 namespace mx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int SWZ_>
+template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NST_>
 struct MxCfg {
-  static constexpr int FMT = FMT_, BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-  static constexpr int SWZ = SWZ_;
-  static constexpr int KB = (FMT == FMT_MXFP8) ? 128 : 64;   // code bytes per row per stage
-  static constexpr int CHUNKS = KB / 16;
-  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int FMT = FMT_, BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NST = NST_;
+  static constexpr int NT = 64 * WAVES_M * WAVES_N, NW = NT / 64;
+  static constexpr int RB = 64;                               // code bytes per row per stage
+  static constexpr int KS = (FMT == FMT_MXFP8) ? 64 : 128;    // K elements per stage
+  static constexpr int SB = 4;                                // scale bytes per row in a stage slot
+                                                              // (fp8: blocks of 2 stages; fp4: of 1 stage)
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  static constexpr int FM = WM / 16, FN = WN / 16;
-  static constexpr int A_STAGE = BM * KB, B_STAGE = BN * KB;
-  static constexpr int A_LOADS = BM * CHUNKS / NT;
-  static constexpr int B_LOADS = BN * CHUNKS / NT;
-  static constexpr int MFMA_FMT = (FMT == FMT_MXFP8) ? 0 : 4;   // E4M3 / E2M1 selector
-  static_assert(A_LOADS * NT == BM * CHUNKS && B_LOADS * NT == BN * CHUNKS, "tile/threads mismatch");
-  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int CODE_BYTES = (BM + BN) * RB;            // per stage
+  static constexpr int SCALE_BYTES = (BM + BN) * SB;
+  static constexpr int STAGE = CODE_BYTES + SCALE_BYTES;
+  static constexpr int LDS = NST * STAGE;
+  static constexpr int CODE_DMA = CODE_BYTES / 1024 / NW;     // 1-KB copies per wave per stage
+  static constexpr int SCALE_DMA = (BM + BN) / 64 / NW;       // 64-row scale copies per wave per stage
+  static constexpr int OPS = CODE_DMA + SCALE_DMA;            // vector memory ops per wave per stage
+  static constexpr int MFMA_FMT = (FMT == FMT_MXFP8) ? 0 : 4;  // E4M3 / E2M1 operand selector
+  static_assert(CODE_DMA * 1024 * NW == CODE_BYTES, "code copies must split evenly over waves");
+  static_assert(SCALE_DMA * 64 * NW == BM + BN && SCALE_DMA >= 1, "scale copies must split evenly");
+  static_assert((BM * RB) % 1024 == 0 && BM % 64 == 0 && BN % 64 == 0, "tile");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-__device__ __forceinline__ int swz_chunk(int r, int c, int chunks, int shift) {
-  return c ^ ((r >> shift) & (chunks - 1));
+// Row r keeps 16-byte chunk c at position c ^ ((r >> 1) & 3).
+__device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 1) & 3); }
+
+__device__ __forceinline__ v4u buffer_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  v4u r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
+  r.w = 0x00020000u;   // raw buffer, 32-bit data format: out-of-range reads return 0
+  return r;
+}
+
+// One wave-wide copy global -> LDS: lane l's SIZE (16 or 4) bytes at `voff`
+// land at lds_addr + SIZE * l. M0 is saved and restored around the copy.
+template <int SIZE>
+__device__ __forceinline__ void dma(v4u rs, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  if (SIZE == 16)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
+}
+
+// Wait until at most N of this wave's vector memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
 // Tile coordinates of this workgroup: XCD-contiguous renumbering, then
@@ -75,54 +119,6 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_group / gm;
 }
 
-// Epilogue store of one fragment: 4 consecutive columns n..n+3 of row m.
-__device__ __forceinline__ void store4(void* C, int M, int N, int m, int n, v4f acc, float scale,
-                                      const uint16_t* bias, int out_f32) {
-  if (m >= M) return;
-  float v[4] = {acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale};
-  const bool full = ((N & 3) == 0) && (n + 3 < N);
-  if (bias) {
-    if (full && (reinterpret_cast<uintptr_t>(bias) & 7) == 0) {
-      uint2 b = *reinterpret_cast<const uint2*>(bias + n);
-      v[0] += bf16_to_f32(b.x & 0xFFFFu); v[1] += bf16_to_f32(b.x >> 16);
-      v[2] += bf16_to_f32(b.y & 0xFFFFu); v[3] += bf16_to_f32(b.y >> 16);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n + j < N) v[j] += bf16_to_f32(bias[n + j]);
-    }
-  }
-  const int64_t off = (int64_t)m * N + n;
-  if (out_f32) {
-    float* c = reinterpret_cast<float*>(C) + off;
-    if (full) {
-      *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n + j < N) c[j] = v[j];
-    }
-  } else {
-    uint16_t* c = reinterpret_cast<uint16_t*>(C) + off;
-    if (full) {
-      uint2 w;
-      w.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-      w.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-      *reinterpret_cast<uint2*>(c) = w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n + j < N) c[j] = (uint16_t)f32_to_bf16_rne(v[j]);
-    }
-  }
-}
-
-// One 16-byte-per-lane copy global -> LDS: lane l's 16 bytes land at
-// lds_base + 16 l (lds_base is wave-uniform).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds_base, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
-}
-
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT) void gemm_mx_kernel(const uint8_t* __restrict__ A,
                                                           const uint8_t* __restrict__ As,
@@ -131,136 +127,220 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_mx_kernel(const uint8_t* __restr
                                                           int M, int N, int kpad,
                                                           const uint16_t* __restrict__ bias, int out_f32,
                                                           int tiles_m, int tiles_n) {
-  constexpr int KB = Cfg::KB, CH = Cfg::CHUNKS, NW = Cfg::NT / 64;
-  constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
-  constexpr int A_DMA = Cfg::A_STAGE / (1024 * NW);    // 1-KB wave copies per stage
-  constexpr int B_DMA = Cfg::B_STAGE / (1024 * NW);
-  static_assert(A_DMA * 1024 * NW == Cfg::A_STAGE && B_DMA * 1024 * NW == Cfg::B_STAGE, "dma split");
-  __shared__ __align__(16) uint8_t lds[2 * (Cfg::A_STAGE + Cfg::B_STAGE)];
+  constexpr int BM = Cfg::BM, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
+  constexpr int RB = Cfg::RB, SB = Cfg::SB, NW = Cfg::NW, NST = Cfg::NST;
+  __shared__ __align__(16) uint8_t lds[Cfg::LDS];
 
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
-  const int row_bytes = (FMT_MXFP8 == Cfg::FMT) ? kpad : kpad / 2;
+  const int row_bytes = (Cfg::FMT == FMT_MXFP8) ? kpad : kpad / 2;
   const int srow = kpad / 32;               // scale bytes per row
-  const int nk = kpad / 128;
-  const int g = lane >> 4, r16 = lane & 15;
+  const int nk = kpad / Cfg::KS;            // stages
+  const int g = lane >> 5, r32 = lane & 31;
 
-  // Buffer resources: reads past the last row return zeros (tail tiles).
-  const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, M * row_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc((void*)B, 0, N * row_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t as_rs = __builtin_amdgcn_make_buffer_rsrc((void*)As, 0, M * srow, 0x00020000);
-  const __amdgpu_buffer_rsrc_t bs_rs = __builtin_amdgcn_make_buffer_rsrc((void*)Bs, 0, N * srow, 0x00020000);
+  const v4u a_rs = buffer_rsrc(A, (uint32_t)(M * row_bytes));
+  const v4u b_rs = buffer_rsrc(B, (uint32_t)(N * row_bytes));
+  const v4u as_rs = buffer_rsrc(As, (uint32_t)(M * srow));
+  const v4u bs_rs = buffer_rsrc(Bs, (uint32_t)(N * srow));
+  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
 
-  // Direct global -> LDS copies: copy j of this wave fills LDS chunks
-  // P = (j * NW + wave) * 64 + lane, i.e. row P / CH, swizzled position
-  // P % CH, which holds global chunk (P % CH) ^ swizzle(row).
-  int a_voff[A_DMA], b_voff[B_DMA];
+  // Copy j of this wave fills the stage's 1-KB code block J = j * NW + wave:
+  // 16-byte chunk P = 64 J + lane, A rows first (4 chunks per row), then B.
+  uint32_t code_voff[Cfg::CODE_DMA];
+  bool code_is_a[Cfg::CODE_DMA];
 #pragma unroll
-  for (int j = 0; j < A_DMA; ++j) {
-    const int P = (j * NW + wave) * 64 + lane, r = P / CH, p = P % CH;
-    a_voff[j] = (m0 + r) * row_bytes + swz_chunk(r, p, CH, Cfg::SWZ) * 16;
+  for (int j = 0; j < Cfg::CODE_DMA; ++j) {
+    const int J = j * NW + wave;
+    const int P = J * 64 + lane;
+    const bool isa = P < BM * 4;
+    const int Pr = isa ? P : P - BM * 4;
+    const int r = Pr >> 2, p = Pr & 3;
+    code_is_a[j] = J * 64 < BM * 4;       // uniform per copy
+    code_voff[j] = (uint32_t)(((isa ? m0 : n0) + r) * row_bytes + swz4(r, p) * 16);
   }
+  // Scale copy j of this wave covers rows 64 J' .. 64 J' + 63 of [A rows, B rows].
+  uint32_t scale_voff[Cfg::SCALE_DMA];
+  bool scale_is_a[Cfg::SCALE_DMA];
 #pragma unroll
-  for (int j = 0; j < B_DMA; ++j) {
-    const int P = (j * NW + wave) * 64 + lane, r = P / CH, p = P % CH;
-    b_voff[j] = (n0 + r) * row_bytes + swz_chunk(r, p, CH, Cfg::SWZ) * 16;
+  for (int j = 0; j < Cfg::SCALE_DMA; ++j) {
+    const int J = j * NW + wave;
+    const int row = J * 64 + lane;
+    scale_is_a[j] = J * 64 < BM;
+    const int r = scale_is_a[j] ? row : row - BM;
+    scale_voff[j] = (uint32_t)(((scale_is_a[j] ? m0 : n0) + r) * srow);
   }
-  // scale dwords (4 K-blocks per stage): one per fragment and lane
-  const int sa_voff = (m0 + wm * WM + r16) * srow;
-  const int sb_voff = (n0 + wn * WN + r16) * srow;
-  const int sshift = 8 * g;
-  // LDS read offsets of this lane's fragment 0 (chunk g and, for fp8, 4+g);
-  // fragment f adds 16 f rows, which keeps the swizzle (it uses row bits < 4).
-  const int ra = wm * WM + r16, rb = wn * WN + r16;
-  const int a_off0 = ra * KB + swz_chunk(ra, g, CH, Cfg::SWZ) * 16;
-  const int a_off1 = ra * KB + swz_chunk(ra, (4 + g) & (CH - 1), CH, Cfg::SWZ) * 16;
-  const int b_off0 = rb * KB + swz_chunk(rb, g, CH, Cfg::SWZ) * 16;
-  const int b_off1 = rb * KB + swz_chunk(rb, (4 + g) & (CH - 1), CH, Cfg::SWZ) * 16;
 
-  auto issue_stage = [&](int ks, int buf) {
-    uint8_t* a_dst = lds + buf * Cfg::A_STAGE;
-    uint8_t* b_dst = lds + 2 * Cfg::A_STAGE + buf * Cfg::B_STAGE;
+  auto issue_stage = [&](int ks) {
+    const uint32_t st = lds_base + (uint32_t)((ks % NST) * Cfg::STAGE);
 #pragma unroll
-    for (int j = 0; j < A_DMA; ++j)
-      dma16(a_rs, a_dst + (j * NW + wave) * 1024, a_voff[j], ks * KB);
+    for (int j = 0; j < Cfg::CODE_DMA; ++j) {
+      const uint32_t dst = st + (uint32_t)((j * NW + wave) * 1024);
+      dma<16>(code_is_a[j] ? a_rs : b_rs, dst, code_voff[j], (uint32_t)(ks * RB));
+    }
 #pragma unroll
-    for (int j = 0; j < B_DMA; ++j)
-      dma16(b_rs, b_dst + (j * NW + wave) * 1024, b_voff[j], ks * KB);
+    for (int j = 0; j < Cfg::SCALE_DMA; ++j) {
+      const uint32_t dst = st + Cfg::CODE_BYTES + (uint32_t)((j * NW + wave) * 64 * SB);
+      const uint32_t sdw = (uint32_t)((Cfg::FMT == FMT_MXFP8 ? (ks >> 1) : ks) * 4);
+      dma<4>(scale_is_a[j] ? as_rs : bs_rs, dst, scale_voff[j], sdw);
+    }
   };
 
-  v4f acc[FM][FN];
+  // LDS read offsets (within a stage) of this lane's fragments.
+  const int ra = wm * WM + r32, rb = wn * WN + r32;     // fragment 0 rows; +32 per fragment keeps the swizzle
+  const int a_code = ra * RB, b_code = BM * RB + rb * RB;
+  const int a_c0 = swz4(ra, g) * 16, a_c1 = swz4(ra, 2 + g) * 16;     // fp8: chunks g, 2+g; fp4: 2t+g
+  const int b_c0 = swz4(rb, g) * 16, b_c1 = swz4(rb, 2 + g) * 16;
+  const int a_sc = Cfg::CODE_BYTES + ra * SB, b_sc = Cfg::CODE_BYTES + (BM + rb) * SB;
+
+  // bias of this lane's output columns, loaded once (consumed after the loop)
+  uint2 bias_v[FN][4];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + wn * WN + 32 * fn + 8 * q + 4 * g;
+      bias_v[fn][q] = make_uint2(0u, 0u);
+      if (bias) {
+        if (((N & 3) == 0) && n + 3 < N && (reinterpret_cast<uintptr_t>(bias) & 7) == 0) {
+          bias_v[fn][q] = *reinterpret_cast<const uint2*>(bias + n);
+        } else {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (n + v < N) w[v] = bias[n + v];
+          bias_v[fn][q] = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+        }
+      }
+    }
+
+  v16f acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-  uint32_t sa_cur[FM], sb_cur[FN], sa_nxt[FM], sb_nxt[FN];
-  issue_stage(0, 0);
+  // prologue: stages 0 .. NST-2 in flight
 #pragma unroll
-  for (int f = 0; f < FM; ++f) sa_cur[f] = __builtin_amdgcn_raw_buffer_load_b32(as_rs, sa_voff + 16 * f * srow, 0, 0) >> sshift;
-#pragma unroll
-  for (int f = 0; f < FN; ++f) sb_cur[f] = __builtin_amdgcn_raw_buffer_load_b32(bs_rs, sb_voff + 16 * f * srow, 0, 0) >> sshift;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nk) issue_stage(s);
 
   for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) {
-      issue_stage(ks + 1, cur ^ 1);
+    // this wave's copies of stage ks have landed when at most the copies of
+    // the (up to NST-2) later stages already issued are still pending
+    const int later = min(nk - 1 - ks, NST - 2);
+    if (later >= 2) wait_vm<2 * Cfg::OPS>();
+    else if (later == 1) wait_vm<Cfg::OPS>();
+    else wait_vm<0>();
+    __syncthreads();                        // every wave's copies of stage ks are visible, and
+                                            // every wave is done with the slot reused below
+    if (ks + NST - 1 < nk) issue_stage(ks + NST - 1);
+
+    const uint8_t* st = lds + (ks % NST) * Cfg::STAGE;
+    if (Cfg::FMT == FMT_MXFP8) {
+      v8i bf[FN], af[FM];
+      int sbv[FN], sav[FM];
+      const int sh = 8 * (2 * (ks & 1) + g);   // this lane's block within the stage pair's dword
 #pragma unroll
-      for (int f = 0; f < FM; ++f)
-        sa_nxt[f] = __builtin_amdgcn_raw_buffer_load_b32(as_rs, sa_voff + 16 * f * srow, 4 * (ks + 1), 0) >> sshift;
+      for (int f = 0; f < FN; ++f) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(st + b_code + 32 * f * RB + b_c0);
+        const uint4 hi = *reinterpret_cast<const uint4*>(st + b_code + 32 * f * RB + b_c1);
+        bf[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sbv[f] = (int)(*reinterpret_cast<const uint32_t*>(st + b_sc + 32 * f * SB) >> sh);
+      }
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(st + a_code + 32 * f * RB + a_c0);
+        const uint4 hi = *reinterpret_cast<const uint4*>(st + a_code + 32 * f * RB + a_c1);
+        af[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sav[f] = (int)(*reinterpret_cast<const uint32_t*>(st + a_sc + 32 * f * SB) >> sh);
+      }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[fn], af[fm], acc[fm][fn], 0, 0, 0, sbv[fn],
+                                                                        0, sav[fm]);
+    } else {
+      int sbv[FN], sav[FM];
 #pragma unroll
       for (int f = 0; f < FN; ++f)
-        sb_nxt[f] = __builtin_amdgcn_raw_buffer_load_b32(bs_rs, sb_voff + 16 * f * srow, 4 * (ks + 1), 0) >> sshift;
-    }
-    const uint8_t* a_buf = lds + cur * Cfg::A_STAGE;
-    const uint8_t* b_buf = lds + 2 * Cfg::A_STAGE + cur * Cfg::B_STAGE;
-    v8i bfrag[FN];
+        sbv[f] = (int)(*reinterpret_cast<const uint32_t*>(st + b_sc + 32 * f * SB) >> (8 * g));
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      uint4 lo = *reinterpret_cast<const uint4*>(b_buf + b_off0 + 16 * f * KB);
-      uint4 hi = make_uint4(0u, 0u, 0u, 0u);
-      if (Cfg::FMT == FMT_MXFP8) hi = *reinterpret_cast<const uint4*>(b_buf + b_off1 + 16 * f * KB);
-      bfrag[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
+      for (int f = 0; f < FM; ++f)
+        sav[f] = (int)(*reinterpret_cast<const uint32_t*>(st + a_sc + 32 * f * SB) >> (8 * g));
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      uint4 lo = *reinterpret_cast<const uint4*>(a_buf + a_off0 + 16 * fm * KB);
-      uint4 hi = make_uint4(0u, 0u, 0u, 0u);
-      if (Cfg::FMT == FMT_MXFP8) hi = *reinterpret_cast<const uint4*>(a_buf + a_off1 + 16 * fm * KB);
-      const v8i afrag = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      for (int t = 0; t < 2; ++t) {         // two 64-element sub-steps; scale byte 2t (after the shift)
+        v8i bf[FN], af[FM];
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            bfrag[fn], afrag, acc[fm][fn], Cfg::MFMA_FMT, Cfg::MFMA_FMT, 0, (int)sb_cur[fn], 0, (int)sa_cur[fm]);
+        for (int f = 0; f < FN; ++f) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(st + b_code + 32 * f * RB + (t ? b_c1 : b_c0));
+          bf[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int f = 0; f < FM; ++f) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(st + a_code + 32 * f * RB + (t ? a_c1 : a_c0));
+          af[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            if (t == 0)
+              acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[fn], af[fm], acc[fm][fn], 4, 4, 0,
+                                                                            sbv[fn], 0, sav[fm]);
+            else
+              acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[fn], af[fm], acc[fm][fn], 4, 4, 2,
+                                                                            sbv[fn], 2, sav[fm]);
+          }
       }
-    }
-    // the copies into the other buffer (and the next scales) must land
-    // before any wave reads them after the barrier
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int f = 0; f < FM; ++f) sa_cur[f] = sa_nxt[f];
-#pragma unroll
-      for (int f = 0; f < FN; ++f) sb_cur[f] = sb_nxt[f];
     }
   }
 
-  // epilogue: lane holds C[m][n..n+3]
+  // epilogue: register 4q + v of acc[fm][fn] is C[m][n + v] with
+  // m = m0 + wm WM + 32 fm + r32, n = n0 + wn WN + 32 fn + 8 q + 4 g
+  const bool vec = ((N & 3) == 0);
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    const int m = m0 + wm * WM + 16 * fm + r16;
+    const int m = m0 + wm * WM + 32 * fm + r32;
+    if (m >= M) continue;
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int n = n0 + wn * WN + 16 * fn + 4 * g;
-      store4(C, M, N, m, n, acc[fm][fn], 1.0f, bias, out_f32);
-    }
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WN + 32 * fn + 8 * q + 4 * g;
+        if (n >= N) continue;
+        const uint2 bb = bias_v[fn][q];
+        float v[4];
+        v[0] = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb.x & 0xFFFFu);
+        v[1] = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb.x >> 16);
+        v[2] = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb.y & 0xFFFFu);
+        v[3] = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb.y >> 16);
+        const int64_t off = (int64_t)m * N + n;
+        if (out_f32) {
+          float* c = reinterpret_cast<float*>(C) + off;
+          if (vec && n + 3 < N) {
+            *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (n + j < N) c[j] = v[j];
+          }
+        } else {
+          uint16_t* c = reinterpret_cast<uint16_t*>(C) + off;
+          if (vec && n + 3 < N) {
+            *reinterpret_cast<uint2*>(c) = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                                      f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (n + j < N) c[j] = (uint16_t)f32_to_bf16_rne(v[j]);
+          }
+        }
+      }
   }
 }
 
@@ -278,16 +358,16 @@ static hipError_t run_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, 
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
                           int64_t M, int64_t N, int64_t K, int fmt, const uint16_t* bias, int out_f32,
                           hipStream_t stream) {
-  // Large problems: 256 x 256 tiles, 8 waves of 128 x 64. Small ones:
-  // 128 x 128 tiles, 4 waves of 64 x 64, so more workgroups fill the chip.
+  // 256 x 256 tiles (8 waves of 128 x 64) when they fill the chip, else
+  // 128 x 128 tiles (4 waves of 64 x 64, two workgroups per CU).
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const bool big = big_tiles >= 256;
   if (fmt == FMT_MXFP8) {
-    if (big) return run_mx<MxCfg<FMT_MXFP8, 256, 256, 2, 2, 0>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-    return run_mx<MxCfg<FMT_MXFP8, 128, 128, 2, 2, 0>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+    if (big) return run_mx<MxCfg<FMT_MXFP8, 256, 256, 2, 4, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+    return run_mx<MxCfg<FMT_MXFP8, 128, 128, 2, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
   }
-  if (big) return run_mx<MxCfg<FMT_MXFP4, 256, 256, 2, 2, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-  return run_mx<MxCfg<FMT_MXFP4, 128, 128, 2, 2, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+  if (big) return run_mx<MxCfg<FMT_MXFP4, 256, 256, 2, 4, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+  return run_mx<MxCfg<FMT_MXFP4, 128, 128, 2, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
 }
 
 }  // namespace mx
