@@ -21,19 +21,24 @@
 // The B tile is fed as the instruction's first operand, so each lane ends up
 // with runs of 4 consecutive output columns of one output row.
 //
-// Pipeline: a K-stage is 64 bytes of codes per row (64 fp8 / 128 fp4
-// elements) plus the aligned scale dword holding that stage's blocks (fp8:
-// the 4 blocks of stages 2j, 2j+1; fp4: the 4 blocks of the stage). NST
-// stages are in flight: each wave copies its share of a stage global -> LDS
-// with buffer_load ... lds (16 bytes of codes or one scale dword per lane,
-// rows past the tensor read as zero), waits with vmcnt for its own copies of
-// the stage about to be used, then a workgroup barrier makes every wave's
-// copies visible. The copies are issued from inline assembly so that the
-// compiler does not conservatively wait for all of them before each LDS
-// read; the kernel does its own counting. Code rows are XOR-swizzled in
-// 16-byte chunks so the 32 lanes reading one chunk column hit distinct
-// banks. Tiles are renumbered so each XCD (own L2) gets a contiguous range,
-// walked in groups of 8 tile-rows.
+// Data movement. A K-stage is 128 bytes of codes per row (128 fp8 / 256 fp4
+// elements); two stages are double-buffered in LDS. Scales travel in chunks
+// of 16 bytes per row (16 blocks, i.e. 512 K elements), double-buffered in
+// their own LDS slots. Both are copied global -> LDS with
+// buffer_load ... lds (16 bytes per lane; rows past the tensor read as
+// zero), issued from inline assembly with the kernel's own waits, so the
+// compiler does not stall every LDS read on copies that are still in
+// flight. A stage's 1-KB wave copies cover 8 rows x 128 bytes, the shape the
+// L2 serves fastest. Code rows are XOR-swizzled in 16-byte chunks so the 8
+// lanes of one LDS read cycle hit distinct banks. Each sub-step's fragments
+// are read into registers before the matrix instructions of the previous
+// sub-step are issued. Tiles are renumbered so each XCD (own L2) gets a
+// contiguous range, walked in groups of 8 tile-rows.
+//
+// Epilogue: the bias is loaded before the K loop. For bf16 output the tile
+// is converted and written to LDS (16-byte chunks XOR-swizzled by row), then
+// stored as whole rows of 16-byte lanes; fp32 output (or N % 8 != 0) is
+// stored straight from registers.
 #include "mx_device.h"
 #include "mx_launch.h"
 
@@ -43,33 +48,32 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NST_>
+template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct MxCfg {
-  static constexpr int FMT = FMT_, BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NST = NST_;
+  static constexpr int FMT = FMT_, BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int NT = 64 * WAVES_M * WAVES_N, NW = NT / 64;
-  static constexpr int RB = 64;                               // code bytes per row per stage
-  static constexpr int KS = (FMT == FMT_MXFP8) ? 64 : 128;    // K elements per stage
-  static constexpr int SB = 4;                                // scale bytes per row in a stage slot
-                                                              // (fp8: blocks of 2 stages; fp4: of 1 stage)
+  static constexpr int RB = 128;                              // code bytes per row per stage
+  static constexpr int CH = RB / 16;                          // 16-byte chunks per row
+  static constexpr int KS = (FMT == FMT_MXFP8) ? RB : 2 * RB; // K elements per stage
+  static constexpr int SUB = KS / 64;                         // 32x32x64 sub-steps per stage
+  static constexpr int SPC = 512 / KS;                        // stages per scale chunk
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int CODE_BYTES = (BM + BN) * RB;            // per stage
-  static constexpr int SCALE_BYTES = (BM + BN) * SB;
-  static constexpr int STAGE = CODE_BYTES + SCALE_BYTES;
-  static constexpr int LDS = NST * STAGE;
-  static constexpr int CODE_DMA = CODE_BYTES / 1024 / NW;     // 1-KB copies per wave per stage
-  static constexpr int SCALE_DMA = (BM + BN) / 64 / NW;       // 64-row scale copies per wave per stage
-  static constexpr int OPS = CODE_DMA + SCALE_DMA;            // vector memory ops per wave per stage
+  static constexpr int STAGE = (BM + BN) * RB;                 // code bytes per stage
+  static constexpr int SCHUNK = (BM + BN) * 16;                // bytes per scale slot
+  static constexpr int LDS = 2 * STAGE + 2 * SCHUNK;
+  static constexpr int CODE_DMA = STAGE / 1024 / NW;          // 1-KB code copies per wave per stage
+  static constexpr int SCALE_COPIES = (BM + BN) / 64;         // 1-KB copies per scale chunk
+  static constexpr int SCALE_DMA = (SCALE_COPIES + NW - 1) / NW;  // per wave (some may be idle)
   static constexpr int MFMA_FMT = (FMT == FMT_MXFP8) ? 0 : 4;  // E4M3 / E2M1 operand selector
-  static_assert(CODE_DMA * 1024 * NW == CODE_BYTES, "code copies must split evenly over waves");
-  static_assert(SCALE_DMA * 64 * NW == BM + BN && SCALE_DMA >= 1, "scale copies must split evenly");
-  static_assert((BM * RB) % 1024 == 0 && BM % 64 == 0 && BN % 64 == 0, "tile");
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(CODE_DMA * 1024 * NW == STAGE, "code copies must split evenly over waves");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
   static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(BM * BN * 2 <= LDS, "the bf16 C tile must fit in LDS");
 };
 
-// Row r keeps 16-byte chunk c at position c ^ ((r >> 1) & 3).
-__device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 1) & 3); }
+// Row r keeps 16-byte chunk c of a 128-byte row at position c ^ (r & 7).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
 
 __device__ __forceinline__ v4u buffer_rsrc(const void* p, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(p);
@@ -81,25 +85,16 @@ __device__ __forceinline__ v4u buffer_rsrc(const void* p, uint32_t bytes) {
   return r;
 }
 
-// One wave-wide copy global -> LDS: lane l's SIZE (16 or 4) bytes at `voff`
-// land at lds_addr + SIZE * l. M0 is saved and restored around the copy.
-template <int SIZE>
-__device__ __forceinline__ void dma(v4u rs, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+// One wave-wide copy global -> LDS: lane l's 16 bytes at `voff` (+ soff)
+// land at lds_addr + 16 l. M0 is saved and restored around the copy.
+__device__ __forceinline__ void dma16(v4u rs, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
   uint32_t saved;
-  if (SIZE == 16)
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
-  else
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
 }
 
-// Wait until at most N of this wave's vector memory operations are pending.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
+// Wait until every vector memory operation of this wave has completed.
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Tile coordinates of this workgroup: XCD-contiguous renumbering, then
 // groups of 8 tile-rows walked column by column.
@@ -119,6 +114,54 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_group / gm;
 }
 
+// One sub-step's operands for one wave: FM A fragments, FN B fragments and
+// their scales, shifted so that this lane's scale byte is byte 0.
+template <class Cfg>
+struct Frags {
+  v8i a[Cfg::FM], b[Cfg::FN];
+  int sa[Cfg::FM], sb[Cfg::FN];
+};
+
+// Sub-step t of the stage held at `st` (codes) whose scales are in the
+// chunk at `sc`, chunk-relative stage index `sj`. fp8: lane chunks 4t+g and
+// 4t+2+g (K 16g.. and 32+16g.. of the sub-step); fp4: chunk 2t+g. This
+// lane's scale byte is block (KS/32) sj + 2t + g of the row's 16-byte chunk.
+template <class Cfg>
+__device__ __forceinline__ void load_frags(Frags<Cfg>& fr, const uint8_t* st, const uint8_t* sc, int t, int sj,
+                                           int g, int ra, int rb) {
+  constexpr int RB = Cfg::RB;
+  const int blk = (Cfg::KS / 32) * sj + 2 * t + g;
+  const int sdw = blk >> 2, sh = 8 * (blk & 3);
+#pragma unroll
+  for (int f = 0; f < Cfg::FN; ++f) {
+    const int r = rb + 32 * f;
+    const uint8_t* row = st + (Cfg::BM + r) * RB;
+    fr.sb[f] = (int)(*reinterpret_cast<const uint32_t*>(sc + (Cfg::BM + r) * 16 + 4 * sdw) >> sh);
+    if (Cfg::FMT == FMT_MXFP8) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(row + swz(r, 4 * t + g) * 16);
+      const uint4 hi = *reinterpret_cast<const uint4*>(row + swz(r, 4 * t + 2 + g) * 16);
+      fr.b[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+      const uint4 lo = *reinterpret_cast<const uint4*>(row + swz(r, 2 * t + g) * 16);
+      fr.b[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < Cfg::FM; ++f) {
+    const int r = ra + 32 * f;
+    const uint8_t* row = st + r * RB;
+    fr.sa[f] = (int)(*reinterpret_cast<const uint32_t*>(sc + r * 16 + 4 * sdw) >> sh);
+    if (Cfg::FMT == FMT_MXFP8) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(row + swz(r, 4 * t + g) * 16);
+      const uint4 hi = *reinterpret_cast<const uint4*>(row + swz(r, 4 * t + 2 + g) * 16);
+      fr.a[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+      const uint4 lo = *reinterpret_cast<const uint4*>(row + swz(r, 2 * t + g) * 16);
+      fr.a[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+    }
+  }
+}
+
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT) void gemm_mx_kernel(const uint8_t* __restrict__ A,
                                                           const uint8_t* __restrict__ As,
@@ -127,19 +170,21 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_mx_kernel(const uint8_t* __restr
                                                           int M, int N, int kpad,
                                                           const uint16_t* __restrict__ bias, int out_f32,
                                                           int tiles_m, int tiles_n) {
-  constexpr int BM = Cfg::BM, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
-  constexpr int RB = Cfg::RB, SB = Cfg::SB, NW = Cfg::NW, NST = Cfg::NST;
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
+  constexpr int RB = Cfg::RB, CH = Cfg::CH, NW = Cfg::NW;
   __shared__ __align__(16) uint8_t lds[Cfg::LDS];
 
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int row_bytes = (Cfg::FMT == FMT_MXFP8) ? kpad : kpad / 2;
   const int srow = kpad / 32;               // scale bytes per row
-  const int nk = kpad / Cfg::KS;            // stages
+  // stages; with fp4 a stage holds 256 elements while K_pad is a multiple
+  // of 128, so the last stage may hold only its first 64 bytes
+  const int nk = (kpad + Cfg::KS - 1) / Cfg::KS;
   const int g = lane >> 5, r32 = lane & 31;
 
   const v4u a_rs = buffer_rsrc(A, (uint32_t)(M * row_bytes));
@@ -147,22 +192,26 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_mx_kernel(const uint8_t* __restr
   const v4u as_rs = buffer_rsrc(As, (uint32_t)(M * srow));
   const v4u bs_rs = buffer_rsrc(Bs, (uint32_t)(N * srow));
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+  const uint32_t sc_base = lds_base + 2 * Cfg::STAGE;
 
-  // Copy j of this wave fills the stage's 1-KB code block J = j * NW + wave:
-  // 16-byte chunk P = 64 J + lane, A rows first (4 chunks per row), then B.
+  // Code copy j of this wave fills the stage's 1-KB block J = j NW + wave,
+  // i.e. 16-byte chunks 64 J + lane: A rows first (CH chunks per row), then B.
   uint32_t code_voff[Cfg::CODE_DMA];
+  int code_byte[Cfg::CODE_DMA];             // byte of the stage this lane copies
   bool code_is_a[Cfg::CODE_DMA];
 #pragma unroll
   for (int j = 0; j < Cfg::CODE_DMA; ++j) {
     const int J = j * NW + wave;
     const int P = J * 64 + lane;
-    const bool isa = P < BM * 4;
-    const int Pr = isa ? P : P - BM * 4;
-    const int r = Pr >> 2, p = Pr & 3;
-    code_is_a[j] = J * 64 < BM * 4;       // uniform per copy
-    code_voff[j] = (uint32_t)(((isa ? m0 : n0) + r) * row_bytes + swz4(r, p) * 16);
+    const bool isa = P < BM * CH;
+    const int Pr = isa ? P : P - BM * CH;
+    const int r = Pr / CH, p = Pr % CH;
+    code_is_a[j] = J * 64 < BM * CH;           // uniform per copy
+    code_byte[j] = swz(r, p) * 16;
+    code_voff[j] = (uint32_t)(((isa ? m0 : n0) + r) * row_bytes + code_byte[j]);
   }
-  // Scale copy j of this wave covers rows 64 J' .. 64 J' + 63 of [A rows, B rows].
+  // Scale copy j of this wave fills rows 64 J .. 64 J + 63 of [A rows, B rows]
+  // with 16 bytes each (copies J >= SCALE_COPIES are skipped).
   uint32_t scale_voff[Cfg::SCALE_DMA];
   bool scale_is_a[Cfg::SCALE_DMA];
 #pragma unroll
@@ -175,26 +224,27 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_mx_kernel(const uint8_t* __restr
   }
 
   auto issue_stage = [&](int ks) {
-    const uint32_t st = lds_base + (uint32_t)((ks % NST) * Cfg::STAGE);
+    if (ks % Cfg::SPC == 0) {               // first stage of a scale chunk: bring the chunk too
+      const int c = ks / Cfg::SPC;
+      const uint32_t dst = sc_base + (uint32_t)((c & 1) * Cfg::SCHUNK);
+#pragma unroll
+      for (int j = 0; j < Cfg::SCALE_DMA; ++j) {
+        const int J = j * NW + wave;
+        if (J < Cfg::SCALE_COPIES) dma16(scale_is_a[j] ? as_rs : bs_rs, dst + (uint32_t)(J * 1024), scale_voff[j],
+                                         (uint32_t)(16 * c));
+      }
+    }
+    const uint32_t st = lds_base + (uint32_t)((ks & 1) * Cfg::STAGE);
+    const int rem = row_bytes - ks * RB;    // bytes of each row left from this stage on
 #pragma unroll
     for (int j = 0; j < Cfg::CODE_DMA; ++j) {
-      const uint32_t dst = st + (uint32_t)((j * NW + wave) * 1024);
-      dma<16>(code_is_a[j] ? a_rs : b_rs, dst, code_voff[j], (uint32_t)(ks * RB));
-    }
-#pragma unroll
-    for (int j = 0; j < Cfg::SCALE_DMA; ++j) {
-      const uint32_t dst = st + Cfg::CODE_BYTES + (uint32_t)((j * NW + wave) * 64 * SB);
-      const uint32_t sdw = (uint32_t)((Cfg::FMT == FMT_MXFP8 ? (ks >> 1) : ks) * 4);
-      dma<4>(scale_is_a[j] ? as_rs : bs_rs, dst, scale_voff[j], sdw);
+      // bytes past the end of the row read as zero (offset beyond the buffer)
+      const uint32_t voff = code_byte[j] < rem ? code_voff[j] : 0x80000000u;
+      dma16(code_is_a[j] ? a_rs : b_rs, st + (uint32_t)((j * NW + wave) * 1024), voff, (uint32_t)(ks * RB));
     }
   };
 
-  // LDS read offsets (within a stage) of this lane's fragments.
-  const int ra = wm * WM + r32, rb = wn * WN + r32;     // fragment 0 rows; +32 per fragment keeps the swizzle
-  const int a_code = ra * RB, b_code = BM * RB + rb * RB;
-  const int a_c0 = swz4(ra, g) * 16, a_c1 = swz4(ra, 2 + g) * 16;     // fp8: chunks g, 2+g; fp4: 2t+g
-  const int b_c0 = swz4(rb, g) * 16, b_c1 = swz4(rb, 2 + g) * 16;
-  const int a_sc = Cfg::CODE_BYTES + ra * SB, b_sc = Cfg::CODE_BYTES + (BM + rb) * SB;
+  const int ra = wm * WM + r32, rb = wn * WN + r32;     // this lane's fragment-0 rows in the tile
 
   // bias of this lane's output columns, loaded once (consumed after the loop)
   uint2 bias_v[FN][4];
@@ -223,85 +273,69 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_mx_kernel(const uint8_t* __restr
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-  // prologue: stages 0 .. NST-2 in flight
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < nk) issue_stage(s);
-
+  issue_stage(0);
   for (int ks = 0; ks < nk; ++ks) {
-    // this wave's copies of stage ks have landed when at most the copies of
-    // the (up to NST-2) later stages already issued are still pending
-    const int later = min(nk - 1 - ks, NST - 2);
-    if (later >= 2) wait_vm<2 * Cfg::OPS>();
-    else if (later == 1) wait_vm<Cfg::OPS>();
-    else wait_vm<0>();
-    __syncthreads();                        // every wave's copies of stage ks are visible, and
-                                            // every wave is done with the slot reused below
-    if (ks + NST - 1 < nk) issue_stage(ks + NST - 1);
+    wait_vm_all();                          // this wave's copies of stage ks (and its scale chunk)
+    __syncthreads();                        // everyone's copies are visible, and everyone is done
+                                            // with the buffers the next copies overwrite
+    if (ks + 1 < nk) issue_stage(ks + 1);
 
-    const uint8_t* st = lds + (ks % NST) * Cfg::STAGE;
-    if (Cfg::FMT == FMT_MXFP8) {
-      v8i bf[FN], af[FM];
-      int sbv[FN], sav[FM];
-      const int sh = 8 * (2 * (ks & 1) + g);   // this lane's block within the stage pair's dword
+    const uint8_t* st = lds + (ks & 1) * Cfg::STAGE;
+    const uint8_t* sc = lds + 2 * Cfg::STAGE + ((ks / Cfg::SPC) & 1) * Cfg::SCHUNK;
+    const int sj = ks % Cfg::SPC;
+    Frags<Cfg> cur_f, nxt_f;
+    load_frags<Cfg>(cur_f, st, sc, 0, sj, g, ra, rb);
 #pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(st + b_code + 32 * f * RB + b_c0);
-        const uint4 hi = *reinterpret_cast<const uint4*>(st + b_code + 32 * f * RB + b_c1);
-        bf[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        sbv[f] = (int)(*reinterpret_cast<const uint32_t*>(st + b_sc + 32 * f * SB) >> sh);
-      }
-#pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(st + a_code + 32 * f * RB + a_c0);
-        const uint4 hi = *reinterpret_cast<const uint4*>(st + a_code + 32 * f * RB + a_c1);
-        af[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        sav[f] = (int)(*reinterpret_cast<const uint32_t*>(st + a_sc + 32 * f * SB) >> sh);
-      }
+    for (int t = 0; t < Cfg::SUB; ++t) {
+      if (t + 1 < Cfg::SUB) load_frags<Cfg>(nxt_f, st, sc, t + 1, sj, g, ra, rb);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[fn], af[fm], acc[fm][fn], 0, 0, 0, sbv[fn],
-                                                                        0, sav[fm]);
-    } else {
-      int sbv[FN], sav[FM];
-#pragma unroll
-      for (int f = 0; f < FN; ++f)
-        sbv[f] = (int)(*reinterpret_cast<const uint32_t*>(st + b_sc + 32 * f * SB) >> (8 * g));
-#pragma unroll
-      for (int f = 0; f < FM; ++f)
-        sav[f] = (int)(*reinterpret_cast<const uint32_t*>(st + a_sc + 32 * f * SB) >> (8 * g));
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {         // two 64-element sub-steps; scale byte 2t (after the shift)
-        v8i bf[FN], af[FM];
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(st + b_code + 32 * f * RB + (t ? b_c1 : b_c0));
-          bf[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int f = 0; f < FM; ++f) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(st + a_code + 32 * f * RB + (t ? a_c1 : a_c0));
-          af[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) {
-            if (t == 0)
-              acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[fn], af[fm], acc[fm][fn], 4, 4, 0,
-                                                                            sbv[fn], 0, sav[fm]);
-            else
-              acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[fn], af[fm], acc[fm][fn], 4, 4, 2,
-                                                                            sbv[fn], 2, sav[fm]);
-          }
-      }
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur_f.b[fn], cur_f.a[fm], acc[fm][fn],
+                                                                        Cfg::MFMA_FMT, Cfg::MFMA_FMT, 0, cur_f.sb[fn],
+                                                                        0, cur_f.sa[fm]);
+      if (t + 1 < Cfg::SUB) cur_f = nxt_f;
     }
   }
 
   // epilogue: register 4q + v of acc[fm][fn] is C[m][n + v] with
-  // m = m0 + wm WM + 32 fm + r32, n = n0 + wn WN + 32 fn + 8 q + 4 g
+  // m = m0 + wm WM + 32 fm + r32, n = n0 + wn WN + 32 fn + 8 q + 4 g.
+  if (!out_f32 && (N & 7) == 0) {
+    constexpr int CPR = BN / 8;                          // 16-byte chunks per tile row
+    __syncthreads();                                     // every wave is done reading the last stage
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int ml = wm * WM + 32 * fm + r32;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wn * WN + 32 * fn + 8 * q + 4 * g;
+          const uint2 bb = bias_v[fn][q];
+          const float v0 = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb.x & 0xFFFFu);
+          const float v1 = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb.x >> 16);
+          const float v2 = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb.y & 0xFFFFu);
+          const float v3 = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb.y >> 16);
+          const int chunk = (nl >> 3) ^ (ml & (CPR - 1));
+          *reinterpret_cast<uint2*>(lds + ml * (BN * 2) + chunk * 16 + (nl & 7) * 2) =
+              make_uint2(f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16),
+                         f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16));
+        }
+    }
+    __syncthreads();
+    constexpr int TOTAL = BM * CPR;
+#pragma unroll 4
+    for (int id = threadIdx.x; id < TOTAL; id += Cfg::NT) {
+      const int row = id / CPR, c = id % CPR;
+      const int m = m0 + row, n = n0 + 8 * c;
+      if (m < M && n < N) {
+        const uint4 w = *reinterpret_cast<const uint4*>(lds + row * (BN * 2) + ((c ^ (row & (CPR - 1))) * 16));
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(C) + (int64_t)m * N + n) = w;
+      }
+    }
+    return;
+  }
   const bool vec = ((N & 3) == 0);
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
@@ -355,19 +389,34 @@ static hipError_t run_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, 
   return hipGetLastError();
 }
 
+// Rounds of workgroups a tiling needs on the 256 CUs (one 256x256 or
+// 192x256 workgroup per CU, LDS-limited), weighted by tile area: the shape
+// with the least MFMA time lost to idle CUs in the last round wins.
+static double tiling_cost(int64_t M, int64_t N, int bm, int bn) {
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const int64_t rounds = (tiles + 255) / 256;
+  return (double)rounds * bm * bn;
+}
+
+template <int FMT>
+static hipError_t dispatch_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
+                              int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
+                              hipStream_t stream) {
+  // 256x256 and 192x256 tiles (8 waves of 128x64 / 96x64) are LDS-bound to
+  // one workgroup per CU; 128x128 (4 waves of 64x64) fits two per CU and
+  // serves problems too small to fill the chip with the large tiles.
+  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big < 128) return run_mx<MxCfg<FMT, 128, 128, 2, 2>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+  if (tiling_cost(M, N, 192, 256) < tiling_cost(M, N, 256, 256))
+    return run_mx<MxCfg<FMT, 192, 256, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+  return run_mx<MxCfg<FMT, 256, 256, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+}
+
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
                           int64_t M, int64_t N, int64_t K, int fmt, const uint16_t* bias, int out_f32,
                           hipStream_t stream) {
-  // 256 x 256 tiles (8 waves of 128 x 64) when they fill the chip, else
-  // 128 x 128 tiles (4 waves of 64 x 64, two workgroups per CU).
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const bool big = big_tiles >= 256;
-  if (fmt == FMT_MXFP8) {
-    if (big) return run_mx<MxCfg<FMT_MXFP8, 256, 256, 2, 4, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-    return run_mx<MxCfg<FMT_MXFP8, 128, 128, 2, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-  }
-  if (big) return run_mx<MxCfg<FMT_MXFP4, 256, 256, 2, 4, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-  return run_mx<MxCfg<FMT_MXFP4, 128, 128, 2, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+  if (fmt == FMT_MXFP8) return dispatch_mx<FMT_MXFP8>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+  return dispatch_mx<FMT_MXFP4>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
 }
 
 }  // namespace mx
