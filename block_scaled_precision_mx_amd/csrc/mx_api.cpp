@@ -76,7 +76,8 @@ mx_status mx_quantize(const void* src, int64_t rows, int64_t cols, int64_t ld, v
   const int64_t kpad = k_pad(L);
   if (R * code_row_bytes(kpad, fmt) >= kMaxBytes || scales_total(R, kpad, fmt) >= kMaxBytes)
     return fail(MX_ERR_UNSUPPORTED, "mx_quantize: output larger than 2 GiB");
-  if (rows > ((int64_t)1 << 40) / ld) return fail(MX_ERR_UNSUPPORTED, "mx_quantize: input too large");
+  if (ld >= ((int64_t)1 << 31) || rows > ((int64_t)1 << 40) / ld)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: input too large (ld must be below 2^31)");
   hipError_t e = mx::launch_quantize(static_cast<const uint16_t*>(src), rows, cols, ld, static_cast<uint8_t*>(codes),
                                      static_cast<uint8_t*>(scales), (int)fmt, (int)axis,
                                      static_cast<hipStream_t>(hip_stream));

@@ -8,22 +8,33 @@
 // quantizer that made that copy ran 6-10x below the read-bandwidth bound).
 //
 // The work is HBM-bound (2 bytes read, 0.5-1.03 bytes written per element),
-// so the kernels are shaped for coalescing, not arithmetic:
-//  * row: each lane reads 8 consecutive bf16 (one 16-byte load), the 4 lanes
-//    of a 32-element MX block (2 lanes of a 16-element NVFP4 block) combine
-//    their amax with cross-lane shuffles, and each lane stores its 8 codes
-//    (8 bytes fp8 / 4 bytes fp4) next to its neighbours'.
+// so the kernels are shaped for coalescing and bytes in flight, and keep all
+// index arithmetic in 32 bits (a 64-bit division is a long software routine
+// on this GPU):
+//  * row: a row of the stored operand is split over TPR = K_pad / 16 threads;
+//    thread j of a row handles 8-element groups j and j + TPR (two 16-byte
+//    loads in flight). The 4 lanes of a 32-element MX block (2 lanes of a
+//    16-element NVFP4 block) are adjacent and combine their amax with
+//    cross-lane shuffles; each lane stores its 8 codes next to its
+//    neighbours'.
 //  * col: a workgroup stages a 128 x 64 bf16 tile through LDS with 16-byte
 //    row loads; each wave then owns 32 consecutive rows (one MX block, two
 //    NVFP4 blocks) of 64 columns and each lane emits its column's 32 codes
 //    as one contiguous 32- or 16-byte store of the transposed output.
 //  * NVFP4 first reduces the tensor amax (bf16 magnitude bits, which order
-//    like the values) into the scale trailer with one atomic max per
-//    workgroup; the quantizer derives s_t from it.
+//    like the values) into the scale trailer with one atomic max per wave;
+//    the quantizer derives s_t from it.
 #include "mx_device.h"
 #include "mx_launch.h"
 
 namespace mx {
+
+// 16-byte streaming load (the source is read once).
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  typedef unsigned v4 __attribute__((ext_vector_type(4)));
+  const v4 v = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 struct NvTrailer {
   float s_t;
@@ -36,7 +47,7 @@ struct NvTrailer {
 // Zeroes the trailer and the (< 16) padding bytes between the last scale
 // byte and the trailer, so the whole scale buffer is defined.
 __global__ void nv_trailer_init_kernel(uint8_t* gap, int gap_bytes, NvTrailer* tr) {
-  if (threadIdx.x < gap_bytes) gap[threadIdx.x] = 0;
+  if ((int)threadIdx.x < gap_bytes) gap[threadIdx.x] = 0;
   if (threadIdx.x == 0) {
     tr->s_t = 0.0f;
     tr->amax_bits = 0u;
@@ -45,119 +56,155 @@ __global__ void nv_trailer_init_kernel(uint8_t* gap, int gap_bytes, NvTrailer* t
   }
 }
 
-__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ src, int64_t rows,
-                                                   int64_t cols, int64_t ld, NvTrailer* tr) {
-  const int64_t gpr = (cols + 7) / 8;          // 8-element groups per row
-  const int64_t total = rows * gpr;
+// Largest |x| of X [rows, cols]: 8-element groups, gpr per row. A grid of
+// about one workgroup per CU walks the tensor with 4 loads in flight per
+// thread; waves reduce through LDS and each workgroup issues one atomic
+// (many atomics on one address serialize in the L2).
+constexpr int kAmaxUnroll = 4;
+
+__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
+                                                   int gpr, NvTrailer* tr) {
+  __shared__ uint32_t wave_max[4];
+  const int total = rows * gpr;
   const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
+  const int stride = gridDim.x * blockDim.x;
   uint32_t m = 0;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    int64_t r = g / gpr;
-    int64_t c = (g - r * gpr) * 8;
-    const uint16_t* p = src + r * ld + c;
-    if (vec_ok && c + 8 <= cols) {
-      uint4 v = *reinterpret_cast<const uint4*>(p);
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int base = blockIdx.x * blockDim.x + threadIdx.x; base < total; base += stride * kAmaxUnroll) {
+    uint4 v[kAmaxUnroll];
+    bool full[kAmaxUnroll];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        m = max(m, w[i] & 0x7FFFu);
-        m = max(m, (w[i] >> 16) & 0x7FFFu);
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const int i = base + u * stride;
+      v[u] = make_uint4(0u, 0u, 0u, 0u);
+      full[u] = false;
+      if (i < total) {
+        const int r = i / gpr;
+        const int c = (i - r * gpr) * 8;
+        const uint16_t* p = src + (int64_t)r * ld + c;
+        if (vec_ok && c + 8 <= cols) {
+          v[u] = load16_stream(p);
+          full[u] = true;
+        } else {
+          uint32_t mm = 0;
+          for (int k = 0; k < 8 && c + k < cols; ++k) mm = max(mm, (uint32_t)p[k] & 0x7FFFu);
+          m = max(m, mm);
+        }
       }
-    } else {
-      for (int i = 0; i < 8 && c + i < cols; ++i) m = max(m, (uint32_t)p[i] & 0x7FFFu);
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      if (!full[u]) continue;
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        m = max(m, w[k] & 0x7FFFu);
+        m = max(m, (w[k] >> 16) & 0x7FFFu);
+      }
     }
   }
-  // wave reduction, then one atomic per wave
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(&tr->amax_bits, m << 16);
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t b = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+    if (b != 0) atomicMax(&tr->amax_bits, b << 16);
+  }
 }
 
-// ------------------------------------------------------------ row quantizer
+// ------------------------------------------------------------ shared encode
 
-// Encode the 8 values of one lane. `mul` is 2^-e (MX); `th` the NVFP4
-// thresholds. Returns packed codes in the low 64 (fp8) or 32 (fp4) bits.
+// Per-block scale of one lane's block given the block's amax bits; returns
+// the scale byte and sets the element multiplier (MX) or thresholds (NVFP4).
+template <int FMT>
+__device__ __forceinline__ uint32_t block_scale(uint32_t amax_bits, float s_t, float& mul, Nv4Thresholds& th) {
+  if (FMT == FMT_NVFP4) {
+    const double q = (s_t == 0.0f) ? 0.0 : (double)bf16_to_f32(amax_bits) / (6.0 * (double)s_t);
+    const uint32_t b = e4m3_encode_pos_f64(q);
+    th = nvfp4_thresholds(e4m3_value(b) * (double)s_t);
+    return b;
+  }
+  const int e = mx_shared_exp(amax_bits, FMT == FMT_MXFP8 ? 8 : 2);
+  mul = pow2_neg(e);
+  return (uint32_t)(e + 127);
+}
+
+// Encode 8 values; packed codes in the low 64 (fp8) or 32 (fp4) bits.
 template <int FMT>
 __device__ __forceinline__ uint64_t encode8(const float (&x)[8], float mul, const Nv4Thresholds& th) {
   uint64_t out = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    uint32_t c;
-    if (FMT == FMT_MXFP8) {
-      c = e4m3_encode(x[i] * mul);
-      out |= (uint64_t)c << (8 * i);
-    } else if (FMT == FMT_MXFP4) {
-      c = e2m1_encode(x[i] * mul);
-      out |= (uint64_t)c << (4 * i);
-    } else {
-      c = nvfp4_encode(x[i], th);
-      out |= (uint64_t)c << (4 * i);
-    }
+    if (FMT == FMT_MXFP8) out |= (uint64_t)e4m3_encode(x[i] * mul) << (8 * i);
+    else if (FMT == FMT_MXFP4) out |= (uint64_t)e2m1_encode(x[i] * mul) << (4 * i);
+    else out |= (uint64_t)nvfp4_encode(x[i], th) << (4 * i);
   }
   return out;
 }
 
+// ------------------------------------------------------------ row quantizer
+
+constexpr int kRowGroupsPerThread = 2;
+
 template <int FMT>
-__global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restrict__ src, int64_t rows,
-                                                        int64_t cols, int64_t ld,
-                                                        uint8_t* __restrict__ codes,
-                                                        uint8_t* __restrict__ scales, int64_t kpad,
-                                                        NvTrailer* tr) {
+__global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
+                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                        int kpad, NvTrailer* tr) {
   constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
   constexpr int LANES_PER_BLOCK = BS / 8;
-  const int64_t gpr = kpad / 8;                 // groups per stored row (multiple of 16)
-  const int64_t total = rows * gpr;
+  constexpr int U = kRowGroupsPerThread;
+  const int gpr = kpad / 8;                       // groups per stored row (multiple of 16)
+  const int tpr = gpr / U;                        // threads per row (multiple of 8)
+  const int total = rows * tpr;
   const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
   float s_t = 0.0f;
   if (FMT == FMT_NVFP4) {
     s_t = nvfp4_tensor_scale(tr->amax_bits);
     if (blockIdx.x == 0 && threadIdx.x == 0) tr->s_t = s_t;
   }
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = g / gpr;
-    const int64_t c = (g - r * gpr) * 8;
-    const uint16_t* p = src + r * ld + c;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (vec_ok && c + 8 <= cols) {
-      uint4 v = *reinterpret_cast<const uint4*>(p);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else {
+  for (int tid = blockIdx.x * blockDim.x + threadIdx.x; tid < total; tid += gridDim.x * blockDim.x) {
+    const int r = tid / tpr;
+    const int j = tid - r * tpr;
+    const uint16_t* row = src + (int64_t)r * ld;
+    uint32_t w[U][4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (c + i < cols) w[i / 2] |= (uint32_t)p[i] << (16 * (i % 2));
-    }
-    float x[8];
-    uint32_t m = 0;
+    for (int u = 0; u < U; ++u) {
+      const int c = (j + tpr * u) * 8;
+      w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0u;
+      if (vec_ok && c + 8 <= cols) {
+        const uint4 v = load16_stream(row + c);
+        w[u][0] = v.x; w[u][1] = v.y; w[u][2] = v.z; w[u][3] = v.w;
+      } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t b = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
-      x[i] = bf16_to_f32(b);
-      m = max(m, b & 0x7FFFu);
+        for (int i = 0; i < 8; ++i)
+          if (c + i < cols) w[u][i / 2] |= (uint32_t)row[c + i] << (16 * (i % 2));
+      }
     }
-    // block amax across the lanes of this block (lane groups are aligned)
 #pragma unroll
-    for (int off = 1; off < LANES_PER_BLOCK; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    uint32_t scale_byte;
-    float mul = 1.0f;
-    Nv4Thresholds th;
-    if (FMT == FMT_NVFP4) {
-      double q = (s_t == 0.0f) ? 0.0 : (double)bf16_to_f32(m) / (6.0 * (double)s_t);
-      scale_byte = e4m3_encode_pos_f64(q);
-      th = nvfp4_thresholds(e4m3_value(scale_byte) * (double)s_t);
-    } else {
-      int e = mx_shared_exp(m, FMT == FMT_MXFP8 ? 8 : 2);
-      scale_byte = (uint32_t)(e + 127);
-      mul = pow2_neg(e);
+    for (int u = 0; u < U; ++u) {
+      const int c = (j + tpr * u) * 8;
+      float x[8];
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b = (w[u][i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+        x[i] = bf16_to_f32(b);
+        m = max(m, b & 0x7FFFu);
+      }
+      // block amax across the adjacent lanes of this block
+#pragma unroll
+      for (int off = 1; off < LANES_PER_BLOCK; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+      float mul = 1.0f;
+      Nv4Thresholds th;
+      const uint32_t sb = block_scale<FMT>(m, s_t, mul, th);
+      const uint64_t packed = encode8<FMT>(x, mul, th);
+      if (FMT == FMT_MXFP8) {
+        *reinterpret_cast<uint2*>(codes + (int64_t)r * kpad + c) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
+      } else {
+        *reinterpret_cast<uint32_t*>(codes + (int64_t)r * (kpad / 2) + c / 2) = (uint32_t)packed;
+      }
+      if ((j % LANES_PER_BLOCK) == 0) scales[(int64_t)r * (kpad / BS) + c / BS] = (uint8_t)sb;
     }
-    uint64_t packed = encode8<FMT>(x, mul, th);
-    if (FMT == FMT_MXFP8) {
-      *reinterpret_cast<uint2*>(codes + r * kpad + c) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
-    } else {
-      *reinterpret_cast<uint32_t*>(codes + r * (kpad / 2) + c / 2) = (uint32_t)packed;
-    }
-    if ((threadIdx.x % LANES_PER_BLOCK) == 0) scales[r * (kpad / BS) + c / BS] = (uint8_t)scale_byte;
   }
 }
 
@@ -169,16 +216,13 @@ constexpr int kColLdsLd = kColTileC + 8;   // padded LDS row (elements), keeps 1
 
 // X [rows, cols] -> codes of X^T: [cols, kpad] with kpad = round_up(rows, 128).
 template <int FMT>
-__global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ src, int64_t rows,
-                                                        int64_t cols, int64_t ld,
-                                                        uint8_t* __restrict__ codes,
-                                                        uint8_t* __restrict__ scales, int64_t kpad,
-                                                        NvTrailer* tr) {
-  constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
+__global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
+                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                        int kpad, NvTrailer* tr) {
   __shared__ __align__(16) uint16_t tile[kColTileR * kColLdsLd];
-  const int64_t tiles_c = (cols + kColTileC - 1) / kColTileC;
-  const int64_t tiles_r = kpad / kColTileR;
-  const int64_t ntiles = tiles_c * tiles_r;
+  const int tiles_c = (cols + kColTileC - 1) / kColTileC;
+  const int tiles_r = kpad / kColTileR;
+  const int ntiles = tiles_c * tiles_r;
   const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
   const int t = threadIdx.x;
   float s_t = 0.0f;
@@ -186,51 +230,52 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
     s_t = nvfp4_tensor_scale(tr->amax_bits);
     if (blockIdx.x == 0 && t == 0) tr->s_t = s_t;
   }
-  for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
-    const int64_t tr_ = tile_id / tiles_c;
-    const int64_t tc = tile_id - tr_ * tiles_c;
-    const int64_t r0 = tr_ * kColTileR, c0 = tc * kColTileC;
+  for (int tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+    const int tr_ = tile_id / tiles_c;
+    const int tc = tile_id - tr_ * tiles_c;
+    const int r0 = tr_ * kColTileR, c0 = tc * kColTileC;
     // stage: 128 rows x 64 cols; thread t loads 8 columns of rows t/8 + 32 p
+    uint4 v[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int lr = t / 8 + 32 * p;
-      const int lc = (t % 8) * 8;
-      const int64_t r = r0 + lr, c = c0 + lc;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      const int r = r0 + t / 8 + 32 * p, c = c0 + (t % 8) * 8;
+      v[p] = make_uint4(0u, 0u, 0u, 0u);
       if (r < rows) {
-        const uint16_t* q = src + r * ld + c;
+        const uint16_t* q = src + (int64_t)r * ld + c;
         if (vec_ok && c + 8 <= cols) {
-          v = *reinterpret_cast<const uint4*>(q);
+          v[p] = load16_stream(q);
         } else {
           uint32_t w[4] = {0u, 0u, 0u, 0u};
           for (int i = 0; i < 8; ++i)
             if (c + i < cols) w[i / 2] |= (uint32_t)q[i] << (16 * (i % 2));
-          v = make_uint4(w[0], w[1], w[2], w[3]);
+          v[p] = make_uint4(w[0], w[1], w[2], w[3]);
         }
       }
-      *reinterpret_cast<uint4*>(&tile[lr * kColLdsLd + lc]) = v;
     }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      *reinterpret_cast<uint4*>(&tile[(t / 8 + 32 * p) * kColLdsLd + (t % 8) * 8]) = v[p];
     __syncthreads();
     // wave w owns tile rows 32w .. 32w+31; lane j owns column j
     const int w = t / 64, j = t % 64;
-    const int64_t oc = c0 + j;                // output row (a column of X)
+    const int oc = c0 + j;                    // output row (a column of X)
     float x[32];
     uint32_t m[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      uint32_t b = tile[(32 * w + i) * kColLdsLd + j];
+      const uint32_t b = tile[(32 * w + i) * kColLdsLd + j];
       x[i] = bf16_to_f32(b);
       m[i / 16] = max(m[i / 16], b & 0x7FFFu);
     }
     if (oc < cols) {
-      const int64_t orow = r0 + 32 * w;       // first element index along the block axis
+      const int orow = r0 + 32 * w;           // first element index along the block axis
       if (FMT == FMT_NVFP4) {
         uint32_t packed[4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          double q = (s_t == 0.0f) ? 0.0 : (double)bf16_to_f32(m[h]) / (6.0 * (double)s_t);
-          uint32_t sb = e4m3_encode_pos_f64(q);
-          Nv4Thresholds th = nvfp4_thresholds(e4m3_value(sb) * (double)s_t);
+          float mul;
+          Nv4Thresholds th;
+          const uint32_t sb = block_scale<FMT>(m[h], s_t, mul, th);
 #pragma unroll
           for (int q2 = 0; q2 < 2; ++q2) {
             uint32_t word = 0;
@@ -238,14 +283,14 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
             for (int i = 0; i < 8; ++i) word |= nvfp4_encode(x[16 * h + 8 * q2 + i], th) << (4 * i);
             packed[2 * h + q2] = word;
           }
-          scales[oc * (kpad / 16) + orow / 16 + h] = (uint8_t)sb;
+          scales[(int64_t)oc * (kpad / 16) + orow / 16 + h] = (uint8_t)sb;
         }
-        *reinterpret_cast<uint4*>(codes + oc * (kpad / 2) + orow / 2) =
+        *reinterpret_cast<uint4*>(codes + (int64_t)oc * (kpad / 2) + orow / 2) =
             make_uint4(packed[0], packed[1], packed[2], packed[3]);
       } else {
-        const uint32_t mm = max(m[0], m[1]);
-        const int e = mx_shared_exp(mm, FMT == FMT_MXFP8 ? 8 : 2);
-        const float mul = pow2_neg(e);
+        float mul = 1.0f;
+        Nv4Thresholds th;
+        const uint32_t sb = block_scale<FMT>(max(m[0], m[1]), s_t, mul, th);
         if (FMT == FMT_MXFP8) {
           uint32_t words[8];
 #pragma unroll
@@ -255,7 +300,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
             for (int i = 0; i < 4; ++i) word |= e4m3_encode(x[4 * q2 + i] * mul) << (8 * i);
             words[q2] = word;
           }
-          uint4* dst = reinterpret_cast<uint4*>(codes + oc * kpad + orow);
+          uint4* dst = reinterpret_cast<uint4*>(codes + (int64_t)oc * kpad + orow);
           dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
           dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
         } else {
@@ -267,10 +312,10 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
             for (int i = 0; i < 8; ++i) word |= e2m1_encode(x[8 * q2 + i] * mul) << (4 * i);
             words[q2] = word;
           }
-          *reinterpret_cast<uint4*>(codes + oc * (kpad / 2) + orow / 2) =
+          *reinterpret_cast<uint4*>(codes + (int64_t)oc * (kpad / 2) + orow / 2) =
               make_uint4(words[0], words[1], words[2], words[3]);
         }
-        scales[oc * (kpad / 32) + orow / 32] = (uint8_t)(e + 127);
+        scales[(int64_t)oc * (kpad / 32) + orow / 32] = (uint8_t)sb;
       }
     }
     __syncthreads();
@@ -279,44 +324,45 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
 
 // ------------------------------------------------------------ launchers
 
-static int grid_for(int64_t work_items, int per_block) {
+static int grid_for(int64_t work_items, int per_block, int cap) {
   int64_t g = (work_items + per_block - 1) / per_block;
   if (g < 1) g = 1;
-  if (g > 65536) g = 65536;
+  if (g > cap) g = cap;
   return (int)g;
 }
 
 hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
                            uint8_t* scales, int fmt, int axis, hipStream_t stream) {
+  // The C ABI bounds every size so that element, group and byte counts fit
+  // in 32 bits (outputs < 2 GiB, input < 2^40 bytes is checked per row).
   const int64_t R = axis == 0 ? rows : cols;        // stored rows
   const int64_t L = axis == 0 ? cols : rows;        // stored length (block axis)
   const int64_t kpad = round_up(L, kAlignK);
   const int bs = fmt == FMT_NVFP4 ? 16 : 32;
+  const int ir = (int)rows, ic = (int)cols, ild = (int)ld, ikp = (int)kpad;
   NvTrailer* tr = nullptr;
   if (fmt == FMT_NVFP4) {
     const int64_t nscale = R * (kpad / bs);
     tr = reinterpret_cast<NvTrailer*>(scales + round_up(nscale, 16));
     nv_trailer_init_kernel<<<1, 64, 0, stream>>>(scales + nscale, (int)(round_up(nscale, 16) - nscale), tr);
-    const int64_t groups = rows * ((cols + 7) / 8);
-    int g = grid_for(groups, 256 * 8);
-    if (g > 2048) g = 2048;
-    amax_kernel<<<g, 256, 0, stream>>>(src, rows, cols, ld, tr);
+    const int gpr = (int)((cols + 7) / 8);
+    amax_kernel<<<grid_for(rows * gpr, 256 * kAmaxUnroll, 512), 256, 0, stream>>>(src, ir, ic, ild, gpr, tr);
   }
   if (axis == 0) {
-    const int64_t groups = R * (kpad / 8);
-    const int g = grid_for(groups, 256 * 2);
+    const int64_t threads = R * (kpad / 8 / kRowGroupsPerThread);
+    const int g = grid_for(threads, 256, 1 << 20);
     switch (fmt) {
-      case FMT_MXFP8: quant_row_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(src, rows, cols, ld, codes, scales, kpad, tr); break;
-      case FMT_MXFP4: quant_row_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, rows, cols, ld, codes, scales, kpad, tr); break;
-      default:        quant_row_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, rows, cols, ld, codes, scales, kpad, tr); break;
+      case FMT_MXFP8: quant_row_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
+      case FMT_MXFP4: quant_row_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
+      default:        quant_row_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
     }
   } else {
     const int64_t ntiles = ((cols + kColTileC - 1) / kColTileC) * (kpad / kColTileR);
-    const int g = grid_for(ntiles, 1);
+    const int g = grid_for(ntiles, 1, 1 << 20);
     switch (fmt) {
-      case FMT_MXFP8: quant_col_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(src, rows, cols, ld, codes, scales, kpad, tr); break;
-      case FMT_MXFP4: quant_col_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, rows, cols, ld, codes, scales, kpad, tr); break;
-      default:        quant_col_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, rows, cols, ld, codes, scales, kpad, tr); break;
+      case FMT_MXFP8: quant_col_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
+      case FMT_MXFP4: quant_col_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
+      default:        quant_col_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
     }
   }
   return hipGetLastError();
