@@ -46,16 +46,19 @@ def parse():
                    choices=["vitl16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack", "vitb16_mxfp8_fwd_stack",
                             "vitl16_nvfp4_fc1fc2_train", "single_mxfp8_256x768x768"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe-mb", type=int, default=0,
+                   help="first run one device-to-device copy of this many MB (a known-size kernel "
+                        "for calibrating memory counters)")
     return p.parse_args()
 
 
 # ------------------------------------------------------------------ workloads
 
 class Op:
-    """One launch of the path: a quantization or a GEMM."""
+    """One launch of the path: a quantization or a GEMM (plan = kernel configuration)."""
 
-    def __init__(self, kind, fn, flops=0.0, nbytes=0.0, label=""):
-        self.kind, self.fn, self.flops, self.nbytes, self.label = kind, fn, flops, nbytes, label
+    def __init__(self, kind, fn, flops=0.0, nbytes=0.0, label="", plan=None):
+        self.kind, self.fn, self.flops, self.nbytes, self.label, self.plan = kind, fn, flops, nbytes, label, plan
 
 
 def build_stack(stack, dev):
@@ -83,7 +86,8 @@ def build_stack(stack, dev):
             ops.append(Op("quant", lambda w=w, qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales),
                           nbytes=qb * w.numel(), label=f"quant_{lin.name}_w"))
             ops.append(Op("gemm", lambda qa=qa, qw=qw, bias=bias, out=out: api.mx_gemm(qa, qw, bias, "bf16", out),
-                          flops=2.0 * stack.m * lin.n * lin.k, label=f"gemm_{lin.name}"))
+                          flops=2.0 * stack.m * lin.n * lin.k, label=f"gemm_{lin.name}",
+                          plan=api.gemm_plan(stack.m, lin.n, lin.k, fmt)))
     return ops
 
 
@@ -117,7 +121,7 @@ def build_train(tp, dev):
     def gemm(name, a, b, bias, m, n, k):
         out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ops.append(Op("gemm", lambda: api.mx_gemm(q[a], q[b], bias, "bf16", out), flops=2.0 * m * n * k,
-                      label=f"gemm_{name}"))
+                      label=f"gemm_{name}", plan=api.gemm_plan(m, n, k, fmt)))
 
     # fc1: fprop X W1^T, dgrad dY1 W1, wgrad dY1^T X
     quant("X_row", X, "row"); quant("W1_row", W1, "row")
@@ -214,6 +218,14 @@ def main():
                   "gemms_per_block": [f"{l.name} {l.n}x{l.k}" for l in wl.linears]}
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20) // 2
+        src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         for op in ops:
@@ -268,9 +280,20 @@ def main():
             e["gbps"] = round(d["bytes"] / (d["ms"] * 1e-3) / 1e9, 1)
         breakdown[lab] = e
 
-    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    # GEMM launches grouped by kernel configuration; the roofline reports the
+    # configuration that takes the most time (the dominant kernel)
+    plans = {}
+    for op, t in zip(ops, per_op):
+        if op.kind != "gemm":
+            continue
+        d = plans.setdefault(op.plan, {"ms": 0.0, "flops": 0.0, "n": 0})
+        d["ms"] += t
+        d["flops"] += op.flops
+        d["n"] += 1
+    dom = max(plans, key=lambda k: plans[k]["ms"])
+    dom_d = plans[dom]
+    achieved = dom_d["flops"] / (dom_d["ms"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[gemm_peak_key]
-    n_gemm = sum(1 for op in ops if op.kind == "gemm")
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
     result = {
         "metric": "block-scaled GEMM TFLOP/s of the whole quantize-then-GEMM step on ViT-L shapes",
@@ -288,17 +311,19 @@ def main():
         "config": config,
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_mx_kernel" if fmt != "nvfp4" else "gemm_nv_kernel",
+            "kernel": dom,
             "achieved": round(achieved, 1),
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": None,
-            "launches_per_step": n_gemm,
-            "avg_launch_us": round(1e3 * gemm_ms / n_gemm, 2),
-            "flops_per_launch_avg": gemm_flops / n_gemm,
+            "launches_per_step": dom_d["n"],
+            "avg_launch_us": round(1e3 * dom_d["ms"] / dom_d["n"], 2),
+            "flops_per_launch_avg": dom_d["flops"] / dom_d["n"],
         },
-        "gemm_only_tflops": round(achieved, 1),
+        "gemm_kernels": {k: {"launches_per_step": d["n"], "avg_launch_us": round(1e3 * d["ms"] / d["n"], 2),
+                             "tflops": round(d["flops"] / (d["ms"] * 1e-3) / 1e12, 1)} for k, d in plans.items()},
+        "gemm_only_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
         "quant": {"gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1), "peak_gbps": PEAK_HBM_GBS,
                   "frac": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                   "ms_per_step": round(quant_ms, 4)},

@@ -7,7 +7,7 @@ from ._lib import LIB_PATH, lib  # noqa: F401
 
 
 def __getattr__(name):
-    if name in ("mx_quantize", "mx_gemm", "Quantized", "codes_bytes", "scales_bytes", "k_pad", "MxError"):
+    if name in ("mx_quantize", "mx_gemm", "Quantized", "codes_bytes", "scales_bytes", "k_pad", "MxError", "gemm_plan"):
         from . import api
         return getattr(api, name)
     raise AttributeError(name)

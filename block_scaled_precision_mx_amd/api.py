@@ -47,6 +47,14 @@ def k_pad(length: int) -> int:
     return lib().mx_k_pad(length)
 
 
+def gemm_plan(M: int, N: int, K: int, fmt: str) -> str:
+    """Kernel configuration mx_gemm launches for these sizes (for profiling)."""
+    name = lib().mx_gemm_plan(M, N, K, FMT[fmt])
+    if name is None:
+        raise ValueError("invalid GEMM sizes or format")
+    return name.decode()
+
+
 def codes_bytes(rows: int, cols: int, fmt: str, axis: str = "row") -> int:
     return lib().mx_codes_bytes(rows, cols, FMT[fmt], AXIS[axis])
 

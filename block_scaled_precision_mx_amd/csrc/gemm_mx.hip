@@ -398,18 +398,27 @@ static double tiling_cost(int64_t M, int64_t N, int bm, int bn) {
   return (double)rounds * bm * bn;
 }
 
+enum MxTile { TILE_128x128 = 0, TILE_192x256 = 1, TILE_256x256 = 2 };
+
+// 256x256 and 192x256 tiles (8 waves of 128x64 / 96x64) are LDS-bound to
+// one workgroup per CU; 128x128 (4 waves of 64x64) fits two per CU and
+// serves problems too small to fill the chip with the large tiles.
+static MxTile choose_tile(int64_t M, int64_t N) {
+  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big < 128) return TILE_128x128;
+  if (tiling_cost(M, N, 192, 256) < tiling_cost(M, N, 256, 256)) return TILE_192x256;
+  return TILE_256x256;
+}
+
 template <int FMT>
 static hipError_t dispatch_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
                               int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
                               hipStream_t stream) {
-  // 256x256 and 192x256 tiles (8 waves of 128x64 / 96x64) are LDS-bound to
-  // one workgroup per CU; 128x128 (4 waves of 64x64) fits two per CU and
-  // serves problems too small to fill the chip with the large tiles.
-  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big < 128) return run_mx<MxCfg<FMT, 128, 128, 2, 2>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-  if (tiling_cost(M, N, 192, 256) < tiling_cost(M, N, 256, 256))
-    return run_mx<MxCfg<FMT, 192, 256, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-  return run_mx<MxCfg<FMT, 256, 256, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+  switch (choose_tile(M, N)) {
+    case TILE_128x128: return run_mx<MxCfg<FMT, 128, 128, 2, 2>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+    case TILE_192x256: return run_mx<MxCfg<FMT, 192, 256, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+    default:           return run_mx<MxCfg<FMT, 256, 256, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+  }
 }
 
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
@@ -417,6 +426,13 @@ hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B,
                           hipStream_t stream) {
   if (fmt == FMT_MXFP8) return dispatch_mx<FMT_MXFP8>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
   return dispatch_mx<FMT_MXFP4>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+}
+
+const char* plan_gemm_mx(int64_t M, int64_t N, int fmt) {
+  static const char* names[2][3] = {
+      {"gemm_mx_kernel<mxfp8, 128x128>", "gemm_mx_kernel<mxfp8, 192x256>", "gemm_mx_kernel<mxfp8, 256x256>"},
+      {"gemm_mx_kernel<mxfp4, 128x128>", "gemm_mx_kernel<mxfp4, 192x256>", "gemm_mx_kernel<mxfp4, 256x256>"}};
+  return names[fmt == FMT_MXFP8 ? 0 : 1][choose_tile(M, N)];
 }
 
 }  // namespace mx

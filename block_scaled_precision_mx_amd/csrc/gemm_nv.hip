@@ -281,6 +281,8 @@ static hipError_t run_nv(const uint8_t* A, const uint8_t* As, const uint8_t* B, 
   return hipGetLastError();
 }
 
+const char* plan_gemm_nvfp4(int64_t, int64_t) { return "gemm_nv_kernel<nvfp4, 128x128>"; }
+
 hipError_t launch_gemm_nvfp4(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
                              int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
                              hipStream_t stream) {

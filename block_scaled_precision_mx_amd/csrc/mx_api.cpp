@@ -120,6 +120,11 @@ mx_status mx_gemm(const void* A, const void* As, const void* B, const void* Bs, 
   return MX_OK;
 }
 
+const char* mx_gemm_plan(int64_t M, int64_t N, int64_t K, mx_fmt fmt) {
+  if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 1) return nullptr;
+  return fmt == MX_FMT_NVFP4 ? mx::plan_gemm_nvfp4(M, N) : mx::plan_gemm_mx(M, N, (int)fmt);
+}
+
 const char* mx_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

@@ -20,4 +20,8 @@ hipError_t launch_gemm_nvfp4(const uint8_t* A, const uint8_t* As, const uint8_t*
                              void* C, int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
                              hipStream_t stream);
 
+// Name of the kernel configuration the launchers above pick for a shape.
+const char* plan_gemm_mx(int64_t M, int64_t N, int fmt);
+const char* plan_gemm_nvfp4(int64_t M, int64_t N);
+
 }  // namespace mx

@@ -108,6 +108,11 @@ mx_status mx_gemm(const void* A, const void* As, const void* B, const void* Bs,
                   void* C, int64_t M, int64_t N, int64_t K, mx_fmt fmt,
                   const void* bias, mx_dtype out_dtype, void* hip_stream);
 
+/* Name of the kernel configuration mx_gemm launches for these sizes and
+ * format (for example "gemm_mx_kernel<mxfp8, 256x256>"), so profiles can be
+ * matched to calls; a static string, or NULL if an argument is invalid. */
+const char* mx_gemm_plan(int64_t M, int64_t N, int64_t K, mx_fmt fmt);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char* mx_last_error(void);
 
