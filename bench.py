@@ -47,8 +47,8 @@ def parse():
                             "vitl16_nvfp4_fc1fc2_train", "single_mxfp8_256x768x768"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe-mb", type=int, default=0,
-                   help="first run one device-to-device copy of this many MB (a known-size kernel "
-                        "for calibrating memory counters)")
+                   help="first run one elementwise bf16 kernel (negation) reading and writing this many "
+                        "MiB: a kernel of known traffic for calibrating memory counters")
     return p.parse_args()
 
 
@@ -144,8 +144,8 @@ def build_train(tp, dev):
 
 def cpu_baseline(workload_name, fmt):
     """The oracle as it stands on a bounded sample of the same workload:
-    the four linears of one block with 1024 of the M token rows (ViT-L
-    shapes) or the fc1 fprop with 1024 rows (training pair); returns GEMM
+    the four linears of one block with 4096 of the M token rows (ViT-L
+    shapes) or the fc1 fprop with 4096 rows (training pair); returns GEMM
     TFLOP/s of quantize + dequantize + float64 GEMM."""
     import numpy as np
     from block_scaled_precision_mx_amd import workloads as W
@@ -157,7 +157,7 @@ def cpu_baseline(workload_name, fmt):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    rows = 1024
+    rows = 4096
     if workload_name.startswith("vitl16_nvfp4"):
         shapes = [("fc1_fprop", W.TRAIN_PAIR.mlp, W.TRAIN_PAIR.hidden, "act")]
         wid = W.TRAIN_PAIR.wid
@@ -223,7 +223,7 @@ def main():
         src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 

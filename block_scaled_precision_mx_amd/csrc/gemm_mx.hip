@@ -21,6 +21,13 @@
 // The B tile is fed as the instruction's first operand, so each lane ends up
 // with runs of 4 consecutive output columns of one output row.
 //
+// Persistent schedule. One workgroup per CU (two for the small tile) walks
+// tiles blockIdx.x, blockIdx.x + gridDim.x, ...; tiles are renumbered so each
+// XCD (own L2) works through a contiguous range, in groups of 8 tile-rows.
+// The copy cursor runs one K-stage ahead of the compute cursor across tile
+// boundaries, so the next tile's first stage is in flight while the current
+// tile finishes and while its epilogue runs.
+//
 // Data movement. A K-stage is 128 bytes of codes per row (128 fp8 / 256 fp4
 // elements); two stages are double-buffered in LDS. Scales travel in chunks
 // of 16 bytes per row (16 blocks, i.e. 512 K elements), double-buffered in
@@ -30,17 +37,23 @@
 // compiler does not stall every LDS read on copies that are still in
 // flight. A stage's 1-KB wave copies cover 8 rows x 128 bytes, the shape the
 // L2 serves fastest. Code rows are XOR-swizzled in 16-byte chunks so the 8
-// lanes of one LDS read cycle hit distinct banks. Each sub-step's fragments
-// are read into registers before the matrix instructions of the previous
-// sub-step are issued. Tiles are renumbered so each XCD (own L2) gets a
-// contiguous range, walked in groups of 8 tile-rows.
+// lanes of one LDS read cycle hit distinct banks. Inside a stage each wave
+// reads the next A fragment (and the next sub-step's B fragments) while the
+// matrix instructions of the current one run.
 //
-// Epilogue: the bias is loaded before the K loop. For bf16 output the tile
-// is converted and written to LDS (16-byte chunks XOR-swizzled by row), then
-// stored as whole rows of 16-byte lanes; fp32 output (or N % 8 != 0) is
-// stored straight from registers.
+// Epilogue. For bf16 output the tile goes through the LDS buffer of the
+// stage just consumed, one wave-row of the tile per pass: bias added,
+// rounded to bf16, written with 16-byte chunks XOR-swizzled by row, then
+// stored as whole rows of 16-byte lanes with range-checked buffer stores
+// (rows and columns outside C are dropped by the buffer's bounds). Every
+// wave issues the same number of stores, so the next tile's first wait lets
+// exactly those stores stay in flight. fp32 output (or N % 8 != 0) is stored
+// straight from registers and drained before the next tile.
 #include "mx_device.h"
 #include "mx_launch.h"
+
+#include <algorithm>
+#include <atomic>
 
 namespace mx {
 
@@ -48,9 +61,10 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_>
 struct MxCfg {
   static constexpr int FMT = FMT_, BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int OCC = OCC_;                            // workgroups per CU (LDS-limited)
   static constexpr int NT = 64 * WAVES_M * WAVES_N, NW = NT / 64;
   static constexpr int RB = 128;                              // code bytes per row per stage
   static constexpr int CH = RB / 16;                          // 16-byte chunks per row
@@ -61,15 +75,22 @@ struct MxCfg {
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int STAGE = (BM + BN) * RB;                 // code bytes per stage
   static constexpr int SCHUNK = (BM + BN) * 16;                // bytes per scale slot
-  static constexpr int LDS = 2 * STAGE + 2 * SCHUNK;
+  static constexpr int BIAS_OFF = 2 * STAGE + 2 * SCHUNK;     // two 1-KB bias slots (tile parity)
+  static constexpr int LDS = BIAS_OFF + 2 * 1024;
   static constexpr int CODE_DMA = STAGE / 1024 / NW;          // 1-KB code copies per wave per stage
   static constexpr int SCALE_COPIES = (BM + BN) / 64;         // 1-KB copies per scale chunk
   static constexpr int SCALE_DMA = (SCALE_COPIES + NW - 1) / NW;  // per wave (some may be idle)
   static constexpr int MFMA_FMT = (FMT == FMT_MXFP8) ? 0 : 4;  // E4M3 / E2M1 operand selector
+  static constexpr int CPR = BN / 8;                          // 16-byte bf16 chunks per C row
+  static constexpr int EPI_STORES = WM * CPR / NT;            // stores per thread per epilogue pass
+  static constexpr int EPI_TOTAL = WAVES_M * EPI_STORES;      // stores per thread per tile
   static_assert(CODE_DMA * 1024 * NW == STAGE, "code copies must split evenly over waves");
   static_assert(BM % 64 == 0 && BN % 64 == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
-  static_assert(LDS <= 160 * 1024, "LDS");
-  static_assert(BM * BN * 2 <= LDS, "the bf16 C tile must fit in LDS");
+  static_assert(LDS * OCC <= 160 * 1024, "LDS");
+  static_assert(WM * BN * 2 <= STAGE, "one wave-row of the bf16 C tile must fit in a stage buffer");
+  static_assert(EPI_STORES * NT == WM * CPR, "epilogue stores must split evenly over threads");
+  static_assert(EPI_TOTAL <= 48, "stores left in flight must stay within the vmcnt range");
+  static_assert(BN * 2 <= 1024, "a tile's bias must fit one bias slot");
 };
 
 // Row r keeps 16-byte chunk c of a 128-byte row at position c ^ (r & 7).
@@ -93,16 +114,26 @@ __device__ __forceinline__ void dma16(v4u rs, uint32_t lds_addr, uint32_t voff, 
                : "=&s"(saved) : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
 }
 
-// Wait until every vector memory operation of this wave has completed.
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector memory operations of this wave are in flight
+// (they complete in issue order). Issued through the builtin so the
+// compiler's own wait bookkeeping sees it too.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
-// Tile coordinates of this workgroup: XCD-contiguous renumbering, then
+// Workgroup barrier after this wave's LDS operations have completed. Global
+// stores still in flight are deliberately not waited for.
+__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Coordinates of tile t: XCD-contiguous renumbering (tile t runs on XCD
+// t % 8 because the grid is a multiple of 8 or covers every tile once), then
 // groups of 8 tile-rows walked column by column.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int nwg = tiles_m * tiles_n;
-  const int i = blockIdx.x;
   const int q = nwg / 8, r = nwg % 8;
-  const int xcd = i % 8, local = i / 8;
+  const int xcd = t % 8, local = t / 8;
   const int wg = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
   constexpr int GROUP = 8;
   const int group_size = GROUP * tiles_n;
@@ -114,56 +145,83 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_group / gm;
 }
 
-// One sub-step's operands for one wave: FM A fragments, FN B fragments and
-// their scales, shifted so that this lane's scale byte is byte 0.
+// fp8: A or B fragment of sub-step t for tile row `row` of a stage: 16-byte
+// chunks 4t+g and 4t+2+g (K 16g.. and 32+16g.. of the sub-step).
+// fp4: chunk 2t+g (K 32g.. of the sub-step) in the first 4 registers.
 template <class Cfg>
-struct Frags {
-  v8i a[Cfg::FM], b[Cfg::FN];
-  int sa[Cfg::FM], sb[Cfg::FN];
-};
-
-// Sub-step t of the stage held at `st` (codes) whose scales are in the
-// chunk at `sc`, chunk-relative stage index `sj`. fp8: lane chunks 4t+g and
-// 4t+2+g (K 16g.. and 32+16g.. of the sub-step); fp4: chunk 2t+g. This
-// lane's scale byte is block (KS/32) sj + 2t + g of the row's 16-byte chunk.
-template <class Cfg>
-__device__ __forceinline__ void load_frags(Frags<Cfg>& fr, const uint8_t* st, const uint8_t* sc, int t, int sj,
-                                           int g, int ra, int rb) {
-  constexpr int RB = Cfg::RB;
-  const int blk = (Cfg::KS / 32) * sj + 2 * t + g;
-  const int sdw = blk >> 2, sh = 8 * (blk & 3);
-#pragma unroll
-  for (int f = 0; f < Cfg::FN; ++f) {
-    const int r = rb + 32 * f;
-    const uint8_t* row = st + (Cfg::BM + r) * RB;
-    fr.sb[f] = (int)(*reinterpret_cast<const uint32_t*>(sc + (Cfg::BM + r) * 16 + 4 * sdw) >> sh);
-    if (Cfg::FMT == FMT_MXFP8) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(row + swz(r, 4 * t + g) * 16);
-      const uint4 hi = *reinterpret_cast<const uint4*>(row + swz(r, 4 * t + 2 + g) * 16);
-      fr.b[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    } else {
-      const uint4 lo = *reinterpret_cast<const uint4*>(row + swz(r, 2 * t + g) * 16);
-      fr.b[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
-    }
+__device__ __forceinline__ v8i load_frag(const uint8_t* st, int row, int t, int g) {
+  const uint8_t* p = st + row * Cfg::RB;
+  if (Cfg::FMT == FMT_MXFP8) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(p + swz(row, 4 * t + g) * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(p + swz(row, 4 * t + 2 + g) * 16);
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  } else {
+    const uint4 lo = *reinterpret_cast<const uint4*>(p + swz(row, 2 * t + g) * 16);
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
   }
+}
+
+// Scale bytes of one stage for tile row `row`, shifted right by 8g so that
+// the block sub-step t needs from this lane (2t + g within the stage) sits
+// in byte 2t (fp8: one word, 4 blocks) or byte 2(t%2) of word t/2 (fp4: 8
+// blocks).
+template <class Cfg>
+__device__ __forceinline__ uint2 load_stage_scales(const uint8_t* sc, int row, int sj, int g) {
+  if (Cfg::FMT == FMT_MXFP8) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(sc + row * 16 + 4 * sj);
+    return make_uint2(w >> (8 * g), 0u);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(sc + row * 16 + 8 * sj);
+    return make_uint2(w.x >> (8 * g), w.y >> (8 * g));
+  }
+}
+
+template <class Cfg>
+__device__ __forceinline__ int substep_scale(uint2 s, int t) {
+  const uint32_t w = (Cfg::FMT == FMT_MXFP8 || t < 2) ? s.x : s.y;
+  return (int)(w >> (16 * (t & 1)));
+}
+
+// All sub-steps of one stage for one wave.
+template <class Cfg>
+__device__ __forceinline__ void mma_stage(v16f (&acc)[Cfg::FM][Cfg::FN], const uint8_t* st, const uint8_t* sc,
+                                          int sj, int g, int ra, int rb) {
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, SUB = Cfg::SUB;
+  uint2 sa[FM], sb[FN];
 #pragma unroll
-  for (int f = 0; f < Cfg::FM; ++f) {
-    const int r = ra + 32 * f;
-    const uint8_t* row = st + r * RB;
-    fr.sa[f] = (int)(*reinterpret_cast<const uint32_t*>(sc + r * 16 + 4 * sdw) >> sh);
-    if (Cfg::FMT == FMT_MXFP8) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(row + swz(r, 4 * t + g) * 16);
-      const uint4 hi = *reinterpret_cast<const uint4*>(row + swz(r, 4 * t + 2 + g) * 16);
-      fr.a[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    } else {
-      const uint4 lo = *reinterpret_cast<const uint4*>(row + swz(r, 2 * t + g) * 16);
-      fr.a[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+  for (int f = 0; f < FN; ++f) sb[f] = load_stage_scales<Cfg>(sc, Cfg::BM + rb + 32 * f, sj, g);
+#pragma unroll
+  for (int f = 0; f < FM; ++f) sa[f] = load_stage_scales<Cfg>(sc, ra + 32 * f, sj, g);
+  v8i b_cur[FN], b_nxt[FN], a_cur, a_nxt;
+#pragma unroll
+  for (int f = 0; f < FN; ++f) b_cur[f] = load_frag<Cfg>(st, Cfg::BM + rb + 32 * f, 0, g);
+  a_cur = load_frag<Cfg>(st, ra, 0, g);
+#pragma unroll
+  for (int t = 0; t < SUB; ++t) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (fm + 1 < FM) a_nxt = load_frag<Cfg>(st, ra + 32 * (fm + 1), t, g);
+      else if (t + 1 < SUB) a_nxt = load_frag<Cfg>(st, ra, t + 1, g);
+      if (fm == 0 && t + 1 < SUB) {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) b_nxt[f] = load_frag<Cfg>(st, Cfg::BM + rb + 32 * f, t + 1, g);
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            b_cur[fn], a_cur, acc[fm][fn], Cfg::MFMA_FMT, Cfg::MFMA_FMT, 0, substep_scale<Cfg>(sb[fn], t), 0,
+            substep_scale<Cfg>(sa[fm], t));
+      if (fm + 1 < FM || t + 1 < SUB) a_cur = a_nxt;
+    }
+    if (t + 1 < SUB) {
+#pragma unroll
+      for (int f = 0; f < FN; ++f) b_cur[f] = b_nxt[f];
     }
   }
 }
 
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NT) void gemm_mx_kernel(const uint8_t* __restrict__ A,
+__global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_t* __restrict__ A,
                                                           const uint8_t* __restrict__ As,
                                                           const uint8_t* __restrict__ B,
                                                           const uint8_t* __restrict__ Bs, void* __restrict__ C,
@@ -171,211 +229,252 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_mx_kernel(const uint8_t* __restr
                                                           const uint16_t* __restrict__ bias, int out_f32,
                                                           int tiles_m, int tiles_n) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
-  constexpr int RB = Cfg::RB, CH = Cfg::CH, NW = Cfg::NW;
+  constexpr int RB = Cfg::RB, CH = Cfg::CH, NW = Cfg::NW, CPR = Cfg::CPR;
   __shared__ __align__(16) uint8_t lds[Cfg::LDS];
 
-  int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int tiles = tiles_m * tiles_n;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int row_bytes = (Cfg::FMT == FMT_MXFP8) ? kpad : kpad / 2;
   const int srow = kpad / 32;               // scale bytes per row
-  // stages; with fp4 a stage holds 256 elements while K_pad is a multiple
-  // of 128, so the last stage may hold only its first 64 bytes
+  // stages per tile; with fp4 a stage holds 256 elements while K_pad is a
+  // multiple of 128, so the last stage may hold only its first 64 bytes
   const int nk = (kpad + Cfg::KS - 1) / Cfg::KS;
   const int g = lane >> 5, r32 = lane & 31;
+  // bf16 output goes through LDS and 32-bit buffer offsets when C is below
+  // 2 GiB; anything else is stored from registers with 64-bit addresses
+  const bool staged = !out_f32 && (N & 7) == 0 && (int64_t)M * N < ((int64_t)1 << 30);
 
   const v4u a_rs = buffer_rsrc(A, (uint32_t)(M * row_bytes));
   const v4u b_rs = buffer_rsrc(B, (uint32_t)(N * row_bytes));
   const v4u as_rs = buffer_rsrc(As, (uint32_t)(M * srow));
   const v4u bs_rs = buffer_rsrc(Bs, (uint32_t)(N * srow));
+  const __amdgpu_buffer_rsrc_t c_rs =
+      __builtin_amdgcn_make_buffer_rsrc(C, (short)0, staged ? M * N * 2 : 0, 0x00020000);
+  // a 16-byte aligned bias with N % 8 == 0 is copied to LDS with each tile's
+  // first stage; otherwise the epilogue reads it from global memory
+  const bool bias_dma = bias != nullptr && (N & 7) == 0 && (reinterpret_cast<uintptr_t>(bias) & 15) == 0;
+  const v4u bias_rs = buffer_rsrc(bias, bias_dma ? (uint32_t)(N * 2) : 0u);
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   const uint32_t sc_base = lds_base + 2 * Cfg::STAGE;
 
-  // Code copy j of this wave fills the stage's 1-KB block J = j NW + wave,
-  // i.e. 16-byte chunks 64 J + lane: A rows first (CH chunks per row), then B.
-  uint32_t code_voff[Cfg::CODE_DMA];
-  int code_byte[Cfg::CODE_DMA];             // byte of the stage this lane copies
-  bool code_is_a[Cfg::CODE_DMA];
-#pragma unroll
-  for (int j = 0; j < Cfg::CODE_DMA; ++j) {
-    const int J = j * NW + wave;
-    const int P = J * 64 + lane;
-    const bool isa = P < BM * CH;
-    const int Pr = isa ? P : P - BM * CH;
-    const int r = Pr / CH, p = Pr % CH;
-    code_is_a[j] = J * 64 < BM * CH;           // uniform per copy
-    code_byte[j] = swz(r, p) * 16;
-    code_voff[j] = (uint32_t)(((isa ? m0 : n0) + r) * row_bytes + code_byte[j]);
-  }
+  // Code copy j of this wave fills the stage's 1-KB block J = j NW + wave:
+  // rows 8 J .. 8 J + 7 of [A rows, B rows] (A iff 8 J < BM, uniform per
+  // copy), lane l taking row 8 J + l / 8 and logical chunk l % 8, which lands
+  // at swizzled position (l % 8) ^ (row % 8) = (l % 8) ^ (l / 8).
+  const uint32_t code_byte = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  // (offsets of rows past the operand may wrap; they only feed rows and
+  // columns of C that are never stored, and every read is range-checked)
+  const uint32_t code_lane = (uint32_t)(lane >> 3) * (uint32_t)row_bytes + code_byte;
   // Scale copy j of this wave fills rows 64 J .. 64 J + 63 of [A rows, B rows]
   // with 16 bytes each (copies J >= SCALE_COPIES are skipped).
-  uint32_t scale_voff[Cfg::SCALE_DMA];
-  bool scale_is_a[Cfg::SCALE_DMA];
-#pragma unroll
-  for (int j = 0; j < Cfg::SCALE_DMA; ++j) {
-    const int J = j * NW + wave;
-    const int row = J * 64 + lane;
-    scale_is_a[j] = J * 64 < BM;
-    const int r = scale_is_a[j] ? row : row - BM;
-    scale_voff[j] = (uint32_t)(((scale_is_a[j] ? m0 : n0) + r) * srow);
-  }
+  const uint32_t scale_lane = (uint32_t)lane * (uint32_t)srow;
 
-  auto issue_stage = [&](int ks) {
-    if (ks % Cfg::SPC == 0) {               // first stage of a scale chunk: bring the chunk too
-      const int c = ks / Cfg::SPC;
-      const uint32_t dst = sc_base + (uint32_t)((c & 1) * Cfg::SCHUNK);
+  // copy cursor: tile lt (rows m0l / n0l), its stage lks; lgs / lgc count
+  // stages / scale chunks issued so far (they pick the LDS buffer and slot)
+  int lt = blockIdx.x, lks = 0, lgs = 0, lgc = 0, ltc = 0, m0l = 0, n0l = 0;
+  auto set_copy_tile = [&](int t) {
+    int tm, tn;
+    tile_coords(t, tiles_m, tiles_n, tm, tn);
+    m0l = tm * BM;
+    n0l = tn * BN;
+  };
+  auto issue_next = [&]() {
+    if (lks == 0 && bias_dma && wave == 0) {  // the tile's bias, into bias slot ltc & 1
+      const uint32_t voff = lane < BN / 8 ? (uint32_t)((n0l + 8 * lane) * 2) : 0x80000000u;
+      dma16(bias_rs, lds_base + (uint32_t)(Cfg::BIAS_OFF + (ltc & 1) * 1024), voff, 0u);
+    }
+    if (lks % Cfg::SPC == 0) {               // first stage of a scale chunk: bring the chunk too
+      const uint32_t dst = sc_base + (uint32_t)((lgc & 1) * Cfg::SCHUNK);
+      const uint32_t soff = (uint32_t)(16 * (lks / Cfg::SPC));
 #pragma unroll
       for (int j = 0; j < Cfg::SCALE_DMA; ++j) {
         const int J = j * NW + wave;
-        if (J < Cfg::SCALE_COPIES) dma16(scale_is_a[j] ? as_rs : bs_rs, dst + (uint32_t)(J * 1024), scale_voff[j],
-                                         (uint32_t)(16 * c));
+        if (J < Cfg::SCALE_COPIES) {
+          const bool isa = J * 64 < BM;
+          const int row0 = (isa ? m0l : n0l - BM) + J * 64;
+          dma16(isa ? as_rs : bs_rs, dst + (uint32_t)(J * 1024), scale_lane + (uint32_t)row0 * (uint32_t)srow, soff);
+        }
       }
+      ++lgc;
     }
-    const uint32_t st = lds_base + (uint32_t)((ks & 1) * Cfg::STAGE);
-    const int rem = row_bytes - ks * RB;    // bytes of each row left from this stage on
+    const uint32_t st = lds_base + (uint32_t)((lgs & 1) * Cfg::STAGE);
+    // bytes past the end of the row (last fp4 stage) read as zero: offset
+    // beyond the buffer
+    const bool in_row = code_byte < (uint32_t)(row_bytes - lks * RB);
 #pragma unroll
     for (int j = 0; j < Cfg::CODE_DMA; ++j) {
-      // bytes past the end of the row read as zero (offset beyond the buffer)
-      const uint32_t voff = code_byte[j] < rem ? code_voff[j] : 0x80000000u;
-      dma16(code_is_a[j] ? a_rs : b_rs, st + (uint32_t)((j * NW + wave) * 1024), voff, (uint32_t)(ks * RB));
+      const int J = j * NW + wave;
+      const bool isa = J * 8 < BM;
+      const int row0 = (isa ? m0l : n0l - BM) + J * 8;
+      const uint32_t voff = in_row ? code_lane + (uint32_t)row0 * (uint32_t)row_bytes : 0x80000000u;
+      dma16(isa ? a_rs : b_rs, st + (uint32_t)(J * 1024), voff, (uint32_t)(lks * RB));
+    }
+    ++lgs;
+    if (++lks == nk) {
+      lks = 0;
+      ++ltc;
+      lt += gridDim.x;
+      if (lt < tiles) set_copy_tile(lt);
     }
   };
 
   const int ra = wm * WM + r32, rb = wn * WN + r32;     // this lane's fragment-0 rows in the tile
 
-  // bias of this lane's output columns, loaded once (consumed after the loop)
-  uint2 bias_v[FN][4];
+  set_copy_tile(lt);
+  issue_next();
+  int gs = 0, gc = 0, ctc = 0;              // compute cursor: stages / scale chunks / tiles consumed
+
+  for (int ct = blockIdx.x; ct < tiles; ct += gridDim.x) {
+    int tm, tn;
+    tile_coords(ct, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    v16f acc[FM][FN];
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = n0 + wn * WN + 32 * fn + 8 * q + 4 * g;
-      bias_v[fn][q] = make_uint2(0u, 0u);
-      if (bias) {
-        if (((N & 3) == 0) && n + 3 < N && (reinterpret_cast<uintptr_t>(bias) & 7) == 0) {
-          bias_v[fn][q] = *reinterpret_cast<const uint2*>(bias + n);
-        } else {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (n + v < N) w[v] = bias[n + v];
-          bias_v[fn][q] = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
-        }
-      }
+      for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
+    int slot = 0;
+
+    for (int ks = 0; ks < nk; ++ks) {
+      // this stage's copies are done; after the previous tile's epilogue its
+      // EPI_TOTAL stores (issued after them) may still be in flight
+      if (ks == 0 && ctc > 0) wait_vm<Cfg::EPI_TOTAL>();
+      else wait_vm<0>();
+      block_sync();                         // everyone's copies are visible, and everyone is done
+                                            // with the buffers the next copies overwrite
+      if (lt < tiles) issue_next();
+      if (ks % Cfg::SPC == 0) slot = gc++ & 1;
+      mma_stage<Cfg>(acc, lds + (gs & 1) * Cfg::STAGE, lds + 2 * Cfg::STAGE + slot * Cfg::SCHUNK, ks % Cfg::SPC, g,
+                     ra, rb);
+      ++gs;
     }
 
-  v16f acc[FM][FN];
+    // epilogue: register 4q + v of acc[fm][fn] is C[m][n + v] with
+    // m = m0 + wm WM + 32 fm + r32, n = n0 + wn WN + 32 fn + 8 q + 4 g.
+    // The tile's bias sits in bias slot ctc & 1 (copied with the tile's first
+    // stage); without that copy it is written here (zeros if there is no
+    // bias), ordered before its readers by the next barrier.
+    uint8_t* lds_bias = lds + Cfg::BIAS_OFF + (ctc & 1) * 1024;
+    if (!bias_dma) {
+      for (int i = (int)threadIdx.x; i < BN; i += Cfg::NT)
+        reinterpret_cast<uint16_t*>(lds_bias)[i] = (bias != nullptr && n0 + i < N) ? bias[n0 + i] : (uint16_t)0;
+    }
+    auto bias4 = [&](int nl) -> uint2 { return *reinterpret_cast<const uint2*>(lds_bias + 2 * nl); };
+    if (staged) {
+      uint8_t* stg = lds + ((gs - 1) & 1) * Cfg::STAGE;   // buffer of the stage just consumed
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+      for (int h = 0; h < Cfg::WAVES_M; ++h) {
+        block_sync();                        // previous readers of the buffer are done
+        if (wm == h) {
+          uint2 bb[FN][4];                   // bias of this lane's columns, read in one batch
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
-
-  issue_stage(0);
-  for (int ks = 0; ks < nk; ++ks) {
-    wait_vm_all();                          // this wave's copies of stage ks (and its scale chunk)
-    __syncthreads();                        // everyone's copies are visible, and everyone is done
-                                            // with the buffers the next copies overwrite
-    if (ks + 1 < nk) issue_stage(ks + 1);
-
-    const uint8_t* st = lds + (ks & 1) * Cfg::STAGE;
-    const uint8_t* sc = lds + 2 * Cfg::STAGE + ((ks / Cfg::SPC) & 1) * Cfg::SCHUNK;
-    const int sj = ks % Cfg::SPC;
-    Frags<Cfg> cur_f, nxt_f;
-    load_frags<Cfg>(cur_f, st, sc, 0, sj, g, ra, rb);
+          for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-    for (int t = 0; t < Cfg::SUB; ++t) {
-      if (t + 1 < Cfg::SUB) load_frags<Cfg>(nxt_f, st, sc, t + 1, sj, g, ra, rb);
+            for (int q = 0; q < 4; ++q) bb[fn][q] = bias4(wn * WN + 32 * fn + 8 * q + 4 * g);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+          for (int fm = 0; fm < FM; ++fm) {
+            const int lr = 32 * fm + r32;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int nl = wn * WN + 32 * fn + 8 * q + 4 * g;
+                const float v0 = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb[fn][q].x & 0xFFFFu);
+                const float v1 = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb[fn][q].x >> 16);
+                const float v2 = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb[fn][q].y & 0xFFFFu);
+                const float v3 = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb[fn][q].y >> 16);
+                const int chunk = (nl >> 3) ^ (lr & (CPR - 1));
+                *reinterpret_cast<uint2*>(stg + lr * (BN * 2) + chunk * 16 + (nl & 7) * 2) =
+                    make_uint2(f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16),
+                               f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16));
+              }
+          }
+        }
+        block_sync();
+        // LDS reads in batches of up to 4, each batch ahead of its stores
+        constexpr int E = Cfg::EPI_STORES;
+        constexpr int BATCH = E % 4 == 0 ? 4 : E % 3 == 0 ? 3 : E % 2 == 0 ? 2 : 1;
+        static_assert(Cfg::EPI_STORES % BATCH == 0, "store batches");
+#pragma unroll
+        for (int j0 = 0; j0 < Cfg::EPI_STORES; j0 += BATCH) {
+          uint4 w[BATCH];
+#pragma unroll
+          for (int j = 0; j < BATCH; ++j) {
+            const int id = (int)threadIdx.x + (j0 + j) * Cfg::NT;
+            const int row = id / CPR, c = id % CPR;
+            w[j] = *reinterpret_cast<const uint4*>(stg + row * (BN * 2) + ((c ^ (row & (CPR - 1))) * 16));
+          }
+#pragma unroll
+          for (int j = 0; j < BATCH; ++j) {
+            const int id = (int)threadIdx.x + (j0 + j) * Cfg::NT;
+            const int row = id / CPR, c = id % CPR;
+            const int m = m0 + h * WM + row, n = n0 + 8 * c;
+            const int off = (m < M && n < N) ? (m * N + n) * 2 : (int)0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b128(v4u{w[j].x, w[j].y, w[j].z, w[j].w}, c_rs, off, 0, 0);
+          }
+        }
+      }
+    } else {
+      block_sync();
+      const bool vec = ((N & 3) == 0);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int m = m0 + wm * WM + 32 * fm + r32;
+        if (m >= M) continue;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur_f.b[fn], cur_f.a[fm], acc[fm][fn],
-                                                                        Cfg::MFMA_FMT, Cfg::MFMA_FMT, 0, cur_f.sb[fn],
-                                                                        0, cur_f.sa[fm]);
-      if (t + 1 < Cfg::SUB) cur_f = nxt_f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn * WN + 32 * fn + 8 * q + 4 * g;
+            if (n >= N) continue;
+            const uint2 bb = bias4(n - n0);
+            float v[4];
+            v[0] = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb.x & 0xFFFFu);
+            v[1] = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb.x >> 16);
+            v[2] = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb.y & 0xFFFFu);
+            v[3] = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb.y >> 16);
+            const int64_t off = (int64_t)m * N + n;
+            if (out_f32) {
+              float* c = reinterpret_cast<float*>(C) + off;
+              if (vec && n + 3 < N) {
+                *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
+              } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  if (n + j < N) c[j] = v[j];
+              }
+            } else {
+              uint16_t* c = reinterpret_cast<uint16_t*>(C) + off;
+              if (vec && n + 3 < N) {
+                *reinterpret_cast<uint2*>(c) = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                                          f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+              } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  if (n + j < N) c[j] = (uint16_t)f32_to_bf16_rne(v[j]);
+              }
+            }
+          }
+      }
+      wait_vm<0>();                          // nothing but the next stage's copies stays in flight
     }
+    ++ctc;
   }
+}
 
-  // epilogue: register 4q + v of acc[fm][fn] is C[m][n + v] with
-  // m = m0 + wm WM + 32 fm + r32, n = n0 + wn WN + 32 fn + 8 q + 4 g.
-  if (!out_f32 && (N & 7) == 0) {
-    constexpr int CPR = BN / 8;                          // 16-byte chunks per tile row
-    __syncthreads();                                     // every wave is done reading the last stage
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int ml = wm * WM + 32 * fm + r32;
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int nl = wn * WN + 32 * fn + 8 * q + 4 * g;
-          const uint2 bb = bias_v[fn][q];
-          const float v0 = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb.x & 0xFFFFu);
-          const float v1 = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb.x >> 16);
-          const float v2 = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb.y & 0xFFFFu);
-          const float v3 = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb.y >> 16);
-          const int chunk = (nl >> 3) ^ (ml & (CPR - 1));
-          *reinterpret_cast<uint2*>(lds + ml * (BN * 2) + chunk * 16 + (nl & 7) * 2) =
-              make_uint2(f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16),
-                         f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16));
-        }
-    }
-    __syncthreads();
-    constexpr int TOTAL = BM * CPR;
-#pragma unroll 4
-    for (int id = threadIdx.x; id < TOTAL; id += Cfg::NT) {
-      const int row = id / CPR, c = id % CPR;
-      const int m = m0 + row, n = n0 + 8 * c;
-      if (m < M && n < N) {
-        const uint4 w = *reinterpret_cast<const uint4*>(lds + row * (BN * 2) + ((c ^ (row & (CPR - 1))) * 16));
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(C) + (int64_t)m * N + n) = w;
-      }
-    }
-    return;
-  }
-  const bool vec = ((N & 3) == 0);
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int m = m0 + wm * WM + 32 * fm + r32;
-    if (m >= M) continue;
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WN + 32 * fn + 8 * q + 4 * g;
-        if (n >= N) continue;
-        const uint2 bb = bias_v[fn][q];
-        float v[4];
-        v[0] = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb.x & 0xFFFFu);
-        v[1] = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb.x >> 16);
-        v[2] = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb.y & 0xFFFFu);
-        v[3] = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb.y >> 16);
-        const int64_t off = (int64_t)m * N + n;
-        if (out_f32) {
-          float* c = reinterpret_cast<float*>(C) + off;
-          if (vec && n + 3 < N) {
-            *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (n + j < N) c[j] = v[j];
-          }
-        } else {
-          uint16_t* c = reinterpret_cast<uint16_t*>(C) + off;
-          if (vec && n + 3 < N) {
-            *reinterpret_cast<uint2*>(c) = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                                      f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (n + j < N) c[j] = (uint16_t)f32_to_bf16_rne(v[j]);
-          }
-        }
-      }
-  }
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 template <class Cfg>
@@ -384,8 +483,14 @@ static hipError_t run_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, 
   const int64_t kpad = round_up(K, kAlignK);
   const int tiles_m = (int)((M + Cfg::BM - 1) / Cfg::BM);
   const int tiles_n = (int)((N + Cfg::BN - 1) / Cfg::BN);
-  gemm_mx_kernel<Cfg><<<tiles_m * tiles_n, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, bias,
-                                                                  out_f32, tiles_m, tiles_n);
+  const int tiles = tiles_m * tiles_n;
+  // persistent grid: one slot per resident workgroup, a multiple of 8 so a
+  // workgroup's tiles all map to its own XCD; smaller problems get one
+  // workgroup per tile
+  const int slots = std::max(8, (Cfg::OCC * cu_count()) / 8 * 8);
+  const int grid = tiles <= slots ? tiles : slots;
+  gemm_mx_kernel<Cfg><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, bias, out_f32,
+                                                    tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -415,9 +520,12 @@ static hipError_t dispatch_mx(const uint8_t* A, const uint8_t* As, const uint8_t
                               int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
                               hipStream_t stream) {
   switch (choose_tile(M, N)) {
-    case TILE_128x128: return run_mx<MxCfg<FMT, 128, 128, 2, 2>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-    case TILE_192x256: return run_mx<MxCfg<FMT, 192, 256, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-    default:           return run_mx<MxCfg<FMT, 256, 256, 2, 4>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+    case TILE_128x128:
+      return run_mx<MxCfg<FMT, 128, 128, 2, 2, 2>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+    case TILE_192x256:
+      return run_mx<MxCfg<FMT, 192, 256, 2, 4, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+    default:
+      return run_mx<MxCfg<FMT, 256, 256, 2, 4, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
   }
 }
 

@@ -170,3 +170,42 @@ def test_gemm_nvfp4_training_full_size(which):
         dy1 = W.np_normal((tp.m, tp.mlp), W.seed(tp.wid, 0, tp.DY1), W.GRAD_STD)
         x = W.np_activation((tp.m, tp.hidden), W.seed(tp.wid, 0, tp.X))
         sampled_check(dy1, x, "nvfp4", None, "col", "col")
+
+
+@pytest.mark.parametrize("fmt,k", [("mxfp8", 128), ("mxfp8", 384), ("mxfp4", 384), ("mxfp4", 640)])
+def test_gemm_many_tiles_full(fmt, k):
+    """More output tiles than resident workgroups (ragged M), every output
+    checked: workgroups walk several tiles with the next tile's first K-stage
+    in flight across the boundary and the previous tile's stores pending.
+    K = 128 (fp8) is a single stage per tile; K = 384 / 640 (fp4) end on a
+    half stage."""
+    m, n = 4160, 4096
+    a = W.np_activation((m, k), seed=91 + k)
+    b = W.np_normal((n, k), seed=92 + k, std=W.W_STD)
+    bias = W.np_normal((n,), seed=93, std=W.BIAS_STD)
+    log(f"gemm many tiles plan={api.gemm_plan(m, n, k, fmt)}")
+    check_full(a, b, fmt, bias, "bf16")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_bias_2byte_aligned(fmt):
+    """A bias pointer that is only 2-byte aligned (a view at element offset 1)
+    takes the kernel's element-wise bias path; the result must not change."""
+    m, n, k = 520, 1024, 256
+    a = W.np_activation((m, k), seed=31)
+    b = W.np_normal((n, k), seed=32, std=W.W_STD)
+    bias = W.np_normal((n,), seed=33, std=W.BIAS_STD)
+    qa = api.mx_quantize(to_device_bf16(a), fmt, "row")
+    qb = api.mx_quantize(to_device_bf16(b), fmt, "row")
+    padded = np.zeros(n + 1, dtype=np.uint16)
+    padded[1:] = bias
+    dev_bias = to_device_bf16(padded.reshape(1, -1)).reshape(-1)
+    aligned = dev_bias[1:].clone()
+    offset = dev_bias[1:]
+    assert offset.data_ptr() % 16 == 2
+    log(f"gemm bias alignment fmt={fmt}")
+    got_offset = f64_of(api.mx_gemm(qa, qb, offset, "bf16"))
+    got_aligned = f64_of(api.mx_gemm(qa, qb, aligned, "bf16"))
+    assert np.array_equal(got_offset, got_aligned)
+    c, s = G.gemm_ref(Q.quantize(a, fmt), Q.quantize(b, fmt), bias)
+    assert G.accept(got_offset, c, s, "bf16").all()
