@@ -143,11 +143,11 @@ def build_train(tp, dev):
 # ------------------------------------------------------------------ CPU oracle
 
 def cpu_baseline(workload_name, fmt):
-    """The oracle as it stands on a bounded sample of the same workload:
-    the four linears of one block with 4096 of the M token rows (ViT-L
-    shapes) or the fc1 fprop with 4096 rows (training pair); returns GEMM
-    TFLOP/s of quantize + dequantize + float64 GEMM."""
-    import numpy as np
+    """The oracle as it stands on a bounded sample of the same workload: the
+    four linears of one ViT block at full M (one of the stack's blocks), or
+    the fc1 fprop GEMM of the training pair at full M; returns GEMM TFLOP/s of
+    quantize + dequantize + float64 GEMM."""
+    import numpy as np  # noqa: F401
     from block_scaled_precision_mx_amd import workloads as W
     from oracle import gemm as G
     from oracle import quantize as Q
@@ -157,12 +157,13 @@ def cpu_baseline(workload_name, fmt):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    rows = 4096
     if workload_name.startswith("vitl16_nvfp4"):
+        rows = W.TRAIN_PAIR.m
         shapes = [("fc1_fprop", W.TRAIN_PAIR.mlp, W.TRAIN_PAIR.hidden, "act")]
         wid = W.TRAIN_PAIR.wid
     else:
         stack = W.STACKS[workload_name]
+        rows = stack.m
         shapes = [(l.name, l.n, l.k, l.a_kind) for l in stack.linears]
         wid = stack.wid
     gen = []
@@ -178,10 +179,51 @@ def cpu_baseline(workload_name, fmt):
         G.gemm_ref(qa, qw, b)
         flops += 2.0 * rows * n * k
     dt = time.perf_counter() - t0
-    sample = f"{len(gen)} GEMM(s) of one block, {rows} token rows each: " + ", ".join(
+    sample = f"{len(gen)} quantize+GEMM(s) of one block at full M: " + ", ".join(
         f"{rows}x{n}x{k}" for _, _, _, n, k in gen)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": sample, "seconds": round(dt, 3)}
+
+
+# ------------------------------------------------------------------ traffic
+
+KERNEL_SOURCES = {"gemm_mx_kernel": "block_scaled_precision_mx_amd/csrc/gemm_mx.hip",
+                  "gemm_nv_kernel": "block_scaled_precision_mx_amd/csrc/gemm_nv.hip"}
+
+
+def source_sha256(kernel):
+    import hashlib
+    path = os.path.join(ROOT, KERNEL_SOURCES[kernel.split("<")[0]])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary under profiles/ (FETCH_SIZE and WRITE_SIZE,
+    each scaled by its copy-kernel calibration factor). None when no summary
+    exists or the kernel source changed since the counters were taken."""
+    prof_dir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(prof_dir):
+        return None
+    for name in sorted(os.listdir(prof_dir)):
+        if not name.endswith(".md"):
+            continue
+        fields = {}
+        with open(os.path.join(prof_dir, name)) as f:
+            for line in f:
+                if line.startswith("- ") and ": " in line:
+                    k, v = line[2:].strip().split(": ", 1)
+                    fields[k.strip("`")] = v.strip().strip("`")
+        if fields.get("roofline_kernel") != kernel or fields.get("workload") != workload:
+            continue
+        if fields.get("kernel_source_sha256") != source_sha256(kernel):
+            return None
+        try:
+            return float(fields["traffic_bytes_per_launch"])
+        except (KeyError, ValueError):
+            return None
+    return None
 
 
 # ------------------------------------------------------------------ main
@@ -247,17 +289,21 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
-    # per-launch durations, same stream, same launches: one event pair per op
+    # per-launch durations on the same stream: each launch of the step is
+    # repeated REPEAT times back to back between one event pair, so the
+    # events' own overhead is spread over the repeats
+    REPEAT = 10
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
     per_op = [0.0] * len(ops)
     for _ in range(args.steps):
         for i, op in enumerate(ops):
             ev[i][0].record(stream)
-            op.fn()
+            for _ in range(REPEAT):
+                op.fn()
             ev[i][1].record(stream)
         torch.cuda.synchronize()
         for i in range(len(ops)):
-            per_op[i] += ev[i][0].elapsed_time(ev[i][1])
+            per_op[i] += ev[i][0].elapsed_time(ev[i][1]) / REPEAT
     per_op = [t / args.steps for t in per_op]
 
     gemm_flops = sum(op.flops for op in ops)
@@ -316,7 +362,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dom, config["workload"]),
             "launches_per_step": dom_d["n"],
             "avg_launch_us": round(1e3 * dom_d["ms"] / dom_d["n"], 2),
             "flops_per_launch_avg": dom_d["flops"] / dom_d["n"],
