@@ -61,10 +61,11 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_>
+template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_, bool SPREAD_>
 struct MxCfg {
   static constexpr int FMT = FMT_, BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int OCC = OCC_;                            // workgroups per CU (LDS-limited)
+  static constexpr bool SPREAD = SPREAD_;                     // spread code copies over the stage
   static constexpr int NT = 64 * WAVES_M * WAVES_N, NW = NT / 64;
   static constexpr int RB = 128;                              // code bytes per row per stage
   static constexpr int CH = RB / 16;                          // 16-byte chunks per row
@@ -85,6 +86,8 @@ struct MxCfg {
   static constexpr int EPI_STORES = WM * CPR / NT;            // stores per thread per epilogue pass
   static constexpr int EPI_TOTAL = WAVES_M * EPI_STORES;      // stores per thread per tile
   static_assert(CODE_DMA * 1024 * NW == STAGE, "code copies must split evenly over waves");
+  static_assert(BM % (8 * NW) == 0, "every wave's copies split into A rows, then B rows");
+  static_assert(NW % 2 == 0, "copy blocks of one wave share the parity of the wave");
   static_assert(BM % 64 == 0 && BN % 64 == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
   static_assert(LDS * OCC <= 160 * 1024, "LDS");
   static_assert(WM * BN * 2 <= STAGE, "one wave-row of the bf16 C tile must fit in a stage buffer");
@@ -93,8 +96,12 @@ struct MxCfg {
   static_assert(BN * 2 <= 1024, "a tile's bias must fit one bias slot");
 };
 
-// Row r keeps 16-byte chunk c of a 128-byte row at position c ^ (r & 7).
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
+// Row r keeps 16-byte chunk c of a 128-byte row at position c ^ ((r / 2) % 8).
+// A 128-byte row covers half of the LDS's 64 four-byte banks, so rows
+// alternate bank halves; a 16-byte read is served 16 lanes at a time, and the
+// 16 consecutive rows those lanes read (same logical chunk) then land on 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 __device__ __forceinline__ v4u buffer_rsrc(const void* p, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(p);
@@ -182,10 +189,13 @@ __device__ __forceinline__ int substep_scale(uint2 s, int t) {
   return (int)(w >> (16 * (t & 1)));
 }
 
-// All sub-steps of one stage for one wave.
-template <class Cfg>
+// All sub-steps of one stage for one wave. after_block(i) runs after the
+// matrix instructions of the i-th (sub-step, A fragment) block, i = 0 ..
+// SUB * FM - 1 (a compile-time value once unrolled): the kernel spreads the
+// next stage's copies over these points instead of issuing them in a burst.
+template <class Cfg, class AfterBlock>
 __device__ __forceinline__ void mma_stage(v16f (&acc)[Cfg::FM][Cfg::FN], const uint8_t* st, const uint8_t* sc,
-                                          int sj, int g, int ra, int rb) {
+                                          int sj, int g, int ra, int rb, AfterBlock&& after_block) {
   constexpr int FM = Cfg::FM, FN = Cfg::FN, SUB = Cfg::SUB;
   uint2 sa[FM], sb[FN];
 #pragma unroll
@@ -211,6 +221,7 @@ __device__ __forceinline__ void mma_stage(v16f (&acc)[Cfg::FM][Cfg::FN], const u
         acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             b_cur[fn], a_cur, acc[fm][fn], Cfg::MFMA_FMT, Cfg::MFMA_FMT, 0, substep_scale<Cfg>(sb[fn], t), 0,
             substep_scale<Cfg>(sa[fm], t));
+      after_block(t * FM + fm);
       if (fm + 1 < FM || t + 1 < SUB) a_cur = a_nxt;
     }
     if (t + 1 < SUB) {
@@ -263,24 +274,40 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   // rows 8 J .. 8 J + 7 of [A rows, B rows] (A iff 8 J < BM, uniform per
   // copy), lane l taking row 8 J + l / 8 and logical chunk l % 8, which lands
   // at swizzled position (l % 8) ^ (row % 8) = (l % 8) ^ (l / 8).
-  const uint32_t code_byte = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  // lane l of copy block J lands at position l % 8 of stage row 8 J + l / 8;
+  // with J = j NW + wave and NW even, (row / 2) % 8 = (4 (wave % 2) + l / 16) % 8
+  const uint32_t code_byte = (uint32_t)(((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7)) * 16);
+  // this lane's row within its wave's first copy: 8 wave + lane / 8
   // (offsets of rows past the operand may wrap; they only feed rows and
   // columns of C that are never stored, and every read is range-checked)
-  const uint32_t code_lane = (uint32_t)(lane >> 3) * (uint32_t)row_bytes + code_byte;
+  const uint32_t code_lane = (uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)row_bytes + code_byte;
+  const uint32_t copy_stride = (uint32_t)(8 * NW) * (uint32_t)row_bytes;   // rows between copy j and j + 1
   // Scale copy j of this wave fills rows 64 J .. 64 J + 63 of [A rows, B rows]
   // with 16 bytes each (copies J >= SCALE_COPIES are skipped).
   const uint32_t scale_lane = (uint32_t)lane * (uint32_t)srow;
 
   // copy cursor: tile lt (rows m0l / n0l), its stage lks; lgs / lgc count
   // stages / scale chunks issued so far (they pick the LDS buffer and slot)
+  // copy cursor: tile lt (first rows m0l / n0l; a_base / b_base are the byte
+  // offsets of its A rows and of its B rows shifted down by BM), its stage
+  // lks; lgs / lgc / ltc count stages / scale chunks / tiles issued so far
   int lt = blockIdx.x, lks = 0, lgs = 0, lgc = 0, ltc = 0, m0l = 0, n0l = 0;
+  uint32_t a_base = 0, b_base = 0;
   auto set_copy_tile = [&](int t) {
     int tm, tn;
     tile_coords(t, tiles_m, tiles_n, tm, tn);
     m0l = tm * BM;
     n0l = tn * BN;
+    a_base = (uint32_t)m0l * (uint32_t)row_bytes;
+    b_base = (uint32_t)(n0l - BM) * (uint32_t)row_bytes;
   };
-  auto issue_next = [&]() {
+  // Copies of the copy cursor's stage. open_copy_stage issues the tile's bias
+  // (first stage) and a new scale chunk (every SPC stages) and fixes where
+  // the stage's code copies go; issue_code(j) issues code copy j of this
+  // wave; close_copy_stage advances the cursor.
+  uint32_t cp_st = 0, cp_soff = 0;
+  bool cp_in_row = false;
+  auto open_copy_stage = [&]() {
     if (lks == 0 && bias_dma && wave == 0) {  // the tile's bias, into bias slot ltc & 1
       const uint32_t voff = lane < BN / 8 ? (uint32_t)((n0l + 8 * lane) * 2) : 0x80000000u;
       dma16(bias_rs, lds_base + (uint32_t)(Cfg::BIAS_OFF + (ltc & 1) * 1024), voff, 0u);
@@ -299,18 +326,22 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
       }
       ++lgc;
     }
-    const uint32_t st = lds_base + (uint32_t)((lgs & 1) * Cfg::STAGE);
+    cp_st = lds_base + (uint32_t)((lgs & 1) * Cfg::STAGE);
+    cp_soff = (uint32_t)(lks * RB);
     // bytes past the end of the row (last fp4 stage) read as zero: offset
     // beyond the buffer
-    const bool in_row = code_byte < (uint32_t)(row_bytes - lks * RB);
-#pragma unroll
-    for (int j = 0; j < Cfg::CODE_DMA; ++j) {
-      const int J = j * NW + wave;
-      const bool isa = J * 8 < BM;
-      const int row0 = (isa ? m0l : n0l - BM) + J * 8;
-      const uint32_t voff = in_row ? code_lane + (uint32_t)row0 * (uint32_t)row_bytes : 0x80000000u;
-      dma16(isa ? a_rs : b_rs, st + (uint32_t)(J * 1024), voff, (uint32_t)(lks * RB));
-    }
+    cp_in_row = code_byte < (uint32_t)(row_bytes - lks * RB);
+  };
+  // copy j of this wave fills 1-KB block J = j NW + wave of the stage: rows
+  // 8 J .. 8 J + 7 of [A rows, B rows]; the first BM / (8 NW) copies of
+  // every wave are A rows
+  auto issue_code = [&](int j) {
+    constexpr int A_COPIES = BM / (8 * NW);
+    const bool isa = j < A_COPIES;
+    const uint32_t voff = cp_in_row ? code_lane + (isa ? a_base : b_base) + (uint32_t)j * copy_stride : 0x80000000u;
+    dma16(isa ? a_rs : b_rs, cp_st + (uint32_t)((j * NW + wave) * 1024), voff, cp_soff);
+  };
+  auto close_copy_stage = [&]() {
     ++lgs;
     if (++lks == nk) {
       lks = 0;
@@ -318,6 +349,38 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
       lt += gridDim.x;
       if (lt < tiles) set_copy_tile(lt);
     }
+  };
+  // The whole next stage in one burst. Everything it needs is local, which
+  // keeps the register budget of the 256 x 256 tile within 256.
+  auto issue_next = [&]() {
+    if (lks == 0 && bias_dma && wave == 0) {
+      const uint32_t voff = lane < BN / 8 ? (uint32_t)((n0l + 8 * lane) * 2) : 0x80000000u;
+      dma16(bias_rs, lds_base + (uint32_t)(Cfg::BIAS_OFF + (ltc & 1) * 1024), voff, 0u);
+    }
+    if (lks % Cfg::SPC == 0) {
+      const uint32_t dst = sc_base + (uint32_t)((lgc & 1) * Cfg::SCHUNK);
+      const uint32_t soff = (uint32_t)(16 * (lks / Cfg::SPC));
+#pragma unroll
+      for (int j = 0; j < Cfg::SCALE_DMA; ++j) {
+        const int J = j * NW + wave;
+        if (J < Cfg::SCALE_COPIES) {
+          const bool isa = J * 64 < BM;
+          const int row0 = (isa ? m0l : n0l - BM) + J * 64;
+          dma16(isa ? as_rs : bs_rs, dst + (uint32_t)(J * 1024), scale_lane + (uint32_t)row0 * (uint32_t)srow, soff);
+        }
+      }
+      ++lgc;
+    }
+    const uint32_t st = lds_base + (uint32_t)((lgs & 1) * Cfg::STAGE);
+    const bool in_row = code_byte < (uint32_t)(row_bytes - lks * RB);
+#pragma unroll
+    for (int j = 0; j < Cfg::CODE_DMA; ++j) {
+      constexpr int A_COPIES = BM / (8 * NW);
+      const bool isa = j < A_COPIES;
+      const uint32_t voff = in_row ? code_lane + (isa ? a_base : b_base) + (uint32_t)j * copy_stride : 0x80000000u;
+      dma16(isa ? a_rs : b_rs, st + (uint32_t)((j * NW + wave) * 1024), voff, (uint32_t)(lks * RB));
+    }
+    close_copy_stage();
   };
 
   const int ra = wm * WM + r32, rb = wn * WN + r32;     // this lane's fragment-0 rows in the tile
@@ -345,10 +408,25 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
       else wait_vm<0>();
       block_sync();                         // everyone's copies are visible, and everyone is done
                                             // with the buffers the next copies overwrite
-      if (lt < tiles) issue_next();
+      // The next stage's copies. SPREAD: bias and scales now, code copies
+      // spread over the stage's matrix-instruction blocks (copy j after
+      // block j * BLOCKS / CODE_DMA); past this workgroup's last tile the
+      // cursor keeps copying the last tile's rows into the buffer, scale
+      // slot and bias slot no later stage reads, so no branch splits the
+      // blocks. Otherwise: all of them now, in one burst.
+      if (Cfg::SPREAD) open_copy_stage();
+      else if (lt < tiles) issue_next();
       if (ks % Cfg::SPC == 0) slot = gc++ & 1;
       mma_stage<Cfg>(acc, lds + (gs & 1) * Cfg::STAGE, lds + 2 * Cfg::STAGE + slot * Cfg::SCHUNK, ks % Cfg::SPC, g,
-                     ra, rb);
+                     ra, rb, [&](int blk) {
+                       constexpr int BLOCKS = Cfg::SUB * FM;
+                       if (Cfg::SPREAD) {
+#pragma unroll
+                         for (int j = 0; j < Cfg::CODE_DMA; ++j)
+                           if (j * BLOCKS / Cfg::CODE_DMA == blk) issue_code(j);
+                       }
+                     });
+      if (Cfg::SPREAD) close_copy_stage();
       ++gs;
     }
 
@@ -369,28 +447,36 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
       for (int h = 0; h < Cfg::WAVES_M; ++h) {
         block_sync();                        // previous readers of the buffer are done
         if (wm == h) {
-          uint2 bb[FN][4];                   // bias of this lane's columns, read in one batch
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
+          for (int fn = 0; fn < FN; ++fn) {
+            uint2 bb[4];                     // bias of this lane's columns of fragment column fn
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bb[fn][q] = bias4(wn * WN + 32 * fn + 8 * q + 4 * g);
+            for (int q = 0; q < 4; ++q) bb[q] = bias4(wn * WN + 32 * fn + 8 * q + 4 * g);
 #pragma unroll
-          for (int fm = 0; fm < FM; ++fm) {
-            const int lr = 32 * fm + r32;
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+            for (int fm = 0; fm < FM; ++fm) {
+              const int lr = 32 * fm + r32;
+              uint32_t P[4][2];
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const int nl = wn * WN + 32 * fn + 8 * q + 4 * g;
-                const float v0 = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb[fn][q].x & 0xFFFFu);
-                const float v1 = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb[fn][q].x >> 16);
-                const float v2 = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb[fn][q].y & 0xFFFFu);
-                const float v3 = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb[fn][q].y >> 16);
-                const int chunk = (nl >> 3) ^ (lr & (CPR - 1));
-                *reinterpret_cast<uint2*>(stg + lr * (BN * 2) + chunk * 16 + (nl & 7) * 2) =
-                    make_uint2(f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16),
-                               f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16));
+                const float v0 = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb[q].x & 0xFFFFu);
+                const float v1 = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb[q].x >> 16);
+                const float v2 = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb[q].y & 0xFFFFu);
+                const float v3 = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb[q].y >> 16);
+                P[q][0] = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
+                P[q][1] = f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16);
               }
+#pragma unroll
+              for (int p = 0; p < 2; ++p) {
+                // the two lanes holding adjacent 4-column runs of a row swap
+                // halves across the wave: lane g = 0 ends with columns
+                // 16p .. 16p + 7 of the fragment, lane g = 1 with 16p + 8 .. + 15
+                const auto s0 = __builtin_amdgcn_permlane32_swap(P[2 * p][0], P[2 * p + 1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(P[2 * p][1], P[2 * p + 1][1], false, false);
+                const int chunk = (wn * WN + 32 * fn + 16 * p + 8 * g) >> 3;
+                *reinterpret_cast<uint4*>(stg + lr * (BN * 2) + ((chunk ^ (lr & (CPR - 1))) * 16)) =
+                    make_uint4(s0[0], s1[0], s0[1], s1[1]);
+              }
+            }
           }
         }
         block_sync();
@@ -463,6 +549,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
     }
     ++ctc;
   }
+  wait_vm<0>();                              // no copy into LDS outlives the workgroup
 }
 
 // Compute units of the current device (cached per device).
@@ -507,11 +594,15 @@ enum MxTile { TILE_128x128 = 0, TILE_192x256 = 1, TILE_256x256 = 2 };
 
 // 256x256 and 192x256 tiles (8 waves of 128x64 / 96x64) are LDS-bound to
 // one workgroup per CU; 128x128 (4 waves of 64x64) fits two per CU and
-// serves problems too small to fill the chip with the large tiles.
-static MxTile choose_tile(int64_t M, int64_t N) {
+// serves problems too small to fill the chip with the large tiles. The
+// 192x256 tile spreads its copies over the stage (the 256x256 tile has no
+// registers left for that), which makes it the faster one on equal cost, and
+// for FP4 (half the bytes per MFMA) on every ViT shape measured.
+static MxTile choose_tile(int64_t M, int64_t N, int fmt) {
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
   if (big < 128) return TILE_128x128;
-  if (tiling_cost(M, N, 192, 256) < tiling_cost(M, N, 256, 256)) return TILE_192x256;
+  const double c192 = tiling_cost(M, N, 192, 256), c256 = tiling_cost(M, N, 256, 256);
+  if (fmt == FMT_MXFP4 ? c192 <= c256 : c192 < c256) return TILE_192x256;
   return TILE_256x256;
 }
 
@@ -519,13 +610,13 @@ template <int FMT>
 static hipError_t dispatch_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
                               int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
                               hipStream_t stream) {
-  switch (choose_tile(M, N)) {
+  switch (choose_tile(M, N, FMT)) {
     case TILE_128x128:
-      return run_mx<MxCfg<FMT, 128, 128, 2, 2, 2>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+      return run_mx<MxCfg<FMT, 128, 128, 2, 2, 2, true>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
     case TILE_192x256:
-      return run_mx<MxCfg<FMT, 192, 256, 2, 4, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+      return run_mx<MxCfg<FMT, 192, 256, 2, 4, 1, true>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
     default:
-      return run_mx<MxCfg<FMT, 256, 256, 2, 4, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+      return run_mx<MxCfg<FMT, 256, 256, 2, 4, 1, false>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
   }
 }
 
@@ -540,7 +631,7 @@ const char* plan_gemm_mx(int64_t M, int64_t N, int fmt) {
   static const char* names[2][3] = {
       {"gemm_mx_kernel<mxfp8, 128x128>", "gemm_mx_kernel<mxfp8, 192x256>", "gemm_mx_kernel<mxfp8, 256x256>"},
       {"gemm_mx_kernel<mxfp4, 128x128>", "gemm_mx_kernel<mxfp4, 192x256>", "gemm_mx_kernel<mxfp4, 256x256>"}};
-  return names[fmt == FMT_MXFP8 ? 0 : 1][choose_tile(M, N)];
+  return names[fmt == FMT_MXFP8 ? 0 : 1][choose_tile(M, N, fmt)];
 }
 
 }  // namespace mx
