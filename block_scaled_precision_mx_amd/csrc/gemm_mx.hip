@@ -49,17 +49,12 @@
 // wave issues the same number of stores, so the next tile's first wait lets
 // exactly those stores stay in flight. fp32 output (or N % 8 != 0) is stored
 // straight from registers and drained before the next tile.
-#include "mx_device.h"
+#include "gemm_common.h"
 #include "mx_launch.h"
 
 #include <algorithm>
-#include <atomic>
 
 namespace mx {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_, bool SPREAD_>
 struct MxCfg {
@@ -95,62 +90,6 @@ struct MxCfg {
   static_assert(EPI_TOTAL <= 48, "stores left in flight must stay within the vmcnt range");
   static_assert(BN * 2 <= 1024, "a tile's bias must fit one bias slot");
 };
-
-// Row r keeps 16-byte chunk c of a 128-byte row at position c ^ ((r / 2) % 8).
-// A 128-byte row covers half of the LDS's 64 four-byte banks, so rows
-// alternate bank halves; a 16-byte read is served 16 lanes at a time, and the
-// 16 consecutive rows those lanes read (same logical chunk) then land on 16
-// distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
-
-__device__ __forceinline__ v4u buffer_rsrc(const void* p, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  v4u r;
-  r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  r.z = __builtin_amdgcn_readfirstlane(bytes);
-  r.w = 0x00020000u;   // raw buffer, 32-bit data format: out-of-range reads return 0
-  return r;
-}
-
-// One wave-wide copy global -> LDS: lane l's 16 bytes at `voff` (+ soff)
-// land at lds_addr + 16 l. M0 is saved and restored around the copy.
-__device__ __forceinline__ void dma16(v4u rs, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
-}
-
-// Wait until at most N vector memory operations of this wave are in flight
-// (they complete in issue order). Issued through the builtin so the
-// compiler's own wait bookkeeping sees it too.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier after this wave's LDS operations have completed. Global
-// stores still in flight are deliberately not waited for.
-__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Coordinates of tile t: XCD-contiguous renumbering (tile t runs on XCD
-// t % 8 because the grid is a multiple of 8 or covers every tile once), then
-// groups of 8 tile-rows walked column by column.
-__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int nwg = tiles_m * tiles_n;
-  const int q = nwg / 8, r = nwg % 8;
-  const int xcd = t % 8, local = t / 8;
-  const int wg = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
-  constexpr int GROUP = 8;
-  const int group_size = GROUP * tiles_n;
-  const int gid = wg / group_size;
-  const int first_m = gid * GROUP;
-  const int gm = min(tiles_m - first_m, GROUP);
-  const int in_group = wg - gid * group_size;
-  tm = first_m + in_group % gm;
-  tn = in_group / gm;
-}
 
 // fp8: A or B fragment of sub-step t for tile row `row` of a stage: 16-byte
 // chunks 4t+g and 4t+2+g (K 16g.. and 32+16g.. of the sub-step).
@@ -552,18 +491,6 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   wait_vm<0>();                              // no copy into LDS outlives the workgroup
 }
 
-// Compute units of the current device (cached per device).
-static int cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-  cache[dev].store(v, std::memory_order_relaxed);
-  return v;
-}
-
 template <class Cfg>
 static hipError_t run_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
                          int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32, hipStream_t stream) {
@@ -579,15 +506,6 @@ static hipError_t run_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, 
   gemm_mx_kernel<Cfg><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, bias, out_f32,
                                                     tiles_m, tiles_n);
   return hipGetLastError();
-}
-
-// Rounds of workgroups a tiling needs on the 256 CUs (one 256x256 or
-// 192x256 workgroup per CU, LDS-limited), weighted by tile area: the shape
-// with the least MFMA time lost to idle CUs in the last round wins.
-static double tiling_cost(int64_t M, int64_t N, int bm, int bn) {
-  const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-  const int64_t rounds = (tiles + 255) / 256;
-  return (double)rounds * bm * bn;
 }
 
 enum MxTile { TILE_128x128 = 0, TILE_192x256 = 1, TILE_256x256 = 2 };

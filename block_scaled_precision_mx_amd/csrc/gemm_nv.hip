@@ -2,7 +2,7 @@
 //
 // lightly-train README "DINOv3 + EoMT on RTX 5090", section 2: NVFP4 is
 // E2M1 elements with an E4M3 scale per 1x16 block plus an fp32 scale per
-// tensor; section 5.3-5.5 use it for the dgrad / wgrad GEMMs of training.
+// tensor; sections 5.3-5.5 use it for the dgrad / wgrad GEMMs of training.
 //
 // CDNA4's scaled matrix instructions take power-of-two (E8M0) scales per 32
 // elements, which cannot express an E4M3 scale per 16. Folding the E4M3
@@ -10,40 +10,55 @@
 // 2 + 4 significant bits and lies in [2^-10, 2688] (normal fp16), so the
 // product of two such values (<= 12 bits) is exact in the fp32 matrix
 // accumulator too. The kernel therefore dequantizes each operand tile to
-// fp16 while staging it into LDS (one pass per tile, shared by all waves):
+// fp16 while staging it into LDS (once per tile row, shared by all waves):
 // nibble -> fp16 via a byte-permute table, times the block scale as a packed
-// fp16 multiply; then runs V_MFMA_F32_16X16X32_F16 with fp32 accumulation
+// fp16 multiply; then runs V_MFMA_F32_32X32X16_F16 with fp32 accumulation
 // and applies s_tA * s_tB in the epilogue. The roof of this path is the fp16
-// matrix rate, a quarter of the FP4 rate; the accuracy is that of the exact
-// method (fp32 accumulation only).
+// matrix rate; the accuracy is that of the exact method (fp32 accumulation
+// only).
 //
-// fp16 operand layout (measured on gfx950): lane l holds row l%16, K
-// 8g..8g+7, g = l/16; output as in the MX kernel (lane: D[4g + v][l%16]).
-#include "mx_device.h"
+// Structure (as in the MX kernel): a persistent walk over output tiles with
+// XCD-contiguous numbering, 8 waves of 128 x 64 (or 96 x 64) outputs, two
+// LDS stages of 64 K elements (128 fp16 bytes per row, chunk-swizzled) and
+// the LDS-staged bf16 epilogue. Staging goes through registers: after a
+// stage's barrier every thread loads one tile row's 32 code bytes and 4
+// scale bytes of the next stage (global -> VGPR), the stage's matrix
+// instructions run, then the thread writes that row, dequantized, into the
+// other LDS buffer before the next barrier.
+//
+// fp16 operand layout of the 32x32x16 instruction (measured on gfx950):
+// lane l holds row l % 32, K 8 (l / 32) .. + 7; output as in the MX kernel.
+#include "gemm_common.h"
 #include "mx_launch.h"
+
+#include <algorithm>
 
 namespace mx {
 
-typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int SWZ_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_>
 struct NvCfg {
-  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, SWZ = SWZ_;
-  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, OCC = OCC_;
+  static constexpr int NT = 64 * WAVES_M * WAVES_N, NW = NT / 64;
+  static constexpr int RB = 128;                              // fp16 bytes per LDS row per stage
+  static constexpr int KS = 64;                               // K elements per stage
+  static constexpr int SUB = KS / 16;                         // 32x32x16 sub-steps per stage
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  static constexpr int FM = WM / 16, FN = WN / 16;
-  static constexpr int KS = 64;                  // K elements per stage
-  static constexpr int ROWB = KS * 2;            // fp16 bytes per LDS row
-  static constexpr int CH = ROWB / 16;           // 16-byte chunks per LDS row (8)
-  static constexpr int A_STAGE = BM * ROWB, B_STAGE = BN * ROWB;
-  static constexpr int A_ITEMS = BM * 2 / NT;    // 16-byte code chunks (32 elements) per thread
-  static constexpr int B_ITEMS = BN * 2 / NT;
-  static_assert(A_ITEMS * NT == BM * 2 && B_ITEMS * NT == BN * 2, "items");
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int STAGE = (BM + BN) * RB;
+  static constexpr int BIAS_OFF = 2 * STAGE;                  // two 1-KB bias slots (tile parity)
+  static constexpr int LDS = BIAS_OFF + 2 * 1024;
+  static constexpr int CPR = BN / 8;
+  static constexpr int EPI_STORES = WM * CPR / NT;
+  static_assert(BM + BN <= NT, "one staged row per thread");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
+  static_assert(LDS * OCC <= 160 * 1024, "LDS");
+  static_assert(WM * BN * 2 <= STAGE, "one wave-row of the bf16 C tile must fit in a stage buffer");
+  static_assert(EPI_STORES * NT == WM * CPR, "epilogue stores must split evenly over threads");
+  static_assert(BN * 2 <= 1024 && BN / 8 <= NT, "a tile's bias must fit one bias slot");
 };
-
-__device__ __forceinline__ int nv_swz(int r, int c, int shift) { return c ^ ((r >> shift) & 7); }
 
 // fp16 bits of a non-negative E4M3 scale byte, replicated into both halves.
 __device__ __forceinline__ uint32_t e4m3_to_h2(uint32_t b) {
@@ -77,194 +92,259 @@ __device__ __forceinline__ uint4 dequant8(uint32_t x, uint32_t scale_h2) {
   return out;
 }
 
-// Same tile numbering as the MX kernel.
-__device__ __forceinline__ void nv_tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int nwg = tiles_m * tiles_n;
-  const int i = blockIdx.x;
-  const int q = nwg / 8, r = nwg % 8;
-  const int xcd = i % 8, local = i / 8;
-  const int wg = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
-  constexpr int GROUP = 8;
-  const int group_size = GROUP * tiles_n;
-  const int gid = wg / group_size;
-  const int first_m = gid * GROUP;
-  const int gm = min(tiles_m - first_m, GROUP);
-  const int in_group = wg - gid * group_size;
-  tm = first_m + in_group % gm;
-  tn = in_group / gm;
-}
-
-__device__ __forceinline__ void nv_store4(void* C, int M, int N, int m, int n, v4f acc, float scale,
-                                         const uint16_t* bias, int out_f32) {
-  if (m >= M) return;
-  float v[4] = {acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale};
-  const bool full = ((N & 3) == 0) && (n + 3 < N);
-  if (bias) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (n + j < N) v[j] += bf16_to_f32(bias[n + j]);
-  }
-  const int64_t off = (int64_t)m * N + n;
-  if (out_f32) {
-    float* c = reinterpret_cast<float*>(C) + off;
-    if (full) {
-      *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n + j < N) c[j] = v[j];
-    }
-  } else {
-    uint16_t* c = reinterpret_cast<uint16_t*>(C) + off;
-    if (full) {
-      uint2 w;
-      w.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-      w.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-      *reinterpret_cast<uint2*>(c) = w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n + j < N) c[j] = (uint16_t)f32_to_bf16_rne(v[j]);
-    }
-  }
+// fp16 fragment of sub-step t for tile row `row`: chunk 2t + g (K 16t + 8g ..).
+template <class Cfg>
+__device__ __forceinline__ v8h nv_frag(const uint8_t* st, int row, int t, int g) {
+  return __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(st + row * Cfg::RB + swz(row, 2 * t + g) * 16));
 }
 
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NT) void gemm_nv_kernel(const uint8_t* __restrict__ A,
-                                                          const uint8_t* __restrict__ As,
-                                                          const uint8_t* __restrict__ B,
-                                                          const uint8_t* __restrict__ Bs, void* __restrict__ C,
-                                                          int M, int N, int kpad,
-                                                          const uint16_t* __restrict__ bias, int out_f32,
-                                                          int tiles_m, int tiles_n, int a_trailer, int b_trailer) {
-  constexpr int NT = Cfg::NT, ROWB = Cfg::ROWB;
+__global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_t* __restrict__ A,
+                                                                    const uint8_t* __restrict__ As,
+                                                                    const uint8_t* __restrict__ B,
+                                                                    const uint8_t* __restrict__ Bs,
+                                                                    void* __restrict__ C, int M, int N, int kpad,
+                                                                    const uint16_t* __restrict__ bias, int out_f32,
+                                                                    int tiles_m, int tiles_n, int a_trailer,
+                                                                    int b_trailer) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
-  __shared__ __align__(16) uint8_t lds[2 * (Cfg::A_STAGE + Cfg::B_STAGE)];
+  constexpr int RB = Cfg::RB, SUB = Cfg::SUB, CPR = Cfg::CPR;
+  __shared__ __align__(16) uint8_t lds[Cfg::LDS];
 
-  int tm, tn;
-  nv_tile_coords(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int tiles = tiles_m * tiles_n;
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
-  const int row_bytes = kpad / 2;           // code bytes per row
-  const int srow = kpad / 16;               // scale bytes per row
-  const int nk = kpad / Cfg::KS;
-  const int g = lane >> 4, r16 = lane & 15;
+  const int row_bytes = kpad / 2;            // code bytes per row
+  const int srow = kpad / 16;                // scale bytes per row
+  const int nk = kpad / Cfg::KS;             // K_pad is a multiple of 128
+  const int g = lane >> 5, r32 = lane & 31;
+  const bool staged = !out_f32 && (N & 7) == 0 && (int64_t)M * N < ((int64_t)1 << 30);
 
-  const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, M * row_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc((void*)B, 0, N * row_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t as_rs = __builtin_amdgcn_make_buffer_rsrc((void*)As, 0, M * srow, 0x00020000);
-  const __amdgpu_buffer_rsrc_t bs_rs = __builtin_amdgcn_make_buffer_rsrc((void*)Bs, 0, N * srow, 0x00020000);
+  const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, M * row_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, N * row_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t as_rs = __builtin_amdgcn_make_buffer_rsrc((void*)As, (short)0, M * srow, 0x00020000);
+  const __amdgpu_buffer_rsrc_t bs_rs = __builtin_amdgcn_make_buffer_rsrc((void*)Bs, (short)0, N * srow, 0x00020000);
+  const __amdgpu_buffer_rsrc_t c_rs =
+      __builtin_amdgcn_make_buffer_rsrc(C, (short)0, staged ? M * N * 2 : 0, 0x00020000);
+  // a 16-byte aligned bias with N % 8 == 0 is loaded 8 columns per thread;
+  // otherwise element by element
+  const bool bias_vec = bias != nullptr && (N & 7) == 0 && (reinterpret_cast<uintptr_t>(bias) & 15) == 0;
+  const __amdgpu_buffer_rsrc_t bias_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)bias, (short)0, bias_vec ? N * 2 : 0, 0x00020000);
 
-  // staging items: item q covers row q/2, code bytes 16 (q%2) .. +15 of the
-  // stage (elements 32 (q%2) .. +31, two 16-element scale blocks)
-  int a_coff[Cfg::A_ITEMS], a_soff[Cfg::A_ITEMS], a_lds[Cfg::A_ITEMS][4];
+  // Staging: thread tid stages row tid of the stage, i.e. A row tid (tid <
+  // BM) or B row tid - BM (threads past BM + BN stage nothing). Loader
+  // cursor: tile lt, its stage lks; lgs / ltc count stages / tiles staged.
+  const bool stager = tid < BM + BN;
+  const bool st_is_a = tid < BM;
+  const int st_row = st_is_a ? tid : tid - BM;
+  int lt = blockIdx.x, lks = 0, lgs = 0, ltc = 0;
+  int code_off = 0, scale_off = 0, bias_col = 0;
+  auto set_load_tile = [&](int t) {
+    int tm, tn;
+    tile_coords(t, tiles_m, tiles_n, tm, tn);
+    const int r = (st_is_a ? tm * BM : tn * BN) + st_row;
+    code_off = r * row_bytes;                // rows past the operand read as zero (range-checked)
+    scale_off = r * srow;
+    bias_col = tn * BN + 8 * tid;            // first bias column of threads tid < BN / 8
+  };
+  uint4 ld_code0 = make_uint4(0u, 0u, 0u, 0u), ld_code1 = ld_code0, ld_bias = ld_code0;
+  uint32_t ld_scale = 0;
+  auto load_next = [&]() {                   // global -> registers
+    const __amdgpu_buffer_rsrc_t crs = st_is_a ? a_rs : b_rs;
+    const __amdgpu_buffer_rsrc_t srs = st_is_a ? as_rs : bs_rs;
+    const int co = stager ? code_off + lks * 32 : (int)0x80000000u;
+    const int so = stager ? scale_off + lks * 4 : (int)0x80000000u;
+    ld_code0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(crs, co, 0, 0));
+    ld_code1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(crs, co, 16, 0));
+    ld_scale = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 0, 0);
+    if (lks == 0 && bias_vec && tid < BN / 8)
+      ld_bias = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bias_rs, bias_col * 2, 0, 0));
+  };
+  auto store_next = [&]() {                  // registers -> dequantized fp16 row in LDS
+    uint8_t* dst = lds + (lgs & 1) * Cfg::STAGE + tid * RB;
+    const uint32_t s[4] = {e4m3_to_h2(ld_scale & 0xFFu), e4m3_to_h2((ld_scale >> 8) & 0xFFu),
+                           e4m3_to_h2((ld_scale >> 16) & 0xFFu), e4m3_to_h2(ld_scale >> 24)};
+    const uint32_t w[8] = {ld_code0.x, ld_code0.y, ld_code0.z, ld_code0.w,
+                           ld_code1.x, ld_code1.y, ld_code1.z, ld_code1.w};
+    if (stager) {
 #pragma unroll
-  for (int i = 0; i < Cfg::A_ITEMS; ++i) {
-    const int q = t + NT * i, r = q / 2, h = q % 2;
-    a_coff[i] = (m0 + r) * row_bytes + 16 * h;
-    a_soff[i] = (m0 + r) * srow + 2 * h;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) a_lds[i][d] = r * ROWB + nv_swz(r, 4 * h + d, Cfg::SWZ) * 16;
-  }
-  int b_coff[Cfg::B_ITEMS], b_soff[Cfg::B_ITEMS], b_lds[Cfg::B_ITEMS][4];
-#pragma unroll
-  for (int i = 0; i < Cfg::B_ITEMS; ++i) {
-    const int q = t + NT * i, r = q / 2, h = q % 2;
-    b_coff[i] = (n0 + r) * row_bytes + 16 * h;
-    b_soff[i] = (n0 + r) * srow + 2 * h;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) b_lds[i][d] = r * ROWB + nv_swz(r, 4 * h + d, Cfg::SWZ) * 16;
-  }
-  const int ra = wm * WM + r16, rb = wn * WN + r16;
-  const int a_off0 = ra * ROWB + nv_swz(ra, g, Cfg::SWZ) * 16;
-  const int a_off1 = ra * ROWB + nv_swz(ra, 4 + g, Cfg::SWZ) * 16;
-  const int b_off0 = rb * ROWB + nv_swz(rb, g, Cfg::SWZ) * 16;
-  const int b_off1 = rb * ROWB + nv_swz(rb, 4 + g, Cfg::SWZ) * 16;
-
-  uint4 a_code[Cfg::A_ITEMS], b_code[Cfg::B_ITEMS];
-  uint32_t a_sc[Cfg::A_ITEMS], b_sc[Cfg::B_ITEMS];
-
-  auto load_stage = [&](int ks) {
-#pragma unroll
-    for (int i = 0; i < Cfg::A_ITEMS; ++i) {
-      a_code[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_coff[i], ks * 32, 0));
-      a_sc[i] = __builtin_amdgcn_raw_buffer_load_b16(as_rs, a_soff[i], ks * 4, 0);
+      for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(dst + swz(tid, c) * 16) = dequant8(w[c], s[c / 2]);
     }
+    if (lks == 0 && bias != nullptr && tid < BN / 8) {   // the tile's bias, into bias slot ltc & 1
+      uint4 v = ld_bias;
+      if (!bias_vec) {
+        uint32_t e[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < Cfg::B_ITEMS; ++i) {
-      b_code[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_coff[i], ks * 32, 0));
-      b_sc[i] = __builtin_amdgcn_raw_buffer_load_b16(bs_rs, b_soff[i], ks * 4, 0);
+        for (int i = 0; i < 8; ++i)
+          if (bias_col + i < N) e[i] = bias[bias_col + i];
+        v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+      }
+      *reinterpret_cast<uint4*>(lds + Cfg::BIAS_OFF + (ltc & 1) * 1024 + 16 * tid) = v;
+    }
+    ++lgs;
+    if (++lks == nk) {
+      lks = 0;
+      ++ltc;
+      lt += gridDim.x;
+      if (lt < tiles) set_load_tile(lt);
     }
   };
-  auto store_stage = [&](int buf) {
-    uint8_t* a_dst = lds + buf * Cfg::A_STAGE;
-    uint8_t* b_dst = lds + 2 * Cfg::A_STAGE + buf * Cfg::B_STAGE;
+
+  const int ra = wm * WM + r32, rb = wn * WN + r32;
+  const float tensor_scale = *reinterpret_cast<const float*>(As + a_trailer) *
+                             *reinterpret_cast<const float*>(Bs + b_trailer);
+
+  set_load_tile(lt);
+  load_next();
+  store_next();
+  int gs = 0, ctc = 0;
+
+  for (int ct = blockIdx.x; ct < tiles; ct += gridDim.x) {
+    int tm, tn;
+    tile_coords(ct, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    v16f acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < Cfg::A_ITEMS; ++i) {
-      const uint32_t s0 = e4m3_to_h2(a_sc[i] & 0xFFu), s1 = e4m3_to_h2((a_sc[i] >> 8) & 0xFFu);
-      *reinterpret_cast<uint4*>(a_dst + a_lds[i][0]) = dequant8(a_code[i].x, s0);
-      *reinterpret_cast<uint4*>(a_dst + a_lds[i][1]) = dequant8(a_code[i].y, s0);
-      *reinterpret_cast<uint4*>(a_dst + a_lds[i][2]) = dequant8(a_code[i].z, s1);
-      *reinterpret_cast<uint4*>(a_dst + a_lds[i][3]) = dequant8(a_code[i].w, s1);
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
+
+    for (int ks = 0; ks < nk; ++ks) {
+      block_sync();                          // stage gs is in LDS; nobody reads the other buffer
+      const bool loading = lt < tiles;
+      if (loading) load_next();
+      const uint8_t* st = lds + (gs & 1) * Cfg::STAGE;
+      v8h b_cur[FN], b_nxt[FN], a_cur, a_nxt;
+#pragma unroll
+      for (int f = 0; f < FN; ++f) b_cur[f] = nv_frag<Cfg>(st, BM + rb + 32 * f, 0, g);
+      a_cur = nv_frag<Cfg>(st, ra, 0, g);
+#pragma unroll
+      for (int t = 0; t < SUB; ++t) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          if (fm + 1 < FM) a_nxt = nv_frag<Cfg>(st, ra + 32 * (fm + 1), t, g);
+          else if (t + 1 < SUB) a_nxt = nv_frag<Cfg>(st, ra, t + 1, g);
+          if (fm == 0 && t + 1 < SUB) {
+#pragma unroll
+            for (int f = 0; f < FN; ++f) b_nxt[f] = nv_frag<Cfg>(st, BM + rb + 32 * f, t + 1, g);
+          }
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b_cur[fn], a_cur, acc[fm][fn], 0, 0, 0);
+          if (fm + 1 < FM || t + 1 < SUB) a_cur = a_nxt;
+        }
+        if (t + 1 < SUB) {
+#pragma unroll
+          for (int f = 0; f < FN; ++f) b_cur[f] = b_nxt[f];
+        }
+      }
+      if (loading) store_next();
+      ++gs;
     }
-#pragma unroll
-    for (int i = 0; i < Cfg::B_ITEMS; ++i) {
-      const uint32_t s0 = e4m3_to_h2(b_sc[i] & 0xFFu), s1 = e4m3_to_h2((b_sc[i] >> 8) & 0xFFu);
-      *reinterpret_cast<uint4*>(b_dst + b_lds[i][0]) = dequant8(b_code[i].x, s0);
-      *reinterpret_cast<uint4*>(b_dst + b_lds[i][1]) = dequant8(b_code[i].y, s0);
-      *reinterpret_cast<uint4*>(b_dst + b_lds[i][2]) = dequant8(b_code[i].z, s1);
-      *reinterpret_cast<uint4*>(b_dst + b_lds[i][3]) = dequant8(b_code[i].w, s1);
-    }
-  };
 
-  v4f acc[FM][FN];
+    // epilogue: register 4q + v of acc[fm][fn] is C[m][n + v] with
+    // m = m0 + wm WM + 32 fm + r32, n = n0 + wn WN + 32 fn + 8 q + 4 g; the
+    // tile's bias is in bias slot ctc & 1 (written with its first stage)
+    const uint8_t* lds_bias = lds + Cfg::BIAS_OFF + (ctc & 1) * 1024;
+    auto bias4 = [&](int nl) -> uint2 {
+      if (bias == nullptr) return make_uint2(0u, 0u);
+      return *reinterpret_cast<const uint2*>(lds_bias + 2 * nl);
+    };
+    if (staged) {
+      uint8_t* stg = lds + ((gs - 1) & 1) * Cfg::STAGE;   // buffer of the stage just consumed
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+      for (int h = 0; h < Cfg::WAVES_M; ++h) {
+        block_sync();                        // previous readers of the buffer are done
+        if (wm == h) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-
-  for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) load_stage(ks + 1);
-    const uint8_t* a_buf = lds + cur * Cfg::A_STAGE;
-    const uint8_t* b_buf = lds + 2 * Cfg::A_STAGE + cur * Cfg::B_STAGE;
+          for (int fn = 0; fn < FN; ++fn) {
+            uint2 bb[4];                     // bias of this lane's columns of fragment column fn
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      v8h bfrag[FN];
+            for (int q = 0; q < 4; ++q) bb[q] = bias4(wn * WN + 32 * fn + 8 * q + 4 * g);
 #pragma unroll
-      for (int f = 0; f < FN; ++f)
-        bfrag[f] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(b_buf + (sub ? b_off1 : b_off0) + 16 * f * ROWB));
+            for (int fm = 0; fm < FM; ++fm) {
+              const int lr = 32 * fm + r32;
+              uint32_t P[4][2];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float v0 = acc[fm][fn][4 * q + 0] * tensor_scale + bf16_to_f32(bb[q].x & 0xFFFFu);
+                const float v1 = acc[fm][fn][4 * q + 1] * tensor_scale + bf16_to_f32(bb[q].x >> 16);
+                const float v2 = acc[fm][fn][4 * q + 2] * tensor_scale + bf16_to_f32(bb[q].y & 0xFFFFu);
+                const float v3 = acc[fm][fn][4 * q + 3] * tensor_scale + bf16_to_f32(bb[q].y >> 16);
+                P[q][0] = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
+                P[q][1] = f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16);
+              }
+#pragma unroll
+              for (int p = 0; p < 2; ++p) {
+                // lane g = 0 ends with columns 16p .. 16p + 7 of the fragment,
+                // lane g = 1 with 16p + 8 .. + 15
+                const auto s0 = __builtin_amdgcn_permlane32_swap(P[2 * p][0], P[2 * p + 1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(P[2 * p][1], P[2 * p + 1][1], false, false);
+                const int chunk = (wn * WN + 32 * fn + 16 * p + 8 * g) >> 3;
+                *reinterpret_cast<uint4*>(stg + lr * (BN * 2) + ((chunk ^ (lr & (CPR - 1))) * 16)) =
+                    make_uint4(s0[0], s1[0], s0[1], s1[1]);
+              }
+            }
+          }
+        }
+        block_sync();
+#pragma unroll
+        for (int j = 0; j < Cfg::EPI_STORES; ++j) {
+          const int id = tid + j * Cfg::NT;
+          const int row = id / CPR, c = id % CPR;
+          const int m = m0 + h * WM + row, n = n0 + 8 * c;
+          const uint4 w = *reinterpret_cast<const uint4*>(stg + row * (BN * 2) + ((c ^ (row & (CPR - 1))) * 16));
+          const int off = (m < M && n < N) ? (m * N + n) * 2 : (int)0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(v4u{w.x, w.y, w.z, w.w}, c_rs, off, 0, 0);
+        }
+      }
+    } else {
+      const bool vec = ((N & 3) == 0);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
-        const v8h afrag =
-            __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(a_buf + (sub ? a_off1 : a_off0) + 16 * fm * ROWB));
+        const int m = m0 + wm * WM + 32 * fm + r32;
+        if (m >= M) continue;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfrag[fn], afrag, acc[fm][fn], 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn * WN + 32 * fn + 8 * q + 4 * g;
+            if (n >= N) continue;
+            const uint2 bb = bias4(n - n0);
+            float v[4];
+            v[0] = acc[fm][fn][4 * q + 0] * tensor_scale + bf16_to_f32(bb.x & 0xFFFFu);
+            v[1] = acc[fm][fn][4 * q + 1] * tensor_scale + bf16_to_f32(bb.x >> 16);
+            v[2] = acc[fm][fn][4 * q + 2] * tensor_scale + bf16_to_f32(bb.y & 0xFFFFu);
+            v[3] = acc[fm][fn][4 * q + 3] * tensor_scale + bf16_to_f32(bb.y >> 16);
+            const int64_t off = (int64_t)m * N + n;
+            if (out_f32) {
+              float* c = reinterpret_cast<float*>(C) + off;
+              if (vec && n + 3 < N) {
+                *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
+              } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  if (n + j < N) c[j] = v[j];
+              }
+            } else {
+              uint16_t* c = reinterpret_cast<uint16_t*>(C) + off;
+              if (vec && n + 3 < N) {
+                *reinterpret_cast<uint2*>(c) = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                                          f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+              } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  if (n + j < N) c[j] = (uint16_t)f32_to_bf16_rne(v[j]);
+              }
+            }
+          }
       }
     }
-    if (more) store_stage(cur ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: the two tensor scales live in the scale buffers' trailers
-  const float sta = *reinterpret_cast<const float*>(As + a_trailer);
-  const float stb = *reinterpret_cast<const float*>(Bs + b_trailer);
-  const float scale = sta * stb;
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int m = m0 + wm * WM + 16 * fm + r16;
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int n = n0 + wn * WN + 16 * fn + 4 * g;
-      nv_store4(C, M, N, m, n, acc[fm][fn], scale, bias, out_f32);
-    }
+    ++ctc;
   }
 }
 
@@ -274,19 +354,49 @@ static hipError_t run_nv(const uint8_t* A, const uint8_t* As, const uint8_t* B, 
   const int64_t kpad = round_up(K, kAlignK);
   const int tiles_m = (int)((M + Cfg::BM - 1) / Cfg::BM);
   const int tiles_n = (int)((N + Cfg::BN - 1) / Cfg::BN);
+  const int tiles = tiles_m * tiles_n;
   const int a_tr = (int)round_up(M * (kpad / 16), 16);
   const int b_tr = (int)round_up(N * (kpad / 16), 16);
-  gemm_nv_kernel<Cfg><<<tiles_m * tiles_n, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, bias,
-                                                                  out_f32, tiles_m, tiles_n, a_tr, b_tr);
+  // persistent grid: one slot per resident workgroup, a multiple of 8
+  const int slots = std::max(8, (Cfg::OCC * cu_count()) / 8 * 8);
+  const int grid = tiles <= slots ? tiles : slots;
+  gemm_nv_kernel<Cfg><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, bias, out_f32,
+                                                    tiles_m, tiles_n, a_tr, b_tr);
   return hipGetLastError();
 }
 
-const char* plan_gemm_nvfp4(int64_t, int64_t) { return "gemm_nv_kernel<nvfp4, 128x128>"; }
+// Tile shape with the least work per CU lost to a partly filled last round:
+// rounds of resident workgroups x tile area x workgroups per CU. 128x128 (4
+// waves of 64x64, two workgroups per CU) fills the chip on the weight-
+// gradient shapes (4096 x 1024 outputs, K = tokens), where the large tiles
+// leave most CUs idle; on ties the larger tiles win.
+enum NvTile { NV_128x128 = 0, NV_192x256 = 1, NV_256x256 = 2 };
+
+static NvTile nv_choose(int64_t M, int64_t N) {
+  auto cost = [&](int bm, int bn, int occ) {
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    const int64_t slots = std::max(8, occ * cu_count() / 8 * 8);
+    return (double)((tiles + slots - 1) / slots) * bm * bn * occ;
+  };
+  const double c128 = cost(128, 128, 2), c192 = cost(192, 256, 1), c256 = cost(256, 256, 1);
+  if (c128 < c192 && c128 < c256) return NV_128x128;
+  return c256 < c192 ? NV_256x256 : NV_192x256;
+}
+
+const char* plan_gemm_nvfp4(int64_t M, int64_t N) {
+  static const char* names[3] = {"gemm_nv_kernel<nvfp4, 128x128>", "gemm_nv_kernel<nvfp4, 192x256>",
+                                 "gemm_nv_kernel<nvfp4, 256x256>"};
+  return names[nv_choose(M, N)];
+}
 
 hipError_t launch_gemm_nvfp4(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
                              int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
                              hipStream_t stream) {
-  return run_nv<NvCfg<128, 128, 2, 2, 0>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+  switch (nv_choose(M, N)) {
+    case NV_128x128: return run_nv<NvCfg<128, 128, 2, 2, 2>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+    case NV_256x256: return run_nv<NvCfg<256, 256, 2, 4, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+    default:         return run_nv<NvCfg<192, 256, 2, 4, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+  }
 }
 
 }  // namespace mx

@@ -187,6 +187,22 @@ def test_gemm_many_tiles_full(fmt, k):
     check_full(a, b, fmt, bias, "bf16")
 
 
+@pytest.mark.parametrize("mnk,plan", [
+    ((1000, 1000, 512), "128x128"),     # few tiles: two 4-wave workgroups per CU
+    ((4160, 4096, 384), "192x256"),     # more tiles than workgroups, ragged M
+    ((4096, 4096, 256), "256x256"),     # one full round of 256 tiles
+])
+def test_gemm_nvfp4_tile_shapes(mnk, plan):
+    """Each NVFP4 tile shape the host can choose, every output checked."""
+    m, n, k = mnk
+    assert api.gemm_plan(m, n, k, "nvfp4").endswith(plan + ">")
+    a = W.np_activation((m, k), seed=71 + k)
+    b = W.np_normal((n, k), seed=72 + k, std=W.W_STD)
+    bias = W.np_normal((n,), seed=73, std=W.BIAS_STD)
+    log(f"gemm nvfp4 plan={api.gemm_plan(m, n, k, 'nvfp4')} m={m} n={n} k={k}")
+    check_full(a, b, "nvfp4", bias, "bf16")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_gemm_bias_2byte_aligned(fmt):
     """A bias pointer that is only 2-byte aligned (a view at element offset 1)
