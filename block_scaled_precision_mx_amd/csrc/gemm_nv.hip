@@ -60,20 +60,26 @@ struct NvCfg {
   static_assert(BN * 2 <= 1024 && BN / 8 <= NT, "a tile's bias must fit one bias slot");
 };
 
-// fp16 bits of a non-negative E4M3 scale byte, replicated into both halves.
-__device__ __forceinline__ uint32_t e4m3_to_h2(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float f = e ? (float)(8u + m) * __uint_as_float((e - 10u + 127u) << 23) : (float)m * 0.001953125f;
-  _Float16 h = (_Float16)f;   // exact: E4M3 values are fp16 values
-  uint32_t hb = (uint32_t)__builtin_bit_cast(uint16_t, h);
-  return hb | (hb << 16);
+// E4M3 scale byte j of `scales` (sign ignored) placed as fp16 bits into both
+// halves of a dword, read as fp16 it is 2^-8 times the E4M3 value: the 4
+// exponent and 3 mantissa bits land in the low bits of fp16's 5-bit exponent
+// and the top of its mantissa, which rebiases the exponent by 8 for normal
+// values and turns E4M3 subnormals into fp16 subnormals of the same
+// significand. The factor 2^8 is carried by the element table below.
+template <int J>
+__device__ __forceinline__ uint32_t e4m3_h2_div256(uint32_t scales) {
+  // bytes {J, 0, J, 0} -> two 16-bit copies of the byte, then shift into place
+  constexpr uint32_t sel = 0x0C000C00u | (J << 16) | J;
+  return __builtin_amdgcn_perm(0u, scales & 0x7F7F7F7Fu, sel) << 7;
 }
 
-// 8 E2M1 codes (one dword, element j in nibble j) times a scale (half2 bits)
-// -> 8 fp16 values in 4 dwords, element order preserved.
+// 8 E2M1 codes (one dword, element j in nibble j) times a scale (fp16 pair
+// from e4m3_h2_div256) -> 8 fp16 values in 4 dwords, element order kept.
+// The table holds 2^8 times the E2M1 magnitudes, so the products are the
+// exact element values (normal fp16: between 2^-10 and 2688 in magnitude).
 __device__ __forceinline__ uint4 dequant8(uint32_t x, uint32_t scale_h2) {
-  // fp16 high byte of each E2M1 magnitude: 0, 0.5, 1, 1.5 | 2, 3, 4, 6
-  constexpr uint32_t LUT_LO = 0x3E3C3800u, LUT_HI = 0x46444240u;
+  // fp16 high byte of 256 x each E2M1 magnitude: 0, 128, 256, 384 | 512, 768, 1024, 1536
+  constexpr uint32_t LUT_LO = 0x5E5C5800u, LUT_HI = 0x66646260u;
   const uint32_t lo = x & 0x0F0F0F0Fu;            // elements 0, 2, 4, 6 (byte k = element 2k)
   const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;     // elements 1, 3, 5, 7
   const uint32_t plo = __builtin_amdgcn_perm(LUT_HI, LUT_LO, lo & 0x07070707u) | ((lo & 0x08080808u) << 4);
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
   // BM) or B row tid - BM (threads past BM + BN stage nothing). Loader
   // cursor: tile lt, its stage lks; lgs / ltc count stages / tiles staged.
   const bool stager = tid < BM + BN;
-  const bool st_is_a = tid < BM;
+  const bool st_is_a = wave < BM / 64;       // wave-uniform: BM is a multiple of 64
   const int st_row = st_is_a ? tid : tid - BM;
   int lt = blockIdx.x, lks = 0, lgs = 0, ltc = 0;
   int code_off = 0, scale_off = 0, bias_col = 0;
@@ -165,8 +171,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
   };
   auto store_next = [&]() {                  // registers -> dequantized fp16 row in LDS
     uint8_t* dst = lds + (lgs & 1) * Cfg::STAGE + tid * RB;
-    const uint32_t s[4] = {e4m3_to_h2(ld_scale & 0xFFu), e4m3_to_h2((ld_scale >> 8) & 0xFFu),
-                           e4m3_to_h2((ld_scale >> 16) & 0xFFu), e4m3_to_h2(ld_scale >> 24)};
+    const uint32_t s[4] = {e4m3_h2_div256<0>(ld_scale), e4m3_h2_div256<1>(ld_scale),
+                           e4m3_h2_div256<2>(ld_scale), e4m3_h2_div256<3>(ld_scale)};
     const uint32_t w[8] = {ld_code0.x, ld_code0.y, ld_code0.z, ld_code0.w,
                            ld_code1.x, ld_code1.y, ld_code1.z, ld_code1.w};
     if (stager) {
