@@ -32,6 +32,7 @@
 #include "mx_launch.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace mx {
 
@@ -49,7 +50,8 @@ struct NvCfg {
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int STAGE = (BM + BN) * RB;
   static constexpr int BIAS_OFF = 2 * STAGE;                  // two 1-KB bias slots (tile parity)
-  static constexpr int LDS = BIAS_OFF + 2 * 1024;
+  static constexpr int SCRATCH_OFF = BIAS_OFF + 2 * 1024;     // rows of threads past BM + BN
+  static constexpr int LDS = SCRATCH_OFF + (NT - BM - BN) * RB;
   static constexpr int CPR = BN / 8;
   static constexpr int EPI_STORES = WM * CPR / NT;
   static_assert(BM + BN <= NT, "one staged row per thread");
@@ -104,7 +106,11 @@ __device__ __forceinline__ v8h nv_frag(const uint8_t* st, int row, int t, int g)
   return __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(st + row * Cfg::RB + swz(row, 2 * t + g) * 16));
 }
 
-template <class Cfg>
+// STAGED: bf16 output written through LDS in 16-byte rows (N % 8 == 0 and
+// M N < 2^30); otherwise each lane writes its own outputs. The two are
+// separate kernels so that the waits of a tile's first stage are the same on
+// every path into it.
+template <class Cfg, bool STAGED>
 __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_t* __restrict__ A,
                                                                     const uint8_t* __restrict__ As,
                                                                     const uint8_t* __restrict__ B,
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
   const int srow = kpad / 16;                // scale bytes per row
   const int nk = kpad / Cfg::KS;             // K_pad is a multiple of 128
   const int g = lane >> 5, r32 = lane & 31;
-  const bool staged = !out_f32 && (N & 7) == 0 && (int64_t)M * N < ((int64_t)1 << 30);
+  constexpr bool staged = STAGED;
 
   const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, M * row_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, N * row_bytes, 0x00020000);
@@ -140,13 +146,22 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
   const __amdgpu_buffer_rsrc_t bias_rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)bias, (short)0, bias_vec ? N * 2 : 0, 0x00020000);
 
-  // Staging: thread tid stages row tid of the stage, i.e. A row tid (tid <
-  // BM) or B row tid - BM (threads past BM + BN stage nothing). Loader
-  // cursor: tile lt, its stage lks; lgs / ltc count stages / tiles staged.
+  // Staging: thread tid stages row tid of the stage, i.e. A row tid (waves
+  // below BM / 64) or B row tid - BM; threads past BM + BN write their
+  // (zero) rows into a scratch area. Loader cursor: tile lt, its stage lks,
+  // ltc tiles begun. The loads of a stage run two stages ahead of the
+  // matrix instructions, into one of two register sets, so that each stage
+  // dequantizes the next stage's rows (loaded a full stage earlier) in the
+  // same instruction stream as its own matrix instructions. Every stage
+  // issues exactly 4 loads per wave (2 x 16 code bytes, 4 scale bytes, 16
+  // bias bytes); those with nothing to load use an offset past the buffer's
+  // range and read zero.
   const bool stager = tid < BM + BN;
   const bool st_is_a = wave < BM / 64;       // wave-uniform: BM is a multiple of 64
   const int st_row = st_is_a ? tid : tid - BM;
-  int lt = blockIdx.x, lks = 0, lgs = 0, ltc = 0;
+  uint8_t* const st_dst = stager ? lds + tid * RB : lds + Cfg::SCRATCH_OFF + (tid - BM - BN) * RB;
+  const int st_buf_stride = stager ? Cfg::STAGE : 0;
+  int lt = blockIdx.x, lks = 0, ltc = 0;
   int code_off = 0, scale_off = 0, bias_col = 0;
   auto set_load_tile = [&](int t) {
     int tm, tn;
@@ -156,31 +171,49 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
     scale_off = r * srow;
     bias_col = tn * BN + 8 * tid;            // first bias column of threads tid < BN / 8
   };
-  uint4 ld_code0 = make_uint4(0u, 0u, 0u, 0u), ld_code1 = ld_code0, ld_bias = ld_code0;
-  uint32_t ld_scale = 0;
-  auto load_next = [&]() {                   // global -> registers
+  struct Raw {
+    uint4 c0, c1, bias;
+    uint32_t sc;
+    int first, slot;                         // wave-uniform: first stage of a tile, its bias slot
+  };
+  constexpr int OOB = (int)0x80000000u;
+  auto load = [&](Raw& R) {                  // global -> registers, then advance the cursor
+    const bool loading = lt < tiles;
     const __amdgpu_buffer_rsrc_t crs = st_is_a ? a_rs : b_rs;
     const __amdgpu_buffer_rsrc_t srs = st_is_a ? as_rs : bs_rs;
-    const int co = stager ? code_off + lks * 32 : (int)0x80000000u;
-    const int so = stager ? scale_off + lks * 4 : (int)0x80000000u;
-    ld_code0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(crs, co, 0, 0));
-    ld_code1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(crs, co, 16, 0));
-    ld_scale = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 0, 0);
-    if (lks == 0 && bias_vec && tid < BN / 8)
-      ld_bias = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bias_rs, bias_col * 2, 0, 0));
-  };
-  auto store_next = [&]() {                  // registers -> dequantized fp16 row in LDS
-    uint8_t* dst = lds + (lgs & 1) * Cfg::STAGE + tid * RB;
-    const uint32_t s[4] = {e4m3_h2_div256<0>(ld_scale), e4m3_h2_div256<1>(ld_scale),
-                           e4m3_h2_div256<2>(ld_scale), e4m3_h2_div256<3>(ld_scale)};
-    const uint32_t w[8] = {ld_code0.x, ld_code0.y, ld_code0.z, ld_code0.w,
-                           ld_code1.x, ld_code1.y, ld_code1.z, ld_code1.w};
-    if (stager) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(dst + swz(tid, c) * 16) = dequant8(w[c], s[c / 2]);
+    const bool row_live = stager && loading;
+    const int co = row_live ? code_off + lks * 32 : OOB;
+    const int so = row_live ? scale_off + lks * 4 : OOB;
+    const int bo = (loading && lks == 0 && bias_vec && tid < BN / 8) ? bias_col * 2 : OOB;
+    R.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(crs, co, 0, 0));
+    R.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(crs, co, 16, 0));
+    R.sc = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 0, 0);
+    R.bias = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bias_rs, bo, 0, 0));
+    R.first = loading && lks == 0;
+    R.slot = ltc & 1;
+    if (loading && ++lks == nk) {
+      lks = 0;
+      ++ltc;
+      lt += gridDim.x;
+      if (lt < tiles) set_load_tile(lt);
     }
-    if (lks == 0 && bias != nullptr && tid < BN / 8) {   // the tile's bias, into bias slot ltc & 1
-      uint4 v = ld_bias;
+  };
+  // registers -> dequantized fp16 row in LDS buffer `buf` (one 16-byte
+  // chunk per call, chunk c covers K 8c .. 8c + 7 of the stage)
+  auto dequant_chunk = [&](const Raw& R, int buf, int c) {
+    const uint32_t w = c < 4 ? (&R.c0.x)[c] : (&R.c1.x)[c - 4];
+    uint32_t sh;
+    switch (c / 2) {
+      case 0: sh = e4m3_h2_div256<0>(R.sc); break;
+      case 1: sh = e4m3_h2_div256<1>(R.sc); break;
+      case 2: sh = e4m3_h2_div256<2>(R.sc); break;
+      default: sh = e4m3_h2_div256<3>(R.sc); break;
+    }
+    *reinterpret_cast<uint4*>(st_dst + buf * st_buf_stride + swz(tid, c) * 16) = dequant8(w, sh);
+  };
+  auto store_bias = [&](const Raw& R) {      // a tile's bias, into bias slot R.slot
+    if (R.first && bias != nullptr && tid < BN / 8) {
+      uint4 v = R.bias;
       if (!bias_vec) {
         uint32_t e[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
@@ -188,14 +221,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
           if (bias_col + i < N) e[i] = bias[bias_col + i];
         v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
       }
-      *reinterpret_cast<uint4*>(lds + Cfg::BIAS_OFF + (ltc & 1) * 1024 + 16 * tid) = v;
-    }
-    ++lgs;
-    if (++lks == nk) {
-      lks = 0;
-      ++ltc;
-      lt += gridDim.x;
-      if (lt < tiles) set_load_tile(lt);
+      *reinterpret_cast<uint4*>(lds + Cfg::BIAS_OFF + R.slot * 1024 + 16 * tid) = v;
     }
   };
 
@@ -203,53 +229,85 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
   const float tensor_scale = *reinterpret_cast<const float*>(As + a_trailer) *
                              *reinterpret_cast<const float*>(Bs + b_trailer);
 
+  Raw R0, R1;
   set_load_tile(lt);
-  load_next();
-  store_next();
-  int gs = 0, ctc = 0;
+  load(R0);
+  load(R1);
+  wait_vm<4>();                              // R0 has landed
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dequant_chunk(R0, 0, c);
+  store_bias(R0);
+  if (STAGED) {
+    // as many (discarded) stores as a tile's epilogue issues, so that the
+    // first stage finds the same operations in flight on every path
+#pragma unroll
+    for (int j = 0; j < Cfg::WAVES_M * Cfg::EPI_STORES; ++j)
+      __builtin_amdgcn_raw_buffer_store_b128(v4u{0u, 0u, 0u, 0u}, c_rs, OOB + 16 * j, 0, 0);   // distinct: kept
+  }
+  int ctc = 0;
+
+  // One stage: matrix instructions on LDS buffer P while the other register
+  // set's rows are dequantized into buffer 1 - P; LS receives the loads of
+  // the stage after next. Every tile has an even number of stages, so its
+  // stages use buffers 0, 1, 0, ..., 1.
+  v16f acc[FM][FN];
+  // DS's loads are waited for by the compiler's own bookkeeping, which
+  // leaves the previous tile's stores and LS's loads in flight.
+  auto stage = [&](auto parity, Raw& LS, Raw& DS) {
+    constexpr int P = decltype(parity)::value;
+    block_sync();                            // buffer P is complete; nobody reads buffer 1 - P
+    load(LS);
+    const uint8_t* st = lds + P * Cfg::STAGE;
+    constexpr int TOTAL = SUB * FM * FN;
+    v8h b_cur[FN], b_nxt[FN], a_cur, a_nxt;
+#pragma unroll
+    for (int f = 0; f < FN; ++f) b_cur[f] = nv_frag<Cfg>(st, BM + rb + 32 * f, 0, g);
+    a_cur = nv_frag<Cfg>(st, ra, 0, g);
+#pragma unroll
+    for (int t = 0; t < SUB; ++t) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        if (fm + 1 < FM) a_nxt = nv_frag<Cfg>(st, ra + 32 * (fm + 1), t, g);
+        else if (t + 1 < SUB) a_nxt = nv_frag<Cfg>(st, ra, t + 1, g);
+        if (fm == 0 && t + 1 < SUB) {
+#pragma unroll
+          for (int f = 0; f < FN; ++f) b_nxt[f] = nv_frag<Cfg>(st, BM + rb + 32 * f, t + 1, g);
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b_cur[fn], a_cur, acc[fm][fn], 0, 0, 0);
+          const int i = (t * FM + fm) * FN + fn;            // matrix instruction index in the stage
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+            if (i == c * TOTAL / 8) dequant_chunk(DS, 1 - P, c);
+        }
+        if (fm + 1 < FM || t + 1 < SUB) a_cur = a_nxt;
+      }
+      if (t + 1 < SUB) {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) b_cur[f] = b_nxt[f];
+      }
+    }
+    store_bias(DS);
+  };
 
   for (int ct = blockIdx.x; ct < tiles; ct += gridDim.x) {
     int tm, tn;
     tile_coords(ct, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    v16f acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-    for (int ks = 0; ks < nk; ++ks) {
-      block_sync();                          // stage gs is in LDS; nobody reads the other buffer
-      const bool loading = lt < tiles;
-      if (loading) load_next();
-      const uint8_t* st = lds + (gs & 1) * Cfg::STAGE;
-      v8h b_cur[FN], b_nxt[FN], a_cur, a_nxt;
-#pragma unroll
-      for (int f = 0; f < FN; ++f) b_cur[f] = nv_frag<Cfg>(st, BM + rb + 32 * f, 0, g);
-      a_cur = nv_frag<Cfg>(st, ra, 0, g);
-#pragma unroll
-      for (int t = 0; t < SUB; ++t) {
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          if (fm + 1 < FM) a_nxt = nv_frag<Cfg>(st, ra + 32 * (fm + 1), t, g);
-          else if (t + 1 < SUB) a_nxt = nv_frag<Cfg>(st, ra, t + 1, g);
-          if (fm == 0 && t + 1 < SUB) {
-#pragma unroll
-            for (int f = 0; f < FN; ++f) b_nxt[f] = nv_frag<Cfg>(st, BM + rb + 32 * f, t + 1, g);
-          }
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b_cur[fn], a_cur, acc[fm][fn], 0, 0, 0);
-          if (fm + 1 < FM || t + 1 < SUB) a_cur = a_nxt;
-        }
-        if (t + 1 < SUB) {
-#pragma unroll
-          for (int f = 0; f < FN; ++f) b_cur[f] = b_nxt[f];
-        }
-      }
-      if (loading) store_next();
-      ++gs;
+    // the first pair is peeled: its predecessors are the prologue and the
+    // previous tile's epilogue, not the loop's back edge
+    stage(std::integral_constant<int, 0>{}, R0, R1);
+    stage(std::integral_constant<int, 1>{}, R1, R0);
+    for (int ks = 2; ks < nk; ks += 2) {
+      stage(std::integral_constant<int, 0>{}, R0, R1);
+      stage(std::integral_constant<int, 1>{}, R1, R0);
     }
 
     // epilogue: register 4q + v of acc[fm][fn] is C[m][n + v] with
@@ -260,8 +318,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
       if (bias == nullptr) return make_uint2(0u, 0u);
       return *reinterpret_cast<const uint2*>(lds_bias + 2 * nl);
     };
-    if (staged) {
-      uint8_t* stg = lds + ((gs - 1) & 1) * Cfg::STAGE;   // buffer of the stage just consumed
+    if constexpr (STAGED) {
+      uint8_t* stg = lds + Cfg::STAGE;     // buffer 1: the last stage's, just consumed
 #pragma unroll
       for (int h = 0; h < Cfg::WAVES_M; ++h) {
         block_sync();                        // previous readers of the buffer are done
@@ -352,6 +410,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
     }
     ++ctc;
   }
+  wait_vm<0>();                              // the drained loader's zero loads and the last stores
 }
 
 template <class Cfg>
@@ -366,43 +425,40 @@ static hipError_t run_nv(const uint8_t* A, const uint8_t* As, const uint8_t* B, 
   // persistent grid: one slot per resident workgroup, a multiple of 8
   const int slots = std::max(8, (Cfg::OCC * cu_count()) / 8 * 8);
   const int grid = tiles <= slots ? tiles : slots;
-  gemm_nv_kernel<Cfg><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, bias, out_f32,
-                                                    tiles_m, tiles_n, a_tr, b_tr);
+  const bool staged = !out_f32 && (N & 7) == 0 && M * N < ((int64_t)1 << 30);
+  if (staged)
+    gemm_nv_kernel<Cfg, true><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, bias,
+                                                            out_f32, tiles_m, tiles_n, a_tr, b_tr);
+  else
+    gemm_nv_kernel<Cfg, false><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, bias,
+                                                             out_f32, tiles_m, tiles_n, a_tr, b_tr);
   return hipGetLastError();
 }
 
 // Tile shape with the least work per CU lost to a partly filled last round:
 // rounds of resident workgroups x tile area x workgroups per CU. 128x128 (4
 // waves of 64x64, two workgroups per CU) fills the chip on the weight-
-// gradient shapes (4096 x 1024 outputs, K = tokens), where the large tiles
-// leave most CUs idle; on ties the larger tiles win.
-enum NvTile { NV_128x128 = 0, NV_192x256 = 1, NV_256x256 = 2 };
-
-static NvTile nv_choose(int64_t M, int64_t N) {
+// gradient shapes (4096 x 1024 outputs, K = tokens), where 192x256 tiles
+// leave most CUs idle; on ties the larger tiles win (less dequantization
+// and LDS traffic per output).
+static bool nv_small_tiles(int64_t M, int64_t N) {
   auto cost = [&](int bm, int bn, int occ) {
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const int64_t slots = std::max(8, occ * cu_count() / 8 * 8);
     return (double)((tiles + slots - 1) / slots) * bm * bn * occ;
   };
-  const double c128 = cost(128, 128, 2), c192 = cost(192, 256, 1), c256 = cost(256, 256, 1);
-  if (c128 < c192 && c128 < c256) return NV_128x128;
-  return c256 < c192 ? NV_256x256 : NV_192x256;
+  return cost(128, 128, 2) < cost(192, 256, 1);
 }
 
 const char* plan_gemm_nvfp4(int64_t M, int64_t N) {
-  static const char* names[3] = {"gemm_nv_kernel<nvfp4, 128x128>", "gemm_nv_kernel<nvfp4, 192x256>",
-                                 "gemm_nv_kernel<nvfp4, 256x256>"};
-  return names[nv_choose(M, N)];
+  return nv_small_tiles(M, N) ? "gemm_nv_kernel<nvfp4, 128x128>" : "gemm_nv_kernel<nvfp4, 192x256>";
 }
 
 hipError_t launch_gemm_nvfp4(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
                              int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
                              hipStream_t stream) {
-  switch (nv_choose(M, N)) {
-    case NV_128x128: return run_nv<NvCfg<128, 128, 2, 2, 2>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-    case NV_256x256: return run_nv<NvCfg<256, 256, 2, 4, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-    default:         return run_nv<NvCfg<192, 256, 2, 4, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-  }
+  if (nv_small_tiles(M, N)) return run_nv<NvCfg<128, 128, 2, 2, 2>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+  return run_nv<NvCfg<192, 256, 2, 4, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
 }
 
 }  // namespace mx

@@ -113,6 +113,6 @@ def test_gemm_plan_names(L):
     assert L.mx_gemm_plan(4096, 1024, 11235, 3).decode() == "gemm_nv_kernel<nvfp4, 128x128>"
     assert L.mx_gemm_plan(1024, 4096, 11235, 3).decode() == "gemm_nv_kernel<nvfp4, 128x128>"
     assert L.mx_gemm_plan(11235, 4096, 1024, 3).decode() == "gemm_nv_kernel<nvfp4, 192x256>"
-    assert L.mx_gemm_plan(4096, 4096, 256, 3).decode() == "gemm_nv_kernel<nvfp4, 256x256>"
+    assert L.mx_gemm_plan(4160, 4096, 384, 3).decode() == "gemm_nv_kernel<nvfp4, 192x256>"
     assert L.mx_gemm_plan(0, 4, 4, 1) is None
     assert L.mx_gemm_plan(4, 4, 4, 9) is None

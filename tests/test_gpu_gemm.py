@@ -190,7 +190,7 @@ def test_gemm_many_tiles_full(fmt, k):
 @pytest.mark.parametrize("mnk,plan", [
     ((1000, 1000, 512), "128x128"),     # few tiles: two 4-wave workgroups per CU
     ((4160, 4096, 384), "192x256"),     # more tiles than workgroups, ragged M
-    ((4096, 4096, 256), "256x256"),     # one full round of 256 tiles
+    ((2048, 8192, 256), "128x128"),     # two rounds of 128x128 workgroups, every slot walks 2 tiles
 ])
 def test_gemm_nvfp4_tile_shapes(mnk, plan):
     """Each NVFP4 tile shape the host can choose, every output checked."""
