@@ -11,8 +11,8 @@
 // product of two such values (<= 12 bits) is exact in the fp32 matrix
 // accumulator too. The kernel therefore dequantizes each operand tile to
 // fp16 while staging it into LDS (once per tile row, shared by all waves):
-// nibble -> fp16 via a byte-permute table, times the block scale as a packed
-// fp16 multiply; then runs V_MFMA_F32_32X32X16_F16 with fp32 accumulation
+// two codes -> fp16 pair by the hardware conversion, times the block scale
+// as a packed fp16 multiply; then runs V_MFMA_F32_32X32X16_F16 with fp32 accumulation
 // and applies s_tA * s_tB in the epilogue. The roof of this path is the fp16
 // matrix rate; the accuracy is that of the exact method (fp32 accumulation
 // only).
@@ -67,7 +67,7 @@ struct NvCfg {
 // exponent and 3 mantissa bits land in the low bits of fp16's 5-bit exponent
 // and the top of its mantissa, which rebiases the exponent by 8 for normal
 // values and turns E4M3 subnormals into fp16 subnormals of the same
-// significand. The factor 2^8 is carried by the element table below.
+// significand. The factor 2^8 is carried by the element conversion below.
 template <int J>
 __device__ __forceinline__ uint32_t e4m3_h2_div256(uint32_t scales) {
   // bytes {J, 0, J, 0} -> two 16-bit copies of the byte, then shift into place
@@ -77,26 +77,18 @@ __device__ __forceinline__ uint32_t e4m3_h2_div256(uint32_t scales) {
 
 // 8 E2M1 codes (one dword, element j in nibble j) times a scale (fp16 pair
 // from e4m3_h2_div256) -> 8 fp16 values in 4 dwords, element order kept.
-// The table holds 2^8 times the E2M1 magnitudes, so the products are the
-// exact element values (normal fp16: between 2^-10 and 2688 in magnitude).
+// The hardware conversion turns the two codes of one byte into fp16 (low
+// nibble -> low half) times a power of two taken from its fp32 scale
+// operand (only the exponent is used); with 2^8 there, the packed multiply
+// by the E4M3 scale / 2^8 gives the exact element values (products of at
+// most 6 significant bits, between 2^-10 and 2688 in magnitude: normal fp16).
 __device__ __forceinline__ uint4 dequant8(uint32_t x, uint32_t scale_h2) {
-  // fp16 high byte of 256 x each E2M1 magnitude: 0, 128, 256, 384 | 512, 768, 1024, 1536
-  constexpr uint32_t LUT_LO = 0x5E5C5800u, LUT_HI = 0x66646260u;
-  const uint32_t lo = x & 0x0F0F0F0Fu;            // elements 0, 2, 4, 6 (byte k = element 2k)
-  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;     // elements 1, 3, 5, 7
-  const uint32_t plo = __builtin_amdgcn_perm(LUT_HI, LUT_LO, lo & 0x07070707u) | ((lo & 0x08080808u) << 4);
-  const uint32_t phi = __builtin_amdgcn_perm(LUT_HI, LUT_LO, hi & 0x07070707u) | ((hi & 0x08080808u) << 4);
-  uint32_t h[4];
-  h[0] = __builtin_amdgcn_perm(phi, plo, 0x040C000Cu);   // {elem0, elem1}
-  h[1] = __builtin_amdgcn_perm(phi, plo, 0x050C010Cu);
-  h[2] = __builtin_amdgcn_perm(phi, plo, 0x060C020Cu);
-  h[3] = __builtin_amdgcn_perm(phi, plo, 0x070C030Cu);
   const v2h s = __builtin_bit_cast(v2h, scale_h2);
   uint4 out;
-  out.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, h[0]) * s);
-  out.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, h[1]) * s);
-  out.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, h[2]) * s);
-  out.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, h[3]) * s);
+  out.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 0) * s);
+  out.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 1) * s);
+  out.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 2) * s);
+  out.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 3) * s);
   return out;
 }
 
