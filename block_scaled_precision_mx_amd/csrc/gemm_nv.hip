@@ -331,8 +331,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
                 const float v1 = acc[fm][fn][4 * q + 1] * tensor_scale + bf16_to_f32(bb[q].x >> 16);
                 const float v2 = acc[fm][fn][4 * q + 2] * tensor_scale + bf16_to_f32(bb[q].y & 0xFFFFu);
                 const float v3 = acc[fm][fn][4 * q + 3] * tensor_scale + bf16_to_f32(bb[q].y >> 16);
-                P[q][0] = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
-                P[q][1] = f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16);
+                P[q][0] = pack_bf16x2(v0, v1);
+                P[q][1] = pack_bf16x2(v2, v3);
               }
 #pragma unroll
               for (int p = 0; p < 2; ++p) {
@@ -389,8 +389,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
             } else {
               uint16_t* c = reinterpret_cast<uint16_t*>(C) + off;
               if (vec && n + 3 < N) {
-                *reinterpret_cast<uint2*>(c) = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                                          f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+                *reinterpret_cast<uint2*>(c) = make_uint2(pack_bf16x2(v[0], v[1]),
+                                                          pack_bf16x2(v[2], v[3]));
               } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)

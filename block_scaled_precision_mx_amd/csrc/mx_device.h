@@ -28,6 +28,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two fp32 values -> two bf16 (lo in bits 0-15), round to nearest even:
+// one V_CVT_PK_BF16_F32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float v2f_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f_t{lo, hi}), v2bf_t));
+}
+
 // MX shared exponent from the magnitude bits of the block's largest bf16
 // element: e = floor(log2 amax) - emax, clamped to [-127, 127]; a zero or
 // subnormal amax gives -127 (for subnormals floor(log2) - emax < -127).
