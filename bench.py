@@ -187,15 +187,20 @@ def cpu_baseline(workload_name, fmt):
 
 # ------------------------------------------------------------------ traffic
 
-KERNEL_SOURCES = {"gemm_mx_kernel": "block_scaled_precision_mx_amd/csrc/gemm_mx.hip",
-                  "gemm_nv_kernel": "block_scaled_precision_mx_amd/csrc/gemm_nv.hip"}
+# the sources a kernel's machine code is built from (its file and the device
+# headers it includes); their hash ties a counter summary to one build
+_DEVICE_HEADERS = ["block_scaled_precision_mx_amd/csrc/gemm_common.h", "block_scaled_precision_mx_amd/csrc/mx_device.h"]
+KERNEL_SOURCES = {"gemm_mx_kernel": ["block_scaled_precision_mx_amd/csrc/gemm_mx.hip"] + _DEVICE_HEADERS,
+                  "gemm_nv_kernel": ["block_scaled_precision_mx_amd/csrc/gemm_nv.hip"] + _DEVICE_HEADERS}
 
 
 def source_sha256(kernel):
     import hashlib
-    path = os.path.join(ROOT, KERNEL_SOURCES[kernel.split("<")[0]])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel.split("<")[0]]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel, workload):
