@@ -184,9 +184,23 @@ def nvfp4_element_codes(x: np.ndarray, S: np.ndarray) -> np.ndarray:
     return (sign | mag).astype(np.uint8)
 
 
-def _quantize_nvfp4(x: np.ndarray, k_pad: int, tensor_amax: float):
+def nvfp4_delayed_scale(amax_prev: float, headroom: float) -> np.float32:
+    """Per-tensor scale from an earlier amax (README section 5.5, delayed
+    amax): the amax found while quantizing one step, times a headroom,
+    serves as the scale amax of the next step, so no pass over the tensor
+    precedes its quantization.
+
+    Reading (the page gives no formula): s_t is the NVFP4 tensor scale of the
+    value headroom * amax_prev, computed as
+    fp32_RNE(fp64(fp64(headroom * amax_prev) / 2688)), the same operation
+    order on every side. With headroom 1 and amax_prev the tensor's own amax
+    this is nvfp4_tensor_scale(amax).
+    """
+    return np.float32((np.float64(headroom) * np.float64(amax_prev)) / 2688.0)
+
+
+def _quantize_nvfp4(x: np.ndarray, k_pad: int, s_t: np.float32):
     bs = 16
-    s_t = nvfp4_tensor_scale(tensor_amax)
     blocks = _blocks(x, bs, k_pad)
     bamax = np.abs(blocks).max(axis=2)
     scales = nvfp4_block_bytes(bamax, s_t)
@@ -195,11 +209,14 @@ def _quantize_nvfp4(x: np.ndarray, k_pad: int, tensor_amax: float):
     return codes.reshape(x.shape[0], k_pad), scales, s_t
 
 
-def quantize(bits: np.ndarray, fmt: str, axis: str = "row") -> Quantized:
+def quantize(bits: np.ndarray, fmt: str, axis: str = "row", s_t=None) -> Quantized:
     """Quantize a bf16 tensor X [R, C] (given as uint16 bit patterns).
 
     axis="row": blocks run along C; stored operand is [R, round_up(C,128)].
     axis="col": blocks run along R; stored operand is X^T: [C, round_up(R,128)].
+    NVFP4: s_t=None derives the tensor scale from X's own amax; a given s_t
+    (e.g. nvfp4_delayed_scale) is used as is. The recorded amax is X's own
+    either way.
     """
     if fmt not in FORMATS:
         raise ValueError(f"unknown format {fmt!r}")
@@ -209,11 +226,24 @@ def quantize(bits: np.ndarray, fmt: str, axis: str = "row") -> Quantized:
     k_pad = round_up(length, K_ALIGN)
     if fmt == "nvfp4":
         tensor_amax = float(np.abs(x).max()) if x.size else 0.0
-        codes, scales, s_t = _quantize_nvfp4(x, k_pad, tensor_amax)
+        st = nvfp4_tensor_scale(tensor_amax) if s_t is None else np.float32(s_t)
+        codes, scales, s_t = _quantize_nvfp4(x, k_pad, st)
         return Quantized(fmt, rows, length, k_pad, codes, scales,
                          s_t=s_t, amax=np.float32(tensor_amax))
     codes, scales = _quantize_mx(x, fmt, k_pad)
     return Quantized(fmt, rows, length, k_pad, codes, scales)
+
+
+def quantize_dual(bits: np.ndarray, fmt: str, amax_prev=None, headroom: float = 32.0):
+    """Both copies a training step needs (README section 5.5: one read of
+    X, the row copy and the transposed copy written together): the
+    quantization along axis "row" and along axis "col". For NVFP4 both use
+    one tensor scale: X's own (amax_prev None) or the delayed scale
+    nvfp4_delayed_scale(amax_prev, headroom)."""
+    s_t = None
+    if fmt == "nvfp4" and amax_prev is not None:
+        s_t = nvfp4_delayed_scale(amax_prev, headroom)
+    return quantize(bits, fmt, "row", s_t), quantize(bits, fmt, "col", s_t)
 
 
 def codes_bytes(rows: int, cols: int, fmt: str, axis: str) -> int:

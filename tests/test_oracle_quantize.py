@@ -48,8 +48,9 @@ def ref_fp32_round(v: Fraction) -> Fraction:
     return fl * q
 
 
-def ref_quantize(bits: np.ndarray, fmt: str):
-    """Row quantization, one block at a time, in exact arithmetic."""
+def ref_quantize(bits: np.ndarray, fmt: str, s_t_given=None):
+    """Row quantization, one block at a time, in exact arithmetic. NVFP4:
+    s_t_given (a Fraction) replaces the scale derived from the tensor."""
     rows, length = bits.shape
     bs = 16 if fmt == "nvfp4" else 32
     k_pad = -(-length // 128) * 128
@@ -61,6 +62,8 @@ def ref_quantize(bits: np.ndarray, fmt: str):
     if fmt == "nvfp4":
         amax_t = max((abs(v) for row in xs for v in row), default=Fraction(0))
         s_t = ref_fp32_round(amax_t / 2688) if amax_t else Fraction(0)
+        if s_t_given is not None:
+            s_t = s_t_given
     for r in range(rows):
         for b in range(k_pad // bs):
             blk = xs[r][b * bs: min((b + 1) * bs, length)]
@@ -352,3 +355,103 @@ def test_fp4_nibble_order():
     x[0, 1] = -0.5         # element 1 -> code 9 in the high nibble of byte 0
     q = Q.quantize(bits_of(x), "mxfp4")
     assert q.packed_codes()[0, 0] == (9 << 4) | 7
+
+
+# ------------------------------------------------------------ delayed tensor scale (fused dual quantizer)
+
+@pytest.mark.parametrize("s_t", [2.0 ** -12, 1.0 / 2688, 3.0e-4, 0.75, 40.0, 1.0e-9])
+def test_nvfp4_given_scale_matches_exact_reference(s_t):
+    """Quantizing with a tensor scale supplied from outside (the delayed
+    amax of README section 5.5) against the exact block-by-block reference:
+    small scales saturate block bytes at 448 and codes at 6, large ones send
+    blocks to zero."""
+    st = np.float32(s_t)
+    rng = np.random.default_rng(int(s_t * 1e9) % 2**32)
+    bits = special_tensor(rng, 4, 99)
+    q = Q.quantize(bits, "nvfp4", "row", s_t=st)
+    codes, scales, _ = ref_quantize(bits, "nvfp4", Fraction(float(st)))
+    assert np.array_equal(q.codes, codes)
+    assert np.array_equal(q.scales, scales)
+    assert q.s_t == st
+    assert q.amax == np.float32(np.abs(F.bf16_to_f64(bits)).max())
+
+
+@pytest.mark.parametrize("h", [1.0, 8.0, 16.0, 32.0, 2.0 ** -3])
+def test_nvfp4_delayed_scale_closed_form(h):
+    """s_t = RNE_fp32((headroom * amax_prev) / 2688). With a power-of-two
+    headroom and a bf16 amax the product is exact and has 8 significant bits,
+    so the float64 quotient rounds to the same fp32 value as the exact one."""
+    for a in [2688.0, 1992.0, 7.0, 0.0078125, 1.0e-30, 3.0e30]:
+        s = Q.nvfp4_delayed_scale(a, h)
+        assert Fraction(float(s)) == ref_fp32_round(Fraction(h) * Fraction(a) / 2688)
+    assert Q.nvfp4_delayed_scale(2688.0, 32.0) == 32.0
+    assert Q.nvfp4_delayed_scale(1.0, 2688.0) == 1.0
+    assert Q.nvfp4_delayed_scale(0.0, 32.0) == 0.0
+
+
+def test_nvfp4_delayed_headroom_one_is_the_plain_definition():
+    """headroom 1 with the tensor's own amax reproduces both plain copies."""
+    rng = np.random.default_rng(44)
+    bits = special_tensor(rng, 37, 70)
+    amax = float(np.abs(F.bf16_to_f64(bits)).max())
+    row, col = Q.quantize_dual(bits, "nvfp4", amax_prev=amax, headroom=1.0)
+    for q, axis in ((row, "row"), (col, "col")):
+        p = Q.quantize(bits, "nvfp4", axis)
+        assert np.array_equal(q.codes, p.codes) and np.array_equal(q.scales, p.scales)
+        assert q.s_t == p.s_t and q.amax == p.amax
+
+
+@pytest.mark.parametrize("fmt", Q.FORMATS)
+def test_dual_copies_are_row_and_transposed_row(fmt):
+    """The second copy is the row quantization of the contiguous X^T, with
+    the same tensor scale; MX formats ignore amax_prev / headroom."""
+    rng = np.random.default_rng(45)
+    bits = special_tensor(rng, 33, 50)
+    row, col = Q.quantize_dual(bits, fmt, amax_prev=3.5, headroom=32.0)
+    s_t = row.s_t if fmt == "nvfp4" else None
+    r = Q.quantize(bits, fmt, "row", s_t=s_t)
+    t = Q.quantize(np.ascontiguousarray(bits.T), fmt, "row", s_t=s_t)
+    assert np.array_equal(row.codes, r.codes) and np.array_equal(row.scales, r.scales)
+    assert np.array_equal(col.codes, t.codes) and np.array_equal(col.scales, t.scales)
+    if fmt == "nvfp4":
+        assert row.s_t == col.s_t == Q.nvfp4_delayed_scale(3.5, 32.0)
+    else:
+        p = Q.quantize(bits, fmt, "row")
+        assert np.array_equal(row.codes, p.codes) and np.array_equal(row.scales, p.scales)
+
+
+def test_nvfp4_saturation_worked_example():
+    """amax_prev 1, headroom 1: s_t = fp32(1/2688). A block whose amax is 100
+    needs 100 / (6 s_t) ~ 44800 > 448, so its byte saturates at 448 (0x7E);
+    its scale is 448 s_t ~ 1/6, so 100 -> 600 saturates at code 6 (0x7),
+    -3 -> -18 saturates too (0xF), and 0.1 (bf16 0.10009765625) -> 0.6006,
+    nearest E2M1 value 0.5 (0x1)."""
+    x = np.zeros((1, 16))
+    x[0, 0], x[0, 1], x[0, 2] = 100.0, -3.0, 0.1
+    bits = bits_of(x)
+    row, _ = Q.quantize_dual(bits, "nvfp4", amax_prev=1.0, headroom=1.0)
+    assert row.s_t == np.float32(1.0 / 2688)
+    assert row.scales[0, 0] == 0x7E
+    assert list(row.codes[0, :4]) == [0x7, 0xF, 0x1, 0x0]
+    assert row.amax == np.float32(100.0)
+
+
+def test_nvfp4_scale_power_of_two_invariance():
+    """Doubling s_t halves every block scale and leaves the codes alone, as
+    long as both bytes stay normal and unsaturated."""
+    rng = np.random.default_rng(46)
+    x = rng.standard_normal((8, 128)) + 4.0 * np.sign(rng.standard_normal((8, 128)))   # no padding blocks
+    bits = bits_of(x)
+    amax = float(np.abs(F.bf16_to_f64(bits)).max())
+    s0 = Q.nvfp4_delayed_scale(amax, 4.0)
+    s1 = Q.nvfp4_delayed_scale(amax, 8.0)
+    assert s1 == 2 * s0
+    q0 = Q.quantize(bits, "nvfp4", "row", s_t=s0)
+    q1 = Q.quantize(bits, "nvfp4", "row", s_t=s1)
+    d0, d1 = F.e4m3_decode(q0.scales), F.e4m3_decode(q1.scales)
+    ok = (d1 >= 2.0 ** -6) & (d0 <= 448.0 / 2)
+    assert ok.sum() > 0.9 * ok.size
+    assert np.all(d0[ok] == 2 * d1[ok])
+    blk0 = q0.codes.reshape(8, -1, 16)
+    blk1 = q1.codes.reshape(8, -1, 16)
+    assert np.array_equal(blk0[ok], blk1[ok])
