@@ -193,10 +193,14 @@ def nvfp4_delayed_scale(amax_prev: float, headroom: float) -> np.float32:
     Reading (the page gives no formula): s_t is the NVFP4 tensor scale of the
     value headroom * amax_prev, computed as
     fp32_RNE(fp64(fp64(headroom * amax_prev) / 2688)), the same operation
-    order on every side. With headroom 1 and amax_prev the tensor's own amax
-    this is nvfp4_tensor_scale(amax).
+    order on every side. Both inputs are fp32 quantities (an amax is kept as
+    fp32 in the scale trailer, and the headroom is an fp32 argument), so they
+    are rounded to fp32 first. With headroom 1 and amax_prev the tensor's own
+    amax this is nvfp4_tensor_scale(amax).
     """
-    return np.float32((np.float64(headroom) * np.float64(amax_prev)) / 2688.0)
+    h = np.float64(np.float32(headroom))
+    a = np.float64(np.float32(amax_prev))
+    return np.float32((h * a) / 2688.0)
 
 
 def _quantize_nvfp4(x: np.ndarray, k_pad: int, s_t: np.float32):

@@ -389,6 +389,16 @@ def test_nvfp4_delayed_scale_closed_form(h):
     assert Q.nvfp4_delayed_scale(0.0, 32.0) == 0.0
 
 
+def test_nvfp4_delayed_scale_inputs_are_fp32():
+    """amax_prev and headroom enter as fp32 values (the trailer's amax field,
+    the fp32 argument): 0.001 acts as fp32(0.001) = 0.0010000000474974513."""
+    a32 = float(np.float32(0.001))
+    assert a32 != 0.001
+    s = Q.nvfp4_delayed_scale(0.001, 16.0)
+    assert Fraction(float(s)) == ref_fp32_round(Fraction(a32) * 16 / 2688)
+    assert s == Q.nvfp4_delayed_scale(a32, 16.0)
+
+
 def test_nvfp4_delayed_headroom_one_is_the_plain_definition():
     """headroom 1 with the tensor's own amax reproduces both plain copies."""
     rng = np.random.default_rng(44)
