@@ -84,6 +84,43 @@ def mx_quantize(x: torch.Tensor, fmt: str, axis: str = "row", codes: torch.Tenso
     return Quantized(codes, scales, fmt, stored_rows, length)
 
 
+def mx_quantize_dual(x: torch.Tensor, fmt: str, amax_prev: torch.Tensor | None = None, headroom: float = 32.0,
+                     out: tuple[Quantized, Quantized] | None = None, stream=None) -> tuple[Quantized, Quantized]:
+    """Row copy and transposed (column) copy of a 2-D bf16 device tensor from
+    one read. NVFP4: amax_prev (a device float32 tensor of one element, e.g.
+    amax_field(previous.scales)) selects the delayed tensor scale. `out`
+    reuses the buffers of an earlier call's result."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D bfloat16 device tensor")
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit stride along its last dimension")
+    ptr = 0
+    if amax_prev is not None:
+        if amax_prev.dtype != torch.float32 or amax_prev.numel() < 1 or not amax_prev.is_cuda:
+            raise ValueError("amax_prev must be a float32 device tensor")
+        ptr = amax_prev.data_ptr()
+    rows, cols = x.shape
+    bufs = []
+    for i, axis in enumerate(("row", "col")):
+        nc, ns = codes_bytes(rows, cols, fmt, axis), scales_bytes(rows, cols, fmt, axis)
+        if out is None:
+            bufs.append(torch.empty(nc, dtype=torch.uint8, device=x.device))
+            bufs.append(torch.empty(ns, dtype=torch.uint8, device=x.device))
+        else:
+            if out[i].codes.numel() < nc or out[i].scales.numel() < ns:
+                raise ValueError("out buffers are too small")
+            bufs += [out[i].codes, out[i].scales]
+    _check(lib().mx_quantize_dual(x.data_ptr(), rows, cols, x.stride(0), bufs[0].data_ptr(), bufs[1].data_ptr(),
+                                  bufs[2].data_ptr(), bufs[3].data_ptr(), FMT[fmt], ptr or None, float(headroom),
+                                  _stream(stream)))
+    return (Quantized(bufs[0], bufs[1], fmt, rows, cols), Quantized(bufs[2], bufs[3], fmt, cols, rows))
+
+
+def amax_field(scales: torch.Tensor) -> torch.Tensor:
+    """The fp32 amax of an NVFP4 scale buffer's trailer, as a one-element view."""
+    return scales[-16:].view(torch.float32)[1:2]
+
+
 def mx_gemm(a: Quantized, b: Quantized, bias: torch.Tensor | None = None, out_dtype: str = "bf16",
             out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """C[M, N] = A * B^T (+ bias) from two operands quantized in one format."""

@@ -9,6 +9,13 @@ namespace mx {
 hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
                            uint8_t* scales, int fmt, int axis, hipStream_t stream);
 
+// Both quantized copies (row, and column stored transposed) from one read.
+// NVFP4: amax_prev NULL -> tensor scale from this tensor; else delayed scale
+// fp32(fp64(headroom * *amax_prev) / 2688).
+hipError_t launch_quantize_dual(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* rcodes,
+                                uint8_t* rscales, uint8_t* ccodes, uint8_t* cscales, int fmt, const float* amax_prev,
+                                float headroom, hipStream_t stream);
+
 // MXFP8 / MXFP4: scaled-MFMA GEMM. C = A * B^T (+ bias), fp32 accumulate.
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs,
                           void* C, int64_t M, int64_t N, int64_t K, int fmt, const uint16_t* bias,

@@ -322,6 +322,206 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
   }
 }
 
+// ------------------------------------------------------------ fused row + col
+
+// README section 5.5: the weight-gradient GEMM needs each operand twice,
+// quantized along its rows and along its columns (stored transposed); one
+// kernel reads X once and writes both copies. A 128 x 64 tile is loaded as
+// in quant_col_kernel: thread t holds 8 consecutive elements of rows
+// t / 8 + 32 p, which the 4 (MX) or 2 (NVFP4) adjacent lanes of a row block
+// quantize straight from registers into the row copy, while the tile goes
+// through LDS for the column copy. The tiles cover round_up(cols, 128)
+// columns so that the row copy's padding is written too, and round_up(rows,
+// 128) rows for the column copy's.
+//
+// NVFP4 tensor scale: either from this tensor's amax (reduced first into the
+// row copy's trailer, as mx_quantize does), or delayed (README section 5.5):
+// set before this kernel from an earlier amax times a headroom, in which case
+// this kernel reduces the tensor's own amax into both trailers on the side
+// (one atomic max per workgroup), for the next call.
+
+// Trailers of both copies and the padding before them; with `delayed`,
+// s_t = fp32(fp64(headroom * *amax_prev) / 2688), read before anything is
+// written (amax_prev may be the amax field of either trailer).
+__global__ void nv_dual_init_kernel(uint8_t* rgap, int rgap_bytes, NvTrailer* rtr, uint8_t* cgap, int cgap_bytes,
+                                    NvTrailer* ctr, const float* amax_prev, float headroom, int delayed) {
+  const int t = threadIdx.x;
+  if (t == 0) {
+    float s_t = 0.0f;
+    if (delayed) s_t = (float)(((double)headroom * (double)*amax_prev) / 2688.0);
+    rtr->s_t = s_t;
+    ctr->s_t = s_t;
+    rtr->amax_bits = ctr->amax_bits = 0u;
+    rtr->pad[0] = rtr->pad[1] = ctr->pad[0] = ctr->pad[1] = 0u;
+  }
+  if (t < rgap_bytes) rgap[t] = 0;
+  if (t < cgap_bytes) cgap[t] = 0;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
+                                                         uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
+                                                         int rkpad, uint8_t* __restrict__ ccodes,
+                                                         uint8_t* __restrict__ cscales, int ckpad, NvTrailer* rtr,
+                                                         NvTrailer* ctr, int delayed) {
+  constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
+  constexpr int LANES_PER_BLOCK = BS / 8;
+  __shared__ __align__(16) uint16_t tile[kColTileR * kColLdsLd];
+  __shared__ uint32_t wave_max[4];
+  const int tiles_c = rkpad / kColTileC;
+  const int tiles_r = ckpad / kColTileR;
+  const int ntiles = tiles_c * tiles_r;
+  const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
+  const int t = threadIdx.x;
+  float s_t = 0.0f;
+  if (FMT == FMT_NVFP4) {
+    if (delayed) {
+      s_t = rtr->s_t;
+    } else {
+      s_t = nvfp4_tensor_scale(rtr->amax_bits);
+      if (blockIdx.x == 0 && t == 0) {
+        rtr->s_t = s_t;
+        ctr->s_t = s_t;
+        ctr->amax_bits = rtr->amax_bits;
+      }
+    }
+  }
+  uint32_t own_max = 0u;                      // largest |x| bits this thread saw (delayed NVFP4)
+  for (int tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+    const int tr_ = tile_id / tiles_c;
+    const int tc = tile_id - tr_ * tiles_c;
+    const int r0 = tr_ * kColTileR, c0 = tc * kColTileC;
+    uint4 v[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = r0 + t / 8 + 32 * p, c = c0 + (t % 8) * 8;
+      v[p] = make_uint4(0u, 0u, 0u, 0u);
+      if (r < rows && c < cols) {
+        const uint16_t* q = src + (int64_t)r * ld + c;
+        if (vec_ok && c + 8 <= cols) {
+          v[p] = load16_stream(q);
+        } else {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+          for (int i = 0; i < 8; ++i)
+            if (c + i < cols) w[i / 2] |= (uint32_t)q[i] << (16 * (i % 2));
+          v[p] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      *reinterpret_cast<uint4*>(&tile[(t / 8 + 32 * p) * kColLdsLd + (t % 8) * 8]) = v[p];
+
+    // row copy, from registers: the lanes of a row block are adjacent
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = r0 + t / 8 + 32 * p, c = c0 + (t % 8) * 8;
+      const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+      float x[8];
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+        x[i] = bf16_to_f32(b);
+        m = max(m, b & 0x7FFFu);
+      }
+      own_max = max(own_max, m);
+#pragma unroll
+      for (int off = 1; off < LANES_PER_BLOCK; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+      float mul = 1.0f;
+      Nv4Thresholds th;
+      const uint32_t sb = block_scale<FMT>(m, s_t, mul, th);
+      const uint64_t packed = encode8<FMT>(x, mul, th);
+      if (r < rows) {
+        if (FMT == FMT_MXFP8) {
+          *reinterpret_cast<uint2*>(rcodes + (int64_t)r * rkpad + c) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
+        } else {
+          *reinterpret_cast<uint32_t*>(rcodes + (int64_t)r * (rkpad / 2) + c / 2) = (uint32_t)packed;
+        }
+        if (((t % 8) % LANES_PER_BLOCK) == 0) rscales[(int64_t)r * (rkpad / BS) + c / BS] = (uint8_t)sb;
+      }
+    }
+    __syncthreads();
+
+    // column copy, from LDS: wave w owns tile rows 32w .. 32w + 31, lane j column j
+    const int w = t / 64, j = t % 64;
+    const int oc = c0 + j;
+    float x[32];
+    uint32_t m2[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t b = tile[(32 * w + i) * kColLdsLd + j];
+      x[i] = bf16_to_f32(b);
+      m2[i / 16] = max(m2[i / 16], b & 0x7FFFu);
+    }
+    if (oc < cols) {
+      const int orow = r0 + 32 * w;
+      if (FMT == FMT_NVFP4) {
+        uint32_t packed[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float mul;
+          Nv4Thresholds th;
+          const uint32_t sb = block_scale<FMT>(m2[h], s_t, mul, th);
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) word |= nvfp4_encode(x[16 * h + 8 * q2 + i], th) << (4 * i);
+            packed[2 * h + q2] = word;
+          }
+          cscales[(int64_t)oc * (ckpad / 16) + orow / 16 + h] = (uint8_t)sb;
+        }
+        *reinterpret_cast<uint4*>(ccodes + (int64_t)oc * (ckpad / 2) + orow / 2) =
+            make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      } else {
+        float mul = 1.0f;
+        Nv4Thresholds th;
+        const uint32_t sb = block_scale<FMT>(max(m2[0], m2[1]), s_t, mul, th);
+        if (FMT == FMT_MXFP8) {
+          uint32_t words[8];
+#pragma unroll
+          for (int q2 = 0; q2 < 8; ++q2) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) word |= e4m3_encode(x[4 * q2 + i] * mul) << (8 * i);
+            words[q2] = word;
+          }
+          uint4* dst = reinterpret_cast<uint4*>(ccodes + (int64_t)oc * ckpad + orow);
+          dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
+          dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+        } else {
+          uint32_t words[4];
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) word |= e2m1_encode(x[8 * q2 + i] * mul) << (4 * i);
+            words[q2] = word;
+          }
+          *reinterpret_cast<uint4*>(ccodes + (int64_t)oc * (ckpad / 2) + orow / 2) =
+              make_uint4(words[0], words[1], words[2], words[3]);
+        }
+        cscales[(int64_t)oc * (ckpad / 32) + orow / 32] = (uint8_t)sb;
+      }
+    }
+    __syncthreads();
+  }
+  if (FMT == FMT_NVFP4 && delayed) {          // this tensor's amax, for the next call
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) own_max = max(own_max, (uint32_t)__shfl_xor((int)own_max, off));
+    if ((t & 63) == 0) wave_max[t >> 6] = own_max;
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t b = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+      if (b != 0) {
+        atomicMax(&rtr->amax_bits, b << 16);
+        atomicMax(&ctr->amax_bits, b << 16);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ launchers
 
 static int grid_for(int64_t work_items, int per_block, int cap) {
@@ -364,6 +564,44 @@ hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int6
       case FMT_MXFP4: quant_col_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
       default:        quant_col_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
     }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_dual(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* rcodes,
+                                uint8_t* rscales, uint8_t* ccodes, uint8_t* cscales, int fmt, const float* amax_prev,
+                                float headroom, hipStream_t stream) {
+  const int64_t rkpad = round_up(cols, kAlignK);    // row copy: rows x rkpad
+  const int64_t ckpad = round_up(rows, kAlignK);    // column copy: cols x ckpad
+  const int ir = (int)rows, ic = (int)cols, ild = (int)ld;
+  NvTrailer *rtr = nullptr, *ctr = nullptr;
+  const int delayed = (fmt == FMT_NVFP4 && amax_prev != nullptr) ? 1 : 0;
+  if (fmt == FMT_NVFP4) {
+    const int64_t rn = rows * (rkpad / 16), cn = cols * (ckpad / 16);
+    rtr = reinterpret_cast<NvTrailer*>(rscales + round_up(rn, 16));
+    ctr = reinterpret_cast<NvTrailer*>(cscales + round_up(cn, 16));
+    nv_dual_init_kernel<<<1, 64, 0, stream>>>(rscales + rn, (int)(round_up(rn, 16) - rn), rtr, cscales + cn,
+                                              (int)(round_up(cn, 16) - cn), ctr, amax_prev, headroom, delayed);
+    if (!delayed) {
+      const int gpr = (int)((cols + 7) / 8);
+      amax_kernel<<<grid_for(rows * gpr, 256 * kAmaxUnroll, 512), 256, 0, stream>>>(src, ir, ic, ild, gpr, rtr);
+    }
+  }
+  const int64_t ntiles = (rkpad / kColTileC) * (ckpad / kColTileR);
+  const int g = grid_for(ntiles, 1, 1 << 20);
+  switch (fmt) {
+    case FMT_MXFP8:
+      quant_dual_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, (int)rkpad, ccodes, cscales,
+                                                          (int)ckpad, rtr, ctr, delayed);
+      break;
+    case FMT_MXFP4:
+      quant_dual_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, (int)rkpad, ccodes, cscales,
+                                                          (int)ckpad, rtr, ctr, delayed);
+      break;
+    default:
+      quant_dual_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, (int)rkpad, ccodes, cscales,
+                                                          (int)ckpad, rtr, ctr, delayed);
+      break;
   }
   return hipGetLastError();
 }

@@ -100,7 +100,30 @@ mx_status mx_quantize(const void* src, int64_t rows, int64_t cols, int64_t ld,
                       void* codes, void* scales, mx_fmt fmt, mx_axis axis,
                       void* hip_stream);
 
-/* C = A * B^T (+ bias) from quantized operands (README section 4.3 GEMMs,
+/* Both copies a training step needs, from one read of X (README section
+ * 5.5: a fused quantizer reads the tensor once and writes the row copy and
+ * the transposed copy): row_codes / row_scales receive exactly the bytes of
+ * mx_quantize(..., MX_AXIS_ROW) and col_codes / col_scales those of
+ * mx_quantize(..., MX_AXIS_COL) (sizes from mx_codes_bytes /
+ * mx_scales_bytes with the respective axis).
+ * NVFP4 tensor scale (README section 5.5, delayed amax):
+ *   amax_prev == NULL: s_t from this tensor's amax, as mx_quantize (one
+ *     extra read of X for the amax); both trailers get {s_t, amax}.
+ *   amax_prev != NULL: a device pointer to one fp32 value, typically the
+ *     amax field of a trailer from the previous step (it may be a trailer
+ *     this call writes: the value is read before anything is written);
+ *     s_t = fp32 RNE of fp64(fp64(headroom * amax_prev) / 2688), no extra
+ *     read; blocks whose amax exceeds 2688 s_t saturate. Both trailers get
+ *     {s_t, this tensor's amax}, for the next call. headroom must be finite
+ *     and > 0 (the pages' study suggests 32 for gradients).
+ *   MX formats ignore amax_prev and headroom.
+ * Errors and memory rules as for mx_quantize; the four outputs must not
+ * overlap. */
+mx_status mx_quantize_dual(const void* src, int64_t rows, int64_t cols, int64_t ld,
+                           void* row_codes, void* row_scales, void* col_codes, void* col_scales,
+                           mx_fmt fmt, const float* amax_prev, float headroom, void* hip_stream);
+
+/* C = A * B^T (+ bias) from quantized operands/* C = A * B^T (+ bias) from quantized operands (README section 4.3 GEMMs,
  * section 5.5 TN layout). A / As: codes and scales of an M-row operand,
  * B / Bs: of an N-row operand, both of logical length K. bias: bf16[N] or
  * NULL. out_dtype selects bf16 or fp32 C. */

@@ -87,6 +87,31 @@ def test_gemm_validation(L, args, status, msg):
     assert msg in L.mx_last_error().decode()
 
 
+@pytest.mark.parametrize("args,status,msg", [
+    ((ALIGNED, 4, 4, 4) + (ALIGNED,) * 4 + (7, None, 32.0), 1, "unknown format"),
+    ((ALIGNED, 4, 0, 4) + (ALIGNED,) * 4 + (1, None, 32.0), 1, "empty"),
+    ((ALIGNED, 4, 8, 4) + (ALIGNED,) * 4 + (1, None, 32.0), 1, "ld"),
+    ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, None, ALIGNED, 1, None, 32.0), 1, "null"),
+    ((ALIGNED, 4, 4, 4) + (ALIGNED,) * 4 + (3, ALIGNED, 0.0), 1, "headroom"),
+    ((ALIGNED, 4, 4, 4) + (ALIGNED,) * 4 + (3, ALIGNED, float("inf")), 1, "headroom"),
+    ((ALIGNED, 4, 4, 4) + (ALIGNED,) * 4 + (3, ALIGNED + 2, 32.0), 3, "amax_prev"),
+    ((ALIGNED + 1, 4, 4, 4) + (ALIGNED,) * 4 + (1, None, 32.0), 3, "2-byte"),
+    ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, ALIGNED, ALIGNED + 8, 1, None, 32.0), 3, "16-byte"),
+    ((ALIGNED, 1 << 20, 1 << 12, 1 << 12) + (ALIGNED,) * 4 + (1, None, 32.0), 2, "2 GiB"),
+])
+def test_quantize_dual_validation(L, args, status, msg):
+    assert L.mx_quantize_dual(*args, None) == status
+    assert msg in L.mx_last_error().decode()
+
+
+def test_quantize_dual_ignores_headroom_for_mx(L):
+    """MX formats never read amax_prev / headroom: a bad headroom is not an
+    error there (the call then fails later on the 2 GiB check, still before
+    any launch)."""
+    args = (ALIGNED, 1 << 20, 1 << 12, 1 << 12) + (ALIGNED,) * 4 + (1, ALIGNED, 0.0)
+    assert L.mx_quantize_dual(*args, None) == 2
+
+
 def test_last_error_is_per_thread(L):
     import threading
     L.mx_quantize(None, 4, 4, 4, ALIGNED, ALIGNED, 1, 0, None)
