@@ -5,7 +5,8 @@ and every linear layer (qkv, proj, fc1, fc2) quantize the activation and the
 weight row-wise (mx_quantize) and run the block-scaled GEMM with its bias
 epilogue (mx_gemm). For the NVFP4 training workload a step is the fc1/fc2
 pair's fprop, dgrad and wgrad GEMMs with every operand quantized along its
-own K axis (row and transposed copies, tensor amax included).
+own K axis (row and transposed copies from one read with mx_quantize_dual,
+tensor amax included).
 
 Inputs are seeded synthetic bf16 tensors (the value recipe of
 block_scaled_precision_mx_amd.workloads) generated on the device before the
@@ -109,14 +110,19 @@ def build_train(tp, dev):
     ops = []
     q = {}
 
-    def quant(name, t, axis):
+    def quant_dual(name, t):
+        """Both copies of t (row, and transposed for the other GEMMs) from one
+        read (mx_quantize_dual); s_t from t's own amax, as the config defines."""
         r, c = t.shape
-        buf = api.Quantized(torch.empty(api.codes_bytes(r, c, fmt, axis), dtype=torch.uint8, device=dev),
-                            torch.empty(api.scales_bytes(r, c, fmt, axis), dtype=torch.uint8, device=dev),
-                            fmt, r if axis == "row" else c, c if axis == "row" else r)
-        q[name] = buf
-        ops.append(Op("quant", lambda: api.mx_quantize(t, fmt, axis, buf.codes, buf.scales),
-                      nbytes=(QUANT_BYTES[fmt] + NVFP4_AMAX_BYTES) * t.numel(), label=f"quant_{name}"))
+        bufs = []
+        for axis, rows, length in (("row", r, c), ("col", c, r)):
+            bufs.append(api.Quantized(torch.empty(api.codes_bytes(r, c, fmt, axis), dtype=torch.uint8, device=dev),
+                                      torch.empty(api.scales_bytes(r, c, fmt, axis), dtype=torch.uint8, device=dev),
+                                      fmt, rows, length))
+        q[name + "_row"], q[name + "_col"] = bufs
+        ops.append(Op("quant", lambda: api.mx_quantize_dual(t, fmt, None, 1.0, out=(bufs[0], bufs[1])),
+                      nbytes=(2.0 + NVFP4_AMAX_BYTES + 2 * (QUANT_BYTES[fmt] - 2.0)) * t.numel(),
+                      label=f"quant_{name}_rowcol"))
 
     def gemm(name, a, b, bias, m, n, k):
         out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
@@ -124,18 +130,16 @@ def build_train(tp, dev):
                       label=f"gemm_{name}", plan=api.gemm_plan(m, n, k, fmt)))
 
     # fc1: fprop X W1^T, dgrad dY1 W1, wgrad dY1^T X
-    quant("X_row", X, "row"); quant("W1_row", W1, "row")
+    quant_dual("X", X); quant_dual("W1", W1)
     gemm("fc1_fprop", "X_row", "W1_row", b1, tp.m, tp.mlp, tp.hidden)
-    quant("dY1_row", dY1, "row"); quant("W1_col", W1, "col")
+    quant_dual("dY1", dY1)
     gemm("fc1_dgrad", "dY1_row", "W1_col", None, tp.m, tp.hidden, tp.mlp)
-    quant("dY1_col", dY1, "col"); quant("X_col", X, "col")
     gemm("fc1_wgrad", "dY1_col", "X_col", None, tp.mlp, tp.hidden, tp.m)
     # fc2: fprop H W2^T, dgrad dY2 W2, wgrad dY2^T H
-    quant("H_row", H, "row"); quant("W2_row", W2, "row")
+    quant_dual("H", H); quant_dual("W2", W2)
     gemm("fc2_fprop", "H_row", "W2_row", b2, tp.m, tp.hidden, tp.mlp)
-    quant("dY2_row", dY2, "row"); quant("W2_col", W2, "col")
+    quant_dual("dY2", dY2)
     gemm("fc2_dgrad", "dY2_row", "W2_col", None, tp.m, tp.mlp, tp.hidden)
-    quant("dY2_col", dY2, "col"); quant("H_col", H, "col")
     gemm("fc2_wgrad", "dY2_col", "H_col", None, tp.hidden, tp.mlp, tp.m)
     return ops
 
