@@ -46,36 +46,41 @@ __device__ __forceinline__ int mx_shared_exp(uint32_t amax_mag_bits, int emax) {
   return e < -127 ? -127 : e;   // upper clamp cannot trigger for bf16 input
 }
 
-// 2^-e as fp32 for e in [-127, 127 - emax]; always a normal number.
-__device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+// MX elements are x * 2^-e rounded to nearest even onto the element grid,
+// saturating, sign copied. gfx950's scaled conversions do exactly that: they
+// divide by the power of two held in the exponent field of their fp32 scale
+// operand (the E8M0 byte; mantissa ignored, field 0 = 2^-127) and round to
+// nearest even; the E2M1 form saturates at 6, the E4M3 form turns magnitudes
+// past 448 into NaN, so its inputs are clamped to +-448 * 2^e first (exact).
+// Checked on the chip against exact software encoders for every finite bf16
+// input and every e in [-127, 126] (bf16 inputs give e <= 119 / 125).
 
-// E4M3FN code of an exactly scaled value v (|v| < 512 or saturating).
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x43E00000u) {               // |v| >= 448: saturate
-    code = 0x7Eu;
-  } else if (a >= 0x3C800000u) {        // |v| >= 2^-6: normal E4M3
-    // keep 3 of the 23 mantissa bits, round half to even, rebias 127 -> 7
-    uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-    code = r - (120u << 3);
-  } else {                              // subnormal E4M3: m * 2^-9, m = 0..8
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  }
-  return sign | code;
+// The scale operand for scale byte sb = e + 127.
+__device__ __forceinline__ float mx_scale_operand(uint32_t sb) { return __uint_as_float(sb << 23); }
+
+// 4 values -> 4 E4M3FN codes of v * 2^-e (byte i = value i).
+__device__ __forceinline__ uint32_t e4m3x4_scaled(float a, float b, float c, float d, uint32_t sb) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  // 448 * 2^e = 1.75 * 2^(e + 8): a normal float for every e >= -127
+  const float lim = __uint_as_float((min(sb + 8u, 254u) << 23) | 0x600000u);
+  const float s = mx_scale_operand(sb);
+  a = __builtin_amdgcn_fmed3f(a, -lim, lim);
+  b = __builtin_amdgcn_fmed3f(b, -lim, lim);
+  c = __builtin_amdgcn_fmed3f(c, -lim, lim);
+  d = __builtin_amdgcn_fmed3f(d, -lim, lim);
+  v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, s, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, s, true);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
-// E2M1 code of an exactly scaled value v: count the midpoints crossed; a
-// value equal to a midpoint moves up only when the upper neighbour is even.
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-  uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
-  float a = __builtin_fabsf(v);
-  uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-               (uint32_t)(a > 5.0f);
-  return sign | m;
+// 8 values -> 8 E2M1 codes of v * 2^-e (nibble i = value i).
+__device__ __forceinline__ uint32_t e2m1x8_scaled(const float* x, uint32_t sb) {
+  const float s = mx_scale_operand(sb);
+  uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0], x[1], s, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[2], x[3], s, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[4], x[5], s, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[6], x[7], s, 3);
+  return r;
 }
 
 // E4M3 code (sign 0) of a non-negative double q, RNE + saturation. Used for

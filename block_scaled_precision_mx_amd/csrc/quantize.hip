@@ -115,9 +115,9 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
 // ------------------------------------------------------------ shared encode
 
 // Per-block scale of one lane's block given the block's amax bits; returns
-// the scale byte and sets the element multiplier (MX) or thresholds (NVFP4).
+// the scale byte and, for NVFP4, sets the element thresholds.
 template <int FMT>
-__device__ __forceinline__ uint32_t block_scale(uint32_t amax_bits, float s_t, float& mul, Nv4Thresholds& th) {
+__device__ __forceinline__ uint32_t block_scale(uint32_t amax_bits, float s_t, Nv4Thresholds& th) {
   if (FMT == FMT_NVFP4) {
     const double q = (s_t == 0.0f) ? 0.0 : (double)bf16_to_f32(amax_bits) / (6.0 * (double)s_t);
     const uint32_t b = e4m3_encode_pos_f64(q);
@@ -125,20 +125,19 @@ __device__ __forceinline__ uint32_t block_scale(uint32_t amax_bits, float s_t, f
     return b;
   }
   const int e = mx_shared_exp(amax_bits, FMT == FMT_MXFP8 ? 8 : 2);
-  mul = pow2_neg(e);
   return (uint32_t)(e + 127);
 }
 
-// Encode 8 values; packed codes in the low 64 (fp8) or 32 (fp4) bits.
+// Encode 8 values with scale byte sb; packed codes in the low 64 (fp8) or
+// 32 (fp4) bits.
 template <int FMT>
-__device__ __forceinline__ uint64_t encode8(const float (&x)[8], float mul, const Nv4Thresholds& th) {
+__device__ __forceinline__ uint64_t encode8(const float (&x)[8], uint32_t sb, const Nv4Thresholds& th) {
+  if (FMT == FMT_MXFP8)
+    return (uint64_t)e4m3x4_scaled(x[0], x[1], x[2], x[3], sb) | ((uint64_t)e4m3x4_scaled(x[4], x[5], x[6], x[7], sb) << 32);
+  if (FMT == FMT_MXFP4) return e2m1x8_scaled(x, sb);
   uint64_t out = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (FMT == FMT_MXFP8) out |= (uint64_t)e4m3_encode(x[i] * mul) << (8 * i);
-    else if (FMT == FMT_MXFP4) out |= (uint64_t)e2m1_encode(x[i] * mul) << (4 * i);
-    else out |= (uint64_t)nvfp4_encode(x[i], th) << (4 * i);
-  }
+  for (int i = 0; i < 8; ++i) out |= (uint64_t)nvfp4_encode(x[i], th) << (4 * i);
   return out;
 }
 
@@ -194,10 +193,9 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restri
       // block amax across the adjacent lanes of this block
 #pragma unroll
       for (int off = 1; off < LANES_PER_BLOCK; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-      float mul = 1.0f;
       Nv4Thresholds th;
-      const uint32_t sb = block_scale<FMT>(m, s_t, mul, th);
-      const uint64_t packed = encode8<FMT>(x, mul, th);
+      const uint32_t sb = block_scale<FMT>(m, s_t, th);
+      const uint64_t packed = encode8<FMT>(x, sb, th);
       if (FMT == FMT_MXFP8) {
         *reinterpret_cast<uint2*>(codes + (int64_t)r * kpad + c) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
       } else {
@@ -273,9 +271,8 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
         uint32_t packed[4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          float mul;
           Nv4Thresholds th;
-          const uint32_t sb = block_scale<FMT>(m[h], s_t, mul, th);
+          const uint32_t sb = block_scale<FMT>(m[h], s_t, th);
 #pragma unroll
           for (int q2 = 0; q2 < 2; ++q2) {
             uint32_t word = 0;
@@ -288,17 +285,13 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
         *reinterpret_cast<uint4*>(codes + (int64_t)oc * (kpad / 2) + orow / 2) =
             make_uint4(packed[0], packed[1], packed[2], packed[3]);
       } else {
-        float mul = 1.0f;
         Nv4Thresholds th;
-        const uint32_t sb = block_scale<FMT>(max(m[0], m[1]), s_t, mul, th);
+        const uint32_t sb = block_scale<FMT>(max(m[0], m[1]), s_t, th);
         if (FMT == FMT_MXFP8) {
           uint32_t words[8];
 #pragma unroll
           for (int q2 = 0; q2 < 8; ++q2) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) word |= e4m3_encode(x[4 * q2 + i] * mul) << (8 * i);
-            words[q2] = word;
+            words[q2] = e4m3x4_scaled(x[4 * q2], x[4 * q2 + 1], x[4 * q2 + 2], x[4 * q2 + 3], sb);
           }
           uint4* dst = reinterpret_cast<uint4*>(codes + (int64_t)oc * kpad + orow);
           dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
@@ -307,10 +300,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
           uint32_t words[4];
 #pragma unroll
           for (int q2 = 0; q2 < 4; ++q2) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) word |= e2m1_encode(x[8 * q2 + i] * mul) << (4 * i);
-            words[q2] = word;
+            words[q2] = e2m1x8_scaled(&x[8 * q2], sb);
           }
           *reinterpret_cast<uint4*>(codes + (int64_t)oc * (kpad / 2) + orow / 2) =
               make_uint4(words[0], words[1], words[2], words[3]);
@@ -428,10 +418,9 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
       own_max = max(own_max, m);
 #pragma unroll
       for (int off = 1; off < LANES_PER_BLOCK; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-      float mul = 1.0f;
       Nv4Thresholds th;
-      const uint32_t sb = block_scale<FMT>(m, s_t, mul, th);
-      const uint64_t packed = encode8<FMT>(x, mul, th);
+      const uint32_t sb = block_scale<FMT>(m, s_t, th);
+      const uint64_t packed = encode8<FMT>(x, sb, th);
       if (r < rows) {
         if (FMT == FMT_MXFP8) {
           *reinterpret_cast<uint2*>(rcodes + (int64_t)r * rkpad + c) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
@@ -460,9 +449,8 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
         uint32_t packed[4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          float mul;
           Nv4Thresholds th;
-          const uint32_t sb = block_scale<FMT>(m2[h], s_t, mul, th);
+          const uint32_t sb = block_scale<FMT>(m2[h], s_t, th);
 #pragma unroll
           for (int q2 = 0; q2 < 2; ++q2) {
             uint32_t word = 0;
@@ -475,17 +463,13 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
         *reinterpret_cast<uint4*>(ccodes + (int64_t)oc * (ckpad / 2) + orow / 2) =
             make_uint4(packed[0], packed[1], packed[2], packed[3]);
       } else {
-        float mul = 1.0f;
         Nv4Thresholds th;
-        const uint32_t sb = block_scale<FMT>(max(m2[0], m2[1]), s_t, mul, th);
+        const uint32_t sb = block_scale<FMT>(max(m2[0], m2[1]), s_t, th);
         if (FMT == FMT_MXFP8) {
           uint32_t words[8];
 #pragma unroll
           for (int q2 = 0; q2 < 8; ++q2) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) word |= e4m3_encode(x[4 * q2 + i] * mul) << (8 * i);
-            words[q2] = word;
+            words[q2] = e4m3x4_scaled(x[4 * q2], x[4 * q2 + 1], x[4 * q2 + 2], x[4 * q2 + 3], sb);
           }
           uint4* dst = reinterpret_cast<uint4*>(ccodes + (int64_t)oc * ckpad + orow);
           dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
@@ -494,10 +478,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
           uint32_t words[4];
 #pragma unroll
           for (int q2 = 0; q2 < 4; ++q2) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) word |= e2m1_encode(x[8 * q2 + i] * mul) << (4 * i);
-            words[q2] = word;
+            words[q2] = e2m1x8_scaled(&x[8 * q2], sb);
           }
           *reinterpret_cast<uint4*>(ccodes + (int64_t)oc * (ckpad / 2) + orow / 2) =
               make_uint4(words[0], words[1], words[2], words[3]);
