@@ -28,6 +28,11 @@ def _check(status: int) -> None:
         raise MxError(status, lib().mx_last_error().decode())
 
 
+def _ld(x: torch.Tensor) -> int:
+    """Leading dimension in elements (a single row's stride is arbitrary)."""
+    return x.stride(0) if x.shape[0] > 1 else x.shape[1]
+
+
 def _stream(stream) -> int:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
@@ -68,7 +73,7 @@ def mx_quantize(x: torch.Tensor, fmt: str, axis: str = "row", codes: torch.Tenso
     """Quantize a 2-D bf16 device tensor (unit column stride) along `axis`."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
         raise ValueError("x must be a 2-D bfloat16 device tensor")
-    if x.stride(1) != 1:
+    if x.stride(1) != 1 and x.shape[1] > 1:
         raise ValueError("x must have unit stride along its last dimension")
     rows, cols = x.shape
     nc, ns = codes_bytes(rows, cols, fmt, axis), scales_bytes(rows, cols, fmt, axis)
@@ -78,7 +83,7 @@ def mx_quantize(x: torch.Tensor, fmt: str, axis: str = "row", codes: torch.Tenso
         scales = torch.empty(ns, dtype=torch.uint8, device=x.device)
     if codes.numel() < nc or scales.numel() < ns:
         raise ValueError("codes / scales buffers are too small")
-    _check(lib().mx_quantize(x.data_ptr(), rows, cols, x.stride(0), codes.data_ptr(), scales.data_ptr(),
+    _check(lib().mx_quantize(x.data_ptr(), rows, cols, _ld(x), codes.data_ptr(), scales.data_ptr(),
                              FMT[fmt], AXIS[axis], _stream(stream)))
     stored_rows, length = (rows, cols) if axis == "row" else (cols, rows)
     return Quantized(codes, scales, fmt, stored_rows, length)
@@ -92,7 +97,7 @@ def mx_quantize_dual(x: torch.Tensor, fmt: str, amax_prev: torch.Tensor | None =
     reuses the buffers of an earlier call's result."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
         raise ValueError("x must be a 2-D bfloat16 device tensor")
-    if x.stride(1) != 1:
+    if x.stride(1) != 1 and x.shape[1] > 1:
         raise ValueError("x must have unit stride along its last dimension")
     ptr = 0
     if amax_prev is not None:
@@ -110,7 +115,7 @@ def mx_quantize_dual(x: torch.Tensor, fmt: str, amax_prev: torch.Tensor | None =
             if out[i].codes.numel() < nc or out[i].scales.numel() < ns:
                 raise ValueError("out buffers are too small")
             bufs += [out[i].codes, out[i].scales]
-    _check(lib().mx_quantize_dual(x.data_ptr(), rows, cols, x.stride(0), bufs[0].data_ptr(), bufs[1].data_ptr(),
+    _check(lib().mx_quantize_dual(x.data_ptr(), rows, cols, _ld(x), bufs[0].data_ptr(), bufs[1].data_ptr(),
                                   bufs[2].data_ptr(), bufs[3].data_ptr(), FMT[fmt], ptr or None, float(headroom),
                                   _stream(stream)))
     return (Quantized(bufs[0], bufs[1], fmt, rows, cols), Quantized(bufs[2], bufs[3], fmt, cols, rows))

@@ -130,3 +130,34 @@ def test_quantize_full_size(fmt, axis, shape, kind):
     else:
         bits = W.np_normal(shape, seed, W.W_STD)
     compare(bits, fmt, axis)
+
+
+def every_value_blocks(amax_bits: int, bs: int) -> np.ndarray:
+    """Rows of blocks that start with +amax and hold every finite bf16 value
+    of magnitude <= amax (both signs) in the other bs - 1 places, so the
+    block exponent is fixed by amax and every representable input meets it."""
+    mags = np.arange(0, 0x7F80, dtype=np.uint32)
+    mags = mags[mags <= amax_bits]
+    vals = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+    per = bs - 1
+    nblk = -(-len(vals) // per)
+    body = np.zeros(nblk * per, dtype=np.uint16)
+    body[:len(vals)] = vals
+    blocks = np.concatenate([np.full((nblk, 1), amax_bits, dtype=np.uint16), body.reshape(nblk, per)], axis=1)
+    blocks_per_row = 8
+    nrow = -(-nblk // blocks_per_row)
+    out = np.zeros((nrow * blocks_per_row, bs), dtype=np.uint16)
+    out[:nblk] = blocks
+    return out.reshape(nrow, blocks_per_row * bs)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("amax_bits", [0x7F7F, 0x4380, 0x3F80, 0x3B80, 0x1000, 0x0080, 0x0001])
+def test_quantize_every_bf16_value(fmt, amax_bits):
+    """Every finite bf16 input under block exponents from -127 (amax the
+    smallest subnormal) to 119 / 125 (amax the largest finite value), both
+    axes: the encoders' rounding, saturation and signed zero against the
+    oracle."""
+    bits = every_value_blocks(amax_bits, 32)
+    compare(bits, fmt, "row")
+    compare(np.ascontiguousarray(bits.T), fmt, "col")
