@@ -38,14 +38,16 @@ QUANT_BYTES = {"mxfp8": 2 + 1 + 1 / 32, "mxfp4": 2 + 0.5 + 1 / 32, "nvfp4": 2 + 
 NVFP4_AMAX_BYTES = 2.0
 
 
+WORKLOADS = ["vitl16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack", "vitb16_mxfp8_fwd_stack",
+             "vitl16_nvfp4_fc1fc2_train", "vitl16_mxfp8_fc1fc2_train", "single_mxfp8_256x768x768"]
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="vitl16_mxfp8_fwd_stack",
-                   choices=["vitl16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack", "vitb16_mxfp8_fwd_stack",
-                            "vitl16_nvfp4_fc1fc2_train", "single_mxfp8_256x768x768"])
+    p.add_argument("--workload", default="vitl16_mxfp8_fwd_stack", choices=WORKLOADS)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="first run one elementwise bf16 kernel (negation) reading and writing this many "
@@ -97,7 +99,7 @@ def build_train(tp, dev):
     from block_scaled_precision_mx_amd import api
     from block_scaled_precision_mx_amd import workloads as W
 
-    fmt = "nvfp4"
+    fmt = tp.fmt
     S = lambda tid: W.seed(tp.wid, 0, tid)   # noqa: E731
     X = W.torch_activation((tp.m, tp.hidden), S(tp.X), dev)
     H = W.torch_activation((tp.m, tp.mlp), S(tp.H), dev, gelu=True)
@@ -110,9 +112,14 @@ def build_train(tp, dev):
     ops = []
     q = {}
 
+    # bytes per element of one dual quantization: the read, both copies'
+    # codes and scales, and for NVFP4 the amax pass (s_t from the tensor's
+    # own amax, as the config defines)
+    dual_bytes = 2.0 + 2 * (QUANT_BYTES[fmt] - 2.0) + (NVFP4_AMAX_BYTES if fmt == "nvfp4" else 0.0)
+
     def quant_dual(name, t):
         """Both copies of t (row, and transposed for the other GEMMs) from one
-        read (mx_quantize_dual); s_t from t's own amax, as the config defines."""
+        read (mx_quantize_dual)."""
         r, c = t.shape
         bufs = []
         for axis, rows, length in (("row", r, c), ("col", c, r)):
@@ -121,7 +128,7 @@ def build_train(tp, dev):
                                       fmt, rows, length))
         q[name + "_row"], q[name + "_col"] = bufs
         ops.append(Op("quant", lambda: api.mx_quantize_dual(t, fmt, None, 1.0, out=(bufs[0], bufs[1])),
-                      nbytes=(2.0 + NVFP4_AMAX_BYTES + 2 * (QUANT_BYTES[fmt] - 2.0)) * t.numel(),
+                      nbytes=dual_bytes * t.numel(),
                       label=f"quant_{name}_rowcol"))
 
     def gemm(name, a, b, bias, m, n, k):
@@ -161,10 +168,11 @@ def cpu_baseline(workload_name, fmt):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    if workload_name.startswith("vitl16_nvfp4"):
-        rows = W.TRAIN_PAIR.m
-        shapes = [("fc1_fprop", W.TRAIN_PAIR.mlp, W.TRAIN_PAIR.hidden, "act")]
-        wid = W.TRAIN_PAIR.wid
+    if workload_name in W.TRAIN_PAIRS:
+        tp = W.TRAIN_PAIRS[workload_name]
+        rows = tp.m
+        shapes = [("fc1_fprop", tp.mlp, tp.hidden, "act")]
+        wid = tp.wid
     else:
         stack = W.STACKS[workload_name]
         rows = stack.m
@@ -251,14 +259,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    if args.workload == "vitl16_nvfp4_fc1fc2_train":
-        wl = W.TRAIN_PAIR
-        fmt = "nvfp4"
+    if args.workload in W.TRAIN_PAIRS:
+        wl = W.TRAIN_PAIRS[args.workload]
+        fmt = wl.fmt
         ops = build_train(wl, dev)
-        gemm_peak_key = "fp16"
+        gemm_peak_key = "fp16" if fmt == "nvfp4" else fmt
         config = {"workload": wl.name, "M": wl.m, "hidden": wl.hidden, "mlp": wl.mlp, "tokens_per_image": W.TOKENS,
-                  "batch": wl.m // W.TOKENS, "format": "nvfp4", "gemms": "fc1/fc2 fprop+dgrad+wgrad",
-                  "quantizations": 12}
+                  "batch": wl.m // W.TOKENS, "format": fmt, "gemms": "fc1/fc2 fprop+dgrad+wgrad",
+                  "quantizations": "6 tensors, row and transposed copies from one read each"}
     else:
         wl = W.STACKS[args.workload]
         fmt = wl.fmt

@@ -150,7 +150,8 @@ STACKS = {s.name: s for s in (SINGLE_LAYER, VITB_MXFP8, VITL_MXFP8, VITL_MXFP4)}
 
 @dataclass(frozen=True)
 class TrainPair:
-    """fc1/fc2 of one ViT-L block: fprop, dgrad and wgrad GEMMs in NVFP4."""
+    """fc1/fc2 of one ViT-L block: fprop, dgrad and wgrad GEMMs, every
+    operand quantized in `fmt` (its row copy and its transposed copy)."""
     wid: int = 5
     name: str = "vitl16_nvfp4_fc1fc2_train"
     fmt: str = "nvfp4"
@@ -172,6 +173,9 @@ class TrainPair:
 
 
 TRAIN_PAIR = TrainPair()
+# the same pair in MXFP8: the MXFP8 training stack's dgrad / wgrad GEMMs
+TRAIN_PAIR_MXFP8 = TrainPair(wid=6, name="vitl16_mxfp8_fc1fc2_train", fmt="mxfp8")
+TRAIN_PAIRS = {tp.name: tp for tp in (TRAIN_PAIR, TRAIN_PAIR_MXFP8)}
 
 
 def seed(wid: int, block: int, tensor_id: int) -> int:

@@ -141,3 +141,15 @@ def test_gemm_plan_names(L):
     assert L.mx_gemm_plan(4160, 4096, 384, 3).decode() == "gemm_nv_kernel<nvfp4, 192x256>"
     assert L.mx_gemm_plan(0, 4, 4, 1) is None
     assert L.mx_gemm_plan(4, 4, 4, 9) is None
+
+
+
+def test_bench_workloads_are_defined():
+    """Every workload bench.py offers is a stack or a training pair of the
+    workloads module, and each names its own format."""
+    import bench
+    from block_scaled_precision_mx_amd import workloads as W
+    assert set(bench.WORKLOADS) == set(W.STACKS) | set(W.TRAIN_PAIRS)
+    for name in bench.WORKLOADS:
+        wl = W.STACKS.get(name) or W.TRAIN_PAIRS[name]
+        assert wl.fmt in name

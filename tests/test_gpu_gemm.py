@@ -105,16 +105,18 @@ def test_gemm_scale_shift(fmt):
     assert np.array_equal(c5, c0 * 32.0)
 
 
-def test_gemm_training_operands_nvfp4():
-    """dgrad and wgrad operands come from column quantization (TN layout)."""
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_training_operands(fmt):
+    """dgrad and wgrad operands come from column quantization (TN layout);
+    m = 300 tokens is a ragged K for wgrad (K_pad 384)."""
     m, h, f = 300, 96, 160
     x = W.np_activation((m, h), seed=1)
     dy = W.np_normal((m, f), seed=2, std=W.GRAD_STD)
     w = W.np_normal((f, h), seed=3, std=W.W_STD)
     # dgrad: dX[m, h] = dY[m, f] * W[f, h]  -> A = dY (row), B = W^T (col of W)
-    check_full(dy, w, "nvfp4", None, "bf16", "row", "col")
+    check_full(dy, w, fmt, None, "bf16", "row", "col")
     # wgrad: dW[f, h] = dY^T * X            -> A = dY^T (col), B = X^T (col)
-    check_full(dy, x, "nvfp4", None, "bf16", "col", "col")
+    check_full(dy, x, fmt, None, "bf16", "col", "col")
 
 
 def sampled_check(a_bits, b_bits, fmt, bias_bits, a_axis="row", b_axis="row", n_samples=4000, seed=0):
@@ -170,6 +172,27 @@ def test_gemm_nvfp4_training_full_size(which):
         dy1 = W.np_normal((tp.m, tp.mlp), W.seed(tp.wid, 0, tp.DY1), W.GRAD_STD)
         x = W.np_activation((tp.m, tp.hidden), W.seed(tp.wid, 0, tp.X))
         sampled_check(dy1, x, "nvfp4", None, "col", "col")
+
+
+@pytest.mark.parametrize("which", ["fprop_fc2", "dgrad_fc1", "wgrad_fc2"])
+def test_gemm_mxfp8_training_full_size(which):
+    """The MXFP8 training pair at full size, in the benchmark's launch
+    configuration: wgrad contracts over the 11235 tokens (K_pad 11264)."""
+    tp = W.TRAIN_PAIR_MXFP8
+    S = lambda tid: W.seed(tp.wid, 0, tid)   # noqa: E731
+    if which == "fprop_fc2":
+        h = W.np_gelu_activation((tp.m, tp.mlp), S(tp.H))
+        w2 = W.np_normal((tp.hidden, tp.mlp), S(tp.W2), W.W_STD)
+        b2 = W.np_normal((tp.hidden,), S(tp.B2), W.BIAS_STD)
+        sampled_check(h, w2, "mxfp8", b2)
+    elif which == "dgrad_fc1":
+        dy1 = W.np_normal((tp.m, tp.mlp), S(tp.DY1), W.GRAD_STD)
+        w1 = W.np_normal((tp.mlp, tp.hidden), S(tp.W1), W.W_STD)
+        sampled_check(dy1, w1, "mxfp8", None, "row", "col")
+    else:
+        dy2 = W.np_normal((tp.m, tp.hidden), S(tp.DY2), W.GRAD_STD)
+        h = W.np_gelu_activation((tp.m, tp.mlp), S(tp.H))
+        sampled_check(dy2, h, "mxfp8", None, "col", "col")
 
 
 @pytest.mark.parametrize("fmt,k", [("mxfp8", 128), ("mxfp8", 384), ("mxfp4", 384), ("mxfp4", 640)])

@@ -98,6 +98,8 @@ def test_dual_nvfp4_delayed_amax_from_own_trailer():
     ("nvfp4", (11235, 1024), "grad", True),      # dY2 with a delayed scale
     ("nvfp4", (4096, 1024), "weight", False),    # W1: fprop and dgrad copies
     ("mxfp8", (11235, 1024), "act", False),
+    ("mxfp8", (11235, 4096), "gelu", False),     # H of the MXFP8 training pair
+    ("mxfp8", (1024, 4096), "weight", False),    # W2: fprop and dgrad copies
 ])
 def test_dual_full_size(fmt, shape, kind, delayed):
     seed = W.seed(9, 1, hash((fmt, shape)) % 97)
