@@ -6,8 +6,18 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmx.so")
 
-# every symbol include/mx.h declares, with (restype, argtypes)
 _c = ctypes
+
+
+class QuantItem(ctypes.Structure):
+    """mx_quant_item of include/mx.h."""
+    _fields_ = [("src", _c.c_void_p), ("rows", _c.c_int64), ("cols", _c.c_int64), ("ld", _c.c_int64),
+                ("codes", _c.c_void_p), ("scales", _c.c_void_p)]
+
+
+QUANT_BATCH_MAX = 32   # MX_QUANT_BATCH_MAX
+
+# every symbol include/mx.h declares, with (restype, argtypes)
 SIGNATURES = {
     "mx_version": (_c.c_int, []),
     "mx_k_pad": (_c.c_int64, [_c.c_int64]),
@@ -15,6 +25,7 @@ SIGNATURES = {
     "mx_scales_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
     "mx_quantize": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
                                _c.c_int, _c.c_int, _c.c_void_p]),
+    "mx_quantize_batch": (_c.c_int, [_c.POINTER(QuantItem), _c.c_int, _c.c_int, _c.c_void_p]),
     "mx_quantize_dual": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
                                     _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_float, _c.c_void_p]),
     "mx_gemm": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,

@@ -89,6 +89,36 @@ def mx_quantize(x: torch.Tensor, fmt: str, axis: str = "row", codes: torch.Tenso
     return Quantized(codes, scales, fmt, stored_rows, length)
 
 
+def mx_quantize_batch(xs: list[torch.Tensor], fmt: str, out: list[Quantized] | None = None,
+                      stream=None) -> list[Quantized]:
+    """Row quantization of several 2-D bf16 device tensors in one launch
+    (MXFP8 / MXFP4; at most QUANT_BATCH_MAX tensors per call). `out` reuses
+    the buffers of an earlier call's result."""
+    from ._lib import QUANT_BATCH_MAX, QuantItem
+    if not 1 <= len(xs) <= QUANT_BATCH_MAX:
+        raise ValueError(f"between 1 and {QUANT_BATCH_MAX} tensors per call")
+    items = (QuantItem * len(xs))()
+    result = []
+    for i, x in enumerate(xs):
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+            raise ValueError("every tensor must be a 2-D bfloat16 device tensor")
+        if x.stride(1) != 1 and x.shape[1] > 1:
+            raise ValueError("every tensor must have unit stride along its last dimension")
+        rows, cols = x.shape
+        nc, ns = codes_bytes(rows, cols, fmt, "row"), scales_bytes(rows, cols, fmt, "row")
+        if out is None:
+            q = Quantized(torch.empty(nc, dtype=torch.uint8, device=x.device),
+                          torch.empty(ns, dtype=torch.uint8, device=x.device), fmt, rows, cols)
+        else:
+            q = out[i]
+            if q.codes.numel() < nc or q.scales.numel() < ns:
+                raise ValueError("out buffers are too small")
+        items[i] = QuantItem(x.data_ptr(), rows, cols, _ld(x), q.codes.data_ptr(), q.scales.data_ptr())
+        result.append(Quantized(q.codes, q.scales, fmt, rows, cols))
+    _check(lib().mx_quantize_batch(items, len(xs), FMT[fmt], _stream(stream)))
+    return result
+
+
 def mx_quantize_dual(x: torch.Tensor, fmt: str, amax_prev: torch.Tensor | None = None, headroom: float = 32.0,
                      out: tuple[Quantized, Quantized] | None = None, stream=None) -> tuple[Quantized, Quantized]:
     """Row copy and transposed (column) copy of a 2-D bf16 device tensor from

@@ -85,6 +85,42 @@ mx_status mx_quantize(const void* src, int64_t rows, int64_t cols, int64_t ld, v
   return MX_OK;
 }
 
+mx_status mx_quantize_batch(const mx_quant_item* items, int n, mx_fmt fmt, void* hip_stream) {
+  if (fmt != MX_FMT_MXFP8 && fmt != MX_FMT_MXFP4) {
+    if (fmt == MX_FMT_NVFP4)
+      return fail(MX_ERR_UNSUPPORTED, "mx_quantize_batch: NVFP4 needs a tensor amax per item; use mx_quantize");
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: unknown format %d", (int)fmt);
+  }
+  if (!items) return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: null item array");
+  if (n < 1 || n > MX_QUANT_BATCH_MAX)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: n = %d outside [1, %d]", n, MX_QUANT_BATCH_MAX);
+  static_assert(MX_QUANT_BATCH_MAX == mx::kQuantBatchMax, "batch size of the header and the launcher");
+  mx::QuantBatchItem q[MX_QUANT_BATCH_MAX];
+  for (int i = 0; i < n; ++i) {
+    const mx_quant_item& it = items[i];
+    if (it.rows < 1 || it.cols < 1)
+      return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: item %d: empty tensor (%lld x %lld)", i, (long long)it.rows,
+                  (long long)it.cols);
+    if (it.ld < it.cols)
+      return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: item %d: ld %lld < cols %lld", i, (long long)it.ld,
+                  (long long)it.cols);
+    if (!it.src || !it.codes || !it.scales) return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: item %d: null pointer", i);
+    if (!aligned(it.src, 2)) return fail(MX_ERR_ALIGNMENT, "mx_quantize_batch: item %d: src must be 2-byte aligned", i);
+    if (!aligned(it.codes, 16) || !aligned(it.scales, 16))
+      return fail(MX_ERR_ALIGNMENT, "mx_quantize_batch: item %d: codes and scales must be 16-byte aligned", i);
+    const int64_t kpad = k_pad(it.cols);
+    if (it.rows * code_row_bytes(kpad, fmt) >= kMaxBytes || scales_total(it.rows, kpad, fmt) >= kMaxBytes)
+      return fail(MX_ERR_UNSUPPORTED, "mx_quantize_batch: item %d: output larger than 2 GiB", i);
+    if (it.ld >= ((int64_t)1 << 31) || it.rows > (((int64_t)1 << 31) - 1) / it.ld)
+      return fail(MX_ERR_UNSUPPORTED, "mx_quantize_batch: item %d: input too large (rows * ld must be below 2^31)", i);
+    q[i] = mx::QuantBatchItem{static_cast<const uint16_t*>(it.src), static_cast<uint8_t*>(it.codes),
+                              static_cast<uint8_t*>(it.scales), (int)it.rows, (int)it.cols, (int)it.ld, (int)kpad};
+  }
+  hipError_t e = mx::launch_quantize_batch(q, n, (int)fmt, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(MX_ERR_HIP, "mx_quantize_batch: launch failed: %s", hipGetErrorString(e));
+  return MX_OK;
+}
+
 mx_status mx_quantize_dual(const void* src, int64_t rows, int64_t cols, int64_t ld, void* row_codes,
                            void* row_scales, void* col_codes, void* col_scales, mx_fmt fmt, const float* amax_prev,
                            float headroom, void* hip_stream) {

@@ -9,6 +9,25 @@ namespace mx {
 hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
                            uint8_t* scales, int fmt, int axis, hipStream_t stream);
 
+// One tensor of a batched row quantization (MX formats): its source, sizes,
+// outputs and K_pad = round_up(cols, 128).
+struct QuantBatchItem {
+  const uint16_t* src;
+  uint8_t* codes;
+  uint8_t* scales;
+  int rows, cols, ld, kpad;
+};
+constexpr int kQuantBatchMax = 32;
+// Passed by value as the kernel argument (about 1.4 KB).
+struct QuantBatch {
+  QuantBatchItem items[kQuantBatchMax];
+  int first_wg[kQuantBatchMax + 1];
+  int n;
+};
+
+// Row quantization of n <= kQuantBatchMax MXFP8 / MXFP4 tensors in one launch.
+hipError_t launch_quantize_batch(const QuantBatchItem* items, int n, int fmt, hipStream_t stream);
+
 // Both quantized copies (row, and column stored transposed) from one read.
 // NVFP4: amax_prev NULL -> tensor scale from this tensor; else delayed scale
 // fp32(fp64(headroom * *amax_prev) / 2688).

@@ -145,10 +145,13 @@ __device__ __forceinline__ uint64_t encode8(const float (&x)[8], uint32_t sb, co
 
 constexpr int kRowGroupsPerThread = 2;
 
+// Row quantization of one tensor by threads first_tid, first_tid + stride,
+// ... of the threads given to it (each thread: U groups of 8 elements of one
+// stored row).
 template <int FMT>
-__global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
-                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                        int kpad, NvTrailer* tr) {
+__device__ __forceinline__ void quant_rows(const uint16_t* __restrict__ src, int rows, int cols, int ld,
+                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad,
+                                           float s_t, int first_tid, int stride) {
   constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
   constexpr int LANES_PER_BLOCK = BS / 8;
   constexpr int U = kRowGroupsPerThread;
@@ -156,12 +159,7 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restri
   const int tpr = gpr / U;                        // threads per row (multiple of 8)
   const int total = rows * tpr;
   const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
-  float s_t = 0.0f;
-  if (FMT == FMT_NVFP4) {
-    s_t = nvfp4_tensor_scale(tr->amax_bits);
-    if (blockIdx.x == 0 && threadIdx.x == 0) tr->s_t = s_t;
-  }
-  for (int tid = blockIdx.x * blockDim.x + threadIdx.x; tid < total; tid += gridDim.x * blockDim.x) {
+  for (int tid = first_tid; tid < total; tid += stride) {
     const int r = tid / tpr;
     const int j = tid - r * tpr;
     const uint16_t* row = src + (int64_t)r * ld;
@@ -204,6 +202,33 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restri
       if ((j % LANES_PER_BLOCK) == 0) scales[(int64_t)r * (kpad / BS) + c / BS] = (uint8_t)sb;
     }
   }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
+                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                        int kpad, NvTrailer* tr) {
+  float s_t = 0.0f;
+  if (FMT == FMT_NVFP4) {
+    s_t = nvfp4_tensor_scale(tr->amax_bits);
+    if (blockIdx.x == 0 && threadIdx.x == 0) tr->s_t = s_t;
+  }
+  quant_rows<FMT>(src, rows, cols, ld, codes, scales, kpad, s_t, blockIdx.x * blockDim.x + threadIdx.x,
+                  gridDim.x * blockDim.x);
+}
+
+// Several MX tensors in one launch: workgroups first_wg[i] .. first_wg[i+1]-1
+// quantize item i (the search is over a handful of kernel-argument entries,
+// uniform per workgroup).
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_row_batch_kernel(const QuantBatch batch) {
+  int i = 0;
+  while (i + 1 < batch.n && (int)blockIdx.x >= batch.first_wg[i + 1]) ++i;
+  const QuantBatchItem& it = batch.items[i];
+  const int wg = (int)blockIdx.x - batch.first_wg[i];
+  const int nwg = batch.first_wg[i + 1] - batch.first_wg[i];
+  quant_rows<FMT>(it.src, it.rows, it.cols, it.ld, it.codes, it.scales, it.kpad, 0.0f, wg * 256 + (int)threadIdx.x,
+                  nwg * 256);
 }
 
 // ------------------------------------------------------------ col quantizer
@@ -546,6 +571,22 @@ hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int6
       default:        quant_col_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
     }
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_batch(const QuantBatchItem* items, int n, int fmt, hipStream_t stream) {
+  QuantBatch batch{};
+  batch.n = n;
+  int64_t wg = 0;
+  for (int i = 0; i < n; ++i) {
+    batch.items[i] = items[i];
+    batch.first_wg[i] = (int)wg;
+    const int64_t threads = (int64_t)items[i].rows * (items[i].kpad / 8 / kRowGroupsPerThread);
+    wg += grid_for(threads, 256, 1 << 16);
+  }
+  batch.first_wg[n] = (int)wg;
+  if (fmt == FMT_MXFP8) quant_row_batch_kernel<FMT_MXFP8><<<(int)wg, 256, 0, stream>>>(batch);
+  else quant_row_batch_kernel<FMT_MXFP4><<<(int)wg, 256, 0, stream>>>(batch);
   return hipGetLastError();
 }
 

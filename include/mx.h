@@ -123,7 +123,38 @@ mx_status mx_quantize_dual(const void* src, int64_t rows, int64_t cols, int64_t 
                            void* row_codes, void* row_scales, void* col_codes, void* col_scales,
                            mx_fmt fmt, const float* amax_prev, float headroom, void* hip_stream);
 
-/* C = A * B^T (+ bias) from quantized operands/* C = A * B^T (+ bias) from quantized operands (README section 4.3 GEMMs,
+/* One tensor of mx_quantize_batch: X [rows, cols] (bf16, leading dimension
+ * ld elements) and its row-axis outputs, sized by mx_codes_bytes /
+ * mx_scales_bytes with MX_AXIS_ROW. */
+typedef struct {
+  const void* src;
+  int64_t rows;
+  int64_t cols;
+  int64_t ld;
+  void* codes;
+  void* scales;
+} mx_quant_item;
+
+/* Most items one mx_quantize_batch call takes. */
+#define MX_QUANT_BATCH_MAX 32
+
+/* Row quantization (README section 2 formats, along K as for mx_quantize
+ * with MX_AXIS_ROW) of n independent tensors in ONE launch: item i's codes
+ * and scales are byte for byte those of mx_quantize(item i, fmt,
+ * MX_AXIS_ROW). Meant for many small tensors quantized together, such as
+ * every weight matrix at the start of a training step, where one launch per
+ * tensor would cost more than the work.
+ *   items: host array of n entries, read during the call only; n in
+ *          [1, MX_QUANT_BATCH_MAX].
+ *   fmt:   MX_FMT_MXFP8 or MX_FMT_MXFP4. NVFP4 needs a tensor-amax pass per
+ *          item and is MX_ERR_UNSUPPORTED here (use mx_quantize).
+ * Every item is validated as mx_quantize validates its arguments (and each
+ * item's input must also satisfy rows * ld < 2^31 elements) before anything
+ * is launched; on an error nothing is written and the message names the
+ * item. Outputs of different items must not overlap. */
+mx_status mx_quantize_batch(const mx_quant_item* items, int n, mx_fmt fmt, void* hip_stream);
+
+/* C = A * B^T (+ bias) from quantized operands (README section 4.3 GEMMs,
  * section 5.5 TN layout). A / As: codes and scales of an M-row operand,
  * B / Bs: of an N-row operand, both of logical length K. bias: bf16[N] or
  * NULL. out_dtype selects bf16 or fp32 C. */

@@ -104,6 +104,41 @@ def test_quantize_dual_validation(L, args, status, msg):
     assert msg in L.mx_last_error().decode()
 
 
+def _items(*specs):
+    arr = (_lib.QuantItem * max(1, len(specs)))()
+    for i, (src, rows, cols, ld, codes, scales) in enumerate(specs):
+        arr[i] = _lib.QuantItem(src, rows, cols, ld, codes, scales)
+    return arr
+
+
+GOOD = (ALIGNED, 4, 4, 4, ALIGNED, ALIGNED)
+
+
+@pytest.mark.parametrize("specs,n,fmt,status,msg", [
+    ((GOOD,), 1, 3, 2, "NVFP4"),
+    ((GOOD,), 1, 9, 1, "unknown format"),
+    ((GOOD,), 0, 1, 1, "outside [1, 32]"),
+    ((GOOD,), 33, 1, 1, "outside [1, 32]"),
+    ((GOOD, (ALIGNED, 0, 4, 4, ALIGNED, ALIGNED)), 2, 1, 1, "item 1: empty"),
+    ((GOOD, GOOD, (ALIGNED, 4, 8, 4, ALIGNED, ALIGNED)), 3, 2, 1, "item 2: ld"),
+    (((None, 4, 4, 4, ALIGNED, ALIGNED),), 1, 1, 1, "item 0: null"),
+    (((ALIGNED + 1, 4, 4, 4, ALIGNED, ALIGNED),), 1, 1, 3, "item 0: src must be 2-byte"),
+    ((GOOD, (ALIGNED, 4, 4, 4, ALIGNED, ALIGNED + 4)), 2, 1, 3, "item 1: codes and scales"),
+    (((ALIGNED, 1 << 20, 1 << 12, 1 << 12, ALIGNED, ALIGNED),), 1, 1, 2, "item 0: output larger"),
+    (((ALIGNED, 1 << 19, 4096, 4096, ALIGNED, ALIGNED),), 1, 2, 2, "item 0: input too large"),
+])
+def test_quantize_batch_validation(L, specs, n, fmt, status, msg):
+    """Every item is checked before anything is launched; the message names
+    the first bad item."""
+    assert L.mx_quantize_batch(_items(*specs), n, fmt, None) == status
+    assert msg in L.mx_last_error().decode()
+
+
+def test_quantize_batch_null_items(L):
+    assert L.mx_quantize_batch(None, 1, 1, None) == 1
+    assert "null item array" in L.mx_last_error().decode()
+
+
 def test_quantize_dual_ignores_headroom_for_mx(L):
     """MX formats never read amax_prev / headroom: a bad headroom is not an
     error there (the call then fails later on the 2 GiB check, still before
