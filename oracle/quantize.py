@@ -265,3 +265,132 @@ def scales_bytes(rows: int, cols: int, fmt: str, axis: str) -> int:
     if fmt == "nvfp4":
         return round_up(n, 16) + 16
     return n
+
+
+# ------------------------------------------------------------------ stochastic rounding
+#
+# README section 5.5 / the training recipe it describes: gradients (dY) are
+# quantized to NVFP4 with stochastic rounding, the random numbers drawn from a
+# counter-based generator (Philox), so that every element's draw is a pure
+# function of (seed, element position) and any implementation that follows
+# the same definition reproduces the codes bit for bit.
+#
+# Readings (the page names the method and the generator, not the details):
+#   * generator: Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw,
+#     "Parallel random numbers: as easy as 1, 2, 3", SC 2011), key = the
+#     two 64-bit seed words, counter = (q, 0, 0, 0) for block q of eight
+#     elements; element i = r * cols + c of the logical X [rows, cols] takes
+#     32 bits of output word (i mod 8) // 2: the low half if i is even, the
+#     high half if odd. The draw of an element does not depend on the axis.
+#   * block scale bytes and s_t are exactly those of round-to-nearest.
+#   * element: S32 = fp32(dec(byte) * s_t), y = fp32(|x| / S32) (IEEE,
+#     round to nearest even); y >= 6 gives code 6 (saturation); otherwise
+#     lo <= y < hi are neighbouring E2M1 grid values, frac = (y - lo) /
+#     (hi - lo) (exact in fp32: Sterbenz for lo >= 0.5, and hi - lo is 0.5,
+#     1 or 2), and the code is hi iff u < ceil(frac * 2^32), u the element's
+#     32-bit draw; else lo. S32 == 0 gives signed zeros. The sign is x's.
+#   These fp32 steps are the kernel's precision, fixed here so both sides
+#   take the same integer decision.
+
+_M64 = (1 << 64) - 1
+_PHILOX_M = (np.uint64(0xD2E7470EE14C6C93), np.uint64(0xCA5A826395121157))
+_PHILOX_W = (np.uint64(0x9E3779B97F4A7C15), np.uint64(0xBB67AE8584CAA73B))
+
+
+def _mulhilo64(a: np.ndarray, b: np.uint64):
+    """(high, low) 64-bit halves of the 128-bit products a * b (uint64)."""
+    m32 = np.uint64(0xFFFFFFFF)
+    s32 = np.uint64(32)
+    a_lo, a_hi = a & m32, a >> s32
+    b_lo, b_hi = b & m32, b >> s32
+    ll, lh, hl, hh = a_lo * b_lo, a_lo * b_hi, a_hi * b_lo, a_hi * b_hi
+    mid = (ll >> s32) + (lh & m32) + (hl & m32)
+    hi = hh + (lh >> s32) + (hl >> s32) + (mid >> s32)
+    return hi, a * b
+
+
+def philox4x64(counters: np.ndarray, key) -> np.ndarray:
+    """Philox4x64-10 of each row of counters [N, 4] (uint64) under the key
+    (k0, k1): ten rounds of the four-word round function (two 64x64 -> 128
+    multiplies whose high halves are xored into the other words together
+    with the round key), the key bumped by the Weyl constants between
+    rounds. Returns [N, 4] uint64."""
+    c = np.array(counters, dtype=np.uint64).reshape(-1, 4)
+    c0, c1, c2, c3 = (c[:, i].copy() for i in range(4))
+    k0, k1 = np.uint64(key[0]), np.uint64(key[1])
+    with np.errstate(over="ignore"):
+        for _ in range(10):
+            hi0, lo0 = _mulhilo64(c0, _PHILOX_M[0])
+            hi1, lo1 = _mulhilo64(c2, _PHILOX_M[1])
+            c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+            k0 = np.uint64((int(k0) + int(_PHILOX_W[0])) & _M64)
+            k1 = np.uint64((int(k1) + int(_PHILOX_W[1])) & _M64)
+    return np.stack([c0, c1, c2, c3], axis=1)
+
+
+def sr_draws(rows: int, cols: int, seed) -> np.ndarray:
+    """The 32-bit draw of every element of X [rows, cols] (uint32 [rows, cols])."""
+    n = rows * cols
+    nq = (n + 7) // 8
+    ctr = np.zeros((nq, 4), dtype=np.uint64)
+    ctr[:, 0] = np.arange(nq, dtype=np.uint64)
+    words = philox4x64(ctr, seed)                              # [nq, 4]
+    halves = np.empty((nq, 8), dtype=np.uint32)
+    halves[:, 0::2] = (words & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+    halves[:, 1::2] = (words >> np.uint64(32)).astype(np.uint32)
+    return halves.reshape(-1)[:n].reshape(rows, cols)
+
+
+def nvfp4_element_codes_sr(x: np.ndarray, S32: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """E2M1 codes of x / S32 rounded stochastically with the draws u (the
+    fp32 steps of the reading above); sign copied from x."""
+    x = np.asarray(x, dtype=np.float64)
+    S32 = np.asarray(S32, dtype=np.float32)
+    a = np.abs(x).astype(np.float32)                           # exact: x is bf16
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        y = np.where(S32 > 0, a / np.where(S32 > 0, S32, np.float32(1)), np.float32(0)).astype(np.float32)
+    grid = F.E2M1_GRID.astype(np.float32)                     # 0, .5, 1, 1.5, 2, 3, 4, 6
+    lo_i = np.clip(np.searchsorted(grid, y, side="right") - 1, 0, 7)
+    sat = y >= np.float32(6.0)
+    hi_i = np.minimum(lo_i + 1, 7)
+    lo, hi = grid[lo_i], grid[hi_i]
+    span = np.where(sat, np.float32(1), hi - lo).astype(np.float32)
+    frac = ((y - lo) / span).astype(np.float32)                # exact (see the reading)
+    T = np.ceil(frac.astype(np.float64) * 4294967296.0)
+    up = (~sat) & (np.asarray(u, dtype=np.float64) < T)
+    mag = np.where(sat, 7, np.where(up, hi_i, lo_i)).astype(np.int64)
+    mag = np.where(S32 > 0, mag, 0)
+    sign = np.signbit(x).astype(np.int64) << 3
+    return (sign | mag).astype(np.uint8)
+
+
+def quantize_sr(bits: np.ndarray, axis: str, seed, s_t=None) -> Quantized:
+    """NVFP4 quantization of X along `axis` with stochastically rounded
+    elements (block scales and s_t as quantize()); seed = (k0, k1)."""
+    rows0, cols0 = np.asarray(bits).shape
+    draws = sr_draws(rows0, cols0, seed)
+    t = _view(bits, axis)
+    u = draws if axis == "row" else np.ascontiguousarray(draws.T)
+    x = F.bf16_to_f64(t)
+    rows, length = x.shape
+    k_pad = round_up(length, K_ALIGN)
+    tensor_amax = float(np.abs(x).max()) if x.size else 0.0
+    st = nvfp4_tensor_scale(tensor_amax) if s_t is None else np.float32(s_t)
+    bs = 16
+    blocks = _blocks(x, bs, k_pad)
+    bamax = np.abs(blocks).max(axis=2)
+    scales = nvfp4_block_bytes(bamax, st)
+    S32 = (F.e4m3_decode(scales).astype(np.float32) * np.float32(st)).astype(np.float32)
+    ublocks = np.zeros((rows, k_pad), dtype=np.uint32)
+    ublocks[:, :length] = u
+    codes = nvfp4_element_codes_sr(blocks, np.repeat(S32[:, :, None], bs, axis=2),
+                                   ublocks.reshape(rows, k_pad // bs, bs))
+    return Quantized("nvfp4", rows, length, k_pad, codes.reshape(rows, k_pad), scales,
+                     s_t=st, amax=np.float32(tensor_amax))
+
+
+def quantize_dual_sr(bits: np.ndarray, seed, amax_prev=None, headroom: float = 32.0):
+    """Row and column NVFP4 copies with stochastic rounding, one tensor scale
+    (X's own, or the delayed one) and one draw per element shared by both."""
+    s_t = None if amax_prev is None else nvfp4_delayed_scale(amax_prev, headroom)
+    return quantize_sr(bits, "row", seed, s_t), quantize_sr(bits, "col", seed, s_t)

@@ -465,3 +465,130 @@ def test_nvfp4_scale_power_of_two_invariance():
     blk0 = q0.codes.reshape(8, -1, 16)
     blk1 = q1.codes.reshape(8, -1, 16)
     assert np.array_equal(blk0[ok], blk1[ok])
+
+
+# ------------------------------------------------------------------ stochastic rounding pins
+
+SR_KEY = (0x0123456789ABCDEF, 0xFEDCBA9876543210)
+
+
+@pytest.mark.parametrize("key", [SR_KEY, (0, 0), (2**64 - 1, 12345)])
+def test_philox_matches_numpy_library_generator(key):
+    """numpy.random.Philox is Philox4x64-10; it increments its 256-bit counter
+    (with carry) before producing each 4-word block."""
+    start = [2**64 - 2, 7, 0, 0]              # crosses a carry into word 1
+    bg = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=np.array(start, dtype=np.uint64))
+    raw = bg.random_raw(4 * 5).reshape(5, 4)
+    ctr = [[2**64 - 1, 7, 0, 0], [0, 8, 0, 0], [1, 8, 0, 0], [2, 8, 0, 0], [3, 8, 0, 0]]
+    assert np.array_equal(Q.philox4x64(np.array(ctr, dtype=np.uint64), key), raw)
+
+
+def test_sr_draws_are_the_generator_stream():
+    """The element draws, in row-major element order, are numpy's Philox
+    stream from counter 0, each 64-bit word split low half first."""
+    rows, cols = 7, 45                         # 315 elements: a partial last group of 8
+    all_ones = np.array([2**64 - 1] * 4, dtype=np.uint64)   # +1 wraps to counter 0
+    bg = np.random.Philox(key=np.array(SR_KEY, dtype=np.uint64), counter=all_ones)
+    words = bg.random_raw(4 * 40)
+    halves = np.stack([words & 0xFFFFFFFF, words >> np.uint64(32)], axis=1).reshape(-1).astype(np.uint32)
+    assert np.array_equal(Q.sr_draws(rows, cols, SR_KEY).reshape(-1), halves[:rows * cols])
+
+
+def _grid_floor_ceil(y):
+    g = [float(v) for v in F.E2M1_GRID]
+    fl = max(i for i in range(8) if g[i] <= y)
+    ce = min((i for i in range(8) if g[i] >= y), default=7)
+    return fl, ce
+
+
+def test_sr_extreme_draws_are_ceil_and_floor():
+    """u = 0 rounds every off-grid value up, u = 2^32 - 1 rounds every value
+    down (frac < 1 - 2^-24 in fp32); checked against a brute-force floor /
+    ceil over the eight grid values."""
+    rng = np.random.default_rng(5)
+    y = np.float32(rng.uniform(0, 6, 4000)).astype(np.float32)
+    y[:8] = F.E2M1_GRID.astype(np.float32)
+    S = np.ones_like(y, dtype=np.float32)
+    x = y.astype(np.float64) * np.where(rng.random(y.size) < 0.5, -1.0, 1.0)
+    up = Q.nvfp4_element_codes_sr(x, S, np.zeros(y.size, dtype=np.uint32))
+    down = Q.nvfp4_element_codes_sr(x, S, np.full(y.size, 0xFFFFFFFF, dtype=np.uint32))
+    for i in range(y.size):
+        fl, ce = _grid_floor_ceil(float(y[i]))
+        sign = 8 if x[i] < 0 or (x[i] == 0 and np.signbit(x[i])) else 0
+        assert down[i] == sign | fl and up[i] == sign | ce, (y[i], down[i], up[i])
+
+
+def test_sr_threshold_is_exact():
+    """frac = 1/4 between grid values 4 and 6 (y = 4.5): the code is 6 exactly
+    for draws below 2^30, and 4 from 2^30 on."""
+    x = np.full(4, 4.5)
+    S = np.ones(4, dtype=np.float32)
+    u = np.array([0, 2**30 - 1, 2**30, 2**32 - 1], dtype=np.uint32)
+    assert Q.nvfp4_element_codes_sr(x, S, u).tolist() == [7, 7, 6, 6]
+
+
+def test_sr_saturation_and_zero_scale():
+    x = np.array([6.0, 7.0, 1e30, -100.0, 3.0, -3.0])
+    S = np.array([1, 1, 1, 1, 0, 0], dtype=np.float32)
+    u = np.zeros(6, dtype=np.uint32)
+    assert Q.nvfp4_element_codes_sr(x, S, u).tolist() == [7, 7, 7, 15, 0, 8]
+
+
+def test_sr_is_unbiased():
+    """The mean of the stochastically rounded values of many copies of one
+    off-grid value is the value itself (within 5 sigma of the binomial
+    count), unlike round-to-nearest."""
+    for y, lo, hi in [(0.3, 0.0, 0.5), (1.2, 1.0, 1.5), (2.7, 2.0, 3.0), (5.1, 4.0, 6.0)]:
+        n = 1 << 16
+        bits = W.to_bf16_bits(np.full((256, n // 256), y))
+        yb = float(F.bf16_to_f64(bits[:1, :1])[0, 0])
+        x = F.bf16_to_f64(bits)
+        u = Q.sr_draws(*bits.shape, SR_KEY)
+        codes = Q.nvfp4_element_codes_sr(x, np.ones(x.shape, dtype=np.float32), u)
+        vals = F.E2M1_GRID[codes & 7]
+        p = (yb - lo) / (hi - lo)
+        k = (vals == hi).sum()
+        assert set(np.unique(vals)) <= {lo, hi}
+        assert abs(k - n * p) <= 5 * np.sqrt(n * p * (1 - p)), (y, k, n * p)
+
+
+def test_sr_keeps_the_rne_scales_and_exact_grid_values():
+    """Block scale bytes and s_t are those of round-to-nearest. With s_t = 1
+    (tensor amax 2688) and power-of-two block scales every quotient is exact,
+    so on-grid inputs get the same codes for any seed."""
+    rng = np.random.default_rng(3)
+    grid = F.E2M1_GRID
+    blocks = []
+    for b in range(64):
+        scale = 2.0 ** rng.integers(-6, 3)              # dec(byte) = scale: a power of two
+        vals = grid[rng.integers(0, 8, 16)] * scale * np.where(rng.random(16) < 0.5, -1, 1)
+        vals[0] = 6.0 * scale                            # block amax = 6 * scale -> byte decodes to scale
+        blocks.append(vals)
+    x = np.concatenate(blocks).reshape(4, 256)
+    x[0, 1] = 2688.0                                     # tensor amax -> s_t = 1
+    bits = W.to_bf16_bits(x)
+    ref = Q.quantize(bits, "nvfp4", "row")
+    assert ref.s_t == np.float32(1.0)
+    for key in [(1, 2), (3, 4), SR_KEY]:
+        q = Q.quantize_sr(bits, "row", key)
+        assert np.array_equal(q.scales, ref.scales) and q.s_t == ref.s_t and q.amax == ref.amax
+        assert np.array_equal(q.codes, ref.codes)
+
+
+def test_sr_col_copy_uses_the_same_draws():
+    """The column copy rounds element (r, c) with the draw of (r, c). With a
+    6 on the diagonal of every 16x16 tile, every row block and every column
+    block has amax 6 and the same scale, so element (r, c) has the same
+    quotient in both copies and the column copy is the row copy transposed.
+    A column copy that drew by its own storage position would differ."""
+    rng = np.random.default_rng(9)
+    x = rng.uniform(0.1, 5.9, (48, 64))
+    for i in range(48):
+        x[i, (i % 16)::16] = 6.0
+    bits = W.to_bf16_bits(x)
+    r, c = Q.quantize_dual_sr(bits, SR_KEY)
+    assert len(np.unique(r.scales[:, :4])) == 1 and len(np.unique(c.scales[:, :3])) == 1
+    assert r.scales[0, 0] == c.scales[0, 0]
+    assert np.array_equal(r.codes[:, :64], c.codes[:, :48].T)
+    swapped = Q.quantize_sr(np.ascontiguousarray(bits.T), "row", SR_KEY)
+    assert not np.array_equal(swapped.codes[:, :48], c.codes[:, :48])
