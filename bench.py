@@ -39,7 +39,8 @@ NVFP4_AMAX_BYTES = 2.0
 
 
 WORKLOADS = ["vitl16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack", "vitb16_mxfp8_fwd_stack",
-             "vitl16_nvfp4_fc1fc2_train", "vitl16_mxfp8_fc1fc2_train", "single_mxfp8_256x768x768"]
+             "vitl16_nvfp4_fc1fc2_train", "vitl16_nvfp4_fc1fc2_train_srgrad", "vitl16_mxfp8_fc1fc2_train",
+             "single_mxfp8_256x768x768"]
 
 
 def parse():
@@ -117,9 +118,10 @@ def build_train(tp, dev):
     # own amax, as the config defines)
     dual_bytes = 2.0 + 2 * (QUANT_BYTES[fmt] - 2.0) + (NVFP4_AMAX_BYTES if fmt == "nvfp4" else 0.0)
 
-    def quant_dual(name, t):
+    def quant_dual(name, t, sr=False):
         """Both copies of t (row, and transposed for the other GEMMs) from one
-        read (mx_quantize_dual)."""
+        read (mx_quantize_dual; mx_quantize_dual_sr for stochastically
+        rounded gradients)."""
         r, c = t.shape
         bufs = []
         for axis, rows, length in (("row", r, c), ("col", c, r)):
@@ -127,9 +129,11 @@ def build_train(tp, dev):
                                       torch.empty(api.scales_bytes(r, c, fmt, axis), dtype=torch.uint8, device=dev),
                                       fmt, rows, length))
         q[name + "_row"], q[name + "_col"] = bufs
-        ops.append(Op("quant", lambda: api.mx_quantize_dual(t, fmt, None, 1.0, out=(bufs[0], bufs[1])),
-                      nbytes=dual_bytes * t.numel(),
-                      label=f"quant_{name}_rowcol"))
+        if sr:
+            fn = lambda: api.mx_quantize_dual_sr(t, tp.sr_seed, None, 1.0, out=(bufs[0], bufs[1]))   # noqa: E731
+        else:
+            fn = lambda: api.mx_quantize_dual(t, fmt, None, 1.0, out=(bufs[0], bufs[1]))             # noqa: E731
+        ops.append(Op("quant", fn, nbytes=dual_bytes * t.numel(), label=f"quant_{name}_rowcol"))
 
     def gemm(name, a, b, bias, m, n, k):
         out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
@@ -139,13 +143,13 @@ def build_train(tp, dev):
     # fc1: fprop X W1^T, dgrad dY1 W1, wgrad dY1^T X
     quant_dual("X", X); quant_dual("W1", W1)
     gemm("fc1_fprop", "X_row", "W1_row", b1, tp.m, tp.mlp, tp.hidden)
-    quant_dual("dY1", dY1)
+    quant_dual("dY1", dY1, sr=tp.sr_grads)
     gemm("fc1_dgrad", "dY1_row", "W1_col", None, tp.m, tp.hidden, tp.mlp)
     gemm("fc1_wgrad", "dY1_col", "X_col", None, tp.mlp, tp.hidden, tp.m)
     # fc2: fprop H W2^T, dgrad dY2 W2, wgrad dY2^T H
     quant_dual("H", H); quant_dual("W2", W2)
     gemm("fc2_fprop", "H_row", "W2_row", b2, tp.m, tp.hidden, tp.mlp)
-    quant_dual("dY2", dY2)
+    quant_dual("dY2", dY2, sr=tp.sr_grads)
     gemm("fc2_dgrad", "dY2_row", "W2_col", None, tp.m, tp.mlp, tp.hidden)
     gemm("fc2_wgrad", "dY2_col", "H_col", None, tp.hidden, tp.mlp, tp.m)
     return ops
@@ -266,7 +270,8 @@ def main():
         gemm_peak_key = "fp16" if fmt == "nvfp4" else fmt
         config = {"workload": wl.name, "M": wl.m, "hidden": wl.hidden, "mlp": wl.mlp, "tokens_per_image": W.TOKENS,
                   "batch": wl.m // W.TOKENS, "format": fmt, "gemms": "fc1/fc2 fprop+dgrad+wgrad",
-                  "quantizations": "6 tensors, row and transposed copies from one read each"}
+                  "quantizations": "6 tensors, row and transposed copies from one read each",
+                  "grad_rounding": "stochastic (Philox4x64-10)" if wl.sr_grads else "nearest-even"}
     else:
         wl = W.STACKS[args.workload]
         fmt = wl.fmt

@@ -151,6 +151,40 @@ def mx_quantize_dual(x: torch.Tensor, fmt: str, amax_prev: torch.Tensor | None =
     return (Quantized(bufs[0], bufs[1], fmt, rows, cols), Quantized(bufs[2], bufs[3], fmt, cols, rows))
 
 
+def mx_quantize_dual_sr(x: torch.Tensor, seed: tuple[int, int], amax_prev: torch.Tensor | None = None,
+                        headroom: float = 32.0, out: tuple[Quantized, Quantized] | None = None,
+                        stream=None) -> tuple[Quantized, Quantized]:
+    """NVFP4 row and column copies of x with stochastically rounded elements
+    (Philox4x64-10 draws keyed by seed = (k0, k1), one per element of x);
+    scales, s_t and trailers as mx_quantize_dual. x.shape[1] % 8 == 0."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D bfloat16 device tensor")
+    if x.stride(1) != 1 and x.shape[1] > 1:
+        raise ValueError("x must have unit stride along its last dimension")
+    ptr = 0
+    if amax_prev is not None:
+        if amax_prev.dtype != torch.float32 or amax_prev.numel() < 1 or not amax_prev.is_cuda:
+            raise ValueError("amax_prev must be a float32 device tensor")
+        ptr = amax_prev.data_ptr()
+    fmt = "nvfp4"
+    rows, cols = x.shape
+    bufs = []
+    for i, axis in enumerate(("row", "col")):
+        nc, ns = codes_bytes(rows, cols, fmt, axis), scales_bytes(rows, cols, fmt, axis)
+        if out is None:
+            bufs.append(torch.empty(nc, dtype=torch.uint8, device=x.device))
+            bufs.append(torch.empty(ns, dtype=torch.uint8, device=x.device))
+        else:
+            if out[i].codes.numel() < nc or out[i].scales.numel() < ns:
+                raise ValueError("out buffers are too small")
+            bufs += [out[i].codes, out[i].scales]
+    k0, k1 = (int(v) & ((1 << 64) - 1) for v in seed)
+    _check(lib().mx_quantize_dual_sr(x.data_ptr(), rows, cols, _ld(x), bufs[0].data_ptr(), bufs[1].data_ptr(),
+                                     bufs[2].data_ptr(), bufs[3].data_ptr(), FMT[fmt], ptr or None, float(headroom),
+                                     k0, k1, _stream(stream)))
+    return (Quantized(bufs[0], bufs[1], fmt, rows, cols), Quantized(bufs[2], bufs[3], fmt, cols, rows))
+
+
 def amax_field(scales: torch.Tensor) -> torch.Tensor:
     """The fp32 amax of an NVFP4 scale buffer's trailer, as a one-element view."""
     return scales[-16:].view(torch.float32)[1:2]

@@ -146,8 +146,43 @@ mx_status mx_quantize_dual(const void* src, int64_t rows, int64_t cols, int64_t 
   hipError_t e = mx::launch_quantize_dual(
       static_cast<const uint16_t*>(src), rows, cols, ld, static_cast<uint8_t*>(row_codes),
       static_cast<uint8_t*>(row_scales), static_cast<uint8_t*>(col_codes), static_cast<uint8_t*>(col_scales), (int)fmt,
-      delayed ? amax_prev : nullptr, headroom, static_cast<hipStream_t>(hip_stream));
+      delayed ? amax_prev : nullptr, headroom, 0, 0, 0, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(MX_ERR_HIP, "mx_quantize_dual: launch failed: %s", hipGetErrorString(e));
+  return MX_OK;
+}
+
+mx_status mx_quantize_dual_sr(const void* src, int64_t rows, int64_t cols, int64_t ld, void* row_codes,
+                              void* row_scales, void* col_codes, void* col_scales, mx_fmt fmt, const float* amax_prev,
+                              float headroom, uint64_t seed0, uint64_t seed1, void* hip_stream) {
+  if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "mx_quantize_dual_sr: unknown format %d", (int)fmt);
+  if (fmt != MX_FMT_NVFP4)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_dual_sr: stochastic rounding is implemented for NVFP4 only");
+  if (rows < 1 || cols < 1)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_dual_sr: empty tensor (%lld x %lld)", (long long)rows, (long long)cols);
+  if (ld < cols) return fail(MX_ERR_INVALID_ARG, "mx_quantize_dual_sr: ld %lld < cols %lld", (long long)ld, (long long)cols);
+  if (cols % 8 != 0)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_dual_sr: cols (%lld) must be a multiple of 8", (long long)cols);
+  if (!src || !row_codes || !row_scales || !col_codes || !col_scales)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_dual_sr: null pointer");
+  const bool delayed = amax_prev != nullptr;
+  if (delayed && !(headroom > 0.0f && headroom <= 3.0e38f))
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_dual_sr: headroom must be finite and > 0");
+  if (!aligned(src, 2)) return fail(MX_ERR_ALIGNMENT, "mx_quantize_dual_sr: src must be 2-byte aligned");
+  if (!aligned(row_codes, 16) || !aligned(row_scales, 16) || !aligned(col_codes, 16) || !aligned(col_scales, 16))
+    return fail(MX_ERR_ALIGNMENT, "mx_quantize_dual_sr: codes and scales must be 16-byte aligned");
+  if (delayed && !aligned(amax_prev, 4))
+    return fail(MX_ERR_ALIGNMENT, "mx_quantize_dual_sr: amax_prev must be 4-byte aligned");
+  const int64_t rkpad = k_pad(cols), ckpad = k_pad(rows);
+  if (rows * code_row_bytes(rkpad, fmt) >= kMaxBytes || scales_total(rows, rkpad, fmt) >= kMaxBytes ||
+      cols * code_row_bytes(ckpad, fmt) >= kMaxBytes || scales_total(cols, ckpad, fmt) >= kMaxBytes)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_dual_sr: output larger than 2 GiB");
+  if (ld >= ((int64_t)1 << 31) || rows > ((int64_t)1 << 40) / ld)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_dual_sr: input too large (ld must be below 2^31)");
+  hipError_t e = mx::launch_quantize_dual(
+      static_cast<const uint16_t*>(src), rows, cols, ld, static_cast<uint8_t*>(row_codes),
+      static_cast<uint8_t*>(row_scales), static_cast<uint8_t*>(col_codes), static_cast<uint8_t*>(col_scales), (int)fmt,
+      delayed ? amax_prev : nullptr, headroom, 1, seed0, seed1, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(MX_ERR_HIP, "mx_quantize_dual_sr: launch failed: %s", hipGetErrorString(e));
   return MX_OK;
 }
 

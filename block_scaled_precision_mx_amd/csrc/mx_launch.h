@@ -30,10 +30,12 @@ hipError_t launch_quantize_batch(const QuantBatchItem* items, int n, int fmt, hi
 
 // Both quantized copies (row, and column stored transposed) from one read.
 // NVFP4: amax_prev NULL -> tensor scale from this tensor; else delayed scale
-// fp32(fp64(headroom * *amax_prev) / 2688).
+// fp32(fp64(headroom * *amax_prev) / 2688). sr (NVFP4, cols % 8 == 0):
+// elements rounded stochastically with Philox4x64-10 draws keyed by
+// (seed0, seed1).
 hipError_t launch_quantize_dual(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* rcodes,
                                 uint8_t* rscales, uint8_t* ccodes, uint8_t* cscales, int fmt, const float* amax_prev,
-                                float headroom, hipStream_t stream);
+                                float headroom, int sr, uint64_t seed0, uint64_t seed1, hipStream_t stream);
 
 // MXFP8 / MXFP4: scaled-MFMA GEMM. C = A * B^T (+ bias), fp32 accumulate.
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs,

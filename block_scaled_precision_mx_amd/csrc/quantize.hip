@@ -373,15 +373,87 @@ __global__ void nv_dual_init_kernel(uint8_t* rgap, int rgap_bytes, NvTrailer* rt
   if (t < cgap_bytes) cgap[t] = 0;
 }
 
-template <int FMT>
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of the four-word round function,
+// the key bumped by the Weyl constants between rounds.
+__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+
+// The eight 32-bit draws of elements 8q .. 8q + 7 of X (row-major element
+// order): Philox4x64-10 of counter (q, 0, 0, 0), each word split low half
+// first.
+__device__ __forceinline__ void sr_draws8(uint64_t q, uint64_t k0, uint64_t k1, uint32_t (&d)[8]) {
+  uint64_t c[4] = {q, 0ull, 0ull, 0ull};
+  philox4x64_10(c, k0, k1);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    d[2 * w] = (uint32_t)c[w];
+    d[2 * w + 1] = (uint32_t)(c[w] >> 32);
+  }
+}
+
+// E2M1 magnitude code of y >= 0 rounded stochastically with draw u: between
+// the grid neighbours lo <= y < hi, hi iff u < ceil(frac * 2^32), frac =
+// (y - lo) / (hi - lo) (exact); y >= 6 saturates.
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) {
+  if (!(y < 6.0f)) return 7u;
+  uint32_t lo;
+  float glo, inv_span;
+  if (y < 2.0f) {
+    lo = (uint32_t)(y * 2.0f);             // 0, 0.5, 1, 1.5: floor of 2y
+    glo = (float)lo * 0.5f;
+    inv_span = 2.0f;
+  } else if (y < 4.0f) {
+    lo = y < 3.0f ? 4u : 5u;               // 2, 3
+    glo = y < 3.0f ? 2.0f : 3.0f;
+    inv_span = 1.0f;
+  } else {
+    lo = 6u;                               // 4 (next: 6)
+    glo = 4.0f;
+    inv_span = 0.5f;
+  }
+  const float frac = (y - glo) * inv_span;                 // exact
+  const uint32_t T = (uint32_t)ceilf(frac * 4294967296.0f); // < 2^32 - 255: exact
+  return u < T ? lo + 1u : lo;
+}
+
+// NVFP4 code of x with scale S32 = fp32(dec(byte) * s_t), rounded
+// stochastically with draw u: y = fp32(|x| / S32), sign copied from x.
+__device__ __forceinline__ uint32_t nvfp4_encode_sr(float x, float S32, uint32_t u) {
+  const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
+  if (!(S32 > 0.0f)) return sign;
+  const float y = __fdiv_rn(fabsf(x), S32);
+  return sign | e2m1_sr(y, u);
+}
+
+template <int FMT, bool SR = false>
 __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
                                                          uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
                                                          int rkpad, uint8_t* __restrict__ ccodes,
                                                          uint8_t* __restrict__ cscales, int ckpad, NvTrailer* rtr,
-                                                         NvTrailer* ctr, int delayed) {
+                                                         NvTrailer* ctr, int delayed, uint64_t seed0 = 0,
+                                                         uint64_t seed1 = 0) {
   constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
   constexpr int LANES_PER_BLOCK = BS / 8;
+  static_assert(!SR || FMT == FMT_NVFP4, "stochastic rounding is an NVFP4 option");
   __shared__ __align__(16) uint16_t tile[kColTileR * kColLdsLd];
+  // stochastic rounding: the draw of every element of the tile, written by
+  // the row pass and read by the column pass (one draw per element of X)
+  __shared__ __align__(16) uint32_t draw[SR ? kColTileR * kColTileC : 4];
   __shared__ uint32_t wave_max[4];
   const int tiles_c = rkpad / kColTileC;
   const int tiles_r = ckpad / kColTileR;
@@ -445,7 +517,24 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
       for (int off = 1; off < LANES_PER_BLOCK; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
       Nv4Thresholds th;
       const uint32_t sb = block_scale<FMT>(m, s_t, th);
-      const uint64_t packed = encode8<FMT>(x, sb, th);
+      uint64_t packed;
+      if constexpr (SR) {
+        // draws of elements (r, c .. c + 7): one Philox block when the
+        // element index r * cols + c is a multiple of 8 (cols % 8 == 0 is a
+        // precondition); tile padding never reaches a code (its x is 0)
+        uint32_t d[8];
+        sr_draws8(((uint64_t)r * (uint64_t)cols + (uint64_t)c) >> 3, seed0, seed1, d);
+        *reinterpret_cast<uint4*>(&draw[(t / 8 + 32 * p) * kColTileC + (t % 8) * 8]) = make_uint4(d[0], d[1], d[2], d[3]);
+        *reinterpret_cast<uint4*>(&draw[(t / 8 + 32 * p) * kColTileC + (t % 8) * 8 + 4]) =
+            make_uint4(d[4], d[5], d[6], d[7]);
+        const float S32 = __fmul_rn((float)e4m3_value(sb), s_t);
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= nvfp4_encode_sr(x[i], S32, d[i]) << (4 * i);
+        packed = word;
+      } else {
+        packed = encode8<FMT>(x, sb, th);
+      }
       if (r < rows) {
         if (FMT == FMT_MXFP8) {
           *reinterpret_cast<uint2*>(rcodes + (int64_t)r * rkpad + c) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
@@ -476,11 +565,17 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
         for (int h = 0; h < 2; ++h) {
           Nv4Thresholds th;
           const uint32_t sb = block_scale<FMT>(m2[h], s_t, th);
+          [[maybe_unused]] float S32 = 0.0f;
+          if constexpr (SR) S32 = __fmul_rn((float)e4m3_value(sb), s_t);
 #pragma unroll
           for (int q2 = 0; q2 < 2; ++q2) {
             uint32_t word = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) word |= nvfp4_encode(x[16 * h + 8 * q2 + i], th) << (4 * i);
+            for (int i = 0; i < 8; ++i) {
+              const int k = 16 * h + 8 * q2 + i;
+              if constexpr (SR) word |= nvfp4_encode_sr(x[k], S32, draw[(32 * w + k) * kColTileC + j]) << (4 * i);
+              else word |= nvfp4_encode(x[k], th) << (4 * i);
+            }
             packed[2 * h + q2] = word;
           }
           cscales[(int64_t)oc * (ckpad / 16) + orow / 16 + h] = (uint8_t)sb;
@@ -592,7 +687,7 @@ hipError_t launch_quantize_batch(const QuantBatchItem* items, int n, int fmt, hi
 
 hipError_t launch_quantize_dual(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* rcodes,
                                 uint8_t* rscales, uint8_t* ccodes, uint8_t* cscales, int fmt, const float* amax_prev,
-                                float headroom, hipStream_t stream) {
+                                float headroom, int sr, uint64_t seed0, uint64_t seed1, hipStream_t stream) {
   const int64_t rkpad = round_up(cols, kAlignK);    // row copy: rows x rkpad
   const int64_t ckpad = round_up(rows, kAlignK);    // column copy: cols x ckpad
   const int ir = (int)rows, ic = (int)cols, ild = (int)ld;
@@ -621,8 +716,12 @@ hipError_t launch_quantize_dual(const uint16_t* src, int64_t rows, int64_t cols,
                                                           (int)ckpad, rtr, ctr, delayed);
       break;
     default:
-      quant_dual_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, (int)rkpad, ccodes, cscales,
-                                                          (int)ckpad, rtr, ctr, delayed);
+      if (sr)
+        quant_dual_kernel<FMT_NVFP4, true><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, (int)rkpad, ccodes,
+                                                                  cscales, (int)ckpad, rtr, ctr, delayed, seed0, seed1);
+      else
+        quant_dual_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, (int)rkpad, ccodes,
+                                                            cscales, (int)ckpad, rtr, ctr, delayed);
       break;
   }
   return hipGetLastError();

@@ -167,6 +167,9 @@ class TrainPair:
     W2: int = 25
     B1: int = 26
     B2: int = 27
+    # gradients (dY1, dY2) rounded stochastically (NVFP4 only), with this seed
+    sr_grads: bool = False
+    sr_seed: tuple = (0x5EED0001, 0x5EED0002)
 
     def gemm_flops(self) -> int:
         return 6 * 2 * self.m * self.hidden * self.mlp
@@ -175,7 +178,9 @@ class TrainPair:
 TRAIN_PAIR = TrainPair()
 # the same pair in MXFP8: the MXFP8 training stack's dgrad / wgrad GEMMs
 TRAIN_PAIR_MXFP8 = TrainPair(wid=6, name="vitl16_mxfp8_fc1fc2_train", fmt="mxfp8")
-TRAIN_PAIRS = {tp.name: tp for tp in (TRAIN_PAIR, TRAIN_PAIR_MXFP8)}
+# the NVFP4 pair with stochastically rounded gradients (same tensors as TRAIN_PAIR)
+TRAIN_PAIR_SR = TrainPair(name="vitl16_nvfp4_fc1fc2_train_srgrad", sr_grads=True)
+TRAIN_PAIRS = {tp.name: tp for tp in (TRAIN_PAIR, TRAIN_PAIR_MXFP8, TRAIN_PAIR_SR)}
 
 
 def seed(wid: int, block: int, tensor_id: int) -> int:

@@ -123,6 +123,30 @@ mx_status mx_quantize_dual(const void* src, int64_t rows, int64_t cols, int64_t 
                            void* row_codes, void* row_scales, void* col_codes, void* col_scales,
                            mx_fmt fmt, const float* amax_prev, float headroom, void* hip_stream);
 
+/* mx_quantize_dual with stochastically rounded NVFP4 elements, for
+ * gradients (README section 5.5: the training recipe rounds dY
+ * stochastically, with draws from a counter-based generator, Philox).
+ * Block scale bytes, s_t and the trailers are exactly mx_quantize_dual's;
+ * only the element codes differ:
+ *   draws: Philox4x64 with 10 rounds (Salmon et al., SC 2011), key
+ *     (seed0, seed1), counter (q, 0, 0, 0) for group q of eight elements;
+ *     element i = r * cols + c of X takes 32 bits of output word
+ *     (i mod 8) / 2, the low half for even i. Both copies use the draw of
+ *     the element, so the draws do not depend on the axis.
+ *   element: S32 = fp32(dec(byte) * s_t); y = fp32(|x| / S32) (IEEE round
+ *     to nearest); y >= 6 gives 6; else with E2M1 neighbours lo <= y < hi,
+ *     frac = (y - lo) / (hi - lo), the code is hi iff u < ceil(frac * 2^32),
+ *     u the element's draw, else lo; S32 == 0 gives signed zeros; the sign
+ *     is x's.
+ * fmt must be MX_FMT_NVFP4 and cols a multiple of 8 (else
+ * MX_ERR_UNSUPPORTED); other arguments, errors and memory rules as for
+ * mx_quantize_dual. Calls with the same inputs and seeds write the same
+ * bytes. */
+mx_status mx_quantize_dual_sr(const void* src, int64_t rows, int64_t cols, int64_t ld,
+                              void* row_codes, void* row_scales, void* col_codes, void* col_scales,
+                              mx_fmt fmt, const float* amax_prev, float headroom,
+                              uint64_t seed0, uint64_t seed1, void* hip_stream);
+
 /* One tensor of mx_quantize_batch: X [rows, cols] (bf16, leading dimension
  * ld elements) and its row-axis outputs, sized by mx_codes_bytes /
  * mx_scales_bytes with MX_AXIS_ROW. */

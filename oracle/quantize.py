@@ -364,11 +364,13 @@ def nvfp4_element_codes_sr(x: np.ndarray, S32: np.ndarray, u: np.ndarray) -> np.
     return (sign | mag).astype(np.uint8)
 
 
-def quantize_sr(bits: np.ndarray, axis: str, seed, s_t=None) -> Quantized:
+def quantize_sr(bits: np.ndarray, axis: str, seed, s_t=None, draws=None) -> Quantized:
     """NVFP4 quantization of X along `axis` with stochastically rounded
-    elements (block scales and s_t as quantize()); seed = (k0, k1)."""
+    elements (block scales and s_t as quantize()); seed = (k0, k1). `draws`
+    may pass sr_draws(rows, cols, seed) computed once for both copies."""
     rows0, cols0 = np.asarray(bits).shape
-    draws = sr_draws(rows0, cols0, seed)
+    if draws is None:
+        draws = sr_draws(rows0, cols0, seed)
     t = _view(bits, axis)
     u = draws if axis == "row" else np.ascontiguousarray(draws.T)
     x = F.bf16_to_f64(t)
@@ -393,4 +395,5 @@ def quantize_dual_sr(bits: np.ndarray, seed, amax_prev=None, headroom: float = 3
     """Row and column NVFP4 copies with stochastic rounding, one tensor scale
     (X's own, or the delayed one) and one draw per element shared by both."""
     s_t = None if amax_prev is None else nvfp4_delayed_scale(amax_prev, headroom)
-    return quantize_sr(bits, "row", seed, s_t), quantize_sr(bits, "col", seed, s_t)
+    draws = sr_draws(*np.asarray(bits).shape, seed)
+    return quantize_sr(bits, "row", seed, s_t, draws), quantize_sr(bits, "col", seed, s_t, draws)

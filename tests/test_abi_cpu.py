@@ -139,6 +139,21 @@ def test_quantize_batch_null_items(L):
     assert "null item array" in L.mx_last_error().decode()
 
 
+@pytest.mark.parametrize("args,status,msg", [
+    ((ALIGNED, 4, 8, 8) + (ALIGNED,) * 4 + (1, None, 32.0), 2, "NVFP4 only"),
+    ((ALIGNED, 4, 8, 8) + (ALIGNED,) * 4 + (9, None, 32.0), 1, "unknown format"),
+    ((ALIGNED, 4, 12, 12) + (ALIGNED,) * 4 + (3, None, 32.0), 2, "multiple of 8"),
+    ((ALIGNED, 0, 8, 8) + (ALIGNED,) * 4 + (3, None, 32.0), 1, "empty"),
+    ((ALIGNED, 4, 8, 8, ALIGNED, None, ALIGNED, ALIGNED, 3, None, 32.0), 1, "null"),
+    ((ALIGNED, 4, 8, 8) + (ALIGNED,) * 4 + (3, ALIGNED, -1.0), 1, "headroom"),
+    ((ALIGNED, 4, 8, 8) + (ALIGNED,) * 3 + (ALIGNED + 4, 3, None, 32.0), 3, "16-byte"),
+    ((ALIGNED, 1 << 21, 1 << 12, 1 << 12) + (ALIGNED,) * 4 + (3, None, 32.0), 2, "2 GiB"),
+])
+def test_quantize_dual_sr_validation(L, args, status, msg):
+    assert L.mx_quantize_dual_sr(*args, 1, 2, None) == status
+    assert msg in L.mx_last_error().decode()
+
+
 def test_quantize_dual_ignores_headroom_for_mx(L):
     """MX formats never read amax_prev / headroom: a bad headroom is not an
     error there (the call then fails later on the 2 GiB check, still before

@@ -112,3 +112,58 @@ def test_dual_full_size(fmt, shape, kind, delayed):
     else:
         bits = W.np_normal(shape, seed, W.W_STD)
     compare_dual(bits, fmt, 2.5e-3 if delayed else None, 32.0)
+
+
+
+# ------------------------------------------------------------------ stochastic rounding
+
+SR_SEED = (0x0123456789ABCDEF, 0xFEDCBA9876543210)
+
+
+def compare_dual_sr(bits, seed, amax_prev=None, headroom=32.0):
+    rows, cols = bits.shape
+    log(f"dual sr shape={rows}x{cols} seed={seed[0]:#x} delayed={amax_prev is not None}")
+    prev = None
+    if amax_prev is not None:
+        prev = torch.tensor([amax_prev], dtype=torch.float32, device="cuda")
+    row, col = api.mx_quantize_dual_sr(to_device_bf16(bits), seed, prev, headroom)
+    r_ref, c_ref = Q.quantize_dual_sr(bits, seed, amax_prev, headroom)
+    check_copy(row, r_ref, "row")
+    check_copy(col, c_ref, "col")
+    return row, col
+
+
+@pytest.mark.parametrize("shape", [(1, 8), (16, 64), (37, 96), (129, 264), (300, 1024)])
+def test_dual_sr_random(shape):
+    compare_dual_sr(W.np_normal(shape, W.seed(9, 2, shape[0] % 97), W.GRAD_STD), SR_SEED)
+
+
+def test_dual_sr_special_values():
+    bits = special(130, 256, seed=17)
+    compare_dual_sr(bits, (7, 11))
+
+
+def test_dual_sr_delayed_scale():
+    """Delayed s_t: blocks past 2688 s_t saturate; the trailers record this
+    tensor's amax."""
+    compare_dual_sr(W.np_normal((200, 512), 77, W.GRAD_STD), SR_SEED, 1.5e-4, 32.0)
+
+
+def test_dual_sr_seed_determines_the_codes():
+    bits = W.np_normal((256, 512), 5, W.GRAD_STD)
+    x = to_device_bf16(bits)
+    a = api.mx_quantize_dual_sr(x, SR_SEED)
+    b = api.mx_quantize_dual_sr(x, SR_SEED)
+    c = api.mx_quantize_dual_sr(x, (SR_SEED[0] + 1, SR_SEED[1]))
+    for u, v in zip(a, b):
+        assert torch.equal(u.codes, v.codes) and torch.equal(u.scales, v.scales)
+    assert torch.equal(a[0].scales, c[0].scales)
+    changed = (a[0].codes != c[0].codes).float().mean().item()
+    assert 0.05 < changed < 0.9, changed
+
+
+def test_dual_sr_full_size_grad():
+    """dY2 of the NVFP4 training pair (11235 x 1024), both copies."""
+    tp = W.TRAIN_PAIR
+    bits = W.np_normal((tp.m, tp.hidden), W.seed(tp.wid, 0, tp.DY2), W.GRAD_STD)
+    compare_dual_sr(bits, SR_SEED)
