@@ -124,8 +124,8 @@ mx_status mx_quantize_dual(const void* src, int64_t rows, int64_t cols, int64_t 
                            mx_fmt fmt, const float* amax_prev, float headroom, void* hip_stream);
 
 /* mx_quantize_dual with stochastically rounded NVFP4 elements, for
- * gradients (README section 5.5: the training recipe rounds dY
- * stochastically, with draws from a counter-based generator, Philox).
+ * gradients (README section 5.3: the P3 recipe rounds dY stochastically;
+ * section 5.5: in software, with draws from Philox).
  * Block scale bytes, s_t and the trailers are exactly mx_quantize_dual's;
  * only the element codes differ:
  *   draws: Philox4x64 with 10 rounds (Salmon et al., SC 2011), key

@@ -269,9 +269,10 @@ def scales_bytes(rows: int, cols: int, fmt: str, axis: str) -> int:
 
 # ------------------------------------------------------------------ stochastic rounding
 #
-# README section 5.5 / the training recipe it describes: gradients (dY) are
-# quantized to NVFP4 with stochastic rounding, the random numbers drawn from a
-# counter-based generator (Philox), so that every element's draw is a pure
+# README section 5.3 (the P3 recipe: dgrad / wgrad in NVFP4 with gradients
+# dY rounded stochastically) and section 5.5 (no hardware stochastic
+# rounding, so it is done in software with Philox): the random numbers come
+# from a counter-based generator, so that every element's draw is a pure
 # function of (seed, element position) and any implementation that follows
 # the same definition reproduces the codes bit for bit.
 #
