@@ -39,6 +39,7 @@ NVFP4_AMAX_BYTES = 2.0
 
 
 WORKLOADS = ["vitl16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack", "vitb16_mxfp8_fwd_stack",
+             "vitl16_mxfp8_fwd_stack_fc1gelu", "vitl16_mxfp4_fwd_stack_fc1gelu",
              "vitl16_nvfp4_fc1fc2_train", "vitl16_nvfp4_fc1fc2_train_srgrad", "vitl16_mxfp8_fc1fc2_train",
              "single_mxfp8_256x768x768"]
 
@@ -73,7 +74,22 @@ def build_stack(stack, dev):
     ops = []
     fmt = stack.fmt
     for blk in range(stack.blocks):
+        fused_out = None            # fc2's operand as fc1's fused epilogue writes it
         for lin in stack.linears:
+            if fused_out is not None and lin.name == "fc2":
+                # fc2's A operand comes from fc1's epilogue: no activation tensor, no quantization
+                w = W.torch_normal((lin.n, lin.k), W.seed(stack.wid, blk, lin.w_id), W.W_STD, dev)
+                bias = W.torch_normal((lin.n,), W.seed(stack.wid, blk, lin.bias_id), W.BIAS_STD, dev)
+                qw = api.Quantized(torch.empty(api.codes_bytes(lin.n, lin.k, fmt), dtype=torch.uint8, device=dev),
+                                   torch.empty(api.scales_bytes(lin.n, lin.k, fmt), dtype=torch.uint8, device=dev),
+                                   fmt, lin.n, lin.k)
+                out = torch.empty((stack.m, lin.n), dtype=torch.bfloat16, device=dev)
+                ops.append(Op("quant", lambda w=w, qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales),
+                              nbytes=QUANT_BYTES[fmt] * w.numel(), label=f"quant_{lin.name}_w"))
+                ops.append(Op("gemm", lambda qa=fused_out, qw=qw, bias=bias, out=out: api.mx_gemm(qa, qw, bias, "bf16", out),
+                              flops=2.0 * stack.m * lin.n * lin.k, label=f"gemm_{lin.name}",
+                              plan=api.gemm_plan(stack.m, lin.n, lin.k, fmt)))
+                continue
             a = W.torch_activation((stack.m, lin.k), W.seed(stack.wid, blk, lin.a_id), dev, gelu=lin.a_kind == "gelu")
             w = W.torch_normal((lin.n, lin.k), W.seed(stack.wid, blk, lin.w_id), W.W_STD, dev)
             bias = W.torch_normal((lin.n,), W.seed(stack.wid, blk, lin.bias_id), W.BIAS_STD, dev)
@@ -89,6 +105,17 @@ def build_stack(stack, dev):
                           nbytes=qb * a.numel(), label=f"quant_{lin.name}_act"))
             ops.append(Op("quant", lambda w=w, qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales),
                           nbytes=qb * w.numel(), label=f"quant_{lin.name}_w"))
+            if stack.fuse_fc1_gelu and lin.name == "fc1":
+                del out
+                fused_out = api.Quantized(
+                    torch.empty(api.codes_bytes(stack.m, lin.n, fmt), dtype=torch.uint8, device=dev),
+                    torch.empty(api.scales_bytes(stack.m, lin.n, fmt), dtype=torch.uint8, device=dev),
+                    fmt, stack.m, lin.n)
+                ops.append(Op("gemm", lambda qa=qa, qw=qw, bias=bias, q=fused_out:
+                              api.mx_gemm_gelu_quantize(qa, qw, bias, out=q),
+                              flops=2.0 * stack.m * lin.n * lin.k, label=f"gemm_{lin.name}_gelu_quant",
+                              plan=api.gemm_plan(stack.m, lin.n, lin.k, fmt) + "+gelu+quant"))
+                continue
             ops.append(Op("gemm", lambda qa=qa, qw=qw, bias=bias, out=out: api.mx_gemm(qa, qw, bias, "bf16", out),
                           flops=2.0 * stack.m * lin.n * lin.k, label=f"gemm_{lin.name}",
                           plan=api.gemm_plan(stack.m, lin.n, lin.k, fmt)))

@@ -33,6 +33,9 @@ SIGNATURES = {
                                        _c.c_uint64, _c.c_void_p]),
     "mx_gemm": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
                            _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p]),
+    "mx_gemm_gelu_quantize": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
+                                         _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                         _c.c_void_p]),
     "mx_gemm_plan": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "mx_last_error": (_c.c_char_p, []),
 }

@@ -207,3 +207,26 @@ def mx_gemm(a: Quantized, b: Quantized, bias: torch.Tensor | None = None, out_dt
                          out.data_ptr(), M, N, K, FMT[a.fmt], None if bias is None else bias.data_ptr(),
                          OUT[out_dtype], _stream(stream)))
     return out
+
+
+def mx_gemm_gelu_quantize(a: Quantized, b: Quantized, bias: torch.Tensor | None = None,
+                          out: Quantized | None = None, stream=None) -> Quantized:
+    """GELU(A * B^T (+ bias)) row-quantized in the operands' MX format, ready
+    to be the A operand of the next GEMM (K = N); the activation itself is
+    never stored."""
+    if a.fmt != b.fmt or a.length != b.length:
+        raise ValueError("operands must share format and K")
+    M, N, K = a.rows, b.rows, a.length
+    nc, ns = codes_bytes(M, N, a.fmt, "row"), scales_bytes(M, N, a.fmt, "row")
+    if out is None:
+        out = Quantized(torch.empty(nc, dtype=torch.uint8, device=a.codes.device),
+                        torch.empty(ns, dtype=torch.uint8, device=a.codes.device), a.fmt, M, N)
+    elif out.codes.numel() < nc or out.scales.numel() < ns:
+        raise ValueError("out buffers are too small")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bf16 tensor of N elements")
+    _check(lib().mx_gemm_gelu_quantize(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
+                                       b.scales.data_ptr(), M, N, K, FMT[a.fmt],
+                                       None if bias is None else bias.data_ptr(), out.codes.data_ptr(),
+                                       out.scales.data_ptr(), _stream(stream)))
+    return Quantized(out.codes, out.scales, a.fmt, M, N)

@@ -12,6 +12,7 @@ namespace mx {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 // Row r keeps 16-byte chunk c of a 128-byte row at position c ^ ((r / 2) % 8).
 // A 128-byte row covers half of the LDS's 64 four-byte banks, so rows

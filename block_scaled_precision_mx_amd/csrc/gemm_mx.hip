@@ -56,9 +56,12 @@
 
 namespace mx {
 
-template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_, bool SPREAD_>
+// EPI_ = 0: C (bf16 / fp32) out. EPI_ = 1: the output is GELU-activated and
+// quantized along N in the operand format (fc1 -> fc2's A operand).
+template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_, bool SPREAD_, int EPI_ = 0>
 struct MxCfg {
   static constexpr int FMT = FMT_, BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int EPI = EPI_;
   static constexpr int OCC = OCC_;                            // workgroups per CU (LDS-limited)
   static constexpr bool SPREAD = SPREAD_;                     // spread code copies over the stage
   static constexpr int NT = 64 * WAVES_M * WAVES_N, NW = NT / 64;
@@ -79,7 +82,9 @@ struct MxCfg {
   static constexpr int MFMA_FMT = (FMT == FMT_MXFP8) ? 0 : 4;  // E4M3 / E2M1 operand selector
   static constexpr int CPR = BN / 8;                          // 16-byte bf16 chunks per C row
   static constexpr int EPI_STORES = WM * CPR / NT;            // stores per thread per epilogue pass
-  static constexpr int EPI_TOTAL = WAVES_M * EPI_STORES;      // stores per thread per tile
+  // stores per thread per tile: one per 16-byte chunk of C, or a code store
+  // and a scale-byte store per chunk of the quantized output
+  static constexpr int EPI_TOTAL = WAVES_M * EPI_STORES * (EPI_ == 1 ? 2 : 1);
   static_assert(CODE_DMA * 1024 * NW == STAGE, "code copies must split evenly over waves");
   static_assert(BM % (8 * NW) == 0, "every wave's copies split into A rows, then B rows");
   static_assert(NW % 2 == 0, "copy blocks of one wave share the parity of the wave");
@@ -170,6 +175,61 @@ __device__ __forceinline__ void mma_stage(v16f (&acc)[Cfg::FM][Cfg::FN], const u
   }
 }
 
+// GELU(h) = h Phi(h) in fp32. With z = |h|, Q(z) = Phi(-z) = exp(-z^2/2) R(z)
+// and R a degree-7 polynomial in t = 1 / (1 + 0.35 z), fitted for relative
+// error on z in [0, 14] (csrc/gelu_fit.py derives the constants): Q's
+// relative error is below 2^-20 in this fp32 evaluation, plus the exp2
+// argument's rounding in the far tail (about 2^-16 at z = 13). Phi(h) is
+// 1 - Q for h >= 0 and Q for h < 0. One v_rcp_f32, one v_exp_f32 and about a
+// dozen multiply-adds, against several dozen operations for erfcf.
+__device__ __forceinline__ float gelu_f32(float h) {
+  const float z = fabsf(h);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3499999940395355f, z, 1.0f));
+  float r = 0.04894101619720459f;
+  r = fmaf(r, t, -0.2021145224571228f);
+  r = fmaf(r, t, 0.24063429236412048f);
+  r = fmaf(r, t, -0.017018629238009453f);
+  r = fmaf(r, t, 0.1559593826532364f);
+  r = fmaf(r, t, 0.13335564732551575f);
+  r = fmaf(r, t, 0.14027026295661926f);
+  r = fmaf(r, t, -2.7310272344038822e-05f);
+  const float q = __builtin_amdgcn_exp2f(-0.7213475204444817f * z * z) * r;   // 2^(-z^2 / (2 ln 2))
+  return h >= 0.0f ? fmaf(-h, q, h) : h * q;
+}
+
+// The quantized-output epilogue for one 16-byte chunk (8 consecutive
+// columns n .. n + 7 of row m, bf16 h = RNE(acc + bias)): g = RNE_bf16(GELU(h))
+// with gelu_f32 above; the four lanes holding one
+// 32-column block (adjacent lanes, one row) combine their amax bits; the MX
+// scale byte and the codes follow as in the row quantizer. Every lane issues
+// both stores (rows past M, columns past the output's K_pad and the scale
+// bytes of three of the four lanes go to an offset past the buffer).
+template <int FMT>
+__device__ __forceinline__ void gelu_quant_store(uint4 w, bool scale_lane, bool in, int code_off, int scale_off,
+                                                 __amdgpu_buffer_rsrc_t q_rs, __amdgpu_buffer_rsrc_t qs_rs) {
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  float g[8];
+  uint32_t amax = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float hv = bf16_to_f32((words[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
+    const uint32_t gb = f32_to_bf16_rne(gelu_f32(hv));
+    g[i] = bf16_to_f32(gb);
+    amax = max(amax, gb & 0x7FFFu);
+  }
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+  const uint32_t sb = (uint32_t)(mx_shared_exp(amax, FMT == FMT_MXFP8 ? 8 : 2) + 127);
+  const int coff = in ? code_off : (int)0x80000000u;
+  if constexpr (FMT == FMT_MXFP8) {
+    const uint32_t lo = e4m3x4_scaled(g[0], g[1], g[2], g[3], sb), hi = e4m3x4_scaled(g[4], g[5], g[6], g[7], sb);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, make_uint2(lo, hi)), q_rs, coff, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(e2m1x8_scaled(g, sb), q_rs, coff, 0, 0);
+  }
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, qs_rs, (in && scale_lane) ? scale_off : (int)0x80000000u, 0, 0);
+}
+
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_t* __restrict__ A,
                                                           const uint8_t* __restrict__ As,
@@ -177,7 +237,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
                                                           const uint8_t* __restrict__ Bs, void* __restrict__ C,
                                                           int M, int N, int kpad,
                                                           const uint16_t* __restrict__ bias, int out_f32,
-                                                          int tiles_m, int tiles_n) {
+                                                          int tiles_m, int tiles_n, uint8_t* __restrict__ qcodes = nullptr,
+                                                          uint8_t* __restrict__ qscales = nullptr, int qld = 0) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int RB = Cfg::RB, CH = Cfg::CH, NW = Cfg::NW, CPR = Cfg::CPR;
   __shared__ __align__(16) uint8_t lds[Cfg::LDS];
@@ -194,7 +255,14 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   const int g = lane >> 5, r32 = lane & 31;
   // bf16 output goes through LDS and 32-bit buffer offsets when C is below
   // 2 GiB; anything else is stored from registers with 64-bit addresses
-  const bool staged = !out_f32 && (N & 7) == 0 && (int64_t)M * N < ((int64_t)1 << 30);
+  // (the quantized output always goes through LDS; the host ensures N % 8 == 0)
+  const bool staged = Cfg::EPI == 1 || (!out_f32 && (N & 7) == 0 && (int64_t)M * N < ((int64_t)1 << 30));
+  // quantized output: rows of qld elements (K_pad of N), codes and scale bytes
+  const int q_row_bytes = (Cfg::FMT == FMT_MXFP8) ? qld : qld / 2;
+  const __amdgpu_buffer_rsrc_t q_rs =
+      __builtin_amdgcn_make_buffer_rsrc(qcodes, (short)0, Cfg::EPI == 1 ? M * q_row_bytes : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t qs_rs =
+      __builtin_amdgcn_make_buffer_rsrc(qscales, (short)0, Cfg::EPI == 1 ? M * (qld / 32) : 0, 0x00020000);
 
   const v4u a_rs = buffer_rsrc(A, (uint32_t)(M * row_bytes));
   const v4u b_rs = buffer_rsrc(B, (uint32_t)(N * row_bytes));
@@ -437,8 +505,13 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
             const int id = (int)threadIdx.x + (j0 + j) * Cfg::NT;
             const int row = id / CPR, c = id % CPR;
             const int m = m0 + h * WM + row, n = n0 + 8 * c;
-            const int off = (m < M && n < N) ? (m * N + n) * 2 : (int)0x80000000u;
-            __builtin_amdgcn_raw_buffer_store_b128(v4u{w[j].x, w[j].y, w[j].z, w[j].w}, c_rs, off, 0, 0);
+            if constexpr (Cfg::EPI == 0) {
+              const int off = (m < M && n < N) ? (m * N + n) * 2 : (int)0x80000000u;
+              __builtin_amdgcn_raw_buffer_store_b128(v4u{w[j].x, w[j].y, w[j].z, w[j].w}, c_rs, off, 0, 0);
+            } else {
+              gelu_quant_store<Cfg::FMT>(w[j], (c & 3) == 0, m < M && n < qld, m * q_row_bytes + ((Cfg::FMT == FMT_MXFP8) ? n : n / 2),
+                                         m * (qld / 32) + n / 32, q_rs, qs_rs);
+            }
           }
         }
       }
@@ -508,6 +581,21 @@ static hipError_t run_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, 
   return hipGetLastError();
 }
 
+template <class Cfg>
+static hipError_t run_mx_q(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, int64_t M,
+                           int64_t N, int64_t K, const uint16_t* bias, uint8_t* qcodes, uint8_t* qscales,
+                           hipStream_t stream) {
+  const int64_t kpad = round_up(K, kAlignK);
+  const int tiles_m = (int)((M + Cfg::BM - 1) / Cfg::BM);
+  const int tiles_n = (int)((N + Cfg::BN - 1) / Cfg::BN);
+  const int tiles = tiles_m * tiles_n;
+  const int slots = std::max(8, (Cfg::OCC * cu_count()) / 8 * 8);
+  const int grid = tiles <= slots ? tiles : slots;
+  gemm_mx_kernel<Cfg><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, qcodes, (int)M, (int)N, (int)kpad, bias, 0, tiles_m,
+                                                    tiles_n, qcodes, qscales, (int)round_up(N, kAlignK));
+  return hipGetLastError();
+}
+
 enum MxTile { TILE_128x128 = 0, TILE_192x256 = 1, TILE_256x256 = 2 };
 
 // 256x256 and 192x256 tiles (8 waves of 128x64 / 96x64) are LDS-bound to
@@ -536,6 +624,27 @@ static hipError_t dispatch_mx(const uint8_t* A, const uint8_t* As, const uint8_t
     default:
       return run_mx<MxCfg<FMT, 256, 256, 2, 4, 1, false>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
   }
+}
+
+template <int FMT>
+static hipError_t dispatch_mx_q(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, int64_t M,
+                                int64_t N, int64_t K, const uint16_t* bias, uint8_t* qcodes, uint8_t* qscales,
+                                hipStream_t stream) {
+  switch (choose_tile(M, N, FMT)) {
+    case TILE_128x128:
+      return run_mx_q<MxCfg<FMT, 128, 128, 2, 2, 2, true, 1>>(A, As, B, Bs, M, N, K, bias, qcodes, qscales, stream);
+    case TILE_192x256:
+      return run_mx_q<MxCfg<FMT, 192, 256, 2, 4, 1, true, 1>>(A, As, B, Bs, M, N, K, bias, qcodes, qscales, stream);
+    default:
+      return run_mx_q<MxCfg<FMT, 256, 256, 2, 4, 1, false, 1>>(A, As, B, Bs, M, N, K, bias, qcodes, qscales, stream);
+  }
+}
+
+hipError_t launch_gemm_mx_gelu_quant(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs,
+                                     int64_t M, int64_t N, int64_t K, int fmt, const uint16_t* bias, uint8_t* qcodes,
+                                     uint8_t* qscales, hipStream_t stream) {
+  if (fmt == FMT_MXFP8) return dispatch_mx_q<FMT_MXFP8>(A, As, B, Bs, M, N, K, bias, qcodes, qscales, stream);
+  return dispatch_mx_q<FMT_MXFP4>(A, As, B, Bs, M, N, K, bias, qcodes, qscales, stream);
 }
 
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,

@@ -221,6 +221,37 @@ mx_status mx_gemm(const void* A, const void* As, const void* B, const void* Bs, 
   return MX_OK;
 }
 
+mx_status mx_gemm_gelu_quantize(const void* A, const void* As, const void* B, const void* Bs, int64_t M, int64_t N,
+                                int64_t K, mx_fmt fmt, const void* bias, void* out_codes, void* out_scales,
+                                void* hip_stream) {
+  if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "mx_gemm_gelu_quantize: unknown format %d", (int)fmt);
+  if (fmt == MX_FMT_NVFP4)
+    return fail(MX_ERR_UNSUPPORTED, "mx_gemm_gelu_quantize: MXFP8 and MXFP4 only");
+  if (M < 1 || N < 1 || K < 1)
+    return fail(MX_ERR_INVALID_ARG, "mx_gemm_gelu_quantize: M, N, K must be >= 1 (got %lld, %lld, %lld)",
+                (long long)M, (long long)N, (long long)K);
+  if (N % 8 != 0) return fail(MX_ERR_UNSUPPORTED, "mx_gemm_gelu_quantize: N (%lld) must be a multiple of 8", (long long)N);
+  if (!A || !As || !B || !Bs || !out_codes || !out_scales)
+    return fail(MX_ERR_INVALID_ARG, "mx_gemm_gelu_quantize: null pointer");
+  if (!aligned(A, 16) || !aligned(As, 16) || !aligned(B, 16) || !aligned(Bs, 16) || !aligned(out_codes, 16) ||
+      !aligned(out_scales, 16))
+    return fail(MX_ERR_ALIGNMENT, "mx_gemm_gelu_quantize: operands and outputs must be 16-byte aligned");
+  if (bias && !aligned(bias, 2)) return fail(MX_ERR_ALIGNMENT, "mx_gemm_gelu_quantize: bias must be 2-byte aligned");
+  const int64_t kpad = k_pad(K), rb = code_row_bytes(kpad, fmt);
+  if (M * rb >= kMaxBytes || N * rb >= kMaxBytes || scales_total(M, kpad, fmt) >= kMaxBytes ||
+      scales_total(N, kpad, fmt) >= kMaxBytes)
+    return fail(MX_ERR_UNSUPPORTED, "mx_gemm_gelu_quantize: operand larger than 2 GiB");
+  const int64_t npad = k_pad(N);
+  if (M * code_row_bytes(npad, fmt) >= kMaxBytes || scales_total(M, npad, fmt) >= kMaxBytes)
+    return fail(MX_ERR_UNSUPPORTED, "mx_gemm_gelu_quantize: output larger than 2 GiB");
+  hipError_t e = mx::launch_gemm_mx_gelu_quant(
+      static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(As), static_cast<const uint8_t*>(B),
+      static_cast<const uint8_t*>(Bs), M, N, K, (int)fmt, static_cast<const uint16_t*>(bias),
+      static_cast<uint8_t*>(out_codes), static_cast<uint8_t*>(out_scales), static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(MX_ERR_HIP, "mx_gemm_gelu_quantize: launch failed: %s", hipGetErrorString(e));
+  return MX_OK;
+}
+
 const char* mx_gemm_plan(int64_t M, int64_t N, int64_t K, mx_fmt fmt) {
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 1) return nullptr;
   return fmt == MX_FMT_NVFP4 ? mx::plan_gemm_nvfp4(M, N) : mx::plan_gemm_mx(M, N, (int)fmt);

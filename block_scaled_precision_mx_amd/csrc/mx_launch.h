@@ -42,6 +42,13 @@ hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B,
                           void* C, int64_t M, int64_t N, int64_t K, int fmt, const uint16_t* bias,
                           int out_f32, hipStream_t stream);
 
+// MXFP8 / MXFP4 GEMM whose output is GELU(bf16(A B^T + bias)) rounded to
+// bf16 and quantized along N in the same format (rows of K_pad(N)
+// elements): fc1 writing fc2's A operand. N % 8 == 0.
+hipError_t launch_gemm_mx_gelu_quant(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs,
+                                     int64_t M, int64_t N, int64_t K, int fmt, const uint16_t* bias, uint8_t* qcodes,
+                                     uint8_t* qscales, hipStream_t stream);
+
 // NVFP4: E2M1 x E4M3 operands dequantized exactly to fp16 on the way into
 // LDS, fp16 MFMA with fp32 accumulate, s_tA * s_tB applied in the epilogue.
 hipError_t launch_gemm_nvfp4(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs,

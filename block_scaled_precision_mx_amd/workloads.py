@@ -120,6 +120,9 @@ class Stack:
     mlp: int
     blocks: int
     linears: tuple = field(default=())
+    # fc1's epilogue applies GELU and writes fc2's quantized operand, so fc2's
+    # input is GELU(fc1's output) instead of a separate synthetic tensor
+    fuse_fc1_gelu: bool = False
 
     def gemm_flops(self) -> int:
         return 2 * self.m * sum(l.n * l.k for l in self.linears) * self.blocks
@@ -145,7 +148,12 @@ VITL_MXFP8 = Stack(3, "vitl16_mxfp8_fwd_stack", "mxfp8", 7 * TOKENS, 1024, 4096,
 VITL_MXFP4 = Stack(4, "vitl16_mxfp4_fwd_stack", "mxfp4", 7 * TOKENS, 1024, 4096, 24,
                    _vit_linears(1024, 4096))
 
-STACKS = {s.name: s for s in (SINGLE_LAYER, VITB_MXFP8, VITL_MXFP8, VITL_MXFP4)}
+VITL_MXFP8_FUSED = Stack(3, "vitl16_mxfp8_fwd_stack_fc1gelu", "mxfp8", 7 * TOKENS, 1024, 4096, 24,
+                         _vit_linears(1024, 4096), fuse_fc1_gelu=True)
+VITL_MXFP4_FUSED = Stack(4, "vitl16_mxfp4_fwd_stack_fc1gelu", "mxfp4", 7 * TOKENS, 1024, 4096, 24,
+                         _vit_linears(1024, 4096), fuse_fc1_gelu=True)
+
+STACKS = {s.name: s for s in (SINGLE_LAYER, VITB_MXFP8, VITL_MXFP8, VITL_MXFP4, VITL_MXFP8_FUSED, VITL_MXFP4_FUSED)}
 
 
 @dataclass(frozen=True)

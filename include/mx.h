@@ -186,6 +186,24 @@ mx_status mx_gemm(const void* A, const void* As, const void* B, const void* Bs,
                   void* C, int64_t M, int64_t N, int64_t K, mx_fmt fmt,
                   const void* bias, mx_dtype out_dtype, void* hip_stream);
 
+/* fc1 writing fc2's operand (README section 4.3, MXFP8 row of the block
+ * table: fc1's epilogue quantizes the GELU output straight into fc2's E4M3
+ * operand). Computes H = A * B^T (+ bias) as mx_gemm with bf16 output
+ * would, applies the exact GELU, GELU(h) = h/2 * erfc(-h / sqrt 2), in fp32
+ * to each bf16 h and rounds it to bf16, and writes the row quantization of
+ * that [M, N] tensor in the operand format fmt: out_codes / out_scales
+ * receive what mx_quantize(GELU tensor, fmt, MX_AXIS_ROW) would write
+ * (sizes mx_codes_bytes / mx_scales_bytes of (M, N, fmt, MX_AXIS_ROW)), so
+ * they serve directly as the A operand of the next mx_gemm (K = N). H itself
+ * is never stored. The accumulation follows mx_gemm's accuracy rule, and the
+ * fp32 GELU lies within 2^-14 |GELU| + 2^-122 of the exact value.
+ * fmt: MX_FMT_MXFP8 or MX_FMT_MXFP4 (NVFP4 would need the tensor amax of H
+ * first: MX_ERR_UNSUPPORTED). N must be a multiple of 8. Other arguments,
+ * errors and memory rules as for mx_gemm. */
+mx_status mx_gemm_gelu_quantize(const void* A, const void* As, const void* B, const void* Bs,
+                                int64_t M, int64_t N, int64_t K, mx_fmt fmt, const void* bias,
+                                void* out_codes, void* out_scales, void* hip_stream);
+
 /* Name of the kernel configuration mx_gemm launches for these sizes and
  * format (for example "gemm_mx_kernel<mxfp8, 256x256>"), so profiles can be
  * matched to calls; a static string, or NULL if an argument is invalid. */

@@ -56,12 +56,12 @@ def gelu(h) -> np.ndarray:
     return 0.5 * h * erfc(-h * SQRT1_2)
 
 
-# what the kernel's fp32 GELU may differ from the exact one by: the fp32
-# product -h / sqrt 2 (relative 2^-24, amplified by about 2 z^2 in erfc's
-# tail, z <= 14 before the result underflows) and a few ulp of erfcf and
-# of the two products
+# what the kernel's fp32 GELU may differ from the exact one by: its fitted
+# tail Q(z) = exp(-z^2/2) R(z) is within 2^-20 relative in fp32, the
+# rounding of the exp2 argument adds up to about 2^-16 near z = 13, and the
+# exp2 of arguments below -126 (|GELU| < 2^-122) may flush to zero
 GELU_REL = 2.0 ** -14
-GELU_ABS = 2.0 ** -126
+GELU_ABS = 2.0 ** -122
 
 
 def _bf16_interval_of_gelu(h_lo, h_hi):

@@ -154,6 +154,21 @@ def test_quantize_dual_sr_validation(L, args, status, msg):
     assert msg in L.mx_last_error().decode()
 
 
+@pytest.mark.parametrize("args,status,msg", [
+    ((ALIGNED,) * 4 + (4, 8, 32, 3, None, ALIGNED, ALIGNED), 2, "MXFP8 and MXFP4 only"),
+    ((ALIGNED,) * 4 + (4, 8, 32, 9, None, ALIGNED, ALIGNED), 1, "unknown format"),
+    ((ALIGNED,) * 4 + (4, 12, 32, 1, None, ALIGNED, ALIGNED), 2, "multiple of 8"),
+    ((ALIGNED,) * 4 + (0, 8, 32, 1, None, ALIGNED, ALIGNED), 1, ">= 1"),
+    ((ALIGNED,) * 4 + (4, 8, 32, 1, None, None, ALIGNED), 1, "null"),
+    ((ALIGNED,) * 4 + (4, 8, 32, 1, None, ALIGNED, ALIGNED + 8), 3, "16-byte"),
+    ((ALIGNED,) * 4 + (4, 8, 32, 2, ALIGNED + 1, ALIGNED, ALIGNED), 3, "bias"),
+    ((ALIGNED,) * 4 + (1 << 22, 1 << 10, 32, 1, None, ALIGNED, ALIGNED), 2, "output larger"),
+])
+def test_gemm_gelu_quantize_validation(L, args, status, msg):
+    assert L.mx_gemm_gelu_quantize(*args, None) == status
+    assert msg in L.mx_last_error().decode()
+
+
 def test_quantize_dual_ignores_headroom_for_mx(L):
     """MX formats never read amax_prev / headroom: a bad headroom is not an
     error there (the call then fails later on the 2 GiB check, still before

@@ -1,0 +1,112 @@
+"""GPU parity of mx_gemm_gelu_quantize (fc1 writing fc2's operand): every
+scale byte and code of the fused output must be explained by the oracle's
+intervals (oracle.fused.check_rows): the GEMM's accuracy rule, the exact
+GELU within the stated fp32 allowance, bf16 roundings, then the MX row
+quantization. With an exactly representable accumulation the only slack is
+the GELU allowance. Ragged N exercises the zero padding up to K_pad(N);
+several tiles per workgroup exercise the epilogue's store accounting."""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_precision_mx_amd import api
+from block_scaled_precision_mx_amd import workloads as W
+from oracle import formats as F
+from oracle import fused as FU
+from oracle import gemm as G
+from oracle import quantize as Q
+from gpu_util import bytes_of, log, to_device_bf16
+from test_gpu_gemm import exact_operand
+
+pytestmark = pytest.mark.gpu
+MX = ["mxfp8", "mxfp4"]
+
+
+def run_fused(a_bits, b_bits, fmt, bias_bits=None, bias_offset=0):
+    qa = api.mx_quantize(to_device_bf16(a_bits), fmt, "row")
+    qb = api.mx_quantize(to_device_bf16(b_bits), fmt, "row")
+    bias = None
+    if bias_bits is not None:
+        padded = np.concatenate([np.zeros(bias_offset, dtype=np.uint16), bias_bits])
+        bias = to_device_bf16(padded.reshape(1, -1)).reshape(-1)[bias_offset:]
+    q = api.mx_gemm_gelu_quantize(qa, qb, bias)
+    m = a_bits.shape[0]
+    return bytes_of(q.codes).reshape(m, -1), bytes_of(q.scales).reshape(m, -1)
+
+
+def check(a_bits, b_bits, fmt, bias_bits=None, rows=None, gemm_tol=G.TOL, bias_offset=0):
+    m, n = a_bits.shape[0], b_bits.shape[0]
+    log(f"gemm+gelu+quant fmt={fmt} M={m} N={n} K={a_bits.shape[1]} rows={'all' if rows is None else len(rows)}")
+    codes, scales = run_fused(a_bits, b_bits, fmt, bias_bits, bias_offset)
+    qa, qb = Q.quantize(a_bits, fmt), Q.quantize(b_bits, fmt)
+    if rows is None:
+        rows = np.arange(m)
+        c, s = G.gemm_ref(qa, qb, bias_bits)
+    else:
+        rows = np.asarray(rows)
+        rr = np.repeat(rows, n)
+        cc = np.tile(np.arange(n), len(rows))
+        c, s = G.gemm_ref_entries(qa, qb, rr, cc, bias_bits)
+        c, s = c.reshape(len(rows), n), s.reshape(len(rows), n)
+    ok_c, ok_s = FU.check_rows(FU.unpack_codes(codes[rows], fmt), scales[rows], c, s, fmt, n, gemm_tol)
+    bad = np.argwhere(~ok_c)
+    assert bad.size == 0, f"{len(bad)} codes outside their intervals, first {bad[:5].tolist()}"
+    assert ok_s.all(), f"{(~ok_s).sum()} scale bytes outside their range, first {np.argwhere(~ok_s)[:5].tolist()}"
+    return codes, scales
+
+
+@pytest.mark.parametrize("fmt", MX)
+@pytest.mark.parametrize("mnk", [(64, 136, 256), (200, 512, 1024)])
+def test_fused_exact_accumulation(fmt, mnk):
+    """Exactly quantized operands (A scaled by 2^-7 so h spans GELU's curved
+    range) make every accumulation exact: no GEMM slack."""
+    m, n, k = mnk
+    rng = np.random.default_rng(m + n + k)
+    a = W.to_bf16_bits(F.bf16_to_f64(exact_operand(m, k, fmt, rng, 0)) * 2.0 ** -7)
+    b = exact_operand(n, k, fmt, rng, 1)
+    check(a, b, fmt, None, gemm_tol=0.0)
+
+
+@pytest.mark.parametrize("fmt", MX)
+@pytest.mark.parametrize("mnk", [(1, 8, 32), (37, 96, 300), (300, 520, 640), (513, 264, 128)])
+def test_fused_random(fmt, mnk):
+    m, n, k = mnk
+    a = W.np_activation((m, k), seed=m + 1)
+    b = W.np_normal((n, k), seed=n + 2, std=W.W_STD * 4)
+    bias = W.np_normal((n,), seed=k + 3, std=W.BIAS_STD * 10)
+    check(a, b, fmt, bias)
+
+
+@pytest.mark.parametrize("fmt", MX)
+def test_fused_unaligned_bias(fmt):
+    """A bias that is not 16-byte aligned is read from global memory instead
+    of being copied to LDS."""
+    a = W.np_activation((130, 256), seed=7)
+    b = W.np_normal((264, 256), seed=8, std=W.W_STD * 4)
+    bias = W.np_normal((264,), seed=9, std=0.5)
+    check(a, b, fmt, bias, bias_offset=3)
+
+
+@pytest.mark.parametrize("fmt", MX)
+def test_fused_many_tiles(fmt):
+    """More output tiles than resident workgroups: each workgroup's epilogue
+    stores stay in flight across the next tile's first stage."""
+    m, n, k = 4160, 4096, 384
+    a = W.np_activation((m, k), seed=31)
+    b = W.np_normal((n, k), seed=32, std=W.W_STD * 2)
+    bias = W.np_normal((n,), seed=33, std=W.BIAS_STD)
+    rows = np.concatenate([np.arange(0, m, 97), [m - 1]])
+    check(a, b, fmt, bias, rows=rows)
+
+
+@pytest.mark.parametrize("fmt", MX)
+def test_fused_vitl_fc1_full_size(fmt):
+    """fc1 of ViT-L at the workload's full size (11235 x 4096 x 1024),
+    sampled rows including the last tile's."""
+    wl = W.VITL_MXFP8 if fmt == "mxfp8" else W.VITL_MXFP4
+    L = {l.name: l for l in wl.linears}["fc1"]
+    a = W.np_activation((wl.m, L.k), W.seed(wl.wid, 0, L.a_id))
+    b = W.np_normal((L.n, L.k), W.seed(wl.wid, 0, L.w_id), W.W_STD)
+    bias = W.np_normal((L.n,), W.seed(wl.wid, 0, L.bias_id), W.BIAS_STD)
+    rows = np.concatenate([np.arange(0, wl.m, 389), [wl.m - 1]])
+    check(a, b, fmt, bias, rows=rows)
