@@ -279,8 +279,8 @@ def measured_traffic(kernel, workload):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the block-scaled path here runs on a single MI355X; "
-              "multi-GPU runs are not part of this build (see DESIGN.md for how it would shard).",
+        print("bench.py measures one GPU only: --gpus must be 1. The kernels here run one GPU's "
+              "share of the work; nothing in this package uses a second GPU or a collective.",
               file=sys.stderr)
         sys.exit(2)
     import torch

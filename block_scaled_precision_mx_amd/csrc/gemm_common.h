@@ -48,6 +48,13 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Cache policy of the GEMMs' output stores: device scope (sc1). The XCD's L2
+// then writes them through rather than holding them dirty until the release
+// at the end of the kernel, which otherwise writes the last tiles' output
+// back after the matrix work is done (measured on gfx950: about 1.5 us less
+// on launches of one round of tiles, no change on longer ones).
+constexpr int kStoreDeviceScope = 16;
+
 // Workgroup barrier after this wave's LDS operations have completed. Global
 // stores still in flight are deliberately not waited for.
 __device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

@@ -223,11 +223,11 @@ __device__ __forceinline__ void gelu_quant_store(uint4 w, bool scale_lane, bool 
   const int coff = in ? code_off : (int)0x80000000u;
   if constexpr (FMT == FMT_MXFP8) {
     const uint32_t lo = e4m3x4_scaled(g[0], g[1], g[2], g[3], sb), hi = e4m3x4_scaled(g[4], g[5], g[6], g[7], sb);
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, make_uint2(lo, hi)), q_rs, coff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, make_uint2(lo, hi)), q_rs, coff, 0, kStoreDeviceScope);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b32(e2m1x8_scaled(g, sb), q_rs, coff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(e2m1x8_scaled(g, sb), q_rs, coff, 0, kStoreDeviceScope);
   }
-  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, qs_rs, (in && scale_lane) ? scale_off : (int)0x80000000u, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, qs_rs, (in && scale_lane) ? scale_off : (int)0x80000000u, 0, kStoreDeviceScope);
 }
 
 template <class Cfg>
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
             const int m = m0 + h * WM + row, n = n0 + 8 * c;
             if constexpr (Cfg::EPI == 0) {
               const int off = (m < M && n < N) ? (m * N + n) * 2 : (int)0x80000000u;
-              __builtin_amdgcn_raw_buffer_store_b128(v4u{w[j].x, w[j].y, w[j].z, w[j].w}, c_rs, off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(v4u{w[j].x, w[j].y, w[j].z, w[j].w}, c_rs, off, 0, kStoreDeviceScope);
             } else {
               gelu_quant_store<Cfg::FMT>(w[j], (c & 3) == 0, m < M && n < qld, m * q_row_bytes + ((Cfg::FMT == FMT_MXFP8) ? n : n / 2),
                                          m * (qld / 32) + n / 32, q_rs, qs_rs);

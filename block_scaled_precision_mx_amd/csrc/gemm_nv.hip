@@ -355,7 +355,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
           const int m = m0 + h * WM + row, n = n0 + 8 * c;
           const uint4 w = *reinterpret_cast<const uint4*>(stg + row * (BN * 2) + ((c ^ (row & (CPR - 1))) * 16));
           const int off = (m < M && n < N) ? (m * N + n) * 2 : (int)0x80000000u;
-          __builtin_amdgcn_raw_buffer_store_b128(v4u{w.x, w.y, w.z, w.w}, c_rs, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v4u{w.x, w.y, w.z, w.w}, c_rs, off, 0, kStoreDeviceScope);
         }
       }
     } else {
