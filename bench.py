@@ -2,8 +2,8 @@
 
 One step = one pass of the whole path over one batch: for every ViT block
 and every linear layer (qkv, proj, fc1, fc2) quantize the activation and the
-weight row-wise (mx_quantize) and run the block-scaled GEMM with its bias
-epilogue (mx_gemm). For the NVFP4 training workload a step is the fc1/fc2
+weight row-wise (both in one mx_quantize_batch launch) and run the
+block-scaled GEMM with its bias epilogue (mx_gemm). For the NVFP4 training workload a step is the fc1/fc2
 pair's fprop, dgrad and wgrad GEMMs with every operand quantized along its
 own K axis (row and transposed copies from one read with mx_quantize_dual,
 tensor amax included).
@@ -100,11 +100,9 @@ def build_stack(stack, dev):
                                torch.empty(api.scales_bytes(lin.n, lin.k, fmt), dtype=torch.uint8, device=dev),
                                fmt, lin.n, lin.k)
             out = torch.empty((stack.m, lin.n), dtype=torch.bfloat16, device=dev)
-            qb = QUANT_BYTES[fmt]
-            ops.append(Op("quant", lambda a=a, qa=qa: api.mx_quantize(a, fmt, "row", qa.codes, qa.scales),
-                          nbytes=qb * a.numel(), label=f"quant_{lin.name}_act"))
-            ops.append(Op("quant", lambda w=w, qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales),
-                          nbytes=qb * w.numel(), label=f"quant_{lin.name}_w"))
+            # the GEMM's two operands in one launch (mx_quantize_batch), just before it
+            ops.append(Op("quant", lambda a=a, w=w, qa=qa, qw=qw: api.mx_quantize_batch([a, w], fmt, out=[qa, qw]),
+                          nbytes=QUANT_BYTES[fmt] * (a.numel() + w.numel()), label=f"quant_{lin.name}_act_w"))
             if stack.fuse_fc1_gelu and lin.name == "fc1":
                 del out
                 fused_out = api.Quantized(
