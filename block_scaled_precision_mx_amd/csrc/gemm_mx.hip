@@ -290,7 +290,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   const uint32_t code_lane = (uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)row_bytes + code_byte;
   const uint32_t copy_stride = (uint32_t)(8 * NW) * (uint32_t)row_bytes;   // rows between copy j and j + 1
   // Scale copy j of this wave fills rows 64 J .. 64 J + 63 of [A rows, B rows]
-  // with 16 bytes each (copies J >= SCALE_COPIES are skipped).
+  // with 16 bytes each (copies J >= SCALE_COPIES are skipped). When K_pad is
+  // not a multiple of 512 the last chunk of the last row runs past the end of
+  // the scale buffer; the buffer range check applies to each dword of a load,
+  // the scalar offset included (probed on gfx950), so those dwords read as
+  // zero and nothing past the buffer is touched.
   const uint32_t scale_lane = (uint32_t)lane * (uint32_t)srow;
 
   // copy cursor: tile lt (rows m0l / n0l), its stage lks; lgs / lgc count
