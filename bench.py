@@ -60,10 +60,18 @@ def parse():
 # ------------------------------------------------------------------ workloads
 
 class Op:
-    """One launch of the path: a quantization or a GEMM (plan = kernel configuration)."""
+    """One launch of the path: a quantization or a GEMM (plan = kernel
+    configuration). `cold`: the same launch on other input tensors of the
+    same shape, used only to time the launch with inputs that are not cached."""
 
-    def __init__(self, kind, fn, flops=0.0, nbytes=0.0, label="", plan=None):
+    def __init__(self, kind, fn, flops=0.0, nbytes=0.0, label="", plan=None, cold=()):
         self.kind, self.fn, self.flops, self.nbytes, self.label, self.plan = kind, fn, flops, nbytes, label, plan
+        self.cold = list(cold)
+
+
+# input bytes of a group of cold launches made of clones: twice the 256 MB
+# Infinity Cache, so the group's inputs come from HBM
+COLD_BYTES = 512 << 20
 
 
 def build_stack(stack, dev):
@@ -84,8 +92,12 @@ def build_stack(stack, dev):
                                    torch.empty(api.scales_bytes(lin.n, lin.k, fmt), dtype=torch.uint8, device=dev),
                                    fmt, lin.n, lin.k)
                 out = torch.empty((stack.m, lin.n), dtype=torch.bfloat16, device=dev)
+                # fc2's weight is the only tensor of this launch: two clones per
+                # block make its cold-timing group larger than the Infinity Cache
                 ops.append(Op("quant", lambda w=w, qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales),
-                              nbytes=QUANT_BYTES[fmt] * w.numel(), label=f"quant_{lin.name}_w"))
+                              nbytes=QUANT_BYTES[fmt] * w.numel(), label=f"quant_{lin.name}_w",
+                              cold=[lambda w=w.clone(), qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales)
+                                    for _ in range(2)]))
                 ops.append(Op("gemm", lambda qa=fused_out, qw=qw, bias=bias, out=out: api.mx_gemm(qa, qw, bias, "bf16", out),
                               flops=2.0 * stack.m * lin.n * lin.k, label=f"gemm_{lin.name}",
                               plan=api.gemm_plan(stack.m, lin.n, lin.k, fmt)))
@@ -154,11 +166,15 @@ def build_train(tp, dev):
                                       torch.empty(api.scales_bytes(r, c, fmt, axis), dtype=torch.uint8, device=dev),
                                       fmt, rows, length))
         q[name + "_row"], q[name + "_col"] = bufs
-        if sr:
-            fn = lambda: api.mx_quantize_dual_sr(t, tp.sr_seed, None, 1.0, out=(bufs[0], bufs[1]))   # noqa: E731
-        else:
-            fn = lambda: api.mx_quantize_dual(t, fmt, None, 1.0, out=(bufs[0], bufs[1]))             # noqa: E731
-        ops.append(Op("quant", fn, nbytes=dual_bytes * t.numel(), label=f"quant_{name}_rowcol"))
+
+        def make_fn(src):
+            if sr:
+                return lambda: api.mx_quantize_dual_sr(src, tp.sr_seed, None, 1.0, out=(bufs[0], bufs[1]))
+            return lambda: api.mx_quantize_dual(src, fmt, None, 1.0, out=(bufs[0], bufs[1]))
+        # clones of t for cold timing only (the step itself reads t)
+        copies = min(64, -(-COLD_BYTES // (2 * t.numel()))) - 1
+        ops.append(Op("quant", make_fn(t), nbytes=dual_bytes * t.numel(), label=f"quant_{name}_rowcol",
+                      cold=[make_fn(t.clone()) for _ in range(copies)]))
 
     def gemm(name, a, b, bias, m, n, k):
         out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
@@ -336,21 +352,40 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
-    # per-launch durations on the same stream: each launch of the step is
-    # repeated REPEAT times back to back between one event pair, so the
-    # events' own overhead is spread over the repeats
+    # per-launch durations on the same stream, several launches between one
+    # event pair so that the events' own overhead is spread over them.
+    # GEMMs: each launch repeated REPEAT times back to back. In the step their
+    # operands were written just before them, so they are cached there too
+    # (rocprofv3's trace of the in-step launches agrees within 2%).
+    # Quantizations: all launches of one label, each on an input no other
+    # launch of the group reads (the stack's blocks, or clones of the
+    # training tensors), more than the 256 MB Infinity Cache per group (428 MB
+    # for the smallest, ViT-B's proj), so the inputs come from HBM as they do
+    # in the step.
     REPEAT = 10
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+    groups = []                                   # (op indices, launches timed together)
+    quant_labels = {}
+    for i, op in enumerate(ops):
+        if op.kind == "quant":
+            quant_labels.setdefault(op.label, []).append(i)
+        else:
+            groups.append(([i], [op.fn] * REPEAT))
+    for idx in quant_labels.values():
+        fns = [f for i in idx for f in [ops[i].fn] + ops[i].cold]
+        groups.append((idx, fns))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
     per_op = [0.0] * len(ops)
     for _ in range(args.steps):
-        for i, op in enumerate(ops):
-            ev[i][0].record(stream)
-            for _ in range(REPEAT):
-                op.fn()
-            ev[i][1].record(stream)
+        for g, (idx, fns) in enumerate(groups):
+            ev[g][0].record(stream)
+            for f in fns:
+                f()
+            ev[g][1].record(stream)
         torch.cuda.synchronize()
-        for i in range(len(ops)):
-            per_op[i] += ev[i][0].elapsed_time(ev[i][1]) / REPEAT
+        for g, (idx, fns) in enumerate(groups):
+            t = ev[g][0].elapsed_time(ev[g][1]) / len(fns)
+            for i in idx:
+                per_op[i] += t
     per_op = [t / args.steps for t in per_op]
 
     gemm_flops = sum(op.flops for op in ops)
