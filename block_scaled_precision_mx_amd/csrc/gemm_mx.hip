@@ -56,6 +56,12 @@
 
 namespace mx {
 
+// Table of RNE_bf16(GELU(h)) for the quantized-output epilogue: bf16 h with
+// biased exponent 111 .. 130 (|h| in [2^-16, 16)), both signs.
+constexpr int kGeluTabExp0 = 111, kGeluTabExps = 20;
+constexpr int kGeluTabEntries = 2 * kGeluTabExps * 128;     // sign x exponent x mantissa
+constexpr int kGeluTabBytes = 2 * kGeluTabEntries;           // bf16 entries
+
 // EPI_ = 0: C (bf16 / fp32) out. EPI_ = 1: the output is GELU-activated and
 // quantized along N in the operand format (fc1 -> fc2's A operand).
 template <int FMT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_, bool SPREAD_, int EPI_ = 0>
@@ -75,7 +81,11 @@ struct MxCfg {
   static constexpr int STAGE = (BM + BN) * RB;                 // code bytes per stage
   static constexpr int SCHUNK = (BM + BN) * 16;                // bytes per scale slot
   static constexpr int BIAS_OFF = 2 * STAGE + 2 * SCHUNK;     // two 1-KB bias slots (tile parity)
-  static constexpr int LDS = BIAS_OFF + 2 * 1024;
+  // quantized output: RNE_bf16(GELU(h)) of every bf16 h with |h| in
+  // [2^-16, 16) as a table in LDS, where the LDS budget leaves room for it
+  static constexpr int GTAB_OFF = BIAS_OFF + 2 * 1024;
+  static constexpr bool GTAB = EPI_ == 1 && (GTAB_OFF + kGeluTabBytes) * OCC_ <= 160 * 1024;
+  static constexpr int LDS = GTAB_OFF + (GTAB ? kGeluTabBytes : 0);
   static constexpr int CODE_DMA = STAGE / 1024 / NW;          // 1-KB code copies per wave per stage
   static constexpr int SCALE_COPIES = (BM + BN) / 64;         // 1-KB copies per scale chunk
   static constexpr int SCALE_DMA = (SCALE_COPIES + NW - 1) / NW;  // per wave (some may be idle)
@@ -197,26 +207,94 @@ __device__ __forceinline__ float gelu_f32(float h) {
   return h >= 0.0f ? fmaf(-h, q, h) : h * q;
 }
 
-// The quantized-output epilogue for one 16-byte chunk (8 consecutive
-// columns n .. n + 7 of row m, bf16 h = RNE(acc + bias)): g = RNE_bf16(GELU(h))
-// with gelu_f32 above; the four lanes holding one
-// 32-column block (adjacent lanes, one row) combine their amax bits; the MX
-// scale byte and the codes follow as in the row quantizer. Every lane issues
-// both stores (rows past M, columns past the output's K_pad and the scale
-// bytes of three of the four lanes go to an offset past the buffer).
-template <int FMT>
-__device__ __forceinline__ void gelu_quant_store(uint4 w, bool scale_lane, bool in, int code_off, int scale_off,
-                                                 __amdgpu_buffer_rsrc_t q_rs, __amdgpu_buffer_rsrc_t qs_rs) {
-  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-  float g[8];
-  uint32_t amax = 0u;
+// RNE_bf16(GELU(h)) depends only on the 16 bits of the bf16 h. For |h| in
+// [2^-16, 16), biased exponents 111 .. 130, it is read from a table that each
+// workgroup fills once with gelu_f32, so the table path gives exactly the
+// values gelu_f32 gives. Outside that range gelu_f32 rounds to closed forms:
+// for exponents 2 .. 110 (|h| < 2^-16) GELU(h) = h/2 (1 + O(h)) and its fp32
+// value is within 2^-15 of h/2 relative, so the bf16 result is h/2 exactly
+// (the exponent minus one); for |h| >= 16 the tail factor exp2(-z^2 / (2 ln 2))
+// underflows, so the result is h for h > 0 and -0 for h < 0 (the exact
+// rounding of a negative value far below the bf16 range; gelu_f32 itself may
+// return +0 there, the sign of its vanishing polynomial tail). Only exponents
+// 0, 1 (zero, values below 2^-125) and 255 are evaluated directly.
+__device__ __forceinline__ uint32_t gelu_bf16_direct(uint32_t b) {
+  return pack_bf16x2(gelu_f32(__uint_as_float(b << 16)), 0.0f) & 0xFFFFu;
+}
+
+__device__ __forceinline__ void fill_gelu_table(uint16_t* tab, int tid, int nt) {
+  for (int i = tid; i < kGeluTabEntries; i += nt) {
+    const uint32_t sign = (uint32_t)(i / (kGeluTabExps * 128)), r = (uint32_t)(i % (kGeluTabExps * 128));
+    tab[i] = (uint16_t)gelu_bf16_direct((sign << 15) | ((kGeluTabExp0 + r / 128) << 7) | (r % 128));
+  }
+}
+
+// RNE_bf16(GELU(h)) of the 8 bf16 values in w (element 2k in the low half of
+// word k): table reads, the closed forms for lanes holding a value outside
+// the table's range (selects, under one branch), and gelu_f32 for exponents 0,
+// 1 and 255 (a second, rarer branch).
+__device__ __forceinline__ void gelu_bf16_lookup8(const uint32_t (&words)[4], const uint16_t* tab, uint32_t (&gb)[8]) {
+  constexpr uint32_t SPAN = kGeluTabExps * 128;
+  uint32_t b[8];
+  bool all_in = true;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float hv = bf16_to_f32((words[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
-    const uint32_t gb = f32_to_bf16_rne(gelu_f32(hv));
-    g[i] = bf16_to_f32(gb);
-    amax = max(amax, gb & 0x7FFFu);
+    b[i] = (words[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+    const uint32_t off = (b[i] & 0x7FFFu) - ((uint32_t)kGeluTabExp0 << 7);   // wraps for small |h|
+    const bool in = off < SPAN;
+    all_in = all_in && in;
+    gb[i] = tab[in ? off + (b[i] >> 15) * SPAN : 0u];
   }
+  if (!all_in) {
+    bool special = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t e = (b[i] >> 7) & 0xFFu;
+      const bool in = e - (uint32_t)kGeluTabExp0 < (uint32_t)kGeluTabExps;
+      const bool small = e - 2u < (uint32_t)(kGeluTabExp0 - 2);                         // exponents 2 .. 110
+      const bool big = e - (uint32_t)(kGeluTabExp0 + kGeluTabExps) < (uint32_t)(255 - kGeluTabExp0 - kGeluTabExps);
+      const uint32_t closed = small ? b[i] - 0x80u : ((b[i] & 0x8000u) ? 0x8000u : b[i]);
+      gb[i] = in ? gb[i] : closed;
+      special = special || !(in || small || big);
+    }
+    if (special) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t e = (b[i] >> 7) & 0xFFu;
+        if (e < 2u || e == 255u) gb[i] = gelu_bf16_direct(b[i]);
+      }
+    }
+  }
+}
+
+// The quantized-output epilogue for one 16-byte chunk (8 consecutive
+// columns n .. n + 7 of row m, bf16 h = RNE(acc + bias)): g = RNE_bf16(GELU(h))
+// with gelu_f32 above, two values per V_CVT_PK_BF16_F32; the four lanes
+// holding one 32-column block (adjacent lanes, one row) combine their amax
+// bits; the MX scale byte and the codes follow as in the row quantizer. Every
+// lane issues both stores (rows past M, columns past the output's K_pad and
+// the scale bytes of three of the four lanes go to an offset past the buffer).
+template <int FMT, bool TAB>
+__device__ __forceinline__ void gelu_quant_store(uint4 w, bool scale_lane, bool in, int code_off, int scale_off,
+                                                 __amdgpu_buffer_rsrc_t q_rs, __amdgpu_buffer_rsrc_t qs_rs,
+                                                 const uint16_t* tab) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  uint32_t gb[8];
+  if constexpr (TAB) gelu_bf16_lookup8(words, tab, gb);
+  float g[8];
+  u16x2 mag = {0, 0};                        // largest |g| bits of each half
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // element 2k in the low half of word k, 2k + 1 in the high half
+    const uint32_t gp =
+        TAB ? gb[2 * k] | (gb[2 * k + 1] << 16)
+            : pack_bf16x2(gelu_f32(__uint_as_float(words[k] << 16)), gelu_f32(__uint_as_float(words[k] & 0xFFFF0000u)));
+    g[2 * k] = __uint_as_float(gp << 16);
+    g[2 * k + 1] = __uint_as_float(gp & 0xFFFF0000u);
+    mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, gp & 0x7FFF7FFFu));
+  }
+  uint32_t amax = max((uint32_t)mag.x, (uint32_t)mag.y);
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
   const uint32_t sb = (uint32_t)(mx_shared_exp(amax, FMT == FMT_MXFP8 ? 8 : 2) + 127);
@@ -396,6 +474,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
 
   const int ra = wm * WM + r32, rb = wn * WN + r32;     // this lane's fragment-0 rows in the tile
 
+  // the GELU table; the first stage barrier orders it before every reader
+  if constexpr (Cfg::GTAB) fill_gelu_table(reinterpret_cast<uint16_t*>(lds + Cfg::GTAB_OFF), (int)threadIdx.x, Cfg::NT);
   set_copy_tile(lt);
   issue_next();
   int gs = 0, gc = 0, ctc = 0;              // compute cursor: stages / scale chunks / tiles consumed
@@ -513,8 +593,10 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
               const int off = (m < M && n < N) ? (m * N + n) * 2 : (int)0x80000000u;
               __builtin_amdgcn_raw_buffer_store_b128(v4u{w[j].x, w[j].y, w[j].z, w[j].w}, c_rs, off, 0, kStoreDeviceScope);
             } else {
-              gelu_quant_store<Cfg::FMT>(w[j], (c & 3) == 0, m < M && n < qld, m * q_row_bytes + ((Cfg::FMT == FMT_MXFP8) ? n : n / 2),
-                                         m * (qld / 32) + n / 32, q_rs, qs_rs);
+              gelu_quant_store<Cfg::FMT, Cfg::GTAB>(w[j], (c & 3) == 0, m < M && n < qld,
+                                                    m * q_row_bytes + ((Cfg::FMT == FMT_MXFP8) ? n : n / 2),
+                                                    m * (qld / 32) + n / 32, q_rs, qs_rs,
+                                                    reinterpret_cast<const uint16_t*>(lds + Cfg::GTAB_OFF));
             }
           }
         }
