@@ -110,3 +110,42 @@ def test_fused_vitl_fc1_full_size(fmt):
     bias = W.np_normal((L.n,), W.seed(wl.wid, 0, L.bias_id), W.BIAS_STD)
     rows = np.concatenate([np.arange(0, wl.m, 389), [wl.m - 1]])
     check(a, b, fmt, bias, rows=rows)
+
+
+# biased bf16 exponents of the pre-activations below: zero and subnormals (0),
+# the bottom of the normal range (1, 2), |h| below 2^-16 (50 .. 110), the
+# GELU curve (111 .. 130, both ends), |h| >= 16 up to the largest finite (131 ..
+# 254); each 32-column block holds one exponent
+EDGE_EXPONENTS = [0, 1, 2, 50, 100, 110, 111, 112, 118, 120, 124, 125, 126, 127, 128, 129, 130, 131, 132, 140,
+                  200, 254]
+
+
+@pytest.mark.parametrize("fmt", MX)
+@pytest.mark.parametrize("m, reps", [(3, 1), (4096, 3)])
+def test_fused_gelu_every_exponent_range(fmt, m, reps):
+    """h = bias exactly (A is zero, so every accumulation is 0): each 32-column
+    block holds bf16 pre-activations of one exponent, half of them negative,
+    with random mantissas and, in the exponent-0 block, signed zeros. Covers
+    every branch of the epilogue's GELU: the in-range values, the closed
+    forms below 2^-16 and from 16 up, and the directly evaluated zero,
+    subnormal and smallest-normal inputs; the block scale follows each
+    block's own magnitude, so every code is checked at its exponent. The
+    small problem runs the 128 x 128 tile (GELU evaluated in fp32 for every
+    element), the large one a tile that reads GELU from its LDS table."""
+    rng = np.random.default_rng(1234)
+    blocks = []
+    for e in EDGE_EXPONENTS * reps:
+        mant = rng.integers(0, 128, 32)
+        sign = np.repeat([0, 1], 16)
+        blk = (sign << 15) | (e << 7) | mant
+        if e == 0:
+            blk[[0, 16]] = [0x0000, 0x8000]
+        blocks.append(blk)
+    bias = np.concatenate(blocks).astype(np.uint16)
+    n = bias.size
+    plan = api.gemm_plan(m, n, 64, fmt)
+    assert ("128x128" in plan) == (m == 3), plan
+    a = np.zeros((m, 64), dtype=np.uint16)
+    b = W.np_normal((n, 64), seed=77, std=W.W_STD)
+    rows = None if m == 3 else np.array([0, 1, 2000, m - 1])
+    check(a, b, fmt, bias, rows=rows, gemm_tol=0.0)
