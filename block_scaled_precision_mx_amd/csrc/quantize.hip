@@ -36,6 +36,17 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Tile of workgroup slot `id` when the grid holds one workgroup per tile:
+// workgroups are dealt to the 8 XCDs round-robin, so tiles are renumbered to
+// give each XCD a contiguous range. Neighbouring tiles along a row then share
+// an L2, which matters where each writes half of a 128-byte line (the row copy
+// of a 64-column tile). With fewer workgroups than tiles, the identity.
+__device__ __forceinline__ int xcd_tile(int id, int ntiles) {
+  if ((int)gridDim.x != ntiles) return id;
+  const int q = ntiles / 8, r = ntiles % 8, xcd = id % 8, local = id / 8;
+  return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
+}
+
 struct NvTrailer {
   float s_t;
   uint32_t amax_bits;   // fp32 bits of the tensor amax
@@ -474,7 +485,8 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
     }
   }
   uint32_t own_max = 0u;                      // largest |x| bits this thread saw (delayed NVFP4)
-  for (int tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+  for (int slot = blockIdx.x; slot < ntiles; slot += gridDim.x) {
+    const int tile_id = xcd_tile(slot, ntiles);
     const int tr_ = tile_id / tiles_c;
     const int tc = tile_id - tr_ * tiles_c;
     const int r0 = tr_ * kColTileR, c0 = tc * kColTileC;
