@@ -101,14 +101,27 @@ def check_rows(codes_rows: np.ndarray, scales_rows: np.ndarray, c: np.ndarray, s
     ok_scales [R, K_pad / 32]) boolean masks."""
     if fmt not in ("mxfp8", "mxfp4"):
         raise ValueError("the fused path emits MX formats")
+    h_lo = F.f64_to_bf16_rne(c - gemm_tol * s)
+    h_hi = F.f64_to_bf16_rne(c + gemm_tol * s)
+    g_lo, g_hi = _bf16_interval_of_gelu(h_lo, h_hi)
+    return check_intervals(codes_rows, scales_rows, g_lo, g_hi, fmt, n)
+
+
+def check_intervals(codes_rows: np.ndarray, scales_rows: np.ndarray, g_lo: np.ndarray, g_hi: np.ndarray, fmt: str,
+                    n: int):
+    """Accept / reject MX row-quantized rows whose bf16 source values are
+    known only to lie in [g_lo, g_hi] (float64 [R, n], bf16 values), the
+    columns n .. K_pad being padding. Returns (ok_codes [R, K_pad],
+    ok_scales [R, K_pad / 32]) boolean masks."""
+    if fmt not in ("mxfp8", "mxfp4"):
+        raise ValueError("interval acceptance is defined for the MX formats")
     emax = F.E4M3_EMAX if fmt == "mxfp8" else F.E2M1_EMAX
     R, k_pad = codes_rows.shape
     nb = k_pad // 32
-    h_lo = F.f64_to_bf16_rne(c - gemm_tol * s)
-    h_hi = F.f64_to_bf16_rne(c + gemm_tol * s)
-    g_lo = np.zeros((R, k_pad))
-    g_hi = np.zeros((R, k_pad))
-    g_lo[:, :n], g_hi[:, :n] = _bf16_interval_of_gelu(h_lo, h_hi)
+    lo = np.zeros((R, k_pad))
+    hi = np.zeros((R, k_pad))
+    lo[:, :n], hi[:, :n] = g_lo, g_hi
+    g_lo, g_hi = lo, hi
     # block amax range
     amin = np.where((g_lo <= 0) & (g_hi >= 0), 0.0, np.minimum(np.abs(g_lo), np.abs(g_hi)))
     amax = np.maximum(np.abs(g_lo), np.abs(g_hi))
