@@ -26,6 +26,8 @@ SIGNATURES = {
     "mx_quantize": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
                                _c.c_int, _c.c_int, _c.c_void_p]),
     "mx_quantize_batch": (_c.c_int, [_c.POINTER(QuantItem), _c.c_int, _c.c_int, _c.c_void_p]),
+    "mx_layernorm_quantize": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
+                                         _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
     "mx_quantize_dual": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
                                     _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_float, _c.c_void_p]),
     "mx_quantize_dual_sr": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,

@@ -119,6 +119,31 @@ def mx_quantize_batch(xs: list[torch.Tensor], fmt: str, out: list[Quantized] | N
     return result
 
 
+def mx_layernorm_quantize(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, eps: float, fmt: str,
+                          out: Quantized | None = None, stream=None) -> Quantized:
+    """LayerNorm of the rows of a 2-D fp32 device tensor (the residual
+    stream; gamma, beta fp32 [cols]) rounded to bf16 and row-quantized in
+    one launch (MXFP8 / MXFP4): the operand of the next GEMM."""
+    if x.dtype != torch.float32 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D float32 device tensor")
+    if x.stride(1) != 1 and x.shape[1] > 1:
+        raise ValueError("x must have unit stride along its last dimension")
+    rows, cols = x.shape
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t.dtype != torch.float32 or t.numel() != cols or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 device tensor of {cols} elements")
+    nc, ns = codes_bytes(rows, cols, fmt, "row"), scales_bytes(rows, cols, fmt, "row")
+    if out is None:
+        out = Quantized(torch.empty(nc, dtype=torch.uint8, device=x.device),
+                        torch.empty(ns, dtype=torch.uint8, device=x.device), fmt, rows, cols)
+    elif out.codes.numel() < nc or out.scales.numel() < ns:
+        raise ValueError("out buffers are too small")
+    _check(lib().mx_layernorm_quantize(x.data_ptr(), rows, cols, _ld(x), gamma.data_ptr(), beta.data_ptr(),
+                                       float(eps), out.codes.data_ptr(), out.scales.data_ptr(), FMT[fmt],
+                                       _stream(stream)))
+    return Quantized(out.codes, out.scales, fmt, rows, cols)
+
+
 def mx_quantize_dual(x: torch.Tensor, fmt: str, amax_prev: torch.Tensor | None = None, headroom: float = 32.0,
                      out: tuple[Quantized, Quantized] | None = None, stream=None) -> tuple[Quantized, Quantized]:
     """Row copy and transposed (column) copy of a 2-D bf16 device tensor from

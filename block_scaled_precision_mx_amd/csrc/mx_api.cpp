@@ -85,6 +85,38 @@ mx_status mx_quantize(const void* src, int64_t rows, int64_t cols, int64_t ld, v
   return MX_OK;
 }
 
+mx_status mx_layernorm_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, const void* gamma,
+                                const void* beta, float eps, void* codes, void* scales, mx_fmt fmt,
+                                void* hip_stream) {
+  if (fmt != MX_FMT_MXFP8 && fmt != MX_FMT_MXFP4) {
+    if (fmt == MX_FMT_NVFP4)
+      return fail(MX_ERR_UNSUPPORTED, "mx_layernorm_quantize: NVFP4 needs the output's tensor amax first");
+    return fail(MX_ERR_INVALID_ARG, "mx_layernorm_quantize: unknown format %d", (int)fmt);
+  }
+  if (rows < 1 || cols < 1)
+    return fail(MX_ERR_INVALID_ARG, "mx_layernorm_quantize: empty tensor (%lld x %lld)", (long long)rows, (long long)cols);
+  if (ld < cols)
+    return fail(MX_ERR_INVALID_ARG, "mx_layernorm_quantize: ld %lld < cols %lld", (long long)ld, (long long)cols);
+  if (!x || !gamma || !beta || !codes || !scales) return fail(MX_ERR_INVALID_ARG, "mx_layernorm_quantize: null pointer");
+  if (!(eps >= 0.0f) || !(eps < 3.0e38f))
+    return fail(MX_ERR_INVALID_ARG, "mx_layernorm_quantize: eps must be finite and >= 0");
+  if (!aligned(x, 4) || !aligned(gamma, 4) || !aligned(beta, 4))
+    return fail(MX_ERR_ALIGNMENT, "mx_layernorm_quantize: x, gamma and beta must be 4-byte aligned");
+  if (!aligned(codes, 16) || !aligned(scales, 16))
+    return fail(MX_ERR_ALIGNMENT, "mx_layernorm_quantize: codes and scales must be 16-byte aligned");
+  const int64_t kpad = k_pad(cols);
+  if (rows * code_row_bytes(kpad, fmt) >= kMaxBytes || scales_total(rows, kpad, fmt) >= kMaxBytes)
+    return fail(MX_ERR_UNSUPPORTED, "mx_layernorm_quantize: output larger than 2 GiB");
+  if (ld >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31))
+    return fail(MX_ERR_UNSUPPORTED, "mx_layernorm_quantize: ld and rows must be below 2^31");
+  hipError_t e = mx::launch_layernorm_quantize(static_cast<const float*>(x), rows, cols, ld,
+                                               static_cast<const float*>(gamma), static_cast<const float*>(beta), eps,
+                                               static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), (int)fmt,
+                                               static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(MX_ERR_HIP, "mx_layernorm_quantize: launch failed: %s", hipGetErrorString(e));
+  return MX_OK;
+}
+
 mx_status mx_quantize_batch(const mx_quant_item* items, int n, mx_fmt fmt, void* hip_stream) {
   if (fmt != MX_FMT_MXFP8 && fmt != MX_FMT_MXFP4) {
     if (fmt == MX_FMT_NVFP4)

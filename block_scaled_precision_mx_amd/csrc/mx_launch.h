@@ -33,6 +33,12 @@ hipError_t launch_quantize_batch(const QuantBatchItem* items, int n, int fmt, hi
 // fp32(fp64(headroom * *amax_prev) / 2688). sr (NVFP4, cols % 8 == 0):
 // elements rounded stochastically with Philox4x64-10 draws keyed by
 // (seed0, seed1).
+// LayerNorm of fp32 rows (gamma, beta fp32, eps) rounded to bf16 and
+// row-quantized (MXFP8 / MXFP4).
+hipError_t launch_layernorm_quantize(const float* x, int64_t rows, int64_t cols, int64_t ld, const float* gamma,
+                                     const float* beta, float eps, uint8_t* codes, uint8_t* scales, int fmt,
+                                     hipStream_t stream);
+
 hipError_t launch_quantize_dual(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* rcodes,
                                 uint8_t* rscales, uint8_t* ccodes, uint8_t* cscales, int fmt, const float* amax_prev,
                                 float headroom, int sr, uint64_t seed0, uint64_t seed1, hipStream_t stream);

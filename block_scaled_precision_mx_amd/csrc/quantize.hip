@@ -697,6 +697,114 @@ hipError_t launch_quantize_batch(const QuantBatchItem* items, int n, int fmt, hi
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ LayerNorm + quantize
+
+// README section 4.3: the MXFP8 stack computes LayerNorm and quantization in
+// one kernel, with the residual stream and the LayerNorm statistics in fp32.
+// The output is what an LN kernel with bf16 output followed by the row
+// quantizer would write: y = (x - mu) / sqrt(var + eps) * gamma + beta in
+// fp32 (mu, var: the row's mean and biased variance), rounded to bf16, then
+// MX-quantized along the row. One wave per row: pass 1 sums the row, pass 2
+// sums the squares of the centred values (the row is read again, from the
+// caches), pass 3 normalizes, rounds and quantizes 8 consecutive values per
+// lane, the 4 adjacent lanes of a 32-element block combining their amax.
+__device__ __forceinline__ void load8_f32(const float* row, int c, int cols, bool vec_ok, float (&v)[8]) {
+  if (vec_ok && c + 8 <= cols) {
+    const float4 a = *reinterpret_cast<const float4*>(row + c), b = *reinterpret_cast<const float4*>(row + c + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (c + i < cols) ? row[c + i] : 0.0f;
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void ln_quant_kernel(const float* __restrict__ x, int rows, int cols, int ld,
+                                                       const float* __restrict__ gamma, const float* __restrict__ beta,
+                                                       float eps, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales, int kpad) {
+  static_assert(FMT != FMT_NVFP4, "NVFP4 needs the tensor amax of the output first");
+  const int lane = threadIdx.x & 63;
+  const bool vec_ok = (ld % 4) == 0 && ((uintptr_t)x % 16) == 0;
+  const bool pvec_ok = ((uintptr_t)gamma % 16) == 0 && ((uintptr_t)beta % 16) == 0;
+  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += gridDim.x * 4) {   // one row per wave
+    const float* xr = x + (int64_t)r * ld;
+    float s = 0.0f;
+    for (int c0 = 0; c0 < cols; c0 += 512) {
+      float v[8];
+      load8_f32(xr, c0 + 8 * lane, cols, vec_ok, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i];
+    }
+    const float mu = wave_sum(s) / (float)cols;
+    float q = 0.0f;
+    for (int c0 = 0; c0 < cols; c0 += 512) {
+      const int c = c0 + 8 * lane;
+      float v[8];
+      load8_f32(xr, c, cols, vec_ok, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float d = (c + i < cols) ? v[i] - mu : 0.0f;
+        q = fmaf(d, d, q);
+      }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)cols + eps);
+    for (int c0 = 0; c0 < kpad; c0 += 512) {
+      const int c = c0 + 8 * lane;
+      float v[8], gm[8], bt[8];
+      load8_f32(xr, c, cols, vec_ok, v);
+      load8_f32(gamma, c, cols, pvec_ok, gm);
+      load8_f32(beta, c, cols, pvec_ok, bt);
+      float y[8];
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        // columns past cols are padding: code 0 (they do not raise the amax)
+        const float y0 = (c + i < cols) ? fmaf((v[i] - mu) * rstd, gm[i], bt[i]) : 0.0f;
+        const float y1 = (c + i + 1 < cols) ? fmaf((v[i + 1] - mu) * rstd, gm[i + 1], bt[i + 1]) : 0.0f;
+        const uint32_t p = pack_bf16x2(y0, y1);   // RNE to bf16
+        y[i] = __uint_as_float(p << 16);
+        y[i + 1] = __uint_as_float(p & 0xFFFF0000u);
+        m = max(m, max(p & 0x7FFFu, (p >> 16) & 0x7FFFu));
+      }
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+      Nv4Thresholds th;
+      const uint32_t sb = block_scale<FMT>(m, 0.0f, th);
+      const uint64_t packed = encode8<FMT>(y, sb, th);
+      if (c < kpad) {
+        if (FMT == FMT_MXFP8) {
+          *reinterpret_cast<uint2*>(codes + (int64_t)r * kpad + c) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
+        } else {
+          *reinterpret_cast<uint32_t*>(codes + (int64_t)r * (kpad / 2) + c / 2) = (uint32_t)packed;
+        }
+        if ((lane & 3) == 0) scales[(int64_t)r * (kpad / 32) + c / 32] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+hipError_t launch_layernorm_quantize(const float* x, int64_t rows, int64_t cols, int64_t ld, const float* gamma,
+                                     const float* beta, float eps, uint8_t* codes, uint8_t* scales, int fmt,
+                                     hipStream_t stream) {
+  const int64_t kpad = round_up(cols, kAlignK);
+  const int g = grid_for(rows, 4, 1 << 16);
+  if (fmt == FMT_MXFP8)
+    ln_quant_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(x, (int)rows, (int)cols, (int)ld, gamma, beta, eps, codes,
+                                                      scales, (int)kpad);
+  else
+    ln_quant_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(x, (int)rows, (int)cols, (int)ld, gamma, beta, eps, codes,
+                                                      scales, (int)kpad);
+  return hipGetLastError();
+}
+
+
 hipError_t launch_quantize_dual(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* rcodes,
                                 uint8_t* rscales, uint8_t* ccodes, uint8_t* cscales, int fmt, const float* amax_prev,
                                 float headroom, int sr, uint64_t seed0, uint64_t seed1, hipStream_t stream) {

@@ -147,6 +147,27 @@ mx_status mx_quantize_dual_sr(const void* src, int64_t rows, int64_t cols, int64
                               mx_fmt fmt, const float* amax_prev, float headroom,
                               uint64_t seed0, uint64_t seed1, void* hip_stream);
 
+/* LayerNorm fused with quantization (README section 4.3: in the MXFP8
+ * stack LayerNorm and quantization are one kernel; the residual stream and
+ * the LayerNorm statistics stay fp32). x: fp32 [rows, cols], leading
+ * dimension ld elements (the residual stream); gamma, beta: fp32 [cols];
+ * eps >= 0. Each row becomes
+ *   y = (x - mu) / sqrt(var + eps) * gamma + beta   (mu, var: the row's mean
+ *       and biased variance, computed in fp32),
+ * rounded to bf16, and codes / scales receive what mx_quantize of that bf16
+ * tensor (axis MX_AXIS_ROW) would write (sizes mx_codes_bytes /
+ * mx_scales_bytes of (rows, cols, fmt, MX_AXIS_ROW)), so they serve directly
+ * as the A operand of the next mx_gemm (K = cols). The bf16 LayerNorm output
+ * itself is never stored. y lies within 2^-16 (|gamma| r (max|x - mu| +
+ * |x - mu| + |mu|) + |beta| + |y|) of the exact value, r = 1/sqrt(var + eps).
+ * fmt: MX_FMT_MXFP8 or MX_FMT_MXFP4 (NVFP4 would need the output's tensor
+ * amax before the first block: MX_ERR_UNSUPPORTED). x, gamma and beta must be
+ * 4-byte aligned (16 bytes, with ld % 4 == 0, takes the vector loads), codes
+ * and scales 16-byte aligned. Errors and memory rules as for mx_quantize. */
+mx_status mx_layernorm_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                                const void* gamma, const void* beta, float eps,
+                                void* codes, void* scales, mx_fmt fmt, void* hip_stream);
+
 /* One tensor of mx_quantize_batch: X [rows, cols] (bf16, leading dimension
  * ld elements) and its row-axis outputs, sized by mx_codes_bytes /
  * mx_scales_bytes with MX_AXIS_ROW. */

@@ -169,6 +169,24 @@ def test_gemm_gelu_quantize_validation(L, args, status, msg):
     assert msg in L.mx_last_error().decode()
 
 
+# mx_layernorm_quantize(x, rows, cols, ld, gamma, beta, eps, codes, scales, fmt)
+@pytest.mark.parametrize("args,status,msg", [
+    ((ALIGNED, 4, 8, 8, ALIGNED, ALIGNED, 1e-6, ALIGNED, ALIGNED, 3), 2, "NVFP4"),
+    ((ALIGNED, 4, 8, 8, ALIGNED, ALIGNED, 1e-6, ALIGNED, ALIGNED, 9), 1, "unknown format"),
+    ((ALIGNED, 0, 8, 8, ALIGNED, ALIGNED, 1e-6, ALIGNED, ALIGNED, 1), 1, "empty"),
+    ((ALIGNED, 4, 8, 7, ALIGNED, ALIGNED, 1e-6, ALIGNED, ALIGNED, 1), 1, "ld"),
+    ((ALIGNED, 4, 8, 8, None, ALIGNED, 1e-6, ALIGNED, ALIGNED, 1), 1, "null"),
+    ((ALIGNED, 4, 8, 8, ALIGNED, ALIGNED, -1.0, ALIGNED, ALIGNED, 1), 1, "eps"),
+    ((ALIGNED, 4, 8, 8, ALIGNED, ALIGNED, float("nan"), ALIGNED, ALIGNED, 2), 1, "eps"),
+    ((ALIGNED + 2, 4, 8, 8, ALIGNED, ALIGNED, 1e-6, ALIGNED, ALIGNED, 1), 3, "4-byte"),
+    ((ALIGNED, 4, 8, 8, ALIGNED, ALIGNED, 1e-6, ALIGNED + 4, ALIGNED, 1), 3, "16-byte"),
+    ((ALIGNED, 1 << 22, 1 << 10, 1 << 10, ALIGNED, ALIGNED, 1e-6, ALIGNED, ALIGNED, 1), 2, "2 GiB"),
+])
+def test_layernorm_quantize_validation(L, args, status, msg):
+    assert L.mx_layernorm_quantize(*args, None) == status
+    assert msg in L.mx_last_error().decode()
+
+
 def test_quantize_dual_ignores_headroom_for_mx(L):
     """MX formats never read amax_prev / headroom: a bad headroom is not an
     error there (the call then fails later on the 2 GiB check, still before
