@@ -3,7 +3,11 @@
 One step = one pass of the whole path over one batch: for every ViT block
 and every linear layer (qkv, proj, fc1, fc2) quantize the activation and the
 weight row-wise (both in one mx_quantize_batch launch) and run the
-block-scaled GEMM with its bias epilogue (mx_gemm). For the NVFP4 training workload a step is the fc1/fc2
+block-scaled GEMM with its bias epilogue (mx_gemm). The *_fc1gelu stacks
+let fc1's epilogue write fc2's operand (mx_gemm_gelu_quantize); the *_lnq_*
+stacks also take qkv's and fc1's inputs as the LayerNorm of an fp32
+residual stream, normalized and quantized in one launch
+(mx_layernorm_quantize). For the NVFP4 training workload a step is the fc1/fc2
 pair's fprop, dgrad and wgrad GEMMs with every operand quantized along its
 own K axis (row and transposed copies from one read with mx_quantize_dual,
 tensor amax included).
@@ -40,6 +44,7 @@ NVFP4_AMAX_BYTES = 2.0
 
 WORKLOADS = ["vitl16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack", "vitb16_mxfp8_fwd_stack",
              "vitl16_mxfp8_fwd_stack_fc1gelu", "vitl16_mxfp4_fwd_stack_fc1gelu",
+             "vitl16_mxfp8_fwd_stack_lnq_fc1gelu", "vitl16_mxfp4_fwd_stack_lnq_fc1gelu",
              "vitl16_nvfp4_fc1fc2_train", "vitl16_nvfp4_fc1fc2_train_srgrad", "vitl16_mxfp8_fc1fc2_train",
              "single_mxfp8_256x768x768"]
 
@@ -102,7 +107,6 @@ def build_stack(stack, dev):
                               flops=2.0 * stack.m * lin.n * lin.k, label=f"gemm_{lin.name}",
                               plan=api.gemm_plan(stack.m, lin.n, lin.k, fmt)))
                 continue
-            a = W.torch_activation((stack.m, lin.k), W.seed(stack.wid, blk, lin.a_id), dev, gelu=lin.a_kind == "gelu")
             w = W.torch_normal((lin.n, lin.k), W.seed(stack.wid, blk, lin.w_id), W.W_STD, dev)
             bias = W.torch_normal((lin.n,), W.seed(stack.wid, blk, lin.bias_id), W.BIAS_STD, dev)
             qa = api.Quantized(torch.empty(api.codes_bytes(stack.m, lin.k, fmt), dtype=torch.uint8, device=dev),
@@ -112,9 +116,24 @@ def build_stack(stack, dev):
                                torch.empty(api.scales_bytes(lin.n, lin.k, fmt), dtype=torch.uint8, device=dev),
                                fmt, lin.n, lin.k)
             out = torch.empty((stack.m, lin.n), dtype=torch.bfloat16, device=dev)
-            # the GEMM's two operands in one launch (mx_quantize_batch), just before it
-            ops.append(Op("quant", lambda a=a, w=w, qa=qa, qw=qw: api.mx_quantize_batch([a, w], fmt, out=[qa, qw]),
-                          nbytes=QUANT_BYTES[fmt] * (a.numel() + w.numel()), label=f"quant_{lin.name}_act_w"))
+            if stack.ln_quant and lin.name in ("qkv", "fc1"):
+                # the input is the LayerNorm of the fp32 residual stream, normalized
+                # and quantized in one launch; the weight in a launch of its own
+                x = W.torch_residual((stack.m, lin.k), W.seed(stack.wid, blk, lin.a_id), dev)
+                gamma, beta = W.torch_ln_params(lin.k, W.seed(stack.wid, blk, 50 + lin.a_id), dev)
+                ops.append(Op("quant", lambda x=x, g=gamma, b=beta, qa=qa:
+                              api.mx_layernorm_quantize(x, g, b, W.LN_EPS, fmt, out=qa),
+                              nbytes=(4 + QUANT_BYTES[fmt] - 2) * x.numel(), label=f"lnquant_{lin.name}_act"))
+                ops.append(Op("quant", lambda w=w, qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales),
+                              nbytes=QUANT_BYTES[fmt] * w.numel(), label=f"quant_{lin.name}_w",
+                              cold=[lambda w=w.clone(), qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales)
+                                    for _ in range(2)]))
+            else:
+                a = W.torch_activation((stack.m, lin.k), W.seed(stack.wid, blk, lin.a_id), dev,
+                                       gelu=lin.a_kind == "gelu")
+                # the GEMM's two operands in one launch (mx_quantize_batch), just before it
+                ops.append(Op("quant", lambda a=a, w=w, qa=qa, qw=qw: api.mx_quantize_batch([a, w], fmt, out=[qa, qw]),
+                              nbytes=QUANT_BYTES[fmt] * (a.numel() + w.numel()), label=f"quant_{lin.name}_act_w"))
             if stack.fuse_fc1_gelu and lin.name == "fc1":
                 del out
                 fused_out = api.Quantized(

@@ -89,6 +89,31 @@ def torch_activation(shape, seed: int, device="cuda", gelu=False):
     return z.to(torch.bfloat16)
 
 
+# LayerNorm inputs (the fp32 residual stream and the affine parameters)
+LN_EPS = 1e-6
+LN_GAMMA_STD = 0.1
+LN_BETA_STD = 0.02
+
+
+def torch_residual(shape, seed: int, device="cuda"):
+    """The fp32 residual stream entering a LayerNorm: the activation recipe
+    (N(0, 1), 0.1% of the entries times 50) kept in fp32."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    z = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    hit = torch.rand(shape, generator=g, device=device) < OUTLIER_P
+    return torch.where(hit, z * OUTLIER_GAIN, z)
+
+
+def torch_ln_params(n: int, seed: int, device="cuda"):
+    """(gamma, beta) fp32: 1 + N(0, LN_GAMMA_STD) and N(0, LN_BETA_STD)."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    gamma = 1.0 + LN_GAMMA_STD * torch.randn(n, generator=g, device=device, dtype=torch.float32)
+    beta = LN_BETA_STD * torch.randn(n, generator=g, device=device, dtype=torch.float32)
+    return gamma, beta
+
+
 def torch_normal(shape, seed: int, std: float, device="cuda"):
     import torch
     g = torch.Generator(device=device).manual_seed(seed)
@@ -123,6 +148,9 @@ class Stack:
     # fc1's epilogue applies GELU and writes fc2's quantized operand, so fc2's
     # input is GELU(fc1's output) instead of a separate synthetic tensor
     fuse_fc1_gelu: bool = False
+    # qkv's and fc1's inputs are the LayerNorm of an fp32 residual stream,
+    # computed and quantized in one launch (mx_layernorm_quantize)
+    ln_quant: bool = False
 
     def gemm_flops(self) -> int:
         return 2 * self.m * sum(l.n * l.k for l in self.linears) * self.blocks
@@ -153,7 +181,15 @@ VITL_MXFP8_FUSED = Stack(3, "vitl16_mxfp8_fwd_stack_fc1gelu", "mxfp8", 7 * TOKEN
 VITL_MXFP4_FUSED = Stack(4, "vitl16_mxfp4_fwd_stack_fc1gelu", "mxfp4", 7 * TOKENS, 1024, 4096, 24,
                          _vit_linears(1024, 4096), fuse_fc1_gelu=True)
 
-STACKS = {s.name: s for s in (SINGLE_LAYER, VITB_MXFP8, VITL_MXFP8, VITL_MXFP4, VITL_MXFP8_FUSED, VITL_MXFP4_FUSED)}
+# the layer structure of the pages' MXFP8 stack: LayerNorm fused with the
+# quantization of qkv's and fc1's inputs, fc1's epilogue writing fc2's operand
+VITL_MXFP8_LAYER = Stack(3, "vitl16_mxfp8_fwd_stack_lnq_fc1gelu", "mxfp8", 7 * TOKENS, 1024, 4096, 24,
+                         _vit_linears(1024, 4096), fuse_fc1_gelu=True, ln_quant=True)
+VITL_MXFP4_LAYER = Stack(4, "vitl16_mxfp4_fwd_stack_lnq_fc1gelu", "mxfp4", 7 * TOKENS, 1024, 4096, 24,
+                         _vit_linears(1024, 4096), fuse_fc1_gelu=True, ln_quant=True)
+
+STACKS = {s.name: s for s in (SINGLE_LAYER, VITB_MXFP8, VITL_MXFP8, VITL_MXFP4, VITL_MXFP8_FUSED, VITL_MXFP4_FUSED,
+                              VITL_MXFP8_LAYER, VITL_MXFP4_LAYER)}
 
 
 @dataclass(frozen=True)
