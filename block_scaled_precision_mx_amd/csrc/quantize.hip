@@ -790,17 +790,120 @@ __global__ __launch_bounds__(256) void ln_quant_kernel(const float* __restrict__
   }
 }
 
+// Rows of at most 512 NCH elements (NCH <= 4): each wave keeps its row in
+// registers (8 NCH values per lane), so the row is read from memory once
+// instead of three times, holds gamma and beta for its columns across all
+// its rows, and issues the loads of its next row before reducing the
+// current one. Same arithmetic in the same order as ln_quant_kernel (the
+// outputs are identical byte for byte); 1.3-1.5x faster on ViT rows.
+template <int FMT, int NCH>
+__global__ __launch_bounds__(256) void ln_quant_reg_kernel(const float* __restrict__ x, int rows, int cols, int ld,
+                                                           const float* __restrict__ gamma,
+                                                           const float* __restrict__ beta, float eps,
+                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                           int kpad) {
+  static_assert(FMT != FMT_NVFP4, "NVFP4 needs the tensor amax of the output first");
+  const int lane = threadIdx.x & 63;
+  const bool vec_ok = (ld % 4) == 0 && ((uintptr_t)x % 16) == 0;
+  const bool pvec_ok = ((uintptr_t)gamma % 16) == 0 && ((uintptr_t)beta % 16) == 0;
+  float gm[NCH][8], bt[NCH][8];
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    load8_f32(gamma, 512 * k + 8 * lane, cols, pvec_ok, gm[k]);
+    load8_f32(beta, 512 * k + 8 * lane, cols, pvec_ok, bt[k]);
+  }
+  const int step = gridDim.x * 4;
+  int r = blockIdx.x * 4 + (threadIdx.x >> 6);    // one row per wave at a time
+  float v[NCH][8];
+  if (r < rows) {
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) load8_f32(x + (int64_t)r * ld, 512 * k + 8 * lane, cols, vec_ok, v[k]);
+  }
+  for (; r < rows; r += step) {
+    float vn[NCH][8];
+    if (r + step < rows) {
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) load8_f32(x + (int64_t)(r + step) * ld, 512 * k + 8 * lane, cols, vec_ok, vn[k]);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[k][i];               // columns past cols were loaded as 0
+    const float mu = wave_sum(s) / (float)cols;
+    float q = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float d = (512 * k + 8 * lane + i < cols) ? v[k][i] - mu : 0.0f;
+        q = fmaf(d, d, q);
+      }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)cols + eps);
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c = 512 * k + 8 * lane;
+      float y[8];
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const float y0 = (c + i < cols) ? fmaf((v[k][i] - mu) * rstd, gm[k][i], bt[k][i]) : 0.0f;
+        const float y1 = (c + i + 1 < cols) ? fmaf((v[k][i + 1] - mu) * rstd, gm[k][i + 1], bt[k][i + 1]) : 0.0f;
+        const uint32_t p = pack_bf16x2(y0, y1);   // RNE to bf16
+        y[i] = __uint_as_float(p << 16);
+        y[i + 1] = __uint_as_float(p & 0xFFFF0000u);
+        m = max(m, max(p & 0x7FFFu, (p >> 16) & 0x7FFFu));
+      }
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+      Nv4Thresholds th;
+      const uint32_t sb = block_scale<FMT>(m, 0.0f, th);
+      const uint64_t packed = encode8<FMT>(y, sb, th);
+      if (c < kpad) {
+        if (FMT == FMT_MXFP8) {
+          *reinterpret_cast<uint2*>(codes + (int64_t)r * kpad + c) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
+        } else {
+          *reinterpret_cast<uint32_t*>(codes + (int64_t)r * (kpad / 2) + c / 2) = (uint32_t)packed;
+        }
+        if ((lane & 3) == 0) scales[(int64_t)r * (kpad / 32) + c / 32] = (uint8_t)sb;
+      }
+    }
+    if (r + step < rows) {
+#pragma unroll
+      for (int k = 0; k < NCH; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[k][i] = vn[k][i];
+    }
+  }
+}
+
+template <int FMT>
+static void launch_ln_quant(const float* x, int rows, int cols, int ld, const float* gamma, const float* beta,
+                            float eps, uint8_t* codes, uint8_t* scales, int kpad, hipStream_t stream) {
+  // one row per wave up to 2^18 rows (a persistent grid of 4 or 8
+  // workgroups per CU, each wave walking rows, measured 5-10% slower on the
+  // 11235-row ViT-L stream); beyond that the waves walk the rows with the
+  // next one in flight
+  const int g = grid_for(rows, 4, 1 << 16);
+  if (cols <= 512)
+    ln_quant_reg_kernel<FMT, 1><<<g, 256, 0, stream>>>(x, rows, cols, ld, gamma, beta, eps, codes, scales, kpad);
+  else if (cols <= 1024)
+    ln_quant_reg_kernel<FMT, 2><<<g, 256, 0, stream>>>(x, rows, cols, ld, gamma, beta, eps, codes, scales, kpad);
+  else if (cols <= 2048)
+    ln_quant_reg_kernel<FMT, 4><<<g, 256, 0, stream>>>(x, rows, cols, ld, gamma, beta, eps, codes, scales, kpad);
+  else
+    ln_quant_kernel<FMT><<<grid_for(rows, 4, 1 << 16), 256, 0, stream>>>(x, rows, cols, ld, gamma, beta, eps, codes,
+                                                                         scales, kpad);
+}
+
 hipError_t launch_layernorm_quantize(const float* x, int64_t rows, int64_t cols, int64_t ld, const float* gamma,
                                      const float* beta, float eps, uint8_t* codes, uint8_t* scales, int fmt,
                                      hipStream_t stream) {
-  const int64_t kpad = round_up(cols, kAlignK);
-  const int g = grid_for(rows, 4, 1 << 16);
+  const int kpad = (int)round_up(cols, kAlignK);
   if (fmt == FMT_MXFP8)
-    ln_quant_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(x, (int)rows, (int)cols, (int)ld, gamma, beta, eps, codes,
-                                                      scales, (int)kpad);
+    launch_ln_quant<FMT_MXFP8>(x, (int)rows, (int)cols, (int)ld, gamma, beta, eps, codes, scales, kpad, stream);
   else
-    ln_quant_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(x, (int)rows, (int)cols, (int)ld, gamma, beta, eps, codes,
-                                                      scales, (int)kpad);
+    launch_ln_quant<FMT_MXFP4>(x, (int)rows, (int)cols, (int)ld, gamma, beta, eps, codes, scales, kpad, stream);
   return hipGetLastError();
 }
 

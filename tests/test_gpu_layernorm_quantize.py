@@ -57,8 +57,12 @@ def check(x, g, b, eps, fmt, rows=None, **kw):
 
 
 @pytest.mark.parametrize("fmt", MX)
-@pytest.mark.parametrize("rc", [(1, 32), (3, 100), (37, 1000), (64, 1024), (130, 768), (9, 4096), (5, 4000)])
+@pytest.mark.parametrize("rc", [(1, 32), (3, 100), (37, 1000), (64, 1024), (130, 768), (17, 2000), (6, 1536),
+                                (9, 4096), (5, 4000)])
 def test_layernorm_quantize_shapes(fmt, rc):
+    """Widths up to 512, 1024 and 2048 take the register-resident kernel with
+    one, two and four 512-column chunks per row; wider rows the three-pass
+    kernel."""
     r, c = rc
     x = residual(r, c, seed=r * 7 + c)
     g, b = params(c, seed=c)
@@ -85,10 +89,12 @@ def test_layernorm_quantize_constant_rows_and_offset(fmt):
 
 
 @pytest.mark.parametrize("fmt", MX)
-def test_layernorm_quantize_more_rows_than_one_grid(fmt):
+@pytest.mark.parametrize("c", [64, 520])
+def test_layernorm_quantize_more_rows_than_one_grid(fmt, c):
     """262148 rows: the grid (65536 workgroups of 4 rows) walks the rows
-    twice; sampled rows from both passes and the last one."""
-    r, c = 262148, 64
+    twice, the waves loading their second row while they finish the first;
+    sampled rows from both passes and the last one."""
+    r = 262148
     x = residual(r, c, seed=8)
     g, b = params(c, seed=9)
     check(x, g, b, 1e-6, fmt, rows=np.concatenate([np.arange(0, r, 4099), [262143, 262144, r - 1]]))
