@@ -154,7 +154,7 @@ __device__ __forceinline__ uint64_t encode8(const float (&x)[8], uint32_t sb, co
 
 // ------------------------------------------------------------ row quantizer
 
-constexpr int kRowGroupsPerThread = 2;
+constexpr int kRowGroupsPerThread = 4;
 
 // Row quantization of one tensor by threads first_tid, first_tid + stride,
 // ... of the threads given to it (each thread: U groups of 8 elements of one
@@ -166,8 +166,10 @@ __device__ __forceinline__ void quant_rows(const uint16_t* __restrict__ src, int
   constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
   constexpr int LANES_PER_BLOCK = BS / 8;
   constexpr int U = kRowGroupsPerThread;
+  static_assert(U == 1 || U == 2 || U == 4, "kpad / 8 (a multiple of 16) / U must stay a multiple of 4");
   const int gpr = kpad / 8;                       // groups per stored row (multiple of 16)
-  const int tpr = gpr / U;                        // threads per row (multiple of 8)
+  const int tpr = gpr / U;                        // threads per row: a multiple of 4, so the lanes of a block
+                                                  // are adjacent, aligned and in one row
   const int total = rows * tpr;
   const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
   for (int tid = first_tid; tid < total; tid += stride) {
