@@ -154,18 +154,22 @@ __device__ __forceinline__ uint64_t encode8(const float (&x)[8], uint32_t sb, co
 
 // ------------------------------------------------------------ row quantizer
 
+// Groups of 8 elements per thread: four loads in flight per thread for
+// large tensors, two for tensors of fewer than 2^20 groups (a few million
+// elements), which then spread over more workgroups and finish sooner.
 constexpr int kRowGroupsPerThread = 4;
+constexpr int kRowGroupsSmall = 2;
+constexpr int64_t kRowSmallGroups = 1 << 20;
 
 // Row quantization of one tensor by threads first_tid, first_tid + stride,
 // ... of the threads given to it (each thread: U groups of 8 elements of one
 // stored row).
-template <int FMT>
+template <int FMT, int U>
 __device__ __forceinline__ void quant_rows(const uint16_t* __restrict__ src, int rows, int cols, int ld,
                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad,
                                            float s_t, int first_tid, int stride) {
   constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
   constexpr int LANES_PER_BLOCK = BS / 8;
-  constexpr int U = kRowGroupsPerThread;
   static_assert(U == 1 || U == 2 || U == 4, "kpad / 8 (a multiple of 16) / U must stay a multiple of 4");
   const int gpr = kpad / 8;                       // groups per stored row (multiple of 16)
   const int tpr = gpr / U;                        // threads per row: a multiple of 4, so the lanes of a block
@@ -217,7 +221,7 @@ __device__ __forceinline__ void quant_rows(const uint16_t* __restrict__ src, int
   }
 }
 
-template <int FMT>
+template <int FMT, int U>
 __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                         int kpad, NvTrailer* tr) {
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restri
     s_t = nvfp4_tensor_scale(tr->amax_bits);
     if (blockIdx.x == 0 && threadIdx.x == 0) tr->s_t = s_t;
   }
-  quant_rows<FMT>(src, rows, cols, ld, codes, scales, kpad, s_t, blockIdx.x * blockDim.x + threadIdx.x,
+  quant_rows<FMT, U>(src, rows, cols, ld, codes, scales, kpad, s_t, blockIdx.x * blockDim.x + threadIdx.x,
                   gridDim.x * blockDim.x);
 }
 
@@ -240,8 +244,8 @@ __global__ __launch_bounds__(256) void quant_row_batch_kernel(const QuantBatch b
   const QuantBatchItem& it = batch.items[i];
   const int wg = (int)blockIdx.x - batch.first_wg[i];
   const int nwg = batch.first_wg[i + 1] - batch.first_wg[i];
-  quant_rows<FMT>(it.src, it.rows, it.cols, it.ld, it.codes, it.scales, it.kpad, 0.0f, wg * 256 + (int)threadIdx.x,
-                  nwg * 256);
+  quant_rows<FMT, kRowGroupsPerThread>(it.src, it.rows, it.cols, it.ld, it.codes, it.scales, it.kpad, 0.0f,
+                                      wg * 256 + (int)threadIdx.x, nwg * 256);
 }
 
 // ------------------------------------------------------------ col quantizer
@@ -646,6 +650,17 @@ static int grid_for(int64_t work_items, int per_block, int cap) {
   return (int)g;
 }
 
+template <int U>
+static void launch_row(const uint16_t* src, int ir, int ic, int ild, uint8_t* codes, uint8_t* scales, int ikp,
+                       NvTrailer* tr, int64_t R, int fmt, hipStream_t stream) {
+  const int g = grid_for(R * (ikp / 8 / U), 256, 1 << 20);
+  switch (fmt) {
+    case FMT_MXFP8: quant_row_kernel<FMT_MXFP8, U><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
+    case FMT_MXFP4: quant_row_kernel<FMT_MXFP4, U><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
+    default:        quant_row_kernel<FMT_NVFP4, U><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
+  }
+}
+
 hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
                            uint8_t* scales, int fmt, int axis, hipStream_t stream) {
   // The C ABI bounds every size so that element, group and byte counts fit
@@ -664,13 +679,10 @@ hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int6
     amax_kernel<<<grid_for(rows * gpr, 256 * kAmaxUnroll, 512), 256, 0, stream>>>(src, ir, ic, ild, gpr, tr);
   }
   if (axis == 0) {
-    const int64_t threads = R * (kpad / 8 / kRowGroupsPerThread);
-    const int g = grid_for(threads, 256, 1 << 20);
-    switch (fmt) {
-      case FMT_MXFP8: quant_row_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
-      case FMT_MXFP4: quant_row_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
-      default:        quant_row_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
-    }
+    if (R * (kpad / 8) >= kRowSmallGroups)
+      launch_row<kRowGroupsPerThread>(src, ir, ic, ild, codes, scales, ikp, tr, R, fmt, stream);
+    else
+      launch_row<kRowGroupsSmall>(src, ir, ic, ild, codes, scales, ikp, tr, R, fmt, stream);
   } else {
     const int64_t ntiles = ((cols + kColTileC - 1) / kColTileC) * (kpad / kColTileR);
     const int g = grid_for(ntiles, 1, 1 << 20);
