@@ -98,8 +98,10 @@ mx_status mx_layernorm_quantize(const void* x, int64_t rows, int64_t cols, int64
   if (ld < cols)
     return fail(MX_ERR_INVALID_ARG, "mx_layernorm_quantize: ld %lld < cols %lld", (long long)ld, (long long)cols);
   if (!x || !gamma || !beta || !codes || !scales) return fail(MX_ERR_INVALID_ARG, "mx_layernorm_quantize: null pointer");
-  if (!(eps >= 0.0f) || !(eps < 3.0e38f))
-    return fail(MX_ERR_INVALID_ARG, "mx_layernorm_quantize: eps must be finite and >= 0");
+  // eps > 0 keeps var + eps positive: a constant row (var = 0) then gives
+  // y = beta instead of 0 * inf
+  if (!(eps > 0.0f) || !(eps < 3.0e38f))
+    return fail(MX_ERR_INVALID_ARG, "mx_layernorm_quantize: eps must be finite and > 0");
   if (!aligned(x, 4) || !aligned(gamma, 4) || !aligned(beta, 4))
     return fail(MX_ERR_ALIGNMENT, "mx_layernorm_quantize: x, gamma and beta must be 4-byte aligned");
   if (!aligned(codes, 16) || !aligned(scales, 16))

@@ -151,7 +151,8 @@ mx_status mx_quantize_dual_sr(const void* src, int64_t rows, int64_t cols, int64
  * stack LayerNorm and quantization are one kernel; the residual stream and
  * the LayerNorm statistics stay fp32). x: fp32 [rows, cols], leading
  * dimension ld elements (the residual stream); gamma, beta: fp32 [cols];
- * eps >= 0. Each row becomes
+ * eps finite and > 0 (so that a constant row, var = 0, gives y = beta).
+ * Each row becomes
  *   y = (x - mu) / sqrt(var + eps) * gamma + beta   (mu, var: the row's mean
  *       and biased variance, computed in fp32),
  * rounded to bf16, and codes / scales receive what mx_quantize of that bf16

@@ -178,6 +178,7 @@ def test_gemm_gelu_quantize_validation(L, args, status, msg):
     ((ALIGNED, 4, 8, 8, None, ALIGNED, 1e-6, ALIGNED, ALIGNED, 1), 1, "null"),
     ((ALIGNED, 4, 8, 8, ALIGNED, ALIGNED, -1.0, ALIGNED, ALIGNED, 1), 1, "eps"),
     ((ALIGNED, 4, 8, 8, ALIGNED, ALIGNED, float("nan"), ALIGNED, ALIGNED, 2), 1, "eps"),
+    ((ALIGNED, 4, 8, 8, ALIGNED, ALIGNED, 0.0, ALIGNED, ALIGNED, 1), 1, "eps"),
     ((ALIGNED + 2, 4, 8, 8, ALIGNED, ALIGNED, 1e-6, ALIGNED, ALIGNED, 1), 3, "4-byte"),
     ((ALIGNED, 4, 8, 8, ALIGNED, ALIGNED, 1e-6, ALIGNED + 4, ALIGNED, 1), 3, "16-byte"),
     ((ALIGNED, 1 << 22, 1 << 10, 1 << 10, ALIGNED, ALIGNED, 1e-6, ALIGNED, ALIGNED, 1), 2, "2 GiB"),
