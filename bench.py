@@ -1,34 +1,43 @@
 """Throughput of the block-scaled quantize-then-GEMM hot path on one MI355X.
 
-One step = one pass of the whole path over one batch: for every ViT block
-and every linear layer (qkv, proj, fc1, fc2) quantize the activation and the
-weight row-wise (both in one mx_quantize_batch launch) and run the
-block-scaled GEMM with its bias epilogue (mx_gemm). The *_fc1gelu stacks
-let fc1's epilogue write fc2's operand (mx_gemm_gelu_quantize); the *_lnq_*
-stacks also take qkv's and fc1's inputs as the LayerNorm of an fp32
-residual stream, normalized and quantized in one launch
-(mx_layernorm_quantize). For the NVFP4 training workload a step is the fc1/fc2
-pair's fprop, dgrad and wgrad GEMMs with every operand quantized along its
-own K axis (row and transposed copies from one read with mx_quantize_dual,
-tensor amax included).
+One step = one pass of the whole path over one batch. For the forward
+stacks: for every ViT block and every linear layer (qkv, proj, fc1, fc2)
+quantize the activation and the weight row-wise (both in one
+mx_quantize_batch launch) and run the block-scaled GEMM with its bias
+epilogue (mx_gemm). The *_fc1gelu stacks let fc1's epilogue write fc2's
+operand (mx_gemm_gelu_quantize); the *_lnq_* stacks also take qkv's and
+fc1's inputs as the LayerNorm of an fp32 residual stream, normalized and
+quantized in one launch (mx_layernorm_quantize). For the training workloads
+a step is the fprop, dgrad and wgrad GEMMs of the fc1/fc2 pair, or of all
+four linears of a ViT block (twelve GEMMs), with every operand quantized
+along its own K axis (row and transposed copies from one read with
+mx_quantize_dual, or mx_quantize_dual_sr for stochastically rounded
+gradients).
 
 Inputs are seeded synthetic bf16 tensors (the value recipe of
 block_scaled_precision_mx_amd.workloads) generated on the device before the
-timed region; every block has its own tensors so repeated launches cannot be
-served from the 256 MB Infinity Cache. The JSON line reports whole-step
-throughput in GEMM TFLOP/s (the GEMM flops of the step over the step time,
-quantization included), the dominant GEMM kernel against the MFMA roofline
-(per-launch HIP events on the stream the kernels run on), the quantizer's
-algorithmic bandwidth, and the CPU oracle on a bounded sample of the same
-workload.
+timed region; the stack's blocks, and the training workloads' alternating
+input sets, have tensors of their own, so consecutive launches cannot be
+served from the 256 MB Infinity Cache.
+
+The JSON line reports, for the headline workload (the ViT-L MXFP8 forward
+stack), whole-step throughput in GEMM TFLOP/s (the GEMM flops of the step
+over the step time, quantization included); the dominant GEMM kernel
+configuration against the MFMA roofline, its average launch duration taken
+from HIP events around every launch of an instrumented replay of the same
+steps on the stream the kernels run on; the quantizer's algorithmic
+bandwidth; the CPU oracle on a bounded sample of the same workload; and,
+under "configs", the same figures for every other configuration.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
+from dataclasses import dataclass
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -41,12 +50,25 @@ PEAK_HBM_GBS = 8000.0
 QUANT_BYTES = {"mxfp8": 2 + 1 + 1 / 32, "mxfp4": 2 + 0.5 + 1 / 32, "nvfp4": 2 + 0.5 + 1 / 16}
 NVFP4_AMAX_BYTES = 2.0
 
-
+HEADLINE = "vitl16_mxfp8_fwd_stack"
+# the other configurations measured in the same run (compact records)
+EXTRA_CONFIGS = ["single_mxfp8_256x768x768", "vitb16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack",
+                 "vitl16_nvfp4_fc1fc2_train", "vitl16_mxfp8_block_train", "vitl16_p3_block_train"]
 WORKLOADS = ["vitl16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack", "vitb16_mxfp8_fwd_stack",
              "vitl16_mxfp8_fwd_stack_fc1gelu", "vitl16_mxfp4_fwd_stack_fc1gelu",
              "vitl16_mxfp8_fwd_stack_lnq_fc1gelu", "vitl16_mxfp4_fwd_stack_lnq_fc1gelu",
              "vitl16_nvfp4_fc1fc2_train", "vitl16_nvfp4_fc1fc2_train_srgrad", "vitl16_mxfp8_fc1fc2_train",
-             "single_mxfp8_256x768x768"]
+             "vitl16_mxfp8_block_train", "vitl16_p3_block_train", "single_mxfp8_256x768x768"]
+# the pages' own figures for the same kind of work (another GPU, another
+# batch): context only, never a ratio
+PAGES_CONTEXT = {
+    "vitl16_mxfp8_block_train": "README section 5.4: the 12 GEMMs of one ViT-L block take 1042 us in MXFP8 on an "
+                                "RTX 5090 (2585 us in BF16), plus 203 us of quantization; batch not stated",
+    "vitl16_p3_block_train": "README section 5.4: backbone dgrad / wgrad GEMM time per step drops from 8.4-8.8 ms "
+                             "(MXFP8) to 4.5-4.6 ms (NVFP4) on an RTX 5090",
+}
+# input sets the training workloads alternate between, one per step
+TRAIN_SETS = 2
 
 
 def parse():
@@ -54,7 +76,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="vitl16_mxfp8_fwd_stack", choices=WORKLOADS)
+    p.add_argument("--workload", default=HEADLINE, choices=WORKLOADS)
+    p.add_argument("--only", action="store_true", help="measure --workload only (no other configurations)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="first run one elementwise bf16 kernel (negation) reading and writing this many "
@@ -62,60 +85,106 @@ def parse():
     return p.parse_args()
 
 
+# ------------------------------------------------------------------ GEMM lists
+
+@dataclass(frozen=True)
+class GemmSpec:
+    """One GEMM launch of a workload's step: C[m, n] from A [m, k], B [n, k]."""
+    label: str
+    m: int
+    n: int
+    k: int
+    fmt: str
+    epilogue: str = "c"          # "c": bf16 C out; "gelu_quant": fc1 writing fc2's operand
+    out: str = "bf16"
+
+
+def workload_gemms(name):
+    """Every GEMM of one step of the workload, in launch order (needs no GPU)."""
+    from block_scaled_precision_mx_amd import workloads as W
+    specs = []
+    if name in W.STACKS:
+        st = W.STACKS[name]
+        for _ in range(st.blocks):
+            for lin in st.linears:
+                fused = st.fuse_fc1_gelu and lin.name == "fc1"
+                specs.append(GemmSpec(f"gemm_{lin.name}" + ("_gelu_quant" if fused else ""), st.m, lin.n, lin.k,
+                                      st.fmt, "gelu_quant" if fused else "c", "q" if fused else "bf16"))
+    elif name in W.TRAIN_PAIRS:
+        tp = W.TRAIN_PAIRS[name]
+        for lin, n_out, k_in in (("fc1", tp.mlp, tp.hidden), ("fc2", tp.hidden, tp.mlp)):
+            specs.append(GemmSpec(f"gemm_{lin}_fprop", tp.m, n_out, k_in, tp.fmt))
+            specs.append(GemmSpec(f"gemm_{lin}_dgrad", tp.m, k_in, n_out, tp.fmt))
+            specs.append(GemmSpec(f"gemm_{lin}_wgrad", n_out, k_in, tp.m, tp.fmt))
+    elif name in W.BLOCK_TRAINS:
+        bt = W.BLOCK_TRAINS[name]
+        lins = bt.linears()
+        for _ in range(bt.blocks):
+            for lin in lins:
+                specs.append(GemmSpec(f"gemm_{lin.name}_fprop", bt.m, lin.n, lin.k, bt.fwd_fmt))
+            for lin in reversed(lins):
+                specs.append(GemmSpec(f"gemm_{lin.name}_dgrad", bt.m, lin.k, lin.n, bt.bwd_fmt))
+                specs.append(GemmSpec(f"gemm_{lin.name}_wgrad", lin.n, lin.k, bt.m, bt.bwd_fmt))
+    else:
+        raise KeyError(name)
+    return specs
+
+
+def gemm_plan(spec: GemmSpec) -> str:
+    from block_scaled_precision_mx_amd import api
+    return api.gemm_plan(spec.m, spec.n, spec.k, spec.fmt) + ("+gelu+quant" if spec.epilogue == "gelu_quant" else "")
+
+
 # ------------------------------------------------------------------ workloads
 
 class Op:
-    """One launch of the path: a quantization or a GEMM (plan = kernel
-    configuration). `cold`: the same launch on other input tensors of the
-    same shape, used only to time the launch with inputs that are not cached."""
+    """One launch of the path: a quantization (nbytes algorithmic) or a GEMM
+    (flops, spec, plan = kernel configuration)."""
 
-    def __init__(self, kind, fn, flops=0.0, nbytes=0.0, label="", plan=None, cold=()):
-        self.kind, self.fn, self.flops, self.nbytes, self.label, self.plan = kind, fn, flops, nbytes, label, plan
-        self.cold = list(cold)
+    def __init__(self, kind, fn, label, flops=0.0, nbytes=0.0, spec=None):
+        self.kind, self.fn, self.label, self.flops, self.nbytes, self.spec = kind, fn, label, flops, nbytes, spec
+        self.plan = gemm_plan(spec) if spec is not None else None
 
 
-# input bytes of a group of cold launches made of clones: twice the 256 MB
-# Infinity Cache, so the group's inputs come from HBM
-COLD_BYTES = 512 << 20
+def _empty_q(rows, cols, fmt, axis, dev):
+    import torch
+    from block_scaled_precision_mx_amd import api
+    stored, length = (rows, cols) if axis == "row" else (cols, rows)
+    return api.Quantized(torch.empty(api.codes_bytes(rows, cols, fmt, axis), dtype=torch.uint8, device=dev),
+                         torch.empty(api.scales_bytes(rows, cols, fmt, axis), dtype=torch.uint8, device=dev),
+                         fmt, stored, length)
+
+
+def _gemm_op(ops, spec, a, b, bias, dev):
+    import torch
+    from block_scaled_precision_mx_amd import api
+    out = torch.empty((spec.m, spec.n), dtype=torch.bfloat16, device=dev)
+    ops.append(Op("gemm", lambda: api.mx_gemm(a, b, bias, "bf16", out), spec.label,
+                  flops=2.0 * spec.m * spec.n * spec.k, spec=spec))
 
 
 def build_stack(stack, dev):
-    import torch
+    """A step of a forward stack: a list of ops."""
     from block_scaled_precision_mx_amd import api
     from block_scaled_precision_mx_amd import workloads as W
 
+    specs = iter(workload_gemms(stack.name))
     ops = []
     fmt = stack.fmt
     for blk in range(stack.blocks):
         fused_out = None            # fc2's operand as fc1's fused epilogue writes it
         for lin in stack.linears:
-            if fused_out is not None and lin.name == "fc2":
-                # fc2's A operand comes from fc1's epilogue: no activation tensor, no quantization
-                w = W.torch_normal((lin.n, lin.k), W.seed(stack.wid, blk, lin.w_id), W.W_STD, dev)
-                bias = W.torch_normal((lin.n,), W.seed(stack.wid, blk, lin.bias_id), W.BIAS_STD, dev)
-                qw = api.Quantized(torch.empty(api.codes_bytes(lin.n, lin.k, fmt), dtype=torch.uint8, device=dev),
-                                   torch.empty(api.scales_bytes(lin.n, lin.k, fmt), dtype=torch.uint8, device=dev),
-                                   fmt, lin.n, lin.k)
-                out = torch.empty((stack.m, lin.n), dtype=torch.bfloat16, device=dev)
-                # fc2's weight is the only tensor of this launch: two clones per
-                # block make its cold-timing group larger than the Infinity Cache
-                ops.append(Op("quant", lambda w=w, qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales),
-                              nbytes=QUANT_BYTES[fmt] * w.numel(), label=f"quant_{lin.name}_w",
-                              cold=[lambda w=w.clone(), qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales)
-                                    for _ in range(2)]))
-                ops.append(Op("gemm", lambda qa=fused_out, qw=qw, bias=bias, out=out: api.mx_gemm(qa, qw, bias, "bf16", out),
-                              flops=2.0 * stack.m * lin.n * lin.k, label=f"gemm_{lin.name}",
-                              plan=api.gemm_plan(stack.m, lin.n, lin.k, fmt)))
-                continue
+            spec = next(specs)
             w = W.torch_normal((lin.n, lin.k), W.seed(stack.wid, blk, lin.w_id), W.W_STD, dev)
             bias = W.torch_normal((lin.n,), W.seed(stack.wid, blk, lin.bias_id), W.BIAS_STD, dev)
-            qa = api.Quantized(torch.empty(api.codes_bytes(stack.m, lin.k, fmt), dtype=torch.uint8, device=dev),
-                               torch.empty(api.scales_bytes(stack.m, lin.k, fmt), dtype=torch.uint8, device=dev),
-                               fmt, stack.m, lin.k)
-            qw = api.Quantized(torch.empty(api.codes_bytes(lin.n, lin.k, fmt), dtype=torch.uint8, device=dev),
-                               torch.empty(api.scales_bytes(lin.n, lin.k, fmt), dtype=torch.uint8, device=dev),
-                               fmt, lin.n, lin.k)
-            out = torch.empty((stack.m, lin.n), dtype=torch.bfloat16, device=dev)
+            qw = _empty_q(lin.n, lin.k, fmt, "row", dev)
+            if fused_out is not None and lin.name == "fc2":
+                # fc2's A operand comes from fc1's epilogue: only the weight is quantized
+                ops.append(Op("quant", lambda w=w, qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales),
+                              f"quant_{lin.name}_w", nbytes=QUANT_BYTES[fmt] * w.numel()))
+                _gemm_op(ops, spec, fused_out, qw, bias, dev)
+                continue
+            qa = _empty_q(stack.m, lin.k, fmt, "row", dev)
             if stack.ln_quant and lin.name in ("qkv", "fc1"):
                 # the input is the LayerNorm of the fp32 residual stream, normalized
                 # and quantized in one launch; the weight in a launch of its own
@@ -123,106 +192,258 @@ def build_stack(stack, dev):
                 gamma, beta = W.torch_ln_params(lin.k, W.seed(stack.wid, blk, 50 + lin.a_id), dev)
                 ops.append(Op("quant", lambda x=x, g=gamma, b=beta, qa=qa:
                               api.mx_layernorm_quantize(x, g, b, W.LN_EPS, fmt, out=qa),
-                              nbytes=(4 + QUANT_BYTES[fmt] - 2) * x.numel(), label=f"lnquant_{lin.name}_act"))
+                              f"lnquant_{lin.name}_act", nbytes=(4 + QUANT_BYTES[fmt] - 2) * x.numel()))
                 ops.append(Op("quant", lambda w=w, qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales),
-                              nbytes=QUANT_BYTES[fmt] * w.numel(), label=f"quant_{lin.name}_w",
-                              cold=[lambda w=w.clone(), qw=qw: api.mx_quantize(w, fmt, "row", qw.codes, qw.scales)
-                                    for _ in range(2)]))
+                              f"quant_{lin.name}_w", nbytes=QUANT_BYTES[fmt] * w.numel()))
             else:
                 a = W.torch_activation((stack.m, lin.k), W.seed(stack.wid, blk, lin.a_id), dev,
                                        gelu=lin.a_kind == "gelu")
                 # the GEMM's two operands in one launch (mx_quantize_batch), just before it
                 ops.append(Op("quant", lambda a=a, w=w, qa=qa, qw=qw: api.mx_quantize_batch([a, w], fmt, out=[qa, qw]),
-                              nbytes=QUANT_BYTES[fmt] * (a.numel() + w.numel()), label=f"quant_{lin.name}_act_w"))
-            if stack.fuse_fc1_gelu and lin.name == "fc1":
-                del out
-                fused_out = api.Quantized(
-                    torch.empty(api.codes_bytes(stack.m, lin.n, fmt), dtype=torch.uint8, device=dev),
-                    torch.empty(api.scales_bytes(stack.m, lin.n, fmt), dtype=torch.uint8, device=dev),
-                    fmt, stack.m, lin.n)
+                              f"quant_{lin.name}_act_w", nbytes=QUANT_BYTES[fmt] * (a.numel() + w.numel())))
+            if spec.epilogue == "gelu_quant":
+                fused_out = _empty_q(stack.m, lin.n, fmt, "row", dev)
                 ops.append(Op("gemm", lambda qa=qa, qw=qw, bias=bias, q=fused_out:
-                              api.mx_gemm_gelu_quantize(qa, qw, bias, out=q),
-                              flops=2.0 * stack.m * lin.n * lin.k, label=f"gemm_{lin.name}_gelu_quant",
-                              plan=api.gemm_plan(stack.m, lin.n, lin.k, fmt) + "+gelu+quant"))
+                              api.mx_gemm_gelu_quantize(qa, qw, bias, out=q), spec.label,
+                              flops=2.0 * spec.m * spec.n * spec.k, spec=spec))
                 continue
-            ops.append(Op("gemm", lambda qa=qa, qw=qw, bias=bias, out=out: api.mx_gemm(qa, qw, bias, "bf16", out),
-                          flops=2.0 * stack.m * lin.n * lin.k, label=f"gemm_{lin.name}",
-                          plan=api.gemm_plan(stack.m, lin.n, lin.k, fmt)))
-    return ops
+            _gemm_op(ops, spec, qa, qw, bias, dev)
+    return [ops]
+
+
+def _dual_bytes(fmt):
+    """Bytes per element of one dual quantization: the read, both copies'
+    codes and scales, and for NVFP4 the amax pass (s_t from the tensor's own
+    amax, as the configuration defines)."""
+    return 2.0 + 2 * (QUANT_BYTES[fmt] - 2.0) + (NVFP4_AMAX_BYTES if fmt == "nvfp4" else 0.0)
+
+
+def _quant_dual(ops, label, t, fmt, dev, sr_seed=None):
+    """Both copies of t (row, and transposed for the other GEMMs) from one
+    read; returns (row copy, col copy)."""
+    from block_scaled_precision_mx_amd import api
+    r, c = t.shape
+    row, col = _empty_q(r, c, fmt, "row", dev), _empty_q(r, c, fmt, "col", dev)
+    if sr_seed is not None:
+        fn = lambda: api.mx_quantize_dual_sr(t, sr_seed, None, 1.0, out=(row, col))   # noqa: E731
+    else:
+        fn = lambda: api.mx_quantize_dual(t, fmt, None, 1.0, out=(row, col))          # noqa: E731
+    ops.append(Op("quant", fn, label, nbytes=_dual_bytes(fmt) * t.numel()))
+    return row, col
 
 
 def build_train(tp, dev):
-    import torch
-    from block_scaled_precision_mx_amd import api
+    """TRAIN_SETS steps of the fc1/fc2 training pair, each on its own tensors."""
     from block_scaled_precision_mx_amd import workloads as W
 
     fmt = tp.fmt
-    S = lambda tid: W.seed(tp.wid, 0, tid)   # noqa: E731
-    X = W.torch_activation((tp.m, tp.hidden), S(tp.X), dev)
-    H = W.torch_activation((tp.m, tp.mlp), S(tp.H), dev, gelu=True)
-    dY1 = W.torch_normal((tp.m, tp.mlp), S(tp.DY1), W.GRAD_STD, dev)
-    dY2 = W.torch_normal((tp.m, tp.hidden), S(tp.DY2), W.GRAD_STD, dev)
-    W1 = W.torch_normal((tp.mlp, tp.hidden), S(tp.W1), W.W_STD, dev)
-    W2 = W.torch_normal((tp.hidden, tp.mlp), S(tp.W2), W.W_STD, dev)
-    b1 = W.torch_normal((tp.mlp,), S(tp.B1), W.BIAS_STD, dev)
-    b2 = W.torch_normal((tp.hidden,), S(tp.B2), W.BIAS_STD, dev)
+    sets = []
+    for s in range(TRAIN_SETS):
+        S = lambda tid: W.seed(tp.wid, s, tid)   # noqa: E731
+        X = W.torch_activation((tp.m, tp.hidden), S(tp.X), dev)
+        H = W.torch_activation((tp.m, tp.mlp), S(tp.H), dev, gelu=True)
+        dY1 = W.torch_normal((tp.m, tp.mlp), S(tp.DY1), W.GRAD_STD, dev)
+        dY2 = W.torch_normal((tp.m, tp.hidden), S(tp.DY2), W.GRAD_STD, dev)
+        W1 = W.torch_normal((tp.mlp, tp.hidden), S(tp.W1), W.W_STD, dev)
+        W2 = W.torch_normal((tp.hidden, tp.mlp), S(tp.W2), W.W_STD, dev)
+        b1 = W.torch_normal((tp.mlp,), S(tp.B1), W.BIAS_STD, dev)
+        b2 = W.torch_normal((tp.hidden,), S(tp.B2), W.BIAS_STD, dev)
+        sr = tp.sr_seed if tp.sr_grads else None
+        specs = iter(workload_gemms(tp.name))
+        ops = []
+        for x, w, dy, bias, lin in ((X, W1, dY1, b1, "fc1"), (H, W2, dY2, b2, "fc2")):
+            x_row, x_col = _quant_dual(ops, f"quant_{lin}_x_rowcol", x, fmt, dev)
+            w_row, w_col = _quant_dual(ops, f"quant_{lin}_w_rowcol", w, fmt, dev)
+            _gemm_op(ops, next(specs), x_row, w_row, bias, dev)                       # fprop
+            dy_row, dy_col = _quant_dual(ops, f"quant_{lin}_dy_rowcol", dy, fmt, dev, sr)
+            _gemm_op(ops, next(specs), dy_row, w_col, None, dev)                      # dgrad
+            _gemm_op(ops, next(specs), dy_col, x_col, None, dev)                      # wgrad
+        sets.append(ops)
+    return sets
+
+
+def build_block_train(bt, dev):
+    """One step = the twelve GEMMs of `bt.blocks` ViT blocks with their
+    quantizations, in the order a training step runs them: the forward GEMMs
+    (fprop), then per linear in reverse order the backward ones (dgrad,
+    wgrad). FINAL (one format): each of X, W and dY is dual-quantized once
+    (X and W when the forward pass uses them, dY in the backward pass). P3
+    (MXFP8 forward, NVFP4 backward): X and W are row-quantized in MXFP8 for
+    fprop (one batch launch) and quantized again along the other axis in
+    NVFP4 for the backward GEMMs; dY gets both NVFP4 copies, stochastically
+    rounded, from one read."""
+    from block_scaled_precision_mx_amd import api
+    from block_scaled_precision_mx_amd import workloads as W
+
+    specs = iter(workload_gemms(bt.name))
+    lins = bt.linears()
+    ff, bf = bt.fwd_fmt, bt.bwd_fmt
+    sr = bt.sr_seed if bt.sr_grads else None
     ops = []
-    q = {}
+    for blk in range(bt.blocks):
+        S = lambda tid: W.seed(bt.wid, blk, tid)   # noqa: E731
+        saved = []
+        for i, lin in enumerate(lins):                       # forward
+            xi, wi, bi, di = bt.ids(i)
+            x = W.torch_activation((bt.m, lin.k), S(xi), dev, gelu=lin.a_kind == "gelu")
+            w = W.torch_normal((lin.n, lin.k), S(wi), W.W_STD, dev)
+            bias = W.torch_normal((lin.n,), S(bi), W.BIAS_STD, dev)
+            dy = W.torch_normal((bt.m, lin.n), S(di), W.GRAD_STD, dev)
+            if ff == bf:
+                x_row, x_col = _quant_dual(ops, f"quant_{lin.name}_x_rowcol", x, ff, dev)
+                w_row, w_col = _quant_dual(ops, f"quant_{lin.name}_w_rowcol", w, ff, dev)
+            else:
+                x_row, w_row = _empty_q(bt.m, lin.k, ff, "row", dev), _empty_q(lin.n, lin.k, ff, "row", dev)
+                ops.append(Op("quant", lambda x=x, w=w, qa=x_row, qw=w_row:
+                              api.mx_quantize_batch([x, w], ff, out=[qa, qw]), f"quant_{lin.name}_x_w",
+                              nbytes=QUANT_BYTES[ff] * (x.numel() + w.numel())))
+                x_col, w_col = None, None
+            _gemm_op(ops, next(specs), x_row, w_row, bias, dev)
+            saved.append((lin, x, w, dy, x_col, w_col))
+        for lin, x, w, dy, x_col, w_col in reversed(saved):  # backward
+            if x_col is None:
+                # the backward format's copies along the token / output axis
+                x_col, w_col = _empty_q(bt.m, lin.k, bf, "col", dev), _empty_q(lin.n, lin.k, bf, "col", dev)
+                amax = 2.0 if bf == "nvfp4" else 0.0
+                ops.append(Op("quant", lambda x=x, q=x_col: api.mx_quantize(x, bf, "col", q.codes, q.scales),
+                              f"quant_{lin.name}_x_col", nbytes=(QUANT_BYTES[bf] + amax) * x.numel()))
+                ops.append(Op("quant", lambda w=w, q=w_col: api.mx_quantize(w, bf, "col", q.codes, q.scales),
+                              f"quant_{lin.name}_w_col", nbytes=(QUANT_BYTES[bf] + amax) * w.numel()))
+            dy_row, dy_col = _quant_dual(ops, f"quant_{lin.name}_dy_rowcol", dy, bf, dev, sr)
+            _gemm_op(ops, next(specs), dy_row, w_col, None, dev)       # dgrad: dX = dY W
+            _gemm_op(ops, next(specs), dy_col, x_col, None, dev)       # wgrad: dW = dY^T X
+    return [ops]
 
-    # bytes per element of one dual quantization: the read, both copies'
-    # codes and scales, and for NVFP4 the amax pass (s_t from the tensor's
-    # own amax, as the config defines)
-    dual_bytes = 2.0 + 2 * (QUANT_BYTES[fmt] - 2.0) + (NVFP4_AMAX_BYTES if fmt == "nvfp4" else 0.0)
 
-    def quant_dual(name, t, sr=False):
-        """Both copies of t (row, and transposed for the other GEMMs) from one
-        read (mx_quantize_dual; mx_quantize_dual_sr for stochastically
-        rounded gradients)."""
-        r, c = t.shape
-        bufs = []
-        for axis, rows, length in (("row", r, c), ("col", c, r)):
-            bufs.append(api.Quantized(torch.empty(api.codes_bytes(r, c, fmt, axis), dtype=torch.uint8, device=dev),
-                                      torch.empty(api.scales_bytes(r, c, fmt, axis), dtype=torch.uint8, device=dev),
-                                      fmt, rows, length))
-        q[name + "_row"], q[name + "_col"] = bufs
+def build(name, dev):
+    """(step op lists, description) of a workload; the GEMMs built are checked
+    against workload_gemms."""
+    from block_scaled_precision_mx_amd import workloads as W
+    if name in W.STACKS:
+        wl = W.STACKS[name]
+        sets = build_stack(wl, dev)
+        config = {"workload": wl.name, "M": wl.m, "hidden": wl.hidden, "mlp": wl.mlp, "blocks": wl.blocks,
+                  "tokens_per_image": W.TOKENS, "batch": wl.m // W.TOKENS, "format": wl.fmt,
+                  "gemms_per_block": [f"{l.name} {l.n}x{l.k}" for l in wl.linears]}
+        peak_key = wl.fmt
+    elif name in W.TRAIN_PAIRS:
+        wl = W.TRAIN_PAIRS[name]
+        sets = build_train(wl, dev)
+        config = {"workload": wl.name, "M": wl.m, "hidden": wl.hidden, "mlp": wl.mlp, "tokens_per_image": W.TOKENS,
+                  "batch": wl.m // W.TOKENS, "format": wl.fmt, "gemms": "fc1/fc2 fprop+dgrad+wgrad",
+                  "quantizations": "6 tensors, row and transposed copies from one read each",
+                  "grad_rounding": "stochastic (Philox4x64-10)" if wl.sr_grads else "nearest-even",
+                  "input_sets": TRAIN_SETS}
+        peak_key = "fp16" if wl.fmt == "nvfp4" else wl.fmt
+    else:
+        wl = W.BLOCK_TRAINS[name]
+        sets = build_block_train(wl, dev)
+        config = {"workload": wl.name, "M": wl.m, "hidden": wl.hidden, "mlp": wl.mlp, "blocks": wl.blocks,
+                  "tokens_per_image": W.TOKENS, "batch": wl.m // W.TOKENS, "fprop_format": wl.fwd_fmt,
+                  "dgrad_wgrad_format": wl.bwd_fmt, "gemms_per_block": 12,
+                  "grad_rounding": "stochastic (Philox4x64-10)" if wl.sr_grads else "nearest-even"}
+        peak_key = "fp16" if wl.bwd_fmt == "nvfp4" else wl.fwd_fmt
+    want = [(s.label, s.m, s.n, s.k, s.fmt) for s in workload_gemms(name)]
+    for ops in sets:
+        got = [(o.spec.label, o.spec.m, o.spec.n, o.spec.k, o.spec.fmt) for o in ops if o.kind == "gemm"]
+        if got != want:
+            raise RuntimeError(f"{name}: built GEMMs differ from workload_gemms")
+    return sets, config, peak_key
 
-        def make_fn(src):
-            if sr:
-                return lambda: api.mx_quantize_dual_sr(src, tp.sr_seed, None, 1.0, out=(bufs[0], bufs[1]))
-            return lambda: api.mx_quantize_dual(src, fmt, None, 1.0, out=(bufs[0], bufs[1]))
-        # clones of t for cold timing only (the step itself reads t)
-        copies = min(64, -(-COLD_BYTES // (2 * t.numel()))) - 1
-        ops.append(Op("quant", make_fn(t), nbytes=dual_bytes * t.numel(), label=f"quant_{name}_rowcol",
-                      cold=[make_fn(t.clone()) for _ in range(copies)]))
 
-    def gemm(name, a, b, bias, m, n, k):
-        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        ops.append(Op("gemm", lambda: api.mx_gemm(q[a], q[b], bias, "bf16", out), flops=2.0 * m * n * k,
-                      label=f"gemm_{name}", plan=api.gemm_plan(m, n, k, fmt)))
+# ------------------------------------------------------------------ timing
 
-    # fc1: fprop X W1^T, dgrad dY1 W1, wgrad dY1^T X
-    quant_dual("X", X); quant_dual("W1", W1)
-    gemm("fc1_fprop", "X_row", "W1_row", b1, tp.m, tp.mlp, tp.hidden)
-    quant_dual("dY1", dY1, sr=tp.sr_grads)
-    gemm("fc1_dgrad", "dY1_row", "W1_col", None, tp.m, tp.hidden, tp.mlp)
-    gemm("fc1_wgrad", "dY1_col", "X_col", None, tp.mlp, tp.hidden, tp.m)
-    # fc2: fprop H W2^T, dgrad dY2 W2, wgrad dY2^T H
-    quant_dual("H", H); quant_dual("W2", W2)
-    gemm("fc2_fprop", "H_row", "W2_row", b2, tp.m, tp.hidden, tp.mlp)
-    quant_dual("dY2", dY2, sr=tp.sr_grads)
-    gemm("fc2_dgrad", "dY2_row", "W2_col", None, tp.m, tp.mlp, tp.hidden)
-    gemm("fc2_wgrad", "dY2_col", "H_col", None, tp.hidden, tp.mlp, tp.m)
-    return ops
+def measure(sets, steps, warmup, stream):
+    """ms per step over `steps` timed steps, then per-op average durations
+    from an instrumented replay of as many steps (HIP events around every
+    launch, on the stream the kernels run on). Step s runs input set
+    s % len(sets)."""
+    import torch
+
+    def step(s):
+        for op in sets[s % len(sets)]:
+            op.fn()
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for s in range(steps):
+        step(s)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+
+    per_op = [[0.0] * len(ops) for ops in sets]
+    runs = [0] * len(sets)
+    for s in range(steps):
+        ops = sets[s % len(sets)]
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+        for (e0, e1), op in zip(ev, ops):
+            e0.record(stream)
+            op.fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        for i, (e0, e1) in enumerate(ev):
+            per_op[s % len(sets)][i] += e0.elapsed_time(e1)
+        runs[s % len(sets)] += 1
+    timed = []
+    for si, ops in enumerate(sets):
+        if runs[si]:
+            timed += [(op, t / runs[si]) for op, t in zip(ops, per_op[si])]
+    return ms_per_step, timed, len(sets)
+
+
+def summarize(timed, n_sets):
+    """Per-label, per-kernel-configuration and quantization figures from the
+    instrumented replay. `timed` holds (op, average duration in ms) for the
+    ops of all n_sets input sets; per-step figures divide by n_sets."""
+    by_label, plans = {}, {}
+    gemm_ms = quant_ms = quant_bytes = gemm_flops = 0.0
+    for op, t in timed:
+        d = by_label.setdefault(op.label, {"ms": 0.0, "n": 0, "flops": 0.0, "bytes": 0.0})
+        d["ms"] += t
+        d["n"] += 1
+        d["flops"] += op.flops
+        d["bytes"] += op.nbytes
+        if op.kind == "gemm":
+            gemm_ms += t
+            gemm_flops += op.flops
+            p = plans.setdefault(op.plan, {"ms": 0.0, "flops": 0.0, "n": 0})
+            p["ms"] += t
+            p["flops"] += op.flops
+            p["n"] += 1
+        else:
+            quant_ms += t
+            quant_bytes += op.nbytes
+    breakdown = {}
+    for lab, d in by_label.items():
+        e = {"us_per_launch": round(1e3 * d["ms"] / d["n"], 2), "launches_per_step": d["n"] // n_sets}
+        if d["flops"]:
+            e["tflops"] = round(d["flops"] / (d["ms"] * 1e-3) / 1e12, 1)
+        if d["bytes"]:
+            e["gbps"] = round(d["bytes"] / (d["ms"] * 1e-3) / 1e9, 1)
+        breakdown[lab] = e
+    kernels = {p: {"launches_per_step": d["n"] // n_sets, "avg_launch_us": round(1e3 * d["ms"] / d["n"], 2),
+                   "tflops": round(d["flops"] / (d["ms"] * 1e-3) / 1e12, 1), "ms_per_step": d["ms"] / n_sets,
+                   "flops_per_launch_avg": d["flops"] / d["n"]} for p, d in plans.items()}
+    quant = None
+    if quant_ms:
+        gbps = quant_bytes / (quant_ms * 1e-3) / 1e9
+        quant = {"gbps": round(gbps, 1), "peak_gbps": PEAK_HBM_GBS, "frac": round(gbps / PEAK_HBM_GBS, 4),
+                 "ms_per_step": round(quant_ms / n_sets, 4)}
+    return {"breakdown": breakdown, "kernels": kernels, "quant": quant,
+            "gemm_only_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1)}
 
 
 # ------------------------------------------------------------------ CPU oracle
 
 def cpu_baseline(workload_name, fmt):
     """The oracle as it stands on a bounded sample of the same workload: the
-    four linears of one ViT block at full M (one of the stack's blocks), or
-    the fc1 fprop GEMM of the training pair at full M; returns GEMM TFLOP/s of
-    quantize + dequantize + float64 GEMM."""
-    import numpy as np  # noqa: F401
+    four linears of one ViT block at full M (one of the stack's blocks);
+    returns GEMM TFLOP/s of quantize + dequantize + float64 GEMM."""
     from block_scaled_precision_mx_amd import workloads as W
     from oracle import gemm as G
     from oracle import quantize as Q
@@ -231,23 +452,16 @@ def cpu_baseline(workload_name, fmt):
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    if workload_name in W.TRAIN_PAIRS:
-        tp = W.TRAIN_PAIRS[workload_name]
-        rows = tp.m
-        shapes = [("fc1_fprop", tp.mlp, tp.hidden, "act")]
-        wid = tp.wid
-    else:
-        stack = W.STACKS[workload_name]
-        rows = stack.m
-        shapes = [(l.name, l.n, l.k, l.a_kind) for l in stack.linears]
-        wid = stack.wid
+        threads = 1
+    stack = W.STACKS[workload_name]
+    rows = stack.m
     gen = []
-    for i, (name, n, k, kind) in enumerate(shapes):
-        a = (W.np_gelu_activation if kind == "gelu" else W.np_activation)((rows, k), W.seed(wid, 0, 3 * i))
-        w = W.np_normal((n, k), W.seed(wid, 0, 3 * i + 1), W.W_STD)
-        b = W.np_normal((n,), W.seed(wid, 0, 3 * i + 2), W.BIAS_STD)
-        gen.append((a, w, b, n, k))
+    for lin in stack.linears:
+        a = (W.np_gelu_activation if lin.a_kind == "gelu" else W.np_activation)((rows, lin.k),
+                                                                                W.seed(stack.wid, 0, lin.a_id))
+        w = W.np_normal((lin.n, lin.k), W.seed(stack.wid, 0, lin.w_id), W.W_STD)
+        b = W.np_normal((lin.n,), W.seed(stack.wid, 0, lin.bias_id), W.BIAS_STD)
+        gen.append((a, w, b, lin.n, lin.k))
     t0 = time.perf_counter()
     flops = 0.0
     for a, w, b, n, k in gen:
@@ -255,28 +469,42 @@ def cpu_baseline(workload_name, fmt):
         G.gemm_ref(qa, qw, b)
         flops += 2.0 * rows * n * k
     dt = time.perf_counter() - t0
-    sample = f"{len(gen)} quantize+GEMM(s) of one block at full M: " + ", ".join(
-        f"{rows}x{n}x{k}" for _, _, _, n, k in gen)
+    sample = (f"the {len(gen)} quantize+GEMMs of one block at full M ("
+              + ", ".join(f"{rows}x{n}x{k}" for _, _, _, n, k in gen)
+              + "); quantization single-threaded numpy, GEMMs float64 BLAS")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 3)}
+            "sample": sample, "seconds": round(dt, 3), "host_cpus": os.cpu_count(),
+            "blas_threads": threads}
 
 
 # ------------------------------------------------------------------ traffic
 
 # the sources a kernel's machine code is built from (its file and the device
 # headers it includes); their hash ties a counter summary to one build
-_DEVICE_HEADERS = ["block_scaled_precision_mx_amd/csrc/gemm_common.h", "block_scaled_precision_mx_amd/csrc/mx_device.h"]
-KERNEL_SOURCES = {"gemm_mx_kernel": ["block_scaled_precision_mx_amd/csrc/gemm_mx.hip"] + _DEVICE_HEADERS,
-                  "gemm_nv_kernel": ["block_scaled_precision_mx_amd/csrc/gemm_nv.hip"] + _DEVICE_HEADERS}
+_CSRC = "block_scaled_precision_mx_amd/csrc/"
+_DEVICE_HEADERS = [_CSRC + "gemm_common.h", _CSRC + "mx_device.h"]
+KERNEL_SOURCES = {"gemm_mx_kernel": [_CSRC + "gemm_mx.hip"] + _DEVICE_HEADERS,
+                  "gemm_nv_kernel": [_CSRC + "gemm_nv.hip"] + _DEVICE_HEADERS}
 
 
 def source_sha256(kernel):
-    import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel.split("<")[0]]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def library_sha256():
+    """Hash of every source the library is built from (ties a record to a build)."""
+    h = hashlib.sha256()
+    files = sorted(os.listdir(os.path.join(ROOT, _CSRC)))
+    for name in files + ["../../include/mx.h"]:
+        p = os.path.join(ROOT, _CSRC, name)
+        if os.path.isfile(p) and not name.endswith((".so", ".o")):
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):
@@ -309,6 +537,52 @@ def measured_traffic(kernel, workload):
 
 # ------------------------------------------------------------------ main
 
+def run_workload(name, steps, warmup, dev):
+    """Build, time and summarize one workload; frees its buffers afterwards."""
+    import torch
+    from block_scaled_precision_mx_amd import workloads as W
+    sets, config, peak_key = build(name, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ms_per_step, timed, n_sets = measure(sets, steps, warmup, stream)
+    summ = summarize(timed, n_sets)
+    flops = sum(op.flops for op in sets[0])
+    dom = max(summ["kernels"], key=lambda p: summ["kernels"][p]["ms_per_step"])
+    d = summ["kernels"][dom]
+    achieved = d["flops_per_launch_avg"] / (d["avg_launch_us"] * 1e-6) / 1e12
+    peak = PEAK_TFLOPS[peak_key]
+    res = {"ms_per_step": ms_per_step, "value": flops / (ms_per_step * 1e-3) / 1e12, "config": config,
+           "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                        "traffic": measured_traffic(dom, name), "launches_per_step": d["launches_per_step"],
+                        "avg_launch_us": d["avg_launch_us"], "flops_per_launch_avg": d["flops_per_launch_avg"]},
+           "summary": summ, "fmt": config.get("format", config.get("fprop_format"))}
+    if name in W.BLOCK_TRAINS:
+        res["us_per_block"] = round(1e3 * ms_per_step / W.BLOCK_TRAINS[name].blocks, 1)
+    del sets, timed
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def compact(name, res):
+    """The record of a configuration other than the headline."""
+    s = res["summary"]
+    out = {"ms_per_step": round(res["ms_per_step"], 4), "tflops": round(res["value"], 1),
+           "gemm_only_tflops": s["gemm_only_tflops"],
+           "roofline": {k: res["roofline"][k] for k in ("kernel", "achieved", "peak", "frac", "avg_launch_us",
+                                                         "launches_per_step")},
+           "gemm_kernels": {p: {k: v for k, v in d.items() if k in ("launches_per_step", "avg_launch_us", "tflops")}
+                            for p, d in s["kernels"].items()}}
+    if s["quant"]:
+        out["quant"] = s["quant"]
+    if "us_per_block" in res:
+        out["us_per_block"] = res["us_per_block"]
+    if name in PAGES_CONTEXT:
+        out["pages_context"] = PAGES_CONTEXT[name]
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -317,31 +591,11 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
-    from block_scaled_precision_mx_amd import workloads as W
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    if args.workload in W.TRAIN_PAIRS:
-        wl = W.TRAIN_PAIRS[args.workload]
-        fmt = wl.fmt
-        ops = build_train(wl, dev)
-        gemm_peak_key = "fp16" if fmt == "nvfp4" else fmt
-        config = {"workload": wl.name, "M": wl.m, "hidden": wl.hidden, "mlp": wl.mlp, "tokens_per_image": W.TOKENS,
-                  "batch": wl.m // W.TOKENS, "format": fmt, "gemms": "fc1/fc2 fprop+dgrad+wgrad",
-                  "quantizations": "6 tensors, row and transposed copies from one read each",
-                  "grad_rounding": "stochastic (Philox4x64-10)" if wl.sr_grads else "nearest-even"}
-    else:
-        wl = W.STACKS[args.workload]
-        fmt = wl.fmt
-        ops = build_stack(wl, dev)
-        gemm_peak_key = fmt
-        config = {"workload": wl.name, "M": wl.m, "hidden": wl.hidden, "mlp": wl.mlp, "blocks": wl.blocks,
-                  "tokens_per_image": W.TOKENS, "batch": wl.m // W.TOKENS, "format": fmt,
-                  "gemms_per_block": [f"{l.name} {l.n}x{l.k}" for l in wl.linears]}
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
     if args.copy_probe_mb:
         n = args.copy_probe_mb * (1 << 20) // 2
         src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
@@ -351,133 +605,44 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step():
-        for op in ops:
-            op.fn()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region: K steps, events on the stream the kernels run on
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-
-    # per-launch durations on the same stream, several launches between one
-    # event pair so that the events' own overhead is spread over them.
-    # GEMMs: each launch repeated REPEAT times back to back. In the step their
-    # operands were written just before them, so they are cached there too
-    # (rocprofv3's trace of the in-step launches agrees within 2%).
-    # Quantizations: all launches of one label, each on an input no other
-    # launch of the group reads (the stack's blocks, or clones of the
-    # training tensors), more than the 256 MB Infinity Cache per group (428 MB
-    # for the smallest, ViT-B's proj), so the inputs come from HBM as they do
-    # in the step.
-    REPEAT = 10
-    groups = []                                   # (op indices, launches timed together)
-    quant_labels = {}
-    for i, op in enumerate(ops):
-        if op.kind == "quant":
-            quant_labels.setdefault(op.label, []).append(i)
-        else:
-            groups.append(([i], [op.fn] * REPEAT))
-    for idx in quant_labels.values():
-        fns = [f for i in idx for f in [ops[i].fn] + ops[i].cold]
-        groups.append((idx, fns))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
-    per_op = [0.0] * len(ops)
-    for _ in range(args.steps):
-        for g, (idx, fns) in enumerate(groups):
-            ev[g][0].record(stream)
-            for f in fns:
-                f()
-            ev[g][1].record(stream)
-        torch.cuda.synchronize()
-        for g, (idx, fns) in enumerate(groups):
-            t = ev[g][0].elapsed_time(ev[g][1]) / len(fns)
-            for i in idx:
-                per_op[i] += t
-    per_op = [t / args.steps for t in per_op]
-
-    gemm_flops = sum(op.flops for op in ops)
-    gemm_ms = sum(t for op, t in zip(ops, per_op) if op.kind == "gemm")
-    quant_bytes = sum(op.nbytes for op in ops if op.kind == "quant")
-    quant_ms = sum(t for op, t in zip(ops, per_op) if op.kind == "quant")
-    by_label = {}
-    for op, t in zip(ops, per_op):
-        d = by_label.setdefault(op.label, {"ms": 0.0, "n": 0, "flops": 0.0, "bytes": 0.0})
-        d["ms"] += t
-        d["n"] += 1
-        d["flops"] += op.flops
-        d["bytes"] += op.nbytes
-    breakdown = {}
-    for lab, d in by_label.items():
-        e = {"us_per_launch": round(1e3 * d["ms"] / d["n"], 2)}
-        if d["flops"]:
-            e["tflops"] = round(d["flops"] / (d["ms"] * 1e-3) / 1e12, 1)
-        if d["bytes"]:
-            e["gbps"] = round(d["bytes"] / (d["ms"] * 1e-3) / 1e9, 1)
-        breakdown[lab] = e
-
-    # GEMM launches grouped by kernel configuration; the roofline reports the
-    # configuration that takes the most time (the dominant kernel)
-    plans = {}
-    for op, t in zip(ops, per_op):
-        if op.kind != "gemm":
-            continue
-        d = plans.setdefault(op.plan, {"ms": 0.0, "flops": 0.0, "n": 0})
-        d["ms"] += t
-        d["flops"] += op.flops
-        d["n"] += 1
-    dom = max(plans, key=lambda k: plans[k]["ms"])
-    dom_d = plans[dom]
-    achieved = dom_d["flops"] / (dom_d["ms"] * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[gemm_peak_key]
-    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+    res = run_workload(args.workload, args.steps, args.warmup, dev)
+    print(f"[bench] {args.workload}: {res['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+    fmt = res["fmt"]
+    summ = res["summary"]
     result = {
         "metric": "block-scaled GEMM TFLOP/s of the whole quantize-then-GEMM step on ViT-L shapes",
-        "value": round(value, 2),
+        "value": round(res["value"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(res["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8-e4m3" if fmt == "mxfp8" else ("fp4-e2m1+fp16-mfma" if fmt == "nvfp4" else "fp4-e2m1"),
         "data": "synthetic (seeded, device-generated bf16; no dataset or weights)",
-        "config": config,
-        "roofline": {
-            "bound": "mfma",
-            "kernel": dom,
-            "achieved": round(achieved, 1),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(dom, config["workload"]),
-            "launches_per_step": dom_d["n"],
-            "avg_launch_us": round(1e3 * dom_d["ms"] / dom_d["n"], 2),
-            "flops_per_launch_avg": dom_d["flops"] / dom_d["n"],
-        },
-        "gemm_kernels": {k: {"launches_per_step": d["n"], "avg_launch_us": round(1e3 * d["ms"] / d["n"], 2),
-                             "tflops": round(d["flops"] / (d["ms"] * 1e-3) / 1e12, 1)} for k, d in plans.items()},
-        "gemm_only_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
-        "quant": {"gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1), "peak_gbps": PEAK_HBM_GBS,
-                  "frac": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                  "ms_per_step": round(quant_ms, 4)},
-        "breakdown": breakdown,
+        "config": res["config"],
+        "roofline": res["roofline"],
+        "gemm_kernels": {p: {k: v for k, v in d.items() if k in ("launches_per_step", "avg_launch_us", "tflops")}
+                         for p, d in summ["kernels"].items()},
+        "gemm_only_tflops": summ["gemm_only_tflops"],
+        "quant": summ["quant"],
+        "breakdown": summ["breakdown"],
+        "library_sha256": library_sha256(),
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(config["workload"], fmt)
+    if not args.only:
+        configs = {}
+        for name in EXTRA_CONFIGS:
+            if name == args.workload:
+                continue
+            r = run_workload(name, min(args.steps, 10), min(args.warmup, 2), dev)
+            print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+            configs[name] = compact(name, r)
+        result["configs"] = configs
+    if not args.no_cpu_baseline and args.workload in __import__(
+            "block_scaled_precision_mx_amd.workloads", fromlist=["STACKS"]).STACKS:
+        result["cpu_baseline"] = cpu_baseline(args.workload, fmt)
     print(json.dumps(result))
 
 

@@ -191,7 +191,10 @@ __device__ __forceinline__ void mma_stage(v16f (&acc)[Cfg::FM][Cfg::FN], const u
 // relative error is below 2^-20 in this fp32 evaluation, plus the exp2
 // argument's rounding in the far tail (about 2^-16 at z = 13). Phi(h) is
 // 1 - Q for h >= 0 and Q for h < 0. One v_rcp_f32, one v_exp_f32 and about a
-// dozen multiply-adds, against several dozen operations for erfcf.
+// dozen multiply-adds, against several dozen operations for erfcf. Far out
+// (z in the hundreds, t near 0) the polynomial tends to its negative constant
+// term while the exp2 factor has long flushed to zero; R is clamped at 0 so
+// that Q stays +0 there and the result keeps the sign of h (-0 for h < 0).
 __device__ __forceinline__ float gelu_f32(float h) {
   const float z = fabsf(h);
   const float t = __builtin_amdgcn_rcpf(fmaf(0.3499999940395355f, z, 1.0f));
@@ -203,7 +206,7 @@ __device__ __forceinline__ float gelu_f32(float h) {
   r = fmaf(r, t, 0.13335564732551575f);
   r = fmaf(r, t, 0.14027026295661926f);
   r = fmaf(r, t, -2.7310272344038822e-05f);
-  const float q = __builtin_amdgcn_exp2f(-0.7213475204444817f * z * z) * r;   // 2^(-z^2 / (2 ln 2))
+  const float q = __builtin_amdgcn_exp2f(-0.7213475204444817f * z * z) * fmaxf(r, 0.0f);   // 2^(-z^2 / (2 ln 2))
   return h >= 0.0f ? fmaf(-h, q, h) : h * q;
 }
 
@@ -215,9 +218,9 @@ __device__ __forceinline__ float gelu_f32(float h) {
 // value is within 2^-15 of h/2 relative, so the bf16 result is h/2 exactly
 // (the exponent minus one); for |h| >= 16 the tail factor exp2(-z^2 / (2 ln 2))
 // underflows, so the result is h for h > 0 and -0 for h < 0 (the exact
-// rounding of a negative value far below the bf16 range; gelu_f32 itself may
-// return +0 there, the sign of its vanishing polynomial tail). Only exponents
-// 0, 1 (zero, values below 2^-125) and 255 are evaluated directly.
+// rounding of a negative value far below the bf16 range, which gelu_f32 gives
+// there too). Only exponents 0, 1 (zero, values below 2^-125) and 255 are
+// evaluated directly.
 __device__ __forceinline__ uint32_t gelu_bf16_direct(uint32_t b) {
   return pack_bf16x2(gelu_f32(__uint_as_float(b << 16)), 0.0f) & 0xFFFFu;
 }

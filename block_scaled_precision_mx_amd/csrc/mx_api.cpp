@@ -33,8 +33,14 @@ int64_t code_row_bytes(int64_t kpad, int fmt) { return fmt == MX_FMT_MXFP8 ? kpa
 int block_elems(int fmt) { return fmt == MX_FMT_NVFP4 ? 16 : 32; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Buffer offsets inside the kernels are 32-bit.
+// Buffer offsets inside the kernels are 32-bit, and the launchers pass
+// counts (rows, columns, K_pad) as int: every one of them stays below 2^31.
 constexpr int64_t kMaxBytes = (int64_t)1 << 31;
+constexpr int64_t kMaxCount = ((int64_t)1 << 31) - 256;   // K_pad = round_up(count, 128) stays below 2^31 too
+
+// LayerNorm rows longer than this would let the fp32 row sums (cols / 64
+// values added in sequence per lane) exceed the accuracy the header states.
+constexpr int64_t kMaxLayerNormCols = 8192;
 
 int64_t scales_total(int64_t R, int64_t kpad, int fmt) {
   int64_t n = R * (kpad / block_elems(fmt));
@@ -72,6 +78,8 @@ mx_status mx_quantize(const void* src, int64_t rows, int64_t cols, int64_t ld, v
   if (!aligned(src, 2)) return fail(MX_ERR_ALIGNMENT, "mx_quantize: src must be 2-byte aligned");
   if (!aligned(codes, 16) || !aligned(scales, 16))
     return fail(MX_ERR_ALIGNMENT, "mx_quantize: codes and scales must be 16-byte aligned");
+  if (rows > kMaxCount || cols > kMaxCount)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: rows and cols must be below 2^31 - 256");
   const int64_t R = axis == MX_AXIS_ROW ? rows : cols, L = axis == MX_AXIS_ROW ? cols : rows;
   const int64_t kpad = k_pad(L);
   if (R * code_row_bytes(kpad, fmt) >= kMaxBytes || scales_total(R, kpad, fmt) >= kMaxBytes)
@@ -98,6 +106,9 @@ mx_status mx_layernorm_quantize(const void* x, int64_t rows, int64_t cols, int64
   if (ld < cols)
     return fail(MX_ERR_INVALID_ARG, "mx_layernorm_quantize: ld %lld < cols %lld", (long long)ld, (long long)cols);
   if (!x || !gamma || !beta || !codes || !scales) return fail(MX_ERR_INVALID_ARG, "mx_layernorm_quantize: null pointer");
+  if (cols > kMaxLayerNormCols)
+    return fail(MX_ERR_UNSUPPORTED, "mx_layernorm_quantize: rows longer than %lld columns are not supported",
+                (long long)kMaxLayerNormCols);
   // eps > 0 keeps var + eps positive: a constant row (var = 0) then gives
   // y = beta instead of 0 * inf
   if (!(eps > 0.0f) || !(eps < 3.0e38f))
@@ -142,6 +153,8 @@ mx_status mx_quantize_batch(const mx_quant_item* items, int n, mx_fmt fmt, void*
     if (!aligned(it.src, 2)) return fail(MX_ERR_ALIGNMENT, "mx_quantize_batch: item %d: src must be 2-byte aligned", i);
     if (!aligned(it.codes, 16) || !aligned(it.scales, 16))
       return fail(MX_ERR_ALIGNMENT, "mx_quantize_batch: item %d: codes and scales must be 16-byte aligned", i);
+    if (it.rows > kMaxCount || it.cols > kMaxCount)
+      return fail(MX_ERR_UNSUPPORTED, "mx_quantize_batch: item %d: rows and cols must be below 2^31 - 256", i);
     const int64_t kpad = k_pad(it.cols);
     if (it.rows * code_row_bytes(kpad, fmt) >= kMaxBytes || scales_total(it.rows, kpad, fmt) >= kMaxBytes)
       return fail(MX_ERR_UNSUPPORTED, "mx_quantize_batch: item %d: output larger than 2 GiB", i);
@@ -171,6 +184,8 @@ mx_status mx_quantize_dual(const void* src, int64_t rows, int64_t cols, int64_t 
   if (!aligned(row_codes, 16) || !aligned(row_scales, 16) || !aligned(col_codes, 16) || !aligned(col_scales, 16))
     return fail(MX_ERR_ALIGNMENT, "mx_quantize_dual: codes and scales must be 16-byte aligned");
   if (delayed && !aligned(amax_prev, 4)) return fail(MX_ERR_ALIGNMENT, "mx_quantize_dual: amax_prev must be 4-byte aligned");
+  if (rows > kMaxCount || cols > kMaxCount)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_dual: rows and cols must be below 2^31 - 256");
   const int64_t rkpad = k_pad(cols), ckpad = k_pad(rows);
   if (rows * code_row_bytes(rkpad, fmt) >= kMaxBytes || scales_total(rows, rkpad, fmt) >= kMaxBytes ||
       cols * code_row_bytes(ckpad, fmt) >= kMaxBytes || scales_total(cols, ckpad, fmt) >= kMaxBytes)
@@ -206,6 +221,8 @@ mx_status mx_quantize_dual_sr(const void* src, int64_t rows, int64_t cols, int64
     return fail(MX_ERR_ALIGNMENT, "mx_quantize_dual_sr: codes and scales must be 16-byte aligned");
   if (delayed && !aligned(amax_prev, 4))
     return fail(MX_ERR_ALIGNMENT, "mx_quantize_dual_sr: amax_prev must be 4-byte aligned");
+  if (rows > kMaxCount || cols > kMaxCount)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_dual_sr: rows and cols must be below 2^31 - 256");
   const int64_t rkpad = k_pad(cols), ckpad = k_pad(rows);
   if (rows * code_row_bytes(rkpad, fmt) >= kMaxBytes || scales_total(rows, rkpad, fmt) >= kMaxBytes ||
       cols * code_row_bytes(ckpad, fmt) >= kMaxBytes || scales_total(cols, ckpad, fmt) >= kMaxBytes)
@@ -232,13 +249,13 @@ mx_status mx_gemm(const void* A, const void* As, const void* B, const void* Bs, 
   if (!aligned(A, 16) || !aligned(As, 16) || !aligned(B, 16) || !aligned(Bs, 16) || !aligned(C, 16))
     return fail(MX_ERR_ALIGNMENT, "mx_gemm: A, As, B, Bs and C must be 16-byte aligned");
   if (bias && !aligned(bias, 2)) return fail(MX_ERR_ALIGNMENT, "mx_gemm: bias must be 2-byte aligned");
+  if (M > kMaxCount || N > kMaxCount || K > kMaxCount)
+    return fail(MX_ERR_UNSUPPORTED, "mx_gemm: M, N and K must be below 2^31 - 256");
   const int64_t kpad = k_pad(K);
   const int64_t rb = code_row_bytes(kpad, fmt);
   if (M * rb >= kMaxBytes || N * rb >= kMaxBytes || scales_total(M, kpad, fmt) >= kMaxBytes ||
       scales_total(N, kpad, fmt) >= kMaxBytes)
     return fail(MX_ERR_UNSUPPORTED, "mx_gemm: operand larger than 2 GiB");
-  if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
-    return fail(MX_ERR_UNSUPPORTED, "mx_gemm: M and N must be below 2^31");
   hipError_t e;
   const int out_f32 = out_dtype == MX_OUT_F32;
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -271,6 +288,8 @@ mx_status mx_gemm_gelu_quantize(const void* A, const void* As, const void* B, co
       !aligned(out_scales, 16))
     return fail(MX_ERR_ALIGNMENT, "mx_gemm_gelu_quantize: operands and outputs must be 16-byte aligned");
   if (bias && !aligned(bias, 2)) return fail(MX_ERR_ALIGNMENT, "mx_gemm_gelu_quantize: bias must be 2-byte aligned");
+  if (M > kMaxCount || N > kMaxCount || K > kMaxCount)
+    return fail(MX_ERR_UNSUPPORTED, "mx_gemm_gelu_quantize: M, N and K must be below 2^31 - 256");
   const int64_t kpad = k_pad(K), rb = code_row_bytes(kpad, fmt);
   if (M * rb >= kMaxBytes || N * rb >= kMaxBytes || scales_total(M, kpad, fmt) >= kMaxBytes ||
       scales_total(N, kpad, fmt) >= kMaxBytes)

@@ -13,12 +13,12 @@ README's section 4.3 (qkv, proj, fc1, fc2 per block) and these values:
 
 (the second parameter is a standard deviation). Two generators produce the
 same recipe:
-  * ``np_*``: numpy PCG64 in float64, rounded float64 -> float32 -> bf16, each
-    step round-to-nearest-even. Used by tests, so the oracle sees exactly
-    the bits the GPU sees.
-  * ``torch_*``: torch's device generator in float32 -> bf16 (RNE). Used by
-    the benchmark to fill gigabytes of HBM quickly; same distributions,
-    different random stream.
+  * ``np_*``: numpy PCG64 samples in float64, rounded once to bf16 (round to
+    nearest, ties to even). Used by tests, so the oracle sees exactly the
+    bits the GPU sees.
+  * ``torch_*``: torch's device generator in float32, rounded once to bf16
+    (RNE). Used by the benchmark to fill gigabytes of HBM quickly; same
+    distributions, different random stream.
 
 Seeds: seed = 100000 * workload_id + 100 * block + tensor_id.
 """
@@ -37,15 +37,30 @@ GRAD_STD = 1e-3
 
 # ------------------------------------------------------------- bf16 bits
 
-def _f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
-    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
-
-
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """float64 -> float32 -> bf16 bit patterns (each step RNE)."""
-    return _f32_to_bf16_bits(np.asarray(x, dtype=np.float64).astype(np.float32))
+    """float64 -> bf16 bit patterns, one round to nearest with ties to even
+    (finite inputs; magnitudes that round past the largest bf16 give Inf).
+
+    A bf16 value is m * 2^q with an integer m < 256 and q >= -133: for
+    |x| >= 2^-126, q = floor(log2 |x|) - 7, and below that q = -133
+    (subnormals). Scaling by 2^-q is exact in float64 and np.rint rounds
+    half to even, so m = rint(|x| 2^-q) is the single correctly rounded
+    significand; m = 256 carries into the next binade."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    sign = np.signbit(x).astype(np.uint32) << 15
+    _, e2 = np.frexp(a)                             # a = f 2^e2, f in [0.5, 1)
+    q = np.maximum(e2.astype(np.int64) - 8, -133)
+    m = np.rint(np.ldexp(a, -q)).astype(np.int64)   # 0 .. 256
+    carry = m >= 256
+    m = np.where(carry, m // 2, m)
+    q = q + carry
+    # biased exponent: subnormals (m < 128 at q = -133) keep field 0
+    normal = m >= 128
+    field = np.where(normal, q + 7 + 127, 0)
+    bits = np.where(normal, (field << 7) | (m - 128), m)
+    bits = np.where(field >= 255, 0x7F80, bits)     # overflow to Inf
+    return (sign | bits.astype(np.uint32)).astype(np.uint16)
 
 
 # ------------------------------------------------------------- numpy recipe
@@ -229,3 +244,45 @@ TRAIN_PAIRS = {tp.name: tp for tp in (TRAIN_PAIR, TRAIN_PAIR_MXFP8, TRAIN_PAIR_S
 
 def seed(wid: int, block: int, tensor_id: int) -> int:
     return 100000 * wid + 100 * block + tensor_id
+
+
+@dataclass(frozen=True)
+class BlockTrain:
+    """The twelve GEMMs of one ViT block's training step (README section 5.4
+    measures them per ViT-L block): for each linear L of qkv / proj / fc1 /
+    fc2, fprop Y = X W^T + b, dgrad dX = dY W and wgrad dW = dY^T X, with
+    every operand quantized along its own K axis. `fwd_fmt` is the format of
+    the four fprop GEMMs, `bwd_fmt` that of the eight dgrad / wgrad GEMMs
+    (README section 5.3's format maps: FINAL runs all three GEMMs of a
+    Linear in MXFP8; P3 moves dgrad / wgrad to NVFP4 with the gradient
+    rounded stochastically). `blocks` blocks with their own tensors make one
+    step, so that no launch is served from the Infinity Cache."""
+    wid: int
+    name: str
+    fwd_fmt: str
+    bwd_fmt: str
+    sr_grads: bool = False
+    m: int = 7 * TOKENS
+    hidden: int = 1024
+    mlp: int = 4096
+    blocks: int = 4
+    sr_seed: tuple = (0x5EED0011, 0x5EED0012)
+
+    def linears(self):
+        return _vit_linears(self.hidden, self.mlp)
+
+    # tensor ids of linear i (0 qkv, 1 proj, 2 fc1, 3 fc2): X, W, bias, dY
+    @staticmethod
+    def ids(i: int):
+        return 10 * i, 10 * i + 1, 10 * i + 2, 10 * i + 3
+
+    def gemm_flops(self) -> int:
+        return 3 * 2 * self.m * sum(l.n * l.k for l in self.linears()) * self.blocks
+
+
+# FINAL: every GEMM of the block in MXFP8 (the page keeps qkv's fprop in BF16;
+# its section 5.4 measures all twelve GEMMs of a ViT-L block in MXFP8)
+BLOCK_TRAIN_MXFP8 = BlockTrain(7, "vitl16_mxfp8_block_train", "mxfp8", "mxfp8")
+# P3: fprop MXFP8, dgrad / wgrad NVFP4 with stochastically rounded gradients
+BLOCK_TRAIN_P3 = BlockTrain(8, "vitl16_p3_block_train", "mxfp8", "nvfp4", sr_grads=True)
+BLOCK_TRAINS = {bt.name: bt for bt in (BLOCK_TRAIN_MXFP8, BLOCK_TRAIN_P3)}

@@ -58,6 +58,11 @@
  *   leave every output untouched (MX_ERR_INVALID_ARG, MX_ERR_ALIGNMENT,
  *   MX_ERR_UNSUPPORTED). A failed launch returns MX_ERR_HIP. The message of
  *   the last non-OK status of the calling thread is in mx_last_error().
+ *
+ * Size limits (MX_ERR_UNSUPPORTED beyond them): every count (rows, cols, M,
+ *   N, K) is at most 2^31 - 256, so that K_pad stays below 2^31; every code
+ *   or scale buffer, and a quantizer's input span rows * ld, stays below
+ *   2 GiB (the kernels address them with 32-bit offsets).
  */
 #ifndef MX_H_
 #define MX_H_
@@ -161,6 +166,8 @@ mx_status mx_quantize_dual_sr(const void* src, int64_t rows, int64_t cols, int64
  * as the A operand of the next mx_gemm (K = cols). The bf16 LayerNorm output
  * itself is never stored. y lies within 2^-16 (|gamma| r (max|x - mu| +
  * |x - mu| + |mu|) + |beta| + |y|) of the exact value, r = 1/sqrt(var + eps).
+ * cols is at most 8192 (MX_ERR_UNSUPPORTED beyond: the fp32 row sums of
+ * longer rows could exceed that accuracy statement).
  * fmt: MX_FMT_MXFP8 or MX_FMT_MXFP4 (NVFP4 would need the output's tensor
  * amax before the first block: MX_ERR_UNSUPPORTED). x, gamma and beta must be
  * 4-byte aligned (16 bytes, with ld % 4 == 0, takes the vector loads), codes
@@ -218,7 +225,8 @@ mx_status mx_gemm(const void* A, const void* As, const void* B, const void* Bs,
  * (sizes mx_codes_bytes / mx_scales_bytes of (M, N, fmt, MX_AXIS_ROW)), so
  * they serve directly as the A operand of the next mx_gemm (K = N). H itself
  * is never stored. The accumulation follows mx_gemm's accuracy rule, and the
- * fp32 GELU lies within 2^-14 |GELU| + 2^-122 of the exact value.
+ * fp32 GELU lies within 2^-14 |GELU| + 2^-126 of the exact value and has the
+ * sign of h (-0 for a negative h whose GELU vanishes in fp32).
  * fmt: MX_FMT_MXFP8 or MX_FMT_MXFP4 (NVFP4 would need the tensor amax of H
  * first: MX_ERR_UNSUPPORTED). N must be a multiple of 8. Other arguments,
  * errors and memory rules as for mx_gemm. */

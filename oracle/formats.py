@@ -58,6 +58,47 @@ def f64_to_bf16_rne(x) -> np.ndarray:
     return out
 
 
+def _bf16_spacing_exp(x: np.ndarray) -> np.ndarray:
+    """Exponent of the bf16 spacing at the magnitude of x (8 significant
+    bits, never finer than the subnormal spacing 2^-133)."""
+    _, expo = np.frexp(np.abs(x))
+    return np.maximum(expo - 8, -133)
+
+
+def bf16_floor(x) -> np.ndarray:
+    """Largest bf16 value <= x, for finite x >= 0 (as float64; +inf stays)."""
+    x = np.asarray(x, dtype=np.float64)
+    q = _bf16_spacing_exp(np.where(np.isfinite(x), x, 0.0))
+    out = np.ldexp(np.floor(np.ldexp(x, -q)), q)
+    return np.where(np.isfinite(x), out, x)
+
+
+def bf16_ceil(x) -> np.ndarray:
+    """Smallest bf16 value >= x, for finite x >= 0 (as float64; +inf stays)."""
+    x = np.asarray(x, dtype=np.float64)
+    q = _bf16_spacing_exp(np.where(np.isfinite(x), x, 0.0))
+    out = np.ldexp(np.ceil(np.ldexp(x, -q)), q)
+    return np.where(np.isfinite(x), out, x)
+
+
+def bf16_above(x) -> np.ndarray:
+    """Smallest bf16 value > x, for finite x >= 0 (+inf stays). Scaling by
+    1 + 2^-20 moves a bf16 value past itself but not past the next one."""
+    x = np.asarray(x, dtype=np.float64)
+    c = bf16_ceil(x)
+    nxt = np.where(c > 0, bf16_ceil(c * (1 + 2.0 ** -20)), 2.0 ** -133)
+    return np.where(c > x, c, nxt)
+
+
+def bf16_below(x) -> np.ndarray:
+    """Largest bf16 value < x, for x >= 0 (+inf stays; -1 where none, i.e.
+    x = 0)."""
+    x = np.asarray(x, dtype=np.float64)
+    f = bf16_floor(x)
+    prv = np.where(f > 0, bf16_floor(f * (1 - 2.0 ** -20)), -1.0)
+    return np.where(f < x, f, prv)
+
+
 def f64_to_bf16_bits(x) -> np.ndarray:
     """bf16 bit patterns of float64 values after a single RNE rounding."""
     r = f64_to_bf16_rne(x).astype(np.float32)   # exact: r already has 8 bits

@@ -17,14 +17,22 @@ exact sum, S = sum |a b| + |bias|) and GELU is the exact one,
 GELU(h) = h Phi(h) = h/2 erfc(-h / sqrt 2). So the fused result equals
 mx_quantize of the bf16 GELU of mx_gemm's bf16 output. Neither acc nor the
 kernel's fp32 GELU is bit-fixed: acc lies within the GEMM bound, and the
-kernel's GELU within GELU_REL * |GELU| + GELU_ABS of the exact value. So
-every element has an interval of possible bf16 g values, and check() accepts
-an output iff some choice inside those intervals explains it:
-  * the block's scale byte lies between the shared exponents of the smallest
-    and the largest possible block amax;
-  * every code equals, at that scale, the RNE code of some value of its
-    element's interval (RNE onto the grid is monotone, so the interval's end
-    codes bound it).
+kernel's GELU within GELU_REL * |GELU| + GELU_ABS of the exact value,
+with the sign of h (GELU(h) = h Phi(h) and Phi > 0). So every element has
+an interval of possible bf16 g values, and check_intervals accepts a block
+of the output iff ONE choice of values inside those intervals explains all
+of it at once:
+  * for the GPU's scale byte (shared exponent e), each element's possible
+    values are cut down to those whose RNE code at e is the GPU's code, the
+    sign of a zero code included (a negative value, or -0, gives the
+    negative-zero code);
+  * some choice among what is left has a block amax whose shared exponent
+    is e, i.e. amax in [2^(e + emax), 2^(e + emax + 1)) (any amax below the
+    upper end for e = -127).
+The values are bf16 numbers, so each element's remaining set is an
+interval of bf16 magnitudes [m_i, M_i], and the achievable block amax runs
+from max_i m_i to max_i M_i: the block is explained iff max_i M_i reaches
+the exponent's lower end and max_i m_i stays below its upper end.
 With an exactly representable accumulation (gemm_tol 0) the intervals come
 from the GELU allowance alone and almost every element has one candidate.
 """
@@ -56,24 +64,37 @@ def gelu(h) -> np.ndarray:
     return 0.5 * h * erfc(-h * SQRT1_2)
 
 
-# what the kernel's fp32 GELU may differ from the exact one by: its fitted
-# tail Q(z) = exp(-z^2/2) R(z) is within 2^-20 relative in fp32, the
-# rounding of the exp2 argument adds up to about 2^-16 near z = 13, and the
-# exp2 of arguments below -126 (|GELU| < 2^-122) may flush to zero
+# What the kernel's fp32 GELU may differ from the exact one by, as the C
+# header states it: its fitted tail Q(z) = exp(-z^2/2) R(z) is within 2^-20
+# relative in fp32 and the rounding of the exp2 argument adds up to about
+# 2^-16 near z = 13 (GELU_REL); the exp2 factor may flush results below
+# 2^-126 to zero, which happens only where exp(-z^2/2) < 2^-126, and there
+# |GELU(h)| = z Q(z) < phi(z) = exp(-z^2/2) / sqrt(2 pi) < 2^-127 (the
+# Mills-ratio bound Q(z) < phi(z) / z), so an absolute 2^-126 covers the
+# flush (GELU_ABS). The result keeps the sign of h.
 GELU_REL = 2.0 ** -14
-GELU_ABS = 2.0 ** -122
+GELU_ABS = 2.0 ** -126
 
 
 def _bf16_interval_of_gelu(h_lo, h_hi):
-    """bf16 interval [g_lo, g_hi] of RNE_bf16(fp32 GELU) for h in [h_lo, h_hi]."""
+    """bf16 interval [g_lo, g_hi] of RNE_bf16(fp32 GELU) for h in [h_lo, h_hi]
+    (float64 bf16 values with signed zeros): GELU's image of the interval,
+    widened by the allowance, and clipped at zero on the side that h's sign
+    excludes (GELU(h) has the sign of h, -0 for h = -0)."""
     a, b = gelu(h_lo), gelu(h_hi)
     g_min = np.minimum(a, b)
     g_max = np.maximum(a, b)
     inside = (h_lo < GELU_ARGMIN) & (h_hi > GELU_ARGMIN)
     g_min = np.where(inside, gelu(GELU_ARGMIN) * (1 + 1e-12), g_min)
-    lo = g_min - (GELU_REL * np.abs(g_min) + GELU_ABS)
-    hi = g_max + (GELU_REL * np.abs(g_max) + GELU_ABS)
-    return F.f64_to_bf16_rne(lo), F.f64_to_bf16_rne(hi)
+    lo = F.f64_to_bf16_rne(g_min - (GELU_REL * np.abs(g_min) + GELU_ABS))
+    hi = F.f64_to_bf16_rne(g_max + (GELU_REL * np.abs(g_max) + GELU_ABS))
+    # every h has sign bit 0: no negative g (lo at least +0)
+    pos_only = ~np.signbit(h_lo)
+    lo = np.where(pos_only & (np.signbit(lo) | (lo == 0)), 0.0, lo)
+    # every h has sign bit 1: no positive g (hi at most -0)
+    neg_only = np.signbit(h_hi)
+    hi = np.where(neg_only & ~np.signbit(hi), -0.0, hi)
+    return lo, hi
 
 
 def reference_codes(h_bits: np.ndarray, fmt: str) -> Q.Quantized:
@@ -81,14 +102,6 @@ def reference_codes(h_bits: np.ndarray, fmt: str) -> Q.Quantized:
     once to bf16, then quantize along the rows)."""
     g = F.f64_to_bf16_bits(gelu(F.bf16_to_f64(h_bits)))
     return Q.quantize(g, fmt, "row")
-
-
-def _enc_value(v, e, fmt):
-    """Value of the RNE code of v at shared exponent e (saturating)."""
-    scaled = np.ldexp(v, -e)
-    if fmt == "mxfp8":
-        return np.ldexp(F.e4m3_decode(F.e4m3_encode(scaled)), e)
-    return np.ldexp(F.e2m1_decode(F.e2m1_encode(scaled)), e)
 
 
 def check_rows(codes_rows: np.ndarray, scales_rows: np.ndarray, c: np.ndarray, s: np.ndarray, fmt: str,
@@ -107,35 +120,64 @@ def check_rows(codes_rows: np.ndarray, scales_rows: np.ndarray, c: np.ndarray, s
     return check_intervals(codes_rows, scales_rows, g_lo, g_hi, fmt, n)
 
 
+def _preimage(fmt):
+    """Per magnitude code k: (low end, high end, ends inclusive) of the scaled
+    magnitudes |x| 2^-e that round to k: the midpoints to the neighbours,
+    inclusive for an even code (ties go to it), exclusive for an odd one; 0
+    below code 0 and +inf above the largest code (saturation)."""
+    grid = F.E4M3_GRID if fmt == "mxfp8" else F.E2M1_GRID
+    mids = (grid[:-1] + grid[1:]) * 0.5
+    low = np.concatenate([[0.0], mids])
+    high = np.concatenate([mids, [np.inf]])
+    even = (np.arange(grid.size) % 2) == 0
+    return low, high, even
+
+
 def check_intervals(codes_rows: np.ndarray, scales_rows: np.ndarray, g_lo: np.ndarray, g_hi: np.ndarray, fmt: str,
                     n: int):
     """Accept / reject MX row-quantized rows whose bf16 source values are
-    known only to lie in [g_lo, g_hi] (float64 [R, n], bf16 values), the
-    columns n .. K_pad being padding. Returns (ok_codes [R, K_pad],
-    ok_scales [R, K_pad / 32]) boolean masks."""
+    known only to lie in [g_lo, g_hi] (float64 [R, n], bf16 values; a
+    negative value is possible iff g_lo has its sign bit set, a positive one
+    iff g_hi has not), the columns n .. K_pad being padding (+0, code 0).
+
+    Returns (ok_codes [R, K_pad], ok_scales [R, K_pad / 32]): ok_codes says
+    that some value of the element's interval has the GPU's code at the GPU's
+    block exponent; ok_scales that one choice of such values gives the block
+    an amax whose shared exponent is the GPU's (module docstring)."""
     if fmt not in ("mxfp8", "mxfp4"):
         raise ValueError("interval acceptance is defined for the MX formats")
     emax = F.E4M3_EMAX if fmt == "mxfp8" else F.E2M1_EMAX
+    sign_shift, mag_mask = (7, 0x7F) if fmt == "mxfp8" else (3, 0x7)
     R, k_pad = codes_rows.shape
     nb = k_pad // 32
     lo = np.zeros((R, k_pad))
     hi = np.zeros((R, k_pad))
     lo[:, :n], hi[:, :n] = g_lo, g_hi
-    g_lo, g_hi = lo, hi
-    # block amax range
-    amin = np.where((g_lo <= 0) & (g_hi >= 0), 0.0, np.minimum(np.abs(g_lo), np.abs(g_hi)))
-    amax = np.maximum(np.abs(g_lo), np.abs(g_hi))
-    e_lo = Q.mx_shared_exponent(amin.reshape(R, nb, 32).max(axis=2), emax)
-    e_hi = Q.mx_shared_exponent(amax.reshape(R, nb, 32).max(axis=2), emax)
-    e_gpu = scales_rows.astype(np.int64) - 127
-    ok_scales = (e_gpu >= e_lo) & (e_gpu <= e_hi)
-    e_el = np.repeat(e_gpu, 32, axis=1)
-    got = (F.e4m3_decode(codes_rows) if fmt == "mxfp8" else F.e2m1_decode(codes_rows))
-    got = np.ldexp(got, e_el)
-    lo_v = _enc_value(g_lo, e_el, fmt)
-    hi_v = _enc_value(g_hi, e_el, fmt)
-    ok_codes = (got >= lo_v) & (got <= hi_v)
-    ok_codes[:, n:] &= (codes_rows[:, n:] == 0)          # padding codes are zero
+    codes = np.asarray(codes_rows, dtype=np.int64)
+    e = scales_rows.astype(np.int64) - 127                      # [R, nb]
+    e_el = np.repeat(e, 32, axis=1)
+    neg = ((codes >> sign_shift) & 1) == 1
+    k = codes & mag_mask
+    top = (F.E4M3_GRID.size if fmt == "mxfp8" else F.E2M1_GRID.size) - 1
+    valid = k <= top                                             # 0x7F is NaN in E4M3
+    k = np.minimum(k, top)
+    # magnitudes the interval allows with the code's sign
+    sign_ok = np.where(neg, np.signbit(lo), ~np.signbit(hi))
+    cm_lo = np.where(neg, np.where(hi < 0, -hi, 0.0), np.where(lo > 0, lo, 0.0))
+    cm_hi = np.where(neg, -lo, hi)
+    # magnitudes that round to k at exponent e, as bf16 values
+    p_low, p_high, p_even = _preimage(fmt)
+    low, high, incl = np.ldexp(p_low[k], e_el), np.ldexp(p_high[k], e_el), p_even[k]
+    a = np.maximum(cm_lo, np.where(incl, F.bf16_ceil(low), F.bf16_above(low)))
+    b = np.minimum(cm_hi, np.where(incl, F.bf16_floor(high), F.bf16_below(high)))
+    ok_codes = valid & sign_ok & (a <= b)
+    # the block amax that such a choice can reach: [max m_i, max M_i]
+    m_blk = np.where(ok_codes, a, 0.0).reshape(R, nb, 32).max(axis=2)
+    M_blk = np.where(ok_codes, b, 0.0).reshape(R, nb, 32).max(axis=2)
+    amax_lo = np.where(e > -127, np.ldexp(1.0, e + emax), 0.0)   # e = -127 takes every amax below 2^(emax - 126)
+    amax_hi = np.where(e < 127, np.ldexp(1.0, e + emax + 1), np.inf)
+    ok_scales = (e >= -127) & (e <= 127) & (M_blk >= amax_lo) & (m_blk < amax_hi)
+    ok_codes[:, n:] &= (codes_rows[:, n:] == 0)          # padding codes are +0
     return ok_codes, ok_scales
 
 

@@ -66,6 +66,11 @@ ALIGNED = 1 << 20      # fake, never dereferenced: every call below fails valida
     ((ALIGNED + 1, 4, 4, 4, ALIGNED, ALIGNED, 1, 0), 3, "2-byte"),
     ((ALIGNED, 4, 4, 4, ALIGNED + 8, ALIGNED, 1, 0), 3, "16-byte"),
     ((ALIGNED, 1 << 20, 1 << 12, 1 << 12, ALIGNED, ALIGNED, 1, 0), 2, "2 GiB"),
+    # a column quantization of one column of 3e9 rows: one stored row of
+    # K_pad ~ 3e9 elements (1.5 GB of fp4 codes) would overflow the kernels' int counts
+    ((ALIGNED, 3_000_000_000, 1, 1, ALIGNED, ALIGNED, 2, 1), 2, "below 2^31"),
+    ((ALIGNED, 3_000_000_000, 1, 1, ALIGNED, ALIGNED, 3, 1), 2, "below 2^31"),
+    ((ALIGNED, 1, (1 << 31) - 200, (1 << 31) - 200, ALIGNED, ALIGNED, 2, 0), 2, "below 2^31"),
 ])
 def test_quantize_validation(L, args, status, msg):
     assert L.mx_quantize(*args, None) == status
@@ -81,6 +86,9 @@ def test_quantize_validation(L, args, status, msg):
     ((ALIGNED, ALIGNED, ALIGNED + 4, ALIGNED, ALIGNED, 4, 4, 32, 1, None, 0), 3, "16-byte"),
     ((ALIGNED,) * 5 + (4, 4, 32, 1, ALIGNED + 1, 0), 3, "bias"),
     ((ALIGNED,) * 5 + (1 << 22, 4, 1024, 1, None, 0), 2, "2 GiB"),
+    # one fp4 row of K >= 2^31 elements is only 1 GiB of codes: rejected by the count bound
+    ((ALIGNED,) * 5 + (1, 1, 1 << 31, 2, None, 0), 2, "below 2^31"),
+    ((ALIGNED,) * 5 + (1, 1, (1 << 31) - 200, 3, None, 0), 2, "below 2^31"),
 ])
 def test_gemm_validation(L, args, status, msg):
     assert L.mx_gemm(*args, None) == status
@@ -98,6 +106,7 @@ def test_gemm_validation(L, args, status, msg):
     ((ALIGNED + 1, 4, 4, 4) + (ALIGNED,) * 4 + (1, None, 32.0), 3, "2-byte"),
     ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, ALIGNED, ALIGNED + 8, 1, None, 32.0), 3, "16-byte"),
     ((ALIGNED, 1 << 20, 1 << 12, 1 << 12) + (ALIGNED,) * 4 + (1, None, 32.0), 2, "2 GiB"),
+    ((ALIGNED, 3_000_000_000, 1, 1) + (ALIGNED,) * 4 + (2, None, 32.0), 2, "below 2^31"),
 ])
 def test_quantize_dual_validation(L, args, status, msg):
     assert L.mx_quantize_dual(*args, None) == status
@@ -120,6 +129,7 @@ GOOD = (ALIGNED, 4, 4, 4, ALIGNED, ALIGNED)
     ((GOOD,), 0, 1, 1, "outside [1, 32]"),
     ((GOOD,), 33, 1, 1, "outside [1, 32]"),
     ((GOOD, (ALIGNED, 0, 4, 4, ALIGNED, ALIGNED)), 2, 1, 1, "item 1: empty"),
+    ((GOOD, (ALIGNED, 1, (1 << 31) - 200, (1 << 31) - 200, ALIGNED, ALIGNED)), 2, 2, 2, "item 1: rows and cols"),
     ((GOOD, GOOD, (ALIGNED, 4, 8, 4, ALIGNED, ALIGNED)), 3, 2, 1, "item 2: ld"),
     (((None, 4, 4, 4, ALIGNED, ALIGNED),), 1, 1, 1, "item 0: null"),
     (((ALIGNED + 1, 4, 4, 4, ALIGNED, ALIGNED),), 1, 1, 3, "item 0: src must be 2-byte"),
@@ -148,6 +158,7 @@ def test_quantize_batch_null_items(L):
     ((ALIGNED, 4, 8, 8) + (ALIGNED,) * 4 + (3, ALIGNED, -1.0), 1, "headroom"),
     ((ALIGNED, 4, 8, 8) + (ALIGNED,) * 3 + (ALIGNED + 4, 3, None, 32.0), 3, "16-byte"),
     ((ALIGNED, 1 << 21, 1 << 12, 1 << 12) + (ALIGNED,) * 4 + (3, None, 32.0), 2, "2 GiB"),
+    ((ALIGNED, 3_000_000_000, 8, 8) + (ALIGNED,) * 4 + (3, None, 32.0), 2, "below 2^31"),
 ])
 def test_quantize_dual_sr_validation(L, args, status, msg):
     assert L.mx_quantize_dual_sr(*args, 1, 2, None) == status
@@ -163,6 +174,7 @@ def test_quantize_dual_sr_validation(L, args, status, msg):
     ((ALIGNED,) * 4 + (4, 8, 32, 1, None, ALIGNED, ALIGNED + 8), 3, "16-byte"),
     ((ALIGNED,) * 4 + (4, 8, 32, 2, ALIGNED + 1, ALIGNED, ALIGNED), 3, "bias"),
     ((ALIGNED,) * 4 + (1 << 22, 1 << 10, 32, 1, None, ALIGNED, ALIGNED), 2, "output larger"),
+    ((ALIGNED,) * 4 + (1, 8, 1 << 31, 2, None, ALIGNED, ALIGNED), 2, "below 2^31"),
 ])
 def test_gemm_gelu_quantize_validation(L, args, status, msg):
     assert L.mx_gemm_gelu_quantize(*args, None) == status
@@ -182,6 +194,8 @@ def test_gemm_gelu_quantize_validation(L, args, status, msg):
     ((ALIGNED + 2, 4, 8, 8, ALIGNED, ALIGNED, 1e-6, ALIGNED, ALIGNED, 1), 3, "4-byte"),
     ((ALIGNED, 4, 8, 8, ALIGNED, ALIGNED, 1e-6, ALIGNED + 4, ALIGNED, 1), 3, "16-byte"),
     ((ALIGNED, 1 << 22, 1 << 10, 1 << 10, ALIGNED, ALIGNED, 1e-6, ALIGNED, ALIGNED, 1), 2, "2 GiB"),
+    # rows longer than the stated accuracy covers
+    ((ALIGNED, 4, 8193, 8193, ALIGNED, ALIGNED, 1e-6, ALIGNED, ALIGNED, 1), 2, "8192 columns"),
 ])
 def test_layernorm_quantize_validation(L, args, status, msg):
     assert L.mx_layernorm_quantize(*args, None) == status
@@ -229,11 +243,22 @@ def test_gemm_plan_names(L):
 
 
 def test_bench_workloads_are_defined():
-    """Every workload bench.py offers is a stack or a training pair of the
-    workloads module, and each names its own format."""
+    """Every workload bench.py offers is a stack, a training pair or a
+    block-training workload of the workloads module, and each names its own
+    format; the default line measures the headline and every other
+    configuration."""
     import bench
     from block_scaled_precision_mx_amd import workloads as W
-    assert set(bench.WORKLOADS) == set(W.STACKS) | set(W.TRAIN_PAIRS)
+    assert set(bench.WORKLOADS) == set(W.STACKS) | set(W.TRAIN_PAIRS) | set(W.BLOCK_TRAINS)
     for name in bench.WORKLOADS:
-        wl = W.STACKS.get(name) or W.TRAIN_PAIRS[name]
-        assert wl.fmt in name
+        wl = W.STACKS.get(name) or W.TRAIN_PAIRS.get(name)
+        if wl is not None:
+            assert wl.fmt in name
+        else:
+            bt = W.BLOCK_TRAINS[name]
+            assert (bt.bwd_fmt in name) or ("p3" in name and bt.bwd_fmt == "nvfp4" and bt.sr_grads)
+    assert set(bench.EXTRA_CONFIGS) <= set(bench.WORKLOADS) and bench.HEADLINE not in bench.EXTRA_CONFIGS
+    # the five configurations: single layer, ViT-B MXFP8, ViT-L MXFP8 (headline), ViT-L MXFP4, NVFP4 pair
+    for name in ("single_mxfp8_256x768x768", "vitb16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack",
+                 "vitl16_nvfp4_fc1fc2_train"):
+        assert name in bench.EXTRA_CONFIGS

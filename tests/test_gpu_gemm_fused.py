@@ -15,22 +15,42 @@ from oracle import formats as F
 from oracle import fused as FU
 from oracle import gemm as G
 from oracle import quantize as Q
-from gpu_util import bytes_of, log, to_device_bf16
+from gpu_util import bytes_of, guarded_quantized, log, quantize_guarded, to_device_bf16
 from test_gpu_gemm import exact_operand
 
 pytestmark = pytest.mark.gpu
 MX = ["mxfp8", "mxfp4"]
+EXACT_MNK = [(64, 136, 256), (200, 512, 1024)]
+RANDOM_MNK = [(1, 8, 32), (37, 96, 300), (300, 520, 640), (513, 264, 128)]
+MANY_TILES_MNK = (4160, 4096, 384)
+
+
+def parity_cases():
+    """(M, N, K, fmt, out, epilogue) of every mx_gemm_gelu_quantize this module runs."""
+    cases = []
+    for fmt in MX:
+        cases += [(m, n, k, fmt, "q", "gelu_quant") for (m, n, k) in EXACT_MNK + RANDOM_MNK]
+        cases += [(130, 264, 256, fmt, "q", "gelu_quant"), MANY_TILES_MNK + (fmt, "q", "gelu_quant")]
+        wl = W.VITL_MXFP8 if fmt == "mxfp8" else W.VITL_MXFP4
+        L = {l.name: l for l in wl.linears}["fc1"]
+        cases.append((wl.m, L.n, L.k, fmt, "q", "gelu_quant"))
+        n_edge = 32 * len(EDGE_EXPONENTS)
+        cases += [(3, n_edge, 64, fmt, "q", "gelu_quant"), (4096, 3 * n_edge, 64, fmt, "q", "gelu_quant")]
+    return cases
 
 
 def run_fused(a_bits, b_bits, fmt, bias_bits=None, bias_offset=0):
-    qa = api.mx_quantize(to_device_bf16(a_bits), fmt, "row")
-    qb = api.mx_quantize(to_device_bf16(b_bits), fmt, "row")
+    qa = quantize_guarded(to_device_bf16(a_bits), fmt, "row")
+    qb = quantize_guarded(to_device_bf16(b_bits), fmt, "row")
     bias = None
     if bias_bits is not None:
         padded = np.concatenate([np.zeros(bias_offset, dtype=np.uint16), bias_bits])
         bias = to_device_bf16(padded.reshape(1, -1)).reshape(-1)[bias_offset:]
-    q = api.mx_gemm_gelu_quantize(qa, qb, bias)
-    m = a_bits.shape[0]
+    m, n = a_bits.shape[0], b_bits.shape[0]
+    gc, gs = guarded_quantized(m, n, fmt, "row")
+    q = api.mx_gemm_gelu_quantize(qa, qb, bias, out=api.Quantized(gc.view, gs.view, fmt, m, n))
+    gc.check("fused output codes")
+    gs.check("fused output scales")
     return bytes_of(q.codes).reshape(m, -1), bytes_of(q.scales).reshape(m, -1)
 
 
@@ -56,7 +76,7 @@ def check(a_bits, b_bits, fmt, bias_bits=None, rows=None, gemm_tol=G.TOL, bias_o
 
 
 @pytest.mark.parametrize("fmt", MX)
-@pytest.mark.parametrize("mnk", [(64, 136, 256), (200, 512, 1024)])
+@pytest.mark.parametrize("mnk", EXACT_MNK)
 def test_fused_exact_accumulation(fmt, mnk):
     """Exactly quantized operands (A scaled by 2^-7 so h spans GELU's curved
     range) make every accumulation exact: no GEMM slack."""
@@ -68,7 +88,7 @@ def test_fused_exact_accumulation(fmt, mnk):
 
 
 @pytest.mark.parametrize("fmt", MX)
-@pytest.mark.parametrize("mnk", [(1, 8, 32), (37, 96, 300), (300, 520, 640), (513, 264, 128)])
+@pytest.mark.parametrize("mnk", RANDOM_MNK)
 def test_fused_random(fmt, mnk):
     m, n, k = mnk
     a = W.np_activation((m, k), seed=m + 1)
@@ -91,7 +111,7 @@ def test_fused_unaligned_bias(fmt):
 def test_fused_many_tiles(fmt):
     """More output tiles than resident workgroups: each workgroup's epilogue
     stores stay in flight across the next tile's first stage."""
-    m, n, k = 4160, 4096, 384
+    m, n, k = MANY_TILES_MNK
     a = W.np_activation((m, k), seed=31)
     b = W.np_normal((n, k), seed=32, std=W.W_STD * 2)
     bias = W.np_normal((n,), seed=33, std=W.BIAS_STD)

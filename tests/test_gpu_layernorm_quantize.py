@@ -12,7 +12,7 @@ import torch
 from block_scaled_precision_mx_amd import api
 from oracle import fused as FU
 from oracle import layernorm as L
-from gpu_util import bytes_of, log
+from gpu_util import bytes_of, guarded_quantized, log
 
 pytestmark = pytest.mark.gpu
 MX = ["mxfp8", "mxfp4"]
@@ -42,7 +42,11 @@ def run(x, g, b, eps, fmt, ld=None, offset=0):
     view[:, :cols] = torch.from_numpy(x)
     dev = buf.cuda()
     xd = dev[offset: offset + rows * ld].view(rows, ld)[:, :cols]
-    q = api.mx_layernorm_quantize(xd, torch.from_numpy(g).cuda(), torch.from_numpy(b).cuda(), eps, fmt)
+    gc, gs = guarded_quantized(rows, cols, fmt, "row")
+    q = api.mx_layernorm_quantize(xd, torch.from_numpy(g).cuda(), torch.from_numpy(b).cuda(), eps, fmt,
+                                  out=api.Quantized(gc.view, gs.view, fmt, rows, cols))
+    gc.check("codes")
+    gs.check("scales")
     return bytes_of(q.codes).reshape(rows, -1), bytes_of(q.scales).reshape(rows, -1)
 
 

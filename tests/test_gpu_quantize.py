@@ -10,7 +10,7 @@ import torch
 from block_scaled_precision_mx_amd import api
 from block_scaled_precision_mx_amd import workloads as W
 from oracle import quantize as Q
-from gpu_util import bytes_of, log, to_device_bf16
+from gpu_util import bytes_of, log, quantize_guarded, to_device_bf16
 
 pytestmark = pytest.mark.gpu
 FMTS = ["mxfp8", "mxfp4", "nvfp4"]
@@ -35,7 +35,7 @@ def compare(bits, fmt, axis, src=None):
     rows, cols = bits.shape
     log(f"quantize fmt={fmt} axis={axis} shape={rows}x{cols}")
     x = to_device_bf16(bits) if src is None else src
-    q = api.mx_quantize(x, fmt, axis)
+    q = quantize_guarded(x, fmt, axis)
     ref = Q.quantize(bits, fmt, axis)
     got_codes = bytes_of(q.codes).reshape(ref.rows, -1)
     got_scales = bytes_of(q.scales)

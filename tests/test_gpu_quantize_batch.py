@@ -10,7 +10,7 @@ import torch
 from block_scaled_precision_mx_amd import api
 from block_scaled_precision_mx_amd import workloads as W
 from oracle import quantize as Q
-from gpu_util import bytes_of, log, to_device_bf16
+from gpu_util import bytes_of, guarded_quantized, log, to_device_bf16
 from test_gpu_quantize import special
 
 pytestmark = pytest.mark.gpu
@@ -31,7 +31,12 @@ def test_batch_mixed_shapes(fmt):
     shapes = [(1, 1), (3, 32), (37, 300), (130, 99), (256, 768), (300, 1030), (7, 64), (129, 257)]
     bits_list = [special(*s, seed=11 + i) if i % 2 else W.np_activation(s, seed=11 + i) for i, s in enumerate(shapes)]
     log(f"quantize batch fmt={fmt} items={len(shapes)}")
-    got = api.mx_quantize_batch([to_device_bf16(b) for b in bits_list], fmt)
+    guards = [guarded_quantized(*b.shape, fmt, "row") for b in bits_list]
+    outs = [api.Quantized(gc.view, gs.view, fmt, *b.shape) for (gc, gs), b in zip(guards, bits_list)]
+    got = api.mx_quantize_batch([to_device_bf16(b) for b in bits_list], fmt, out=outs)
+    for i, (gc, gs) in enumerate(guards):
+        gc.check(f"item {i} codes")
+        gs.check(f"item {i} scales")
     check_items(bits_list, got, fmt)
 
 

@@ -11,7 +11,7 @@ import torch
 from block_scaled_precision_mx_amd import api
 from block_scaled_precision_mx_amd import workloads as W
 from oracle import quantize as Q
-from gpu_util import bytes_of, log, to_device_bf16
+from gpu_util import bytes_of, guarded_quantized, log, to_device_bf16
 from test_gpu_quantize import special
 
 pytestmark = pytest.mark.gpu
@@ -26,12 +26,27 @@ def check_copy(q, ref, what):
     assert np.array_equal(got_scales, exp_scales), f"{what}: scales differ at {np.argwhere(got_scales != exp_scales)[:10].tolist()}"
 
 
+def guarded_pair(rows, cols, fmt):
+    """Guarded buffers for the row and the column copy of [rows, cols]."""
+    g = [guarded_quantized(rows, cols, fmt, axis) for axis in ("row", "col")]
+    out = (api.Quantized(g[0][0].view, g[0][1].view, fmt, rows, cols),
+           api.Quantized(g[1][0].view, g[1][1].view, fmt, cols, rows))
+    return out, [b for pair in g for b in pair]
+
+
+def check_guards(guards):
+    for b, what in zip(guards, ("row codes", "row scales", "col codes", "col scales")):
+        b.check(what)
+
+
 def compare_dual(bits, fmt, amax_prev=None, headroom=32.0, src=None):
     rows, cols = bits.shape
     log(f"quantize_dual fmt={fmt} shape={rows}x{cols} amax_prev={amax_prev} headroom={headroom}")
     x = to_device_bf16(bits) if src is None else src
     ap = None if amax_prev is None else torch.tensor([amax_prev], dtype=torch.float32, device="cuda")
-    row, col = api.mx_quantize_dual(x, fmt, ap, headroom)
+    out, guards = guarded_pair(rows, cols, fmt)
+    row, col = api.mx_quantize_dual(x, fmt, ap, headroom, out=out)
+    check_guards(guards)
     rref, cref = Q.quantize_dual(bits, fmt, amax_prev, headroom)
     check_copy(row, rref, "row copy")
     check_copy(col, cref, "col copy")
@@ -126,7 +141,9 @@ def compare_dual_sr(bits, seed, amax_prev=None, headroom=32.0):
     prev = None
     if amax_prev is not None:
         prev = torch.tensor([amax_prev], dtype=torch.float32, device="cuda")
-    row, col = api.mx_quantize_dual_sr(to_device_bf16(bits), seed, prev, headroom)
+    out, guards = guarded_pair(rows, cols, "nvfp4")
+    row, col = api.mx_quantize_dual_sr(to_device_bf16(bits), seed, prev, headroom, out=out)
+    check_guards(guards)
     r_ref, c_ref = Q.quantize_dual_sr(bits, seed, amax_prev, headroom)
     check_copy(row, r_ref, "row")
     check_copy(col, c_ref, "col")

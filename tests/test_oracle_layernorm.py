@@ -163,3 +163,63 @@ def test_padding_codes_must_be_zero():
     ok_c, _ = L.check_rows(codes, q.scales, x, g, b, 1e-6, "mxfp8")
     assert not ok_c[1, 230]
     assert FU.check_intervals  # the shared acceptance used above
+
+
+def _enc(v, e, fmt):
+    x = np.ldexp(np.asarray(v, dtype=np.float64), -e)
+    return F.e4m3_encode(x) if fmt == "mxfp8" else F.e2m1_encode(x)
+
+
+def test_scale_and_codes_must_come_from_one_choice():
+    """A constant row (x = 40, so 1/sqrt(var + eps) = 1000 and the allowance
+    2^-16 (r |mu| + |beta| + |y|) is about 0.61) with beta = 4 in column 0:
+    y0 may be anything in about [3.39, 4.61], straddling MXFP4's binade
+    boundary 4 = 2^emax. Block exponent 0 with every code taken from the
+    intervals' low ends (y0 -> code 3) is explained by no single choice (a
+    y0 that encodes to 3 is below 4, so the amax would give exponent -1),
+    although each code and the exponent are possible on their own. The exact
+    LayerNorm output (exponent 0, y0 = 4) is accepted."""
+    fmt, cols, eps = "mxfp4", 64, 1e-6
+    x = np.full((1, cols), 40.0, np.float32)
+    g = np.ones(cols, np.float32)
+    b = np.full(cols, 0.5, np.float32)
+    b[0] = 4.0
+    y, tol = L.tolerance(x, g, b, eps)
+    lo, hi = F.f64_to_bf16_rne(y - tol), F.f64_to_bf16_rne(y + tol)
+    assert lo[0, 0] < 3.5 and hi[0, 0] >= 4.0
+    planted = np.zeros((1, 128), np.uint8)
+    planted[0, :cols] = _enc(lo, 0, fmt)
+    assert F.e2m1_decode(planted[0, 0]) == 3.0
+    scales = np.array([[127, 0, 0, 0]], np.uint8)
+    scales[0, 1] = L.reference_codes(x, g, b, eps, fmt).scales[0, 1]
+    ok_c, ok_s = L.check_rows(planted, scales, x, g, b, eps, fmt)
+    assert ok_c.all() and not ok_s[0, 0]
+    q = L.reference_codes(x, g, b, eps, fmt)
+    assert q.scales[0, 0] == 127
+    ok_c, ok_s = L.check_rows(q.codes, q.scales, x, g, b, eps, fmt)
+    assert ok_c.all() and ok_s.all()
+
+
+def test_zero_codes_keep_the_sign():
+    """Elements whose LayerNorm output is negative (interval entirely below
+    zero) but rounds to zero at the block's exponent carry the negative-zero
+    code; the positive zero there is rejected. MXFP4 only: for MXFP8 the
+    allowance is wider than the values that round to zero, so every zero
+    code's interval straddles zero and either sign is right."""
+    fmt = "mxfp4"
+    x = rows(16, 512, seed=41, scale=1.0)
+    rng = np.random.default_rng(42)
+    g = (1 + 0.1 * rng.standard_normal(512)).astype(np.float32)
+    b = (0.05 * rng.standard_normal(512)).astype(np.float32)
+    eps = 1e-6
+    q = L.reference_codes(x, g, b, eps, fmt)
+    y, tol = L.tolerance(x, g, b, eps)
+    hi = F.f64_to_bf16_rne(y + tol)
+    neg_zero = 0x80 if fmt == "mxfp8" else 0x8
+    cand = np.argwhere((q.codes[:, :512] == neg_zero) & (hi < 0))
+    assert len(cand) >= 5, len(cand)
+    bad = q.codes.copy()
+    r, c = cand[:, 0], cand[:, 1]
+    bad[r, c] = 0
+    ok_c, _ = L.check_rows(bad, q.scales, x, g, b, eps, fmt)
+    assert not ok_c[r, c].any() and ok_c.sum() == ok_c.size - len(cand)

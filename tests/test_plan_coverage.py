@@ -1,0 +1,67 @@
+"""Every GEMM the benchmark launches runs a kernel configuration that the GPU
+parity tests check (host-side: plans come from the library's own tile
+choice, no GPU needed). A configuration is the kernel instantiation
+(mx_gemm_plan) together with its epilogue, output dtype and whether N is a
+multiple of 8 (which selects the LDS-staged or the register store path)."""
+import bench
+from block_scaled_precision_mx_amd import api
+import test_gpu_gemm
+import test_gpu_gemm_fused
+
+
+def config_key(m, n, k, fmt, out, epilogue):
+    return (api.gemm_plan(m, n, k, fmt), epilogue, out, n % 8 == 0)
+
+
+def parity_cases():
+    return test_gpu_gemm.parity_cases() + test_gpu_gemm_fused.parity_cases()
+
+
+def bench_specs(names):
+    for name in names:
+        for s in bench.workload_gemms(name):
+            yield name, s
+
+
+def test_every_benchmarked_configuration_has_gpu_parity():
+    covered = {config_key(*c) for c in parity_cases()}
+    missing = set()
+    for name, s in bench_specs(bench.WORKLOADS):
+        key = config_key(s.m, s.n, s.k, s.fmt, s.out, s.epilogue)
+        if key not in covered:
+            missing.add((name, s.label, key))
+    assert not missing, sorted(missing)
+
+
+def test_every_measured_shape_has_full_size_gpu_parity():
+    """The headline and every configuration in the default benchmark line:
+    each distinct GEMM shape is itself a GPU parity case (full or sampled)."""
+    shapes = {(m, n, k, fmt, epi) for (m, n, k, fmt, _, epi) in parity_cases()}
+    missing = set()
+    for name, s in bench_specs([bench.HEADLINE] + bench.EXTRA_CONFIGS):
+        if (s.m, s.n, s.k, s.fmt, s.epilogue) not in shapes:
+            missing.add((name, s.label, s.m, s.n, s.k, s.fmt))
+    assert not missing, sorted(missing)
+
+
+def test_workload_gemm_lists():
+    """The GEMM lists are what the workloads define: four linears per block for
+    the stacks, six GEMMs for the fc1/fc2 pair, twelve per block for the
+    block-training workloads (four fprop, then dgrad and wgrad per linear)."""
+    from block_scaled_precision_mx_amd import workloads as W
+    st = W.VITL_MXFP8
+    specs = bench.workload_gemms(st.name)
+    assert len(specs) == 4 * st.blocks
+    assert sum(2 * s.m * s.n * s.k for s in specs) == st.gemm_flops()
+    tp = W.TRAIN_PAIR
+    specs = bench.workload_gemms(tp.name)
+    assert len(specs) == 6 and sum(2 * s.m * s.n * s.k for s in specs) == tp.gemm_flops()
+    for bt in W.BLOCK_TRAINS.values():
+        specs = bench.workload_gemms(bt.name)
+        assert len(specs) == 12 * bt.blocks
+        assert sum(2 * s.m * s.n * s.k for s in specs) == bt.gemm_flops()
+        first = specs[:12]
+        assert [s.label for s in first[:4]] == [f"gemm_{l}_fprop" for l in ("qkv", "proj", "fc1", "fc2")]
+        assert all(s.fmt == bt.fwd_fmt for s in first[:4]) and all(s.fmt == bt.bwd_fmt for s in first[4:])
+        # wgrad contracts over the tokens
+        assert all(s.k == bt.m for s in first if s.label.endswith("wgrad"))
