@@ -24,8 +24,9 @@ The JSON line reports, for the headline workload (the ViT-L MXFP8 forward
 stack), whole-step throughput in GEMM TFLOP/s (the GEMM flops of the step
 over the step time, quantization included); the dominant GEMM kernel
 configuration against the MFMA roofline, its average launch duration taken
-from HIP events around every launch of an instrumented replay of the same
-steps on the stream the kernels run on; the quantizer's algorithmic
+from HIP events on the stream the kernels run on, around replays of the
+step's launches grouped by label (each launch on its own operands, as in
+the step); the quantizer's algorithmic
 bandwidth; the CPU oracle on a bounded sample of the same workload; and,
 under "configs", the same figures for every other configuration.
 """
@@ -67,8 +68,9 @@ PAGES_CONTEXT = {
     "vitl16_p3_block_train": "README section 5.4: backbone dgrad / wgrad GEMM time per step drops from 8.4-8.8 ms "
                              "(MXFP8) to 4.5-4.6 ms (NVFP4) on an RTX 5090",
 }
-# input sets the training workloads alternate between, one per step
-TRAIN_SETS = 2
+# input sets the fc1/fc2 training workloads rotate through, one per step:
+# together they hold more than the 256 MB Infinity Cache
+TRAIN_SETS = 4
 
 
 def parse():
@@ -354,10 +356,13 @@ def build(name, dev):
 # ------------------------------------------------------------------ timing
 
 def measure(sets, steps, warmup, stream):
-    """ms per step over `steps` timed steps, then per-op average durations
-    from an instrumented replay of as many steps (HIP events around every
-    launch, on the stream the kernels run on). Step s runs input set
-    s % len(sets)."""
+    """ms per step over `steps` timed steps (step s runs input set
+    s % len(sets)), then the average duration of every launch, per label:
+    each replay runs all launches of one label (every block's, every set's,
+    each on its own tensors as in the step) back to back between one pair of
+    HIP events on the stream the kernels run on, so that the events' own
+    overhead is spread over many launches; `steps` replays are averaged.
+    Returns (ms per step, [(op, average ms)] for the ops of every set)."""
     import torch
 
     def step(s):
@@ -376,29 +381,28 @@ def measure(sets, steps, warmup, stream):
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / steps
 
-    per_op = [[0.0] * len(ops) for ops in sets]
-    runs = [0] * len(sets)
-    for s in range(steps):
-        ops = sets[s % len(sets)]
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
-        for (e0, e1), op in zip(ev, ops):
-            e0.record(stream)
-            op.fn()
-            e1.record(stream)
+    groups = {}
+    for ops in sets:
+        for op in ops:
+            groups.setdefault(op.label, []).append(op)
+    per_label = {lab: 0.0 for lab in groups}
+    for _ in range(steps):
+        ev = {lab: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for lab in groups}
+        for lab, ops in groups.items():
+            ev[lab][0].record(stream)
+            for op in ops:
+                op.fn()
+            ev[lab][1].record(stream)
         torch.cuda.synchronize()
-        for i, (e0, e1) in enumerate(ev):
-            per_op[s % len(sets)][i] += e0.elapsed_time(e1)
-        runs[s % len(sets)] += 1
-    timed = []
-    for si, ops in enumerate(sets):
-        if runs[si]:
-            timed += [(op, t / runs[si]) for op, t in zip(ops, per_op[si])]
+        for lab, ops in groups.items():
+            per_label[lab] += ev[lab][0].elapsed_time(ev[lab][1]) / len(ops)
+    timed = [(op, per_label[op.label] / steps) for ops in sets for op in ops]
     return ms_per_step, timed, len(sets)
 
 
 def summarize(timed, n_sets):
     """Per-label, per-kernel-configuration and quantization figures from the
-    instrumented replay. `timed` holds (op, average duration in ms) for the
+    grouped replays. `timed` holds (op, average duration in ms) for the
     ops of all n_sets input sets; per-step figures divide by n_sets."""
     by_label, plans = {}, {}
     gemm_ms = quant_ms = quant_bytes = gemm_flops = 0.0

@@ -496,9 +496,12 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
     int slot = 0;
 
     for (int ks = 0; ks < nk; ++ks) {
-      // this stage's copies are done; after the previous tile's epilogue its
-      // EPI_TOTAL stores (issued after them) may still be in flight
-      if (ks == 0 && ctc > 0) wait_vm<Cfg::EPI_TOTAL>();
+      // this stage's copies are done; after the previous tile's LDS-staged
+      // epilogue its EPI_TOTAL stores (issued after them) may still be in
+      // flight. The register epilogue drains its stores itself, so there the
+      // count must be 0: an allowance would let this stage's own copies
+      // (fewer than EPI_TOTAL per wave) still be in flight.
+      if (ks == 0 && ctc > 0 && staged) wait_vm<Cfg::EPI_TOTAL>();
       else wait_vm<0>();
       block_sync();                         // everyone's copies are visible, and everyone is done
                                             // with the buffers the next copies overwrite

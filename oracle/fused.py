@@ -105,17 +105,19 @@ def reference_codes(h_bits: np.ndarray, fmt: str) -> Q.Quantized:
 
 
 def check_rows(codes_rows: np.ndarray, scales_rows: np.ndarray, c: np.ndarray, s: np.ndarray, fmt: str,
-               n: int, gemm_tol: float = G.TOL):
+               n: int, gemm_tol: float = G.TOL, extra=0.0):
     """Accept / reject the fused output of some rows.
 
     codes_rows: [R, K_pad] element codes (unpacked, one per element) of the
     GPU output rows; scales_rows: [R, K_pad / 32] scale bytes; c, s: [R, n]
-    exact (acc + bias) and S of those rows. Returns (ok_codes [R, K_pad],
-    ok_scales [R, K_pad / 32]) boolean masks."""
+    exact (acc + bias) and S of those rows; `extra` [R, n] (or a scalar) widens
+    the GEMM allowance (the MXFP8 matrix instruction's adder term H of
+    oracle.gemm). Returns (ok_codes [R, K_pad], ok_scales [R, K_pad / 32])
+    boolean masks."""
     if fmt not in ("mxfp8", "mxfp4"):
         raise ValueError("the fused path emits MX formats")
-    h_lo = F.f64_to_bf16_rne(c - gemm_tol * s)
-    h_hi = F.f64_to_bf16_rne(c + gemm_tol * s)
+    h_lo = F.f64_to_bf16_rne(c - gemm_tol * s - extra)
+    h_hi = F.f64_to_bf16_rne(c + gemm_tol * s + extra)
     g_lo, g_hi = _bf16_interval_of_gelu(h_lo, h_hi)
     return check_intervals(codes_rows, scales_rows, g_lo, g_hi, fmt, n)
 

@@ -11,6 +11,8 @@
 """
 from fractions import Fraction
 
+import math
+
 import numpy as np
 import pytest
 
@@ -153,3 +155,83 @@ def test_quantization_error_is_format_ordered():
         c, _ = G.gemm_ref(Q.quantize(a_bits, fmt), Q.quantize(b_bits, fmt))
         err[fmt] = np.linalg.norm(c - exact) / np.linalg.norm(exact)
     assert 0.005 < err["mxfp8"] < err["nvfp4"] < err["mxfp4"] < 0.5, err
+
+
+# ---------------------------------------------------------------- MXFP8 adder term
+
+def _emulate_group_adder(ah, bh):
+    """An independent emulation of the adder the MXFP8 term describes: per
+    group of 8 consecutive K elements, every product truncated toward zero to
+    a multiple of 2^(E - 13), E the binade of the group's largest product;
+    groups summed exactly."""
+    from fractions import Fraction
+    total = Fraction(0)
+    for g0 in range(0, len(ah), 8):
+        prods = [Fraction(float(x)) * Fraction(float(y)) for x, y in zip(ah[g0:g0 + 8], bh[g0:g0 + 8])]
+        mx = max(abs(p) for p in prods)
+        if mx == 0:
+            continue
+        e = math.floor(math.log2(mx))
+        while Fraction(2) ** e > mx:
+            e -= 1
+        while Fraction(2) ** (e + 1) <= mx:
+            e += 1
+        q = Fraction(2) ** (e - 13)
+        for p in prods:
+            t = abs(p) // q * q
+            total += t if p >= 0 else -t
+    return total
+
+
+def test_mxfp8_group_term_worked_example():
+    """One group holding 256 and seven products of 0.234375: the adder's
+    quantum is 2^(8 - 13) = 1/32, so H = 7/32; a product in the next group
+    adds nothing (its group's quantum is its own)."""
+    a = np.zeros((1, 32)); b = np.zeros((1, 32))
+    a[0, 0], b[0, 0] = 256.0, 1.0
+    a[0, 1:8], b[0, 1:8] = 0.234375, 1.0
+    a[0, 8], b[0, 8] = 0.234375, 1.0
+    qa, qb = Q.quantize(W.to_bf16_bits(a), "mxfp8"), Q.quantize(W.to_bf16_bits(b), "mxfp8")
+    h = G.mxfp8_group_term(qa, qb, [0], [0])
+    assert h[0] == 7 / 32 + 7 * 2.0 ** (math.floor(math.log2(0.234375)) - 13)
+    emu = _emulate_group_adder(qa.dequantize()[0], qb.dequantize()[0])
+    assert float(emu) == 256 + 7 * 0.21875 + 0.234375      # the hardware's result on the GPU
+
+
+def test_mxfp8_group_term_bounds_the_adder():
+    """On outlier-heavy random operands the emulated adder's sum stays within
+    H of the exact one, H <= 7 * 2^-13 S, and the other formats get H = 0."""
+    rng = np.random.default_rng(5)
+    for trial in range(6):
+        k = 64 + 32 * trial + (trial % 3)
+        a = W.np_activation((3, k), seed=100 + trial)
+        a = W.to_bf16_bits(F.bf16_to_f64(a) * np.where(rng.random((3, k)) < 0.05, 50.0, 1.0))
+        b = W.np_normal((4, k), seed=200 + trial, std=W.W_STD)
+        qa, qb = Q.quantize(a, "mxfp8"), Q.quantize(b, "mxfp8")
+        rows, cols = np.repeat(np.arange(3), 4), np.tile(np.arange(4), 3)
+        c, s = G.gemm_ref_entries(qa, qb, rows, cols)
+        h = G.mxfp8_group_term(qa, qb, rows, cols)
+        assert np.all(h <= 7 * 2.0 ** -13 * s)
+        ah, bh = qa.dequantize(), qb.dequantize()
+        for i, (r, cc) in enumerate(zip(rows, cols)):
+            emu = float(_emulate_group_adder(ah[r], bh[cc]))
+            assert abs(emu - c[i]) <= h[i] + 1e-300, (trial, r, cc, emu - c[i], h[i])
+        for fmt in ("mxfp4", "nvfp4"):
+            q4a, q4b = Q.quantize(a, fmt), Q.quantize(b, fmt)
+            assert not G.mxfp8_group_term(q4a, q4b, rows, cols).any()
+
+
+def test_accept_entries_adds_the_term_only_for_mxfp8():
+    """An output off by more than 2^-12 S but within 2^-12 S + H is accepted
+    for MXFP8 only."""
+    a = np.zeros((1, 32)); b = np.zeros((1, 32))
+    a[0, 0], b[0, 0] = 256.0, 1.0
+    a[0, 1:8], b[0, 1:8] = 0.234375, 1.0
+    bits_a, bits_b = W.to_bf16_bits(a), W.to_bf16_bits(b)
+    qa, qb = Q.quantize(bits_a, "mxfp8"), Q.quantize(bits_b, "mxfp8")
+    c, s = G.gemm_ref_entries(qa, qb, [0], [0])
+    hw = np.array([256 + 7 * 0.21875])
+    assert not G.accept(hw, c, s, "f32").all()
+    assert G.accept_entries(hw, c, s, "f32", qa, qb, [0], [0]).all()
+    wrong = hw - 0.25
+    assert not G.accept_entries(wrong, c, s, "f32", qa, qb, [0], [0]).any()
