@@ -68,6 +68,9 @@ PAGES_CONTEXT = {
     "vitl16_p3_block_train": "README section 5.4: backbone dgrad / wgrad GEMM time per step drops from 8.4-8.8 ms "
                              "(MXFP8) to 4.5-4.6 ms (NVFP4) on an RTX 5090",
 }
+# workspace the training workloads give their GEMMs (mx_gemm_ws): enough for
+# the split-K partials of every weight-gradient GEMM of the ViT-L shapes
+WORKSPACE_BYTES = 64 << 20
 # input sets the fc1/fc2 training workloads rotate through, one per step:
 # together they hold more than the 256 MB Infinity Cache
 TRAIN_SETS = 4
@@ -99,6 +102,7 @@ class GemmSpec:
     fmt: str
     epilogue: str = "c"          # "c": bf16 C out; "gelu_quant": fc1 writing fc2's operand
     out: str = "bf16"
+    ws: bool = False             # launched by mx_gemm_ws with WORKSPACE_BYTES of workspace
 
 
 def workload_gemms(name):
@@ -115,18 +119,18 @@ def workload_gemms(name):
     elif name in W.TRAIN_PAIRS:
         tp = W.TRAIN_PAIRS[name]
         for lin, n_out, k_in in (("fc1", tp.mlp, tp.hidden), ("fc2", tp.hidden, tp.mlp)):
-            specs.append(GemmSpec(f"gemm_{lin}_fprop", tp.m, n_out, k_in, tp.fmt))
-            specs.append(GemmSpec(f"gemm_{lin}_dgrad", tp.m, k_in, n_out, tp.fmt))
-            specs.append(GemmSpec(f"gemm_{lin}_wgrad", n_out, k_in, tp.m, tp.fmt))
+            specs.append(GemmSpec(f"gemm_{lin}_fprop", tp.m, n_out, k_in, tp.fmt, ws=True))
+            specs.append(GemmSpec(f"gemm_{lin}_dgrad", tp.m, k_in, n_out, tp.fmt, ws=True))
+            specs.append(GemmSpec(f"gemm_{lin}_wgrad", n_out, k_in, tp.m, tp.fmt, ws=True))
     elif name in W.BLOCK_TRAINS:
         bt = W.BLOCK_TRAINS[name]
         lins = bt.linears()
         for _ in range(bt.blocks):
             for lin in lins:
-                specs.append(GemmSpec(f"gemm_{lin.name}_fprop", bt.m, lin.n, lin.k, bt.fwd_fmt))
+                specs.append(GemmSpec(f"gemm_{lin.name}_fprop", bt.m, lin.n, lin.k, bt.fwd_fmt, ws=True))
             for lin in reversed(lins):
-                specs.append(GemmSpec(f"gemm_{lin.name}_dgrad", bt.m, lin.k, lin.n, bt.bwd_fmt))
-                specs.append(GemmSpec(f"gemm_{lin.name}_wgrad", lin.n, lin.k, bt.m, bt.bwd_fmt))
+                specs.append(GemmSpec(f"gemm_{lin.name}_dgrad", bt.m, lin.k, lin.n, bt.bwd_fmt, ws=True))
+                specs.append(GemmSpec(f"gemm_{lin.name}_wgrad", lin.n, lin.k, bt.m, bt.bwd_fmt, ws=True))
     else:
         raise KeyError(name)
     return specs
@@ -134,6 +138,8 @@ def workload_gemms(name):
 
 def gemm_plan(spec: GemmSpec) -> str:
     from block_scaled_precision_mx_amd import api
+    if spec.ws:
+        return api.gemm_ws_plan(spec.m, spec.n, spec.k, spec.fmt, WORKSPACE_BYTES)
     return api.gemm_plan(spec.m, spec.n, spec.k, spec.fmt) + ("+gelu+quant" if spec.epilogue == "gelu_quant" else "")
 
 
@@ -157,12 +163,16 @@ def _empty_q(rows, cols, fmt, axis, dev):
                          fmt, stored, length)
 
 
-def _gemm_op(ops, spec, a, b, bias, dev):
+def _gemm_op(ops, spec, a, b, bias, dev, ws=None):
+    """A GEMM launch: mx_gemm, or mx_gemm_ws with the workload's workspace."""
     import torch
     from block_scaled_precision_mx_amd import api
     out = torch.empty((spec.m, spec.n), dtype=torch.bfloat16, device=dev)
-    ops.append(Op("gemm", lambda: api.mx_gemm(a, b, bias, "bf16", out), spec.label,
-                  flops=2.0 * spec.m * spec.n * spec.k, spec=spec))
+    if spec.ws:
+        fn = lambda: api.mx_gemm_ws(a, b, bias, "bf16", ws, out)   # noqa: E731
+    else:
+        fn = lambda: api.mx_gemm(a, b, bias, "bf16", out)          # noqa: E731
+    ops.append(Op("gemm", fn, spec.label, flops=2.0 * spec.m * spec.n * spec.k, spec=spec))
 
 
 def build_stack(stack, dev):
@@ -238,7 +248,9 @@ def build_train(tp, dev):
     """TRAIN_SETS steps of the fc1/fc2 training pair, each on its own tensors."""
     from block_scaled_precision_mx_amd import workloads as W
 
+    import torch
     fmt = tp.fmt
+    ws = torch.empty(WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     sets = []
     for s in range(TRAIN_SETS):
         S = lambda tid: W.seed(tp.wid, s, tid)   # noqa: E731
@@ -256,10 +268,10 @@ def build_train(tp, dev):
         for x, w, dy, bias, lin in ((X, W1, dY1, b1, "fc1"), (H, W2, dY2, b2, "fc2")):
             x_row, x_col = _quant_dual(ops, f"quant_{lin}_x_rowcol", x, fmt, dev)
             w_row, w_col = _quant_dual(ops, f"quant_{lin}_w_rowcol", w, fmt, dev)
-            _gemm_op(ops, next(specs), x_row, w_row, bias, dev)                       # fprop
+            _gemm_op(ops, next(specs), x_row, w_row, bias, dev, ws)                   # fprop
             dy_row, dy_col = _quant_dual(ops, f"quant_{lin}_dy_rowcol", dy, fmt, dev, sr)
-            _gemm_op(ops, next(specs), dy_row, w_col, None, dev)                      # dgrad
-            _gemm_op(ops, next(specs), dy_col, x_col, None, dev)                      # wgrad
+            _gemm_op(ops, next(specs), dy_row, w_col, None, dev, ws)                  # dgrad
+            _gemm_op(ops, next(specs), dy_col, x_col, None, dev, ws)                  # wgrad
         sets.append(ops)
     return sets
 
@@ -277,9 +289,11 @@ def build_block_train(bt, dev):
     from block_scaled_precision_mx_amd import api
     from block_scaled_precision_mx_amd import workloads as W
 
+    import torch
     specs = iter(workload_gemms(bt.name))
     lins = bt.linears()
     ff, bf = bt.fwd_fmt, bt.bwd_fmt
+    ws = torch.empty(WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     sr = bt.sr_seed if bt.sr_grads else None
     ops = []
     for blk in range(bt.blocks):
@@ -300,7 +314,7 @@ def build_block_train(bt, dev):
                               api.mx_quantize_batch([x, w], ff, out=[qa, qw]), f"quant_{lin.name}_x_w",
                               nbytes=QUANT_BYTES[ff] * (x.numel() + w.numel())))
                 x_col, w_col = None, None
-            _gemm_op(ops, next(specs), x_row, w_row, bias, dev)
+            _gemm_op(ops, next(specs), x_row, w_row, bias, dev, ws)
             saved.append((lin, x, w, dy, x_col, w_col))
         for lin, x, w, dy, x_col, w_col in reversed(saved):  # backward
             if x_col is None:
@@ -312,8 +326,8 @@ def build_block_train(bt, dev):
                 ops.append(Op("quant", lambda w=w, q=w_col: api.mx_quantize(w, bf, "col", q.codes, q.scales),
                               f"quant_{lin.name}_w_col", nbytes=(QUANT_BYTES[bf] + amax) * w.numel()))
             dy_row, dy_col = _quant_dual(ops, f"quant_{lin.name}_dy_rowcol", dy, bf, dev, sr)
-            _gemm_op(ops, next(specs), dy_row, w_col, None, dev)       # dgrad: dX = dY W
-            _gemm_op(ops, next(specs), dy_col, x_col, None, dev)       # wgrad: dW = dY^T X
+            _gemm_op(ops, next(specs), dy_row, w_col, None, dev, ws)   # dgrad: dX = dY W
+            _gemm_op(ops, next(specs), dy_col, x_col, None, dev, ws)   # wgrad: dW = dY^T X
     return [ops]
 
 

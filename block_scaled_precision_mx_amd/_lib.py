@@ -38,7 +38,12 @@ SIGNATURES = {
     "mx_gemm_gelu_quantize": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
                                          _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                          _c.c_void_p]),
+    "mx_gemm_ws": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
+                              _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_size_t,
+                              _c.c_void_p]),
+    "mx_gemm_workspace_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "mx_gemm_plan": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
+    "mx_gemm_ws_plan": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_size_t]),
     "mx_last_error": (_c.c_char_p, []),
 }
 

@@ -60,6 +60,19 @@ def gemm_plan(M: int, N: int, K: int, fmt: str) -> str:
     return name.decode()
 
 
+def gemm_workspace_bytes(M: int, N: int, K: int, fmt: str) -> int:
+    """Workspace bytes with which mx_gemm_ws runs its fastest plan (0: no split)."""
+    return lib().mx_gemm_workspace_bytes(M, N, K, FMT[fmt])
+
+
+def gemm_ws_plan(M: int, N: int, K: int, fmt: str, workspace_bytes: int) -> str:
+    """Kernel configuration mx_gemm_ws launches with that much workspace."""
+    name = lib().mx_gemm_ws_plan(M, N, K, FMT[fmt], workspace_bytes)
+    if name is None:
+        raise ValueError("invalid GEMM sizes or format")
+    return name.decode()
+
+
 def codes_bytes(rows: int, cols: int, fmt: str, axis: str = "row") -> int:
     return lib().mx_codes_bytes(rows, cols, FMT[fmt], AXIS[axis])
 
@@ -231,6 +244,26 @@ def mx_gemm(a: Quantized, b: Quantized, bias: torch.Tensor | None = None, out_dt
     _check(lib().mx_gemm(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
                          out.data_ptr(), M, N, K, FMT[a.fmt], None if bias is None else bias.data_ptr(),
                          OUT[out_dtype], _stream(stream)))
+    return out
+
+
+def mx_gemm_ws(a: Quantized, b: Quantized, bias: torch.Tensor | None, out_dtype: str,
+               workspace: torch.Tensor | None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mx_gemm that may split K over a device workspace (uint8 tensor, or None)."""
+    if a.fmt != b.fmt or a.length != b.length:
+        raise ValueError("operands must share format and K")
+    M, N, K = a.rows, b.rows, a.length
+    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=a.codes.device)
+    if out.dtype != dt or out.numel() < M * N or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of M*N elements of the output dtype")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bf16 tensor of N elements")
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    _check(lib().mx_gemm_ws(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
+                            out.data_ptr(), M, N, K, FMT[a.fmt], None if bias is None else bias.data_ptr(),
+                            OUT[out_dtype], ws_ptr, ws_bytes, _stream(stream)))
     return out
 
 

@@ -53,6 +53,8 @@
 #include "mx_launch.h"
 
 #include <algorithm>
+#include <cstdio>
+#include <mutex>
 
 namespace mx {
 
@@ -318,13 +320,17 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
                                                           const uint8_t* __restrict__ Bs, void* __restrict__ C,
                                                           int M, int N, int kpad,
                                                           const uint16_t* __restrict__ bias, int out_f32,
-                                                          int tiles_m, int tiles_n, uint8_t* __restrict__ qcodes = nullptr,
-                                                          uint8_t* __restrict__ qscales = nullptr, int qld = 0) {
+                                                          int tiles_m, int tiles_n, uint8_t* __restrict__ qcodes,
+                                                          uint8_t* __restrict__ qscales, int qld, int splits,
+                                                          float* __restrict__ ws) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int RB = Cfg::RB, CH = Cfg::CH, NW = Cfg::NW, CPR = Cfg::CPR;
   __shared__ __align__(16) uint8_t lds[Cfg::LDS];
 
-  const int tiles = tiles_m * tiles_n;
+  // work items: (tile, split) pairs; with splits > 1 an item covers the K
+  // stages [k0, k1) of its split and writes an fp32 partial tile to
+  // ws + split M N (no bias), summed by the split-K reduction afterwards
+  const int tiles = tiles_m * tiles_n * splits;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
@@ -337,7 +343,16 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   // bf16 output goes through LDS and 32-bit buffer offsets when C is below
   // 2 GiB; anything else is stored from registers with 64-bit addresses
   // (the quantized output always goes through LDS; the host ensures N % 8 == 0)
-  const bool staged = Cfg::EPI == 1 || (!out_f32 && (N & 7) == 0 && (int64_t)M * N < ((int64_t)1 << 30));
+  const bool staged = Cfg::EPI == 1 || (splits == 1 && !out_f32 && (N & 7) == 0 && (int64_t)M * N < ((int64_t)1 << 30));
+  // the coordinates and K-stage range of work item t
+  auto item = [&](int t, int& tm, int& tn, int& sp, int& k0, int& k1) {
+    int tnv;
+    tile_coords(t, tiles_m, tiles_n * splits, tm, tnv);
+    tn = tnv % tiles_n;
+    sp = tnv / tiles_n;
+    k0 = (sp * nk) / splits;
+    k1 = ((sp + 1) * nk) / splits;
+  };
   // quantized output: rows of qld elements (K_pad of N), codes and scale bytes
   const int q_row_bytes = (Cfg::FMT == FMT_MXFP8) ? qld : qld / 2;
   const __amdgpu_buffer_rsrc_t q_rs =
@@ -383,11 +398,12 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   // copy cursor: tile lt (first rows m0l / n0l; a_base / b_base are the byte
   // offsets of its A rows and of its B rows shifted down by BM), its stage
   // lks; lgs / lgc / ltc count stages / scale chunks / tiles issued so far
-  int lt = blockIdx.x, lks = 0, lgs = 0, lgc = 0, ltc = 0, m0l = 0, n0l = 0;
+  int lt = blockIdx.x, lks = 0, lk0 = 0, lk1 = nk, lgs = 0, lgc = 0, ltc = 0, m0l = 0, n0l = 0;
   uint32_t a_base = 0, b_base = 0;
   auto set_copy_tile = [&](int t) {
-    int tm, tn;
-    tile_coords(t, tiles_m, tiles_n, tm, tn);
+    int tm, tn, sp;
+    item(t, tm, tn, sp, lk0, lk1);
+    lks = lk0;
     m0l = tm * BM;
     n0l = tn * BN;
     a_base = (uint32_t)m0l * (uint32_t)row_bytes;
@@ -400,11 +416,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   uint32_t cp_st = 0, cp_soff = 0;
   bool cp_in_row = false;
   auto open_copy_stage = [&]() {
-    if (lks == 0 && bias_dma && wave == 0) {  // the tile's bias, into bias slot ltc & 1
+    if (lks == lk0 && bias_dma && wave == 0) {  // the tile's bias, into bias slot ltc & 1
       const uint32_t voff = lane < BN / 8 ? (uint32_t)((n0l + 8 * lane) * 2) : 0x80000000u;
       dma16(bias_rs, lds_base + (uint32_t)(Cfg::BIAS_OFF + (ltc & 1) * 1024), voff, 0u);
     }
-    if (lks % Cfg::SPC == 0) {               // first stage of a scale chunk: bring the chunk too
+    if (lks == lk0 || lks % Cfg::SPC == 0) {  // first stage of a scale chunk: bring the chunk too
       const uint32_t dst = sc_base + (uint32_t)((lgc & 1) * Cfg::SCHUNK);
       const uint32_t soff = (uint32_t)(16 * (lks / Cfg::SPC));
 #pragma unroll
@@ -435,8 +451,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   };
   auto close_copy_stage = [&]() {
     ++lgs;
-    if (++lks == nk) {
-      lks = 0;
+    if (++lks == lk1) {
+      lks = lk0;
       ++ltc;
       lt += gridDim.x;
       if (lt < tiles) set_copy_tile(lt);
@@ -445,11 +461,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   // The whole next stage in one burst. Everything it needs is local, which
   // keeps the register budget of the 256 x 256 tile within 256.
   auto issue_next = [&]() {
-    if (lks == 0 && bias_dma && wave == 0) {
+    if (lks == lk0 && bias_dma && wave == 0) {
       const uint32_t voff = lane < BN / 8 ? (uint32_t)((n0l + 8 * lane) * 2) : 0x80000000u;
       dma16(bias_rs, lds_base + (uint32_t)(Cfg::BIAS_OFF + (ltc & 1) * 1024), voff, 0u);
     }
-    if (lks % Cfg::SPC == 0) {
+    if (lks == lk0 || lks % Cfg::SPC == 0) {
       const uint32_t dst = sc_base + (uint32_t)((lgc & 1) * Cfg::SCHUNK);
       const uint32_t soff = (uint32_t)(16 * (lks / Cfg::SPC));
 #pragma unroll
@@ -484,9 +500,12 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   int gs = 0, gc = 0, ctc = 0;              // compute cursor: stages / scale chunks / tiles consumed
 
   for (int ct = blockIdx.x; ct < tiles; ct += gridDim.x) {
-    int tm, tn;
-    tile_coords(ct, tiles_m, tiles_n, tm, tn);
+    int tm, tn, sp, k0, k1;
+    item(ct, tm, tn, sp, k0, k1);
     const int m0 = tm * BM, n0 = tn * BN;
+    // a split item's partial goes to its slice of the workspace, in fp32
+    void* const Ct = splits > 1 ? static_cast<void*>(ws + (int64_t)sp * M * N) : C;
+    const int out_f32_t = splits > 1 ? 1 : out_f32;
 
     v16f acc[FM][FN];
 #pragma unroll
@@ -495,13 +514,13 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
       for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
     int slot = 0;
 
-    for (int ks = 0; ks < nk; ++ks) {
+    for (int ks = k0; ks < k1; ++ks) {
       // this stage's copies are done; after the previous tile's LDS-staged
       // epilogue its EPI_TOTAL stores (issued after them) may still be in
       // flight. The register epilogue drains its stores itself, so there the
       // count must be 0: an allowance would let this stage's own copies
       // (fewer than EPI_TOTAL per wave) still be in flight.
-      if (ks == 0 && ctc > 0 && staged) wait_vm<Cfg::EPI_TOTAL>();
+      if (ks == k0 && ctc > 0 && staged) wait_vm<Cfg::EPI_TOTAL>();
       else wait_vm<0>();
       block_sync();                         // everyone's copies are visible, and everyone is done
                                             // with the buffers the next copies overwrite
@@ -513,7 +532,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
       // blocks. Otherwise: all of them now, in one burst.
       if (Cfg::SPREAD) open_copy_stage();
       else if (lt < tiles) issue_next();
-      if (ks % Cfg::SPC == 0) slot = gc++ & 1;
+      if (ks == k0 || ks % Cfg::SPC == 0) slot = gc++ & 1;   // a new scale chunk (as on the copy side)
       mma_stage<Cfg>(acc, lds + (gs & 1) * Cfg::STAGE, lds + 2 * Cfg::STAGE + slot * Cfg::SCHUNK, ks % Cfg::SPC, g,
                      ra, rb, [&](int blk) {
                        constexpr int BLOCKS = Cfg::SUB * FM;
@@ -627,8 +646,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
             v[2] = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb.y & 0xFFFFu);
             v[3] = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb.y >> 16);
             const int64_t off = (int64_t)m * N + n;
-            if (out_f32) {
-              float* c = reinterpret_cast<float*>(C) + off;
+            if (out_f32_t) {
+              float* c = reinterpret_cast<float*>(Ct) + off;
               if (vec && n + 3 < N) {
                 *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
               } else {
@@ -637,7 +656,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
                   if (n + j < N) c[j] = v[j];
               }
             } else {
-              uint16_t* c = reinterpret_cast<uint16_t*>(C) + off;
+              uint16_t* c = reinterpret_cast<uint16_t*>(Ct) + off;
               if (vec && n + 3 < N) {
                 *reinterpret_cast<uint2*>(c) = make_uint2(pack_bf16x2(v[0], v[1]),
                                                           pack_bf16x2(v[2], v[3]));
@@ -658,19 +677,23 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
 
 template <class Cfg>
 static hipError_t run_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
-                         int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32, hipStream_t stream) {
+                         int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32, int splits, float* ws,
+                         hipStream_t stream) {
   const int64_t kpad = round_up(K, kAlignK);
   const int tiles_m = (int)((M + Cfg::BM - 1) / Cfg::BM);
   const int tiles_n = (int)((N + Cfg::BN - 1) / Cfg::BN);
-  const int tiles = tiles_m * tiles_n;
+  const int items = tiles_m * tiles_n * splits;
   // persistent grid: one slot per resident workgroup, a multiple of 8 so a
-  // workgroup's tiles all map to its own XCD; smaller problems get one
-  // workgroup per tile
+  // workgroup's items all map to its own XCD; smaller problems get one
+  // workgroup per item
   const int slots = std::max(8, (Cfg::OCC * cu_count()) / 8 * 8);
-  const int grid = tiles <= slots ? tiles : slots;
-  gemm_mx_kernel<Cfg><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, bias, out_f32,
-                                                    tiles_m, tiles_n);
-  return hipGetLastError();
+  const int grid = items <= slots ? items : slots;
+  gemm_mx_kernel<Cfg><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad,
+                                                    splits > 1 ? nullptr : bias, out_f32, tiles_m, tiles_n, nullptr,
+                                                    nullptr, 0, splits, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_splitk_reduce(ws, splits, M, N, bias, C, out_f32, stream);
 }
 
 template <class Cfg>
@@ -684,7 +707,7 @@ static hipError_t run_mx_q(const uint8_t* A, const uint8_t* As, const uint8_t* B
   const int slots = std::max(8, (Cfg::OCC * cu_count()) / 8 * 8);
   const int grid = tiles <= slots ? tiles : slots;
   gemm_mx_kernel<Cfg><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, qcodes, (int)M, (int)N, (int)kpad, bias, 0, tiles_m,
-                                                    tiles_n, qcodes, qscales, (int)round_up(N, kAlignK));
+                                                    tiles_n, qcodes, qscales, (int)round_up(N, kAlignK), 1, nullptr);
   return hipGetLastError();
 }
 
@@ -704,17 +727,84 @@ static MxTile choose_tile(int64_t M, int64_t N, int fmt) {
   return TILE_256x256;
 }
 
+struct MxPlan {
+  MxTile tile;
+  int splits;
+};
+
+// Time of one K-stage of one workgroup with every CU busy (us), measured on
+// MI355X on the ViT training shapes: fp8 stages hold 128 K elements, fp4
+// stages 256. A 128x128 workgroup sharing its CU with a second one runs its
+// stages 1.36x (fp8) / 1.6x (fp4) slower, so two per CU still nearly double
+// the CU's throughput. The large fp4 tiles are bound by the L2 -> LDS copies
+// once every CU runs them.
+static double mx_stage_us(MxTile t, int fmt, bool shared_cu) {
+  const bool f8 = fmt == FMT_MXFP8;
+  switch (t) {
+    case TILE_128x128: return f8 ? 0.92 * (shared_cu ? 1.36 : 1.0) : 0.98 * (shared_cu ? 1.6 : 1.0);
+    case TILE_192x256: return f8 ? 1.7 : 2.4;
+    default: return f8 ? 2.35 : 3.5;
+  }
+}
+
+static int mx_tile_m(MxTile t) { return t == TILE_128x128 ? 128 : t == TILE_192x256 ? 192 : 256; }
+static int mx_tile_n(MxTile t) { return t == TILE_128x128 ? 128 : 256; }
+
+// Estimated time of a plan: rounds of resident workgroups x stages per work
+// item x stage time, plus for a split plan the partials' cost (written by the
+// GEMM, read back by the reduction: about 3 us + 0.25 us per MB, measured).
+static double mx_plan_us(int64_t M, int64_t N, int64_t K, int fmt, MxPlan p) {
+  const int64_t kpad = round_up(K, kAlignK);
+  const int ks = fmt == FMT_MXFP8 ? 128 : 256;
+  const int64_t nk = (kpad + ks - 1) / ks;
+  const int occ = p.tile == TILE_128x128 ? 2 : 1;
+  const int64_t cus = cu_count();
+  const int64_t items = ((M + mx_tile_m(p.tile) - 1) / mx_tile_m(p.tile)) *
+                        ((N + mx_tile_n(p.tile) - 1) / mx_tile_n(p.tile)) * p.splits;
+  const int64_t rounds = (items + occ * cus - 1) / (occ * cus);
+  const bool shared = occ == 2 && items > cus;
+  double t = (double)rounds * (double)((nk + p.splits - 1) / p.splits) * mx_stage_us(p.tile, fmt, shared);
+  if (p.splits > 1) t += 3.0 + 0.25 * (double)(p.splits * 4) * (double)(M * N) / 1.0e6;
+  return t;
+}
+
+// The plan a GEMM runs: the tile above, or -- when the caller's workspace holds
+// the partials (S M N fp32 values) and the output has too few tiles to fill
+// the chip while K is long (the weight-gradient GEMMs) -- a tile with K split
+// into up to 16 ranges, whichever the estimate says is fastest; a split plan
+// must win by 5% to be taken.
+static MxPlan choose_plan(int64_t M, int64_t N, int64_t K, int fmt, int64_t ws_bytes) {
+  MxPlan best{choose_tile(M, N, fmt), 1};
+  if (ws_bytes < 2 * M * N * 4) return best;
+  double best_us = mx_plan_us(M, N, K, fmt, best);
+  const int64_t kpad = round_up(K, kAlignK);
+  const int64_t nk = (kpad + (fmt == FMT_MXFP8 ? 127 : 255)) / (fmt == FMT_MXFP8 ? 128 : 256);
+  for (MxTile t : {TILE_256x256, TILE_192x256, TILE_128x128}) {
+    const int occ = t == TILE_128x128 ? 2 : 1;
+    const int64_t tiles = ((M + mx_tile_m(t) - 1) / mx_tile_m(t)) * ((N + mx_tile_n(t) - 1) / mx_tile_n(t));
+    for (int s = 2; s <= 16 && tiles * s <= occ * cu_count() && nk >= 4 * s && s * M * N * 4 <= ws_bytes; ++s) {
+      const double us = mx_plan_us(M, N, K, fmt, MxPlan{t, s});
+      if (us < 0.95 * best_us) {
+        best_us = us;
+        best = MxPlan{t, s};
+      }
+    }
+  }
+  return best;
+}
+
 template <int FMT>
 static hipError_t dispatch_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
-                              int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
+                              int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32, MxPlan p, float* ws,
                               hipStream_t stream) {
-  switch (choose_tile(M, N, FMT)) {
+  switch (p.tile) {
     case TILE_128x128:
-      return run_mx<MxCfg<FMT, 128, 128, 2, 2, 2, true>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+      return run_mx<MxCfg<FMT, 128, 128, 2, 2, 2, true>>(A, As, B, Bs, C, M, N, K, bias, out_f32, p.splits, ws, stream);
     case TILE_192x256:
-      return run_mx<MxCfg<FMT, 192, 256, 2, 4, 1, true>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+      return run_mx<MxCfg<FMT, 192, 256, 2, 4, 1, true>>(A, As, B, Bs, C, M, N, K, bias, out_f32, p.splits, ws, stream);
     default:
-      return run_mx<MxCfg<FMT, 256, 256, 2, 4, 1, false>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+      return run_mx<MxCfg<FMT, 256, 256, 2, 4, 1, false>>(A, As, B, Bs, C, M, N, K, bias, out_f32, p.splits, ws,
+                                                          stream);
   }
 }
 
@@ -739,18 +829,34 @@ hipError_t launch_gemm_mx_gelu_quant(const uint8_t* A, const uint8_t* As, const 
   return dispatch_mx_q<FMT_MXFP4>(A, As, B, Bs, M, N, K, bias, qcodes, qscales, stream);
 }
 
-hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
-                          int64_t M, int64_t N, int64_t K, int fmt, const uint16_t* bias, int out_f32,
-                          hipStream_t stream) {
-  if (fmt == FMT_MXFP8) return dispatch_mx<FMT_MXFP8>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-  return dispatch_mx<FMT_MXFP4>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+int64_t gemm_mx_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
+  const MxPlan p = choose_plan(M, N, K, fmt, INT64_MAX);
+  return p.splits > 1 ? (int64_t)p.splits * M * N * 4 : 0;
 }
 
-const char* plan_gemm_mx(int64_t M, int64_t N, int fmt) {
+hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
+                          int64_t M, int64_t N, int64_t K, int fmt, const uint16_t* bias, int out_f32, float* ws,
+                          int64_t ws_bytes, hipStream_t stream) {
+  const MxPlan p = choose_plan(M, N, K, fmt, ws != nullptr ? ws_bytes : 0);
+  if (fmt == FMT_MXFP8) return dispatch_mx<FMT_MXFP8>(A, As, B, Bs, C, M, N, K, bias, out_f32, p, ws, stream);
+  return dispatch_mx<FMT_MXFP4>(A, As, B, Bs, C, M, N, K, bias, out_f32, p, ws, stream);
+}
+
+const char* plan_gemm_mx(int64_t M, int64_t N, int64_t K, int fmt, int64_t ws_bytes) {
   static const char* names[2][3] = {
       {"gemm_mx_kernel<mxfp8, 128x128>", "gemm_mx_kernel<mxfp8, 192x256>", "gemm_mx_kernel<mxfp8, 256x256>"},
       {"gemm_mx_kernel<mxfp4, 128x128>", "gemm_mx_kernel<mxfp4, 192x256>", "gemm_mx_kernel<mxfp4, 256x256>"}};
-  return names[fmt == FMT_MXFP8 ? 0 : 1][choose_tile(M, N, fmt)];
+  // split plans: "<kernel>+splitk<S>", one static string per (format, tile, S)
+  static char split_names[2][3][17][48];
+  static std::once_flag once;
+  std::call_once(once, [] {
+    for (int f = 0; f < 2; ++f)
+      for (int t = 0; t < 3; ++t)
+        for (int sp = 2; sp <= 16; ++sp) snprintf(split_names[f][t][sp], 48, "%s+splitk%d", names[f][t], sp);
+  });
+  const MxPlan p = choose_plan(M, N, K, fmt, ws_bytes);
+  const int f = fmt == FMT_MXFP8 ? 0 : 1;
+  return p.splits > 1 ? split_names[f][p.tile][p.splits] : names[f][p.tile];
 }
 
 }  // namespace mx

@@ -32,6 +32,8 @@
 #include "mx_launch.h"
 
 #include <algorithm>
+#include <cstdio>
+#include <mutex>
 #include <type_traits>
 
 namespace mx {
@@ -110,12 +112,17 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
                                                                     void* __restrict__ C, int M, int N, int kpad,
                                                                     const uint16_t* __restrict__ bias, int out_f32,
                                                                     int tiles_m, int tiles_n, int a_trailer,
-                                                                    int b_trailer) {
+                                                                    int b_trailer, int splits,
+                                                                    float* __restrict__ ws) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int RB = Cfg::RB, SUB = Cfg::SUB, CPR = Cfg::CPR;
   __shared__ __align__(16) uint8_t lds[Cfg::LDS];
 
-  const int tiles = tiles_m * tiles_n;
+  // work items: (tile, split) pairs; with splits > 1 an item covers the K
+  // stages [k0, k1) of its split (an even number: stages come in pairs) and
+  // writes its fp32 partial tile, times s_tA s_tB, to ws + split M N (no
+  // bias), summed by the split-K reduction afterwards
+  const int tiles = tiles_m * tiles_n * splits;
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -125,6 +132,14 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
   const int nk = kpad / Cfg::KS;             // K_pad is a multiple of 128
   const int g = lane >> 5, r32 = lane & 31;
   constexpr bool staged = STAGED;
+  auto item = [&](int t, int& tm, int& tn, int& sp, int& k0, int& k1) {
+    int tnv;
+    tile_coords(t, tiles_m, tiles_n * splits, tm, tnv);
+    tn = tnv % tiles_n;
+    sp = tnv / tiles_n;
+    k0 = 2 * ((sp * (nk / 2)) / splits);
+    k1 = 2 * (((sp + 1) * (nk / 2)) / splits);
+  };
 
   const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, M * row_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, N * row_bytes, 0x00020000);
@@ -153,11 +168,12 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
   const int st_row = st_is_a ? tid : tid - BM;
   uint8_t* const st_dst = stager ? lds + tid * RB : lds + Cfg::SCRATCH_OFF + (tid - BM - BN) * RB;
   const int st_buf_stride = stager ? Cfg::STAGE : 0;
-  int lt = blockIdx.x, lks = 0, ltc = 0;
+  int lt = blockIdx.x, lks = 0, lk0 = 0, lk1 = nk, ltc = 0;
   int code_off = 0, scale_off = 0, bias_col = 0;
   auto set_load_tile = [&](int t) {
-    int tm, tn;
-    tile_coords(t, tiles_m, tiles_n, tm, tn);
+    int tm, tn, sp;
+    item(t, tm, tn, sp, lk0, lk1);
+    lks = lk0;
     const int r = (st_is_a ? tm * BM : tn * BN) + st_row;
     code_off = r * row_bytes;                // rows past the operand read as zero (range-checked)
     scale_off = r * srow;
@@ -176,15 +192,15 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
     const bool row_live = stager && loading;
     const int co = row_live ? code_off + lks * 32 : OOB;
     const int so = row_live ? scale_off + lks * 4 : OOB;
-    const int bo = (loading && lks == 0 && bias_vec && tid < BN / 8) ? bias_col * 2 : OOB;
+    const int bo = (loading && lks == lk0 && bias_vec && tid < BN / 8) ? bias_col * 2 : OOB;
     R.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(crs, co, 0, 0));
     R.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(crs, co, 16, 0));
     R.sc = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 0, 0);
     R.bias = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bias_rs, bo, 0, 0));
-    R.first = loading && lks == 0;
+    R.first = loading && lks == lk0;
     R.slot = ltc & 1;
-    if (loading && ++lks == nk) {
-      lks = 0;
+    if (loading && ++lks == lk1) {
+      lks = lk0;
       ++ltc;
       lt += gridDim.x;
       if (lt < tiles) set_load_tile(lt);
@@ -284,9 +300,12 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
   };
 
   for (int ct = blockIdx.x; ct < tiles; ct += gridDim.x) {
-    int tm, tn;
-    tile_coords(ct, tiles_m, tiles_n, tm, tn);
+    int tm, tn, sp, k0, k1;
+    item(ct, tm, tn, sp, k0, k1);
     const int m0 = tm * BM, n0 = tn * BN;
+    // a split item's partial goes to its slice of the workspace, in fp32
+    void* const Ct = splits > 1 ? static_cast<void*>(ws + (int64_t)sp * M * N) : C;
+    const int out_f32_t = splits > 1 ? 1 : out_f32;
 
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -297,7 +316,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
     // previous tile's epilogue, not the loop's back edge
     stage(std::integral_constant<int, 0>{}, R0, R1);
     stage(std::integral_constant<int, 1>{}, R1, R0);
-    for (int ks = 2; ks < nk; ks += 2) {
+    for (int ks = k0 + 2; ks < k1; ks += 2) {
       stage(std::integral_constant<int, 0>{}, R0, R1);
       stage(std::integral_constant<int, 1>{}, R1, R0);
     }
@@ -377,8 +396,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
             v[2] = acc[fm][fn][4 * q + 2] * tensor_scale + bf16_to_f32(bb.y & 0xFFFFu);
             v[3] = acc[fm][fn][4 * q + 3] * tensor_scale + bf16_to_f32(bb.y >> 16);
             const int64_t off = (int64_t)m * N + n;
-            if (out_f32) {
-              float* c = reinterpret_cast<float*>(C) + off;
+            if (out_f32_t) {
+              float* c = reinterpret_cast<float*>(Ct) + off;
               if (vec && n + 3 < N) {
                 *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
               } else {
@@ -387,7 +406,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
                   if (n + j < N) c[j] = v[j];
               }
             } else {
-              uint16_t* c = reinterpret_cast<uint16_t*>(C) + off;
+              uint16_t* c = reinterpret_cast<uint16_t*>(Ct) + off;
               if (vec && n + 3 < N) {
                 *reinterpret_cast<uint2*>(c) = make_uint2(pack_bf16x2(v[0], v[1]),
                                                           pack_bf16x2(v[2], v[3]));
@@ -407,25 +426,34 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_nv_kernel(const uint8_
 
 template <class Cfg>
 static hipError_t run_nv(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
-                         int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32, hipStream_t stream) {
+                         int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32, int splits, float* ws,
+                         hipStream_t stream) {
   const int64_t kpad = round_up(K, kAlignK);
   const int tiles_m = (int)((M + Cfg::BM - 1) / Cfg::BM);
   const int tiles_n = (int)((N + Cfg::BN - 1) / Cfg::BN);
-  const int tiles = tiles_m * tiles_n;
+  const int items = tiles_m * tiles_n * splits;
   const int a_tr = (int)round_up(M * (kpad / 16), 16);
   const int b_tr = (int)round_up(N * (kpad / 16), 16);
   // persistent grid: one slot per resident workgroup, a multiple of 8
   const int slots = std::max(8, (Cfg::OCC * cu_count()) / 8 * 8);
-  const int grid = tiles <= slots ? tiles : slots;
-  const bool staged = !out_f32 && (N & 7) == 0 && M * N < ((int64_t)1 << 30);
+  const int grid = items <= slots ? items : slots;
+  const bool staged = splits == 1 && !out_f32 && (N & 7) == 0 && M * N < ((int64_t)1 << 30);
+  const uint16_t* kbias = splits > 1 ? nullptr : bias;
   if (staged)
-    gemm_nv_kernel<Cfg, true><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, bias,
-                                                            out_f32, tiles_m, tiles_n, a_tr, b_tr);
+    gemm_nv_kernel<Cfg, true><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, kbias,
+                                                            out_f32, tiles_m, tiles_n, a_tr, b_tr, splits, ws);
   else
-    gemm_nv_kernel<Cfg, false><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, bias,
-                                                             out_f32, tiles_m, tiles_n, a_tr, b_tr);
-  return hipGetLastError();
+    gemm_nv_kernel<Cfg, false><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, C, (int)M, (int)N, (int)kpad, kbias,
+                                                             out_f32, tiles_m, tiles_n, a_tr, b_tr, splits, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_splitk_reduce(ws, splits, M, N, bias, C, out_f32, stream);
 }
+
+struct NvPlan {
+  bool small;                                // 128x128 (two workgroups per CU) instead of 192x256
+  int splits;
+};
 
 // Tile shape with the least work per CU lost to a partly filled last round:
 // rounds of resident workgroups x tile area x workgroups per CU. 128x128 (4
@@ -442,15 +470,68 @@ static bool nv_small_tiles(int64_t M, int64_t N) {
   return cost(128, 128, 2) < cost(192, 256, 1);
 }
 
-const char* plan_gemm_nvfp4(int64_t M, int64_t N) {
-  return nv_small_tiles(M, N) ? "gemm_nv_kernel<nvfp4, 128x128>" : "gemm_nv_kernel<nvfp4, 192x256>";
+// Estimated time of a plan (us): rounds x stages per item x stage time (a
+// 64-K stage of one workgroup with every CU busy, measured on MI355X on the
+// training shapes; two 128x128 workgroups sharing a CU split its throughput,
+// the dequantization being VALU and LDS work), plus the split-K partials
+// (about 3 us + 0.25 us per MB, measured).
+static double nv_plan_us(int64_t M, int64_t N, int64_t K, NvPlan p) {
+  const int64_t nk = round_up(K, kAlignK) / 64;
+  const int bm = p.small ? 128 : 192, bn = p.small ? 128 : 256, occ = p.small ? 2 : 1;
+  const int64_t cus = cu_count();
+  const int64_t items = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * p.splits;
+  const int64_t rounds = (items + occ * cus - 1) / (occ * cus);
+  const double stage = p.small ? 0.73 * (items > cus ? 2.0 : 1.0) : 1.7;
+  double t = (double)rounds * (double)(2 * ((nk / 2 + p.splits - 1) / p.splits)) * stage;
+  if (p.splits > 1) t += 3.0 + 0.25 * (double)(p.splits * 4) * (double)(M * N) / 1.0e6;
+  return t;
+}
+
+// As for the MX GEMM: a split plan only if the workspace holds its partials
+// and the estimate beats the unsplit plan by 5%.
+static NvPlan nv_choose_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes) {
+  NvPlan best{nv_small_tiles(M, N), 1};
+  if (ws_bytes < 2 * M * N * 4) return best;
+  double best_us = nv_plan_us(M, N, K, best);
+  const int64_t pairs = round_up(K, kAlignK) / 128;
+  for (bool small : {false, true}) {
+    const int bm = small ? 128 : 192, bn = small ? 128 : 256, occ = small ? 2 : 1;
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    for (int s = 2; s <= 16 && tiles * s <= occ * cu_count() && pairs >= 2 * s && s * M * N * 4 <= ws_bytes; ++s) {
+      const double us = nv_plan_us(M, N, K, NvPlan{small, s});
+      if (us < 0.95 * best_us) {
+        best_us = us;
+        best = NvPlan{small, s};
+      }
+    }
+  }
+  return best;
+}
+
+int64_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const NvPlan p = nv_choose_plan(M, N, K, INT64_MAX);
+  return p.splits > 1 ? (int64_t)p.splits * M * N * 4 : 0;
+}
+
+const char* plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, int64_t ws_bytes) {
+  static const char* names[2] = {"gemm_nv_kernel<nvfp4, 192x256>", "gemm_nv_kernel<nvfp4, 128x128>"};
+  static char split_names[2][17][48];
+  static std::once_flag once;
+  std::call_once(once, [] {
+    for (int t = 0; t < 2; ++t)
+      for (int sp = 2; sp <= 16; ++sp) snprintf(split_names[t][sp], 48, "%s+splitk%d", names[t], sp);
+  });
+  const NvPlan p = nv_choose_plan(M, N, K, ws_bytes);
+  return p.splits > 1 ? split_names[p.small][p.splits] : names[p.small];
 }
 
 hipError_t launch_gemm_nvfp4(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
-                             int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
-                             hipStream_t stream) {
-  if (nv_small_tiles(M, N)) return run_nv<NvCfg<128, 128, 2, 2, 2>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
-  return run_nv<NvCfg<192, 256, 2, 4, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, stream);
+                             int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32, float* ws,
+                             int64_t ws_bytes, hipStream_t stream) {
+  const NvPlan p = nv_choose_plan(M, N, K, ws != nullptr ? ws_bytes : 0);
+  if (p.small)
+    return run_nv<NvCfg<128, 128, 2, 2, 2>>(A, As, B, Bs, C, M, N, K, bias, out_f32, p.splits, ws, stream);
+  return run_nv<NvCfg<192, 256, 2, 4, 1>>(A, As, B, Bs, C, M, N, K, bias, out_f32, p.splits, ws, stream);
 }
 
 }  // namespace mx

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -237,39 +238,70 @@ mx_status mx_quantize_dual_sr(const void* src, int64_t rows, int64_t cols, int64
   return MX_OK;
 }
 
-mx_status mx_gemm(const void* A, const void* As, const void* B, const void* Bs, void* C, int64_t M, int64_t N,
-                  int64_t K, mx_fmt fmt, const void* bias, mx_dtype out_dtype, void* hip_stream) {
-  if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "mx_gemm: unknown format %d", (int)fmt);
+}  // extern "C"
+
+namespace {
+
+// Shared by mx_gemm and mx_gemm_ws: every check before the launch.
+mx_status gemm_checked(const char* fn, const void* A, const void* As, const void* B, const void* Bs, void* C,
+                       int64_t M, int64_t N, int64_t K, mx_fmt fmt, const void* bias, mx_dtype out_dtype,
+                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "%s: unknown format %d", fn, (int)fmt);
   if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32)
-    return fail(MX_ERR_INVALID_ARG, "mx_gemm: unknown output dtype %d", (int)out_dtype);
+    return fail(MX_ERR_INVALID_ARG, "%s: unknown output dtype %d", fn, (int)out_dtype);
   if (M < 1 || N < 1 || K < 1)
-    return fail(MX_ERR_INVALID_ARG, "mx_gemm: M, N, K must be >= 1 (got %lld, %lld, %lld)", (long long)M, (long long)N,
+    return fail(MX_ERR_INVALID_ARG, "%s: M, N, K must be >= 1 (got %lld, %lld, %lld)", fn, (long long)M, (long long)N,
                 (long long)K);
-  if (!A || !As || !B || !Bs || !C) return fail(MX_ERR_INVALID_ARG, "mx_gemm: null pointer");
+  if (!A || !As || !B || !Bs || !C) return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (!aligned(A, 16) || !aligned(As, 16) || !aligned(B, 16) || !aligned(Bs, 16) || !aligned(C, 16))
-    return fail(MX_ERR_ALIGNMENT, "mx_gemm: A, As, B, Bs and C must be 16-byte aligned");
-  if (bias && !aligned(bias, 2)) return fail(MX_ERR_ALIGNMENT, "mx_gemm: bias must be 2-byte aligned");
+    return fail(MX_ERR_ALIGNMENT, "%s: A, As, B, Bs and C must be 16-byte aligned", fn);
+  if (bias && !aligned(bias, 2)) return fail(MX_ERR_ALIGNMENT, "%s: bias must be 2-byte aligned", fn);
+  if (workspace && !aligned(workspace, 16)) return fail(MX_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", fn);
   if (M > kMaxCount || N > kMaxCount || K > kMaxCount)
-    return fail(MX_ERR_UNSUPPORTED, "mx_gemm: M, N and K must be below 2^31 - 256");
+    return fail(MX_ERR_UNSUPPORTED, "%s: M, N and K must be below 2^31 - 256", fn);
   const int64_t kpad = k_pad(K);
   const int64_t rb = code_row_bytes(kpad, fmt);
   if (M * rb >= kMaxBytes || N * rb >= kMaxBytes || scales_total(M, kpad, fmt) >= kMaxBytes ||
       scales_total(N, kpad, fmt) >= kMaxBytes)
-    return fail(MX_ERR_UNSUPPORTED, "mx_gemm: operand larger than 2 GiB");
+    return fail(MX_ERR_UNSUPPORTED, "%s: operand larger than 2 GiB", fn);
   hipError_t e;
   const int out_f32 = out_dtype == MX_OUT_F32;
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  float* ws = static_cast<float*>(workspace);
+  const int64_t ws_bytes = workspace ? (int64_t)std::min<size_t>(workspace_bytes, (size_t)INT64_MAX) : 0;
   if (fmt == MX_FMT_NVFP4) {
     e = mx::launch_gemm_nvfp4(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(As),
                               static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(Bs), C, M, N, K,
-                              static_cast<const uint16_t*>(bias), out_f32, s);
+                              static_cast<const uint16_t*>(bias), out_f32, ws, ws_bytes, s);
   } else {
     e = mx::launch_gemm_mx(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(As),
                            static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(Bs), C, M, N, K, (int)fmt,
-                           static_cast<const uint16_t*>(bias), out_f32, s);
+                           static_cast<const uint16_t*>(bias), out_f32, ws, ws_bytes, s);
   }
-  if (e != hipSuccess) return fail(MX_ERR_HIP, "mx_gemm: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(MX_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_gemm(const void* A, const void* As, const void* B, const void* Bs, void* C, int64_t M, int64_t N,
+                  int64_t K, mx_fmt fmt, const void* bias, mx_dtype out_dtype, void* hip_stream) {
+  return gemm_checked("mx_gemm", A, As, B, Bs, C, M, N, K, fmt, bias, out_dtype, nullptr, 0, hip_stream);
+}
+
+mx_status mx_gemm_ws(const void* A, const void* As, const void* B, const void* Bs, void* C, int64_t M, int64_t N,
+                     int64_t K, mx_fmt fmt, const void* bias, mx_dtype out_dtype, void* workspace,
+                     size_t workspace_bytes, void* hip_stream) {
+  return gemm_checked("mx_gemm_ws", A, As, B, Bs, C, M, N, K, fmt, bias, out_dtype, workspace, workspace_bytes,
+                      hip_stream);
+}
+
+size_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, mx_fmt fmt) {
+  if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 1 || M > kMaxCount || N > kMaxCount || K > kMaxCount) return 0;
+  return (size_t)(fmt == MX_FMT_NVFP4 ? mx::gemm_nvfp4_workspace_bytes(M, N, K)
+                                      : mx::gemm_mx_workspace_bytes(M, N, K, (int)fmt));
 }
 
 mx_status mx_gemm_gelu_quantize(const void* A, const void* As, const void* B, const void* Bs, int64_t M, int64_t N,
@@ -307,7 +339,13 @@ mx_status mx_gemm_gelu_quantize(const void* A, const void* As, const void* B, co
 
 const char* mx_gemm_plan(int64_t M, int64_t N, int64_t K, mx_fmt fmt) {
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 1) return nullptr;
-  return fmt == MX_FMT_NVFP4 ? mx::plan_gemm_nvfp4(M, N) : mx::plan_gemm_mx(M, N, (int)fmt);
+  return fmt == MX_FMT_NVFP4 ? mx::plan_gemm_nvfp4(M, N, K, 0) : mx::plan_gemm_mx(M, N, K, (int)fmt, 0);
+}
+
+const char* mx_gemm_ws_plan(int64_t M, int64_t N, int64_t K, mx_fmt fmt, size_t workspace_bytes) {
+  if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 1) return nullptr;
+  const int64_t ws = (int64_t)std::min<size_t>(workspace_bytes, (size_t)INT64_MAX);
+  return fmt == MX_FMT_NVFP4 ? mx::plan_gemm_nvfp4(M, N, K, ws) : mx::plan_gemm_mx(M, N, K, (int)fmt, ws);
 }
 
 const char* mx_last_error(void) { return g_last_error.c_str(); }

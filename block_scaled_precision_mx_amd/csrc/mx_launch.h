@@ -44,9 +44,11 @@ hipError_t launch_quantize_dual(const uint16_t* src, int64_t rows, int64_t cols,
                                 float headroom, int sr, uint64_t seed0, uint64_t seed1, hipStream_t stream);
 
 // MXFP8 / MXFP4: scaled-MFMA GEMM. C = A * B^T (+ bias), fp32 accumulate.
+// ws / ws_bytes: a device workspace the plan may use for split-K partials
+// (S M N fp32 values, S <= 16); NULL / 0 runs the unsplit plan.
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs,
                           void* C, int64_t M, int64_t N, int64_t K, int fmt, const uint16_t* bias,
-                          int out_f32, hipStream_t stream);
+                          int out_f32, float* ws, int64_t ws_bytes, hipStream_t stream);
 
 // MXFP8 / MXFP4 GEMM whose output is GELU(bf16(A B^T + bias)) rounded to
 // bf16 and quantized along N in the same format (rows of K_pad(N)
@@ -57,12 +59,23 @@ hipError_t launch_gemm_mx_gelu_quant(const uint8_t* A, const uint8_t* As, const 
 
 // NVFP4: E2M1 x E4M3 operands dequantized exactly to fp16 on the way into
 // LDS, fp16 MFMA with fp32 accumulate, s_tA * s_tB applied in the epilogue.
+// ws / ws_bytes as for launch_gemm_mx.
 hipError_t launch_gemm_nvfp4(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs,
                              void* C, int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32,
-                             hipStream_t stream);
+                             float* ws, int64_t ws_bytes, hipStream_t stream);
 
-// Name of the kernel configuration the launchers above pick for a shape.
-const char* plan_gemm_mx(int64_t M, int64_t N, int fmt);
-const char* plan_gemm_nvfp4(int64_t M, int64_t N);
+// C = sum_{s < splits} P[s] (+ bias) for split-K partials P[s] = ws + s M N
+// (fp32, in order s = 0, 1, ...), stored as bf16 or fp32.
+hipError_t launch_splitk_reduce(const float* ws, int splits, int64_t M, int64_t N, const uint16_t* bias, void* C,
+                                int out_f32, hipStream_t stream);
+
+// Workspace bytes of the fastest plan for a shape (0 if it does not split K).
+int64_t gemm_mx_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt);
+int64_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+// Name of the kernel configuration the launchers above pick for a shape
+// given ws_bytes of workspace.
+const char* plan_gemm_mx(int64_t M, int64_t N, int64_t K, int fmt, int64_t ws_bytes);
+const char* plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, int64_t ws_bytes);
 
 }  // namespace mx

@@ -215,6 +215,28 @@ mx_status mx_gemm(const void* A, const void* As, const void* B, const void* Bs,
                   void* C, int64_t M, int64_t N, int64_t K, mx_fmt fmt,
                   const void* bias, mx_dtype out_dtype, void* hip_stream);
 
+/* Weight-gradient GEMMs contract over the tokens (README section 5.4: the
+ * dgrad / wgrad GEMMs of every block; section 5.5: wgrad takes the token-axis
+ * copies), so K is long while C has few tiles. mx_gemm_ws may then split K
+ * into S <= 16 ranges, each written as an fp32 partial C to `workspace`
+ * (S * M * N * 4 bytes), and sum the partials in the fixed order 0, 1, ...,
+ * S - 1 before the bias and the final rounding, so the result does not
+ * depend on timing. It picks the fastest plan whose partials fit in
+ * workspace_bytes; with workspace == NULL (or too small for any split) it
+ * runs exactly what mx_gemm runs. Accuracy as for mx_gemm (S - 1 more fp32
+ * additions). workspace: caller-owned device memory, 16-byte aligned, not
+ * overlapping any other argument; its contents are scratch (overwritten,
+ * nothing read from a previous call). Other arguments, errors and memory
+ * rules as for mx_gemm. */
+mx_status mx_gemm_ws(const void* A, const void* As, const void* B, const void* Bs,
+                     void* C, int64_t M, int64_t N, int64_t K, mx_fmt fmt,
+                     const void* bias, mx_dtype out_dtype, void* workspace,
+                     size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes with which mx_gemm_ws runs its fastest plan for these sizes
+ * (0 when that plan does not split K, or when an argument is invalid). */
+size_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, mx_fmt fmt);
+
 /* fc1 writing fc2's operand (README section 4.3, MXFP8 row of the block
  * table: fc1's epilogue quantizes the GELU output straight into fc2's E4M3
  * operand). Computes H = A * B^T (+ bias) as mx_gemm with bf16 output
@@ -238,6 +260,10 @@ mx_status mx_gemm_gelu_quantize(const void* A, const void* As, const void* B, co
  * format (for example "gemm_mx_kernel<mxfp8, 256x256>"), so profiles can be
  * matched to calls; a static string, or NULL if an argument is invalid. */
 const char* mx_gemm_plan(int64_t M, int64_t N, int64_t K, mx_fmt fmt);
+
+/* The same for mx_gemm_ws with workspace_bytes of workspace (a split plan
+ * is named "<kernel>+splitk<S>"). */
+const char* mx_gemm_ws_plan(int64_t M, int64_t N, int64_t K, mx_fmt fmt, size_t workspace_bytes);
 
 /* Message for the last non-OK status returned on the calling thread. */
 const char* mx_last_error(void);

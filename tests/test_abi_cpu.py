@@ -262,3 +262,35 @@ def test_bench_workloads_are_defined():
     for name in ("single_mxfp8_256x768x768", "vitb16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack",
                  "vitl16_nvfp4_fc1fc2_train"):
         assert name in bench.EXTRA_CONFIGS
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((ALIGNED,) * 5 + (4, 4, 32, 1, None, 0, ALIGNED + 4, 1 << 20), 3, "workspace must be 16-byte aligned"),
+    ((ALIGNED,) * 5 + (4, 4, 32, 9, None, 0, ALIGNED, 1 << 20), 1, "unknown format"),
+    ((ALIGNED,) * 5 + (0, 4, 32, 1, None, 0, ALIGNED, 1 << 20), 1, ">= 1"),
+    ((ALIGNED,) * 5 + (1, 1, 1 << 31, 2, None, 0, ALIGNED, 1 << 20), 2, "below 2^31"),
+])
+def test_gemm_ws_validation(L, args, status, msg):
+    assert L.mx_gemm_ws(*args, None) == status
+    assert msg in L.mx_last_error().decode()
+    assert L.mx_last_error().decode().startswith("mx_gemm_ws")
+
+
+def test_gemm_ws_plans_follow_the_workspace():
+    """The weight-gradient shapes split K when the workspace holds the
+    partials; less workspace gives fewer splits or none; the forward shapes
+    never split; mx_gemm_workspace_bytes is S M N 4 of the preferred plan."""
+    from block_scaled_precision_mx_amd import api
+    for fmt in ("mxfp8", "nvfp4"):
+        need = api.gemm_workspace_bytes(3072, 1024, 11235, fmt)
+        plan = api.gemm_ws_plan(3072, 1024, 11235, fmt, need)
+        s = int(plan.split("+splitk")[1])
+        assert need == s * 3072 * 1024 * 4
+        assert api.gemm_ws_plan(3072, 1024, 11235, fmt, 0) == api.gemm_plan(3072, 1024, 11235, fmt)
+        fewer = api.gemm_ws_plan(3072, 1024, 11235, fmt, need - 1)
+        assert "+splitk" not in fewer or int(fewer.split("+splitk")[1]) < s
+    for (m, n, k) in [(11235, 3072, 1024), (11235, 1024, 4096), (11235, 4096, 1024), (22470, 768, 3072)]:
+        for fmt in ("mxfp8", "mxfp4", "nvfp4"):
+            assert api.gemm_workspace_bytes(m, n, k, fmt) == 0
+            assert api.gemm_ws_plan(m, n, k, fmt, 1 << 30) == api.gemm_plan(m, n, k, fmt)
+    assert api.gemm_workspace_bytes(0, 4, 4, "mxfp8") == 0

@@ -7,14 +7,17 @@ import bench
 from block_scaled_precision_mx_amd import api
 import test_gpu_gemm
 import test_gpu_gemm_fused
+import test_gpu_gemm_splitk
 
 
-def config_key(m, n, k, fmt, out, epilogue):
-    return (api.gemm_plan(m, n, k, fmt), epilogue, out, n % 8 == 0)
+def config_key(m, n, k, fmt, out, epilogue, ws=0):
+    """The configuration a GEMM runs: plan (for mx_gemm_ws, with ws bytes of
+    workspace), epilogue, output dtype, N % 8 == 0."""
+    return (api.gemm_ws_plan(m, n, k, fmt, ws), epilogue, out, n % 8 == 0)
 
 
 def parity_cases():
-    return test_gpu_gemm.parity_cases() + test_gpu_gemm_fused.parity_cases()
+    return test_gpu_gemm.parity_cases() + test_gpu_gemm_fused.parity_cases() + test_gpu_gemm_splitk.parity_cases()
 
 
 def bench_specs(names):
@@ -27,7 +30,7 @@ def test_every_benchmarked_configuration_has_gpu_parity():
     covered = {config_key(*c) for c in parity_cases()}
     missing = set()
     for name, s in bench_specs(bench.WORKLOADS):
-        key = config_key(s.m, s.n, s.k, s.fmt, s.out, s.epilogue)
+        key = config_key(s.m, s.n, s.k, s.fmt, s.out, s.epilogue, bench.WORKSPACE_BYTES if s.ws else 0)
         if key not in covered:
             missing.add((name, s.label, key))
     assert not missing, sorted(missing)
@@ -36,7 +39,7 @@ def test_every_benchmarked_configuration_has_gpu_parity():
 def test_every_measured_shape_has_full_size_gpu_parity():
     """The headline and every configuration in the default benchmark line:
     each distinct GEMM shape is itself a GPU parity case (full or sampled)."""
-    shapes = {(m, n, k, fmt, epi) for (m, n, k, fmt, _, epi) in parity_cases()}
+    shapes = {c[:4] + (c[5],) for c in parity_cases()}
     missing = set()
     for name, s in bench_specs([bench.HEADLINE] + bench.EXTRA_CONFIGS):
         if (s.m, s.n, s.k, s.fmt, s.epilogue) not in shapes:
