@@ -16,6 +16,7 @@ class QuantItem(ctypes.Structure):
 
 
 QUANT_BATCH_MAX = 32   # MX_QUANT_BATCH_MAX
+SCRATCH_BYTES = 64 << 20   # MX_SCRATCH_BYTES
 
 # every symbol include/mx.h declares, with (restype, argtypes)
 SIGNATURES = {
@@ -42,6 +43,8 @@ SIGNATURES = {
                               _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_size_t,
                               _c.c_void_p]),
     "mx_gemm_workspace_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
+    "mx_gemm_scratch": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
+                                   _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p]),
     "mx_gemm_plan": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "mx_gemm_ws_plan": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_size_t]),
     "mx_last_error": (_c.c_char_p, []),

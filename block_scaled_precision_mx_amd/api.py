@@ -267,6 +267,24 @@ def mx_gemm_ws(a: Quantized, b: Quantized, bias: torch.Tensor | None, out_dtype:
     return out
 
 
+def mx_gemm_scratch(a: Quantized, b: Quantized, bias: torch.Tensor | None, out_dtype: str,
+                    out: torch.Tensor, stream=None) -> torch.Tensor:
+    """mx_gemm_ws with the library's own device scratch (allocates nothing;
+    `out` must be given)."""
+    if a.fmt != b.fmt or a.length != b.length:
+        raise ValueError("operands must share format and K")
+    M, N, K = a.rows, b.rows, a.length
+    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    if out.dtype != dt or out.numel() < M * N or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of M*N elements of the output dtype")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bf16 tensor of N elements")
+    _check(lib().mx_gemm_scratch(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
+                                 out.data_ptr(), M, N, K, FMT[a.fmt], None if bias is None else bias.data_ptr(),
+                                 OUT[out_dtype], _stream(stream)))
+    return out
+
+
 def mx_gemm_gelu_quantize(a: Quantized, b: Quantized, bias: torch.Tensor | None = None,
                           out: Quantized | None = None, stream=None) -> Quantized:
     """GELU(A * B^T (+ bias)) row-quantized in the operands' MX format, ready

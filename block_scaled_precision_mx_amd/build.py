@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libmx.so")
 
-SOURCES = ["quantize.hip", "gemm_mx.hip", "gemm_nv.hip", "splitk.hip", "mx_api.cpp"]
+SOURCES = ["quantize.hip", "gemm_mx.hip", "gemm_nv.hip", "splitk.hip", "scratch.hip", "mx_api.cpp"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -245,7 +245,7 @@ namespace {
 // Shared by mx_gemm and mx_gemm_ws: every check before the launch.
 mx_status gemm_checked(const char* fn, const void* A, const void* As, const void* B, const void* Bs, void* C,
                        int64_t M, int64_t N, int64_t K, mx_fmt fmt, const void* bias, mx_dtype out_dtype,
-                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+                       void* workspace, size_t workspace_bytes, void* hip_stream, bool validate_only = false) {
   if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "%s: unknown format %d", fn, (int)fmt);
   if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32)
     return fail(MX_ERR_INVALID_ARG, "%s: unknown output dtype %d", fn, (int)out_dtype);
@@ -264,6 +264,7 @@ mx_status gemm_checked(const char* fn, const void* A, const void* As, const void
   if (M * rb >= kMaxBytes || N * rb >= kMaxBytes || scales_total(M, kpad, fmt) >= kMaxBytes ||
       scales_total(N, kpad, fmt) >= kMaxBytes)
     return fail(MX_ERR_UNSUPPORTED, "%s: operand larger than 2 GiB", fn);
+  if (validate_only) return MX_OK;
   hipError_t e;
   const int out_f32 = out_dtype == MX_OUT_F32;
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -296,6 +297,26 @@ mx_status mx_gemm_ws(const void* A, const void* As, const void* B, const void* B
                      size_t workspace_bytes, void* hip_stream) {
   return gemm_checked("mx_gemm_ws", A, As, B, Bs, C, M, N, K, fmt, bias, out_dtype, workspace, workspace_bytes,
                       hip_stream);
+}
+
+mx_status mx_gemm_scratch(const void* A, const void* As, const void* B, const void* Bs, void* C, int64_t M,
+                          int64_t N, int64_t K, mx_fmt fmt, const void* bias, mx_dtype out_dtype, void* hip_stream) {
+  static_assert(MX_SCRATCH_BYTES == mx::kScratchBytes, "scratch size of the header and the library");
+  const size_t need = mx_gemm_workspace_bytes(M, N, K, fmt);
+  if (need > mx::kScratchBytes)
+    return fail(MX_ERR_UNSUPPORTED, "mx_gemm_scratch: the plan needs %zu bytes of scratch, more than the %zu the "
+                "library holds", need, mx::kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    // arguments first: a call that fails validation must not take the address
+    const mx_status st = gemm_checked("mx_gemm_scratch", A, As, B, Bs, C, M, N, K, fmt, bias, out_dtype, nullptr, 0,
+                                      nullptr, /*validate_only=*/true);
+    if (st != MX_OK) return st;
+    const hipError_t e = mx::scratch_buffer(&ws);
+    if (e != hipSuccess)
+      return fail(MX_ERR_HIP, "mx_gemm_scratch: no device address for the scratch: %s", hipGetErrorString(e));
+  }
+  return gemm_checked("mx_gemm_scratch", A, As, B, Bs, C, M, N, K, fmt, bias, out_dtype, ws, need, hip_stream);
 }
 
 size_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, mx_fmt fmt) {

@@ -73,6 +73,13 @@ hipError_t launch_splitk_reduce(const float* ws, int splits, int64_t M, int64_t 
 int64_t gemm_mx_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt);
 int64_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+// Size of the library's device scratch (csrc/scratch.hip): the largest
+// split-K workspace any plan needs (S M N 4 bytes with at most one item per
+// resident workgroup: 256 items of a 256x256 tile).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+// Device address of the current device's scratch (taken once per device).
+hipError_t scratch_buffer(void** ptr);
+
 // Name of the kernel configuration the launchers above pick for a shape
 // given ws_bytes of workspace.
 const char* plan_gemm_mx(int64_t M, int64_t N, int64_t K, int fmt, int64_t ws_bytes);

@@ -237,6 +237,29 @@ mx_status mx_gemm_ws(const void* A, const void* As, const void* B, const void* B
  * (0 when that plan does not split K, or when an argument is invalid). */
 size_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, mx_fmt fmt);
 
+/* Bytes of device scratch the library holds per GPU for mx_gemm_scratch. */
+#define MX_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * mx_gemm_ws with the library's own device scratch in place of a caller
+ * workspace. It runs the plan mx_gemm_ws runs with
+ * mx_gemm_workspace_bytes(M, N, K, fmt) bytes of workspace (the same
+ * kernels, the same result bit for bit) and allocates and frees nothing.
+ * The scratch is a device array of MX_SCRATCH_BYTES in the library; each GPU
+ * the library runs on holds its own copy from the library's load until the
+ * process ends, and the first call on a GPU looks up its address once (with
+ * that GPU current). Every plan fits: a split plan has at most one work item
+ * per resident workgroup, so S * M * N * 4 <= MX_SCRATCH_BYTES; a plan that
+ * did not would return MX_ERR_UNSUPPORTED. The partials are fully written
+ * by each call before they are read, so nothing has to start at zero. Every
+ * call on one GPU shares that GPU's scratch: calls that can overlap on one
+ * GPU (on two streams, or from two threads) race, and the caller must order
+ * them. Other arguments, errors and memory rules as for mx_gemm. */
+mx_status mx_gemm_scratch(const void* A, const void* As, const void* B, const void* Bs,
+                          void* C, int64_t M, int64_t N, int64_t K, mx_fmt fmt,
+                          const void* bias, mx_dtype out_dtype, void* hip_stream);
+
 /* fc1 writing fc2's operand (README section 4.3, MXFP8 row of the block
  * table: fc1's epilogue quantizes the GELU output straight into fc2's E4M3
  * operand). Computes H = A * B^T (+ bias) as mx_gemm with bf16 output
