@@ -56,8 +56,13 @@ __device__ __forceinline__ void wait_vm() {
 constexpr int kStoreDeviceScope = 16;
 
 // Workgroup barrier after this wave's LDS operations have completed. Global
-// stores still in flight are deliberately not waited for.
-__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// stores still in flight are deliberately not waited for. The LDS wait goes
+// through the builtin so the compiler knows every earlier LDS read is done
+// (otherwise it re-waits for them, counting later reads in between).
+__device__ __forceinline__ void block_sync() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // Coordinates of tile t: XCD-contiguous renumbering (tile t runs on XCD
 // t % 8 because the grid is a multiple of 8 or covers every tile once), then

@@ -313,6 +313,136 @@ __device__ __forceinline__ void gelu_quant_store(uint4 w, bool scale_lane, bool 
   __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, qs_rs, (in && scale_lane) ? scale_off : (int)0x80000000u, 0, kStoreDeviceScope);
 }
 
+// The epilogue of one tile. acc register 4q + v of fragment [fm][fn] is
+// C[m][n + v] with m = m0 + wm WM + 32 fm + r32, n = n0 + wn WN + 32 fn + 8 q + 4 g;
+// lds_bias holds the tile's BN bias values (zeros without a bias). With
+// `staged` (bf16 C below 2 GiB with N % 8 == 0, or the quantized output) the
+// tile goes through LDS one wave-row at a time, row lr of the staging area at
+// row_ptr(lr) (BN * 2 bytes, free for the whole epilogue): bias added,
+// rounded to bf16, written as 16-byte chunks XOR-swizzled by row, then stored
+// as whole rows with range-checked buffer stores (every thread issues
+// EPI_STORES of them, or twice that for the quantized output). Otherwise it
+// is stored from registers (fp32, or the element-wise fallback).
+template <class Cfg, class RowPtr>
+__device__ __forceinline__ void mx_epilogue(const v16f (&acc)[Cfg::FM][Cfg::FN], const uint8_t* lds_bias, bool staged,
+                                            int M, int N, int m0, int n0, int wm, int wn, int g, int r32, void* Ct,
+                                            int out_f32_t, __amdgpu_buffer_rsrc_t c_rs, __amdgpu_buffer_rsrc_t q_rs,
+                                            __amdgpu_buffer_rsrc_t qs_rs, int qld, int q_row_bytes,
+                                            const uint16_t* gtab, RowPtr row_ptr) {
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, WM = Cfg::WM, WN = Cfg::WN, CPR = Cfg::CPR;
+  auto bias4 = [&](int nl) -> uint2 { return *reinterpret_cast<const uint2*>(lds_bias + 2 * nl); };
+  if (staged) {
+#pragma unroll
+    for (int h = 0; h < Cfg::WAVES_M; ++h) {
+      block_sync();                        // previous readers of the buffer are done
+      if (wm == h) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          uint2 bb[4];                     // bias of this lane's columns of fragment column fn
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bb[q] = bias4(wn * WN + 32 * fn + 8 * q + 4 * g);
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) {
+            const int lr = 32 * fm + r32;
+            uint32_t P[4][2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float v0 = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb[q].x & 0xFFFFu);
+              const float v1 = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb[q].x >> 16);
+              const float v2 = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb[q].y & 0xFFFFu);
+              const float v3 = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb[q].y >> 16);
+              P[q][0] = pack_bf16x2(v0, v1);
+              P[q][1] = pack_bf16x2(v2, v3);
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              // the two lanes holding adjacent 4-column runs of a row swap
+              // halves across the wave: lane g = 0 ends with columns
+              // 16p .. 16p + 7 of the fragment, lane g = 1 with 16p + 8 .. + 15
+              const auto s0 = __builtin_amdgcn_permlane32_swap(P[2 * p][0], P[2 * p + 1][0], false, false);
+              const auto s1 = __builtin_amdgcn_permlane32_swap(P[2 * p][1], P[2 * p + 1][1], false, false);
+              const int chunk = (wn * WN + 32 * fn + 16 * p + 8 * g) >> 3;
+              *reinterpret_cast<uint4*>(row_ptr(lr) + ((chunk ^ (lr & (CPR - 1))) * 16)) =
+                  make_uint4(s0[0], s1[0], s0[1], s1[1]);
+            }
+          }
+        }
+      }
+      block_sync();
+      // LDS reads in batches of up to 4, each batch ahead of its stores
+      constexpr int E = Cfg::EPI_STORES;
+      constexpr int BATCH = E % 4 == 0 ? 4 : E % 3 == 0 ? 3 : E % 2 == 0 ? 2 : 1;
+      static_assert(Cfg::EPI_STORES % BATCH == 0, "store batches");
+#pragma unroll
+      for (int j0 = 0; j0 < Cfg::EPI_STORES; j0 += BATCH) {
+        uint4 w[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+          const int id = (int)threadIdx.x + (j0 + j) * Cfg::NT;
+          const int row = id / CPR, c = id % CPR;
+          w[j] = *reinterpret_cast<const uint4*>(row_ptr(row) + ((c ^ (row & (CPR - 1))) * 16));
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+          const int id = (int)threadIdx.x + (j0 + j) * Cfg::NT;
+          const int row = id / CPR, c = id % CPR;
+          const int m = m0 + h * WM + row, n = n0 + 8 * c;
+          if constexpr (Cfg::EPI == 0) {
+            const int off = (m < M && n < N) ? (m * N + n) * 2 : (int)0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b128(v4u{w[j].x, w[j].y, w[j].z, w[j].w}, c_rs, off, 0, kStoreDeviceScope);
+          } else {
+            gelu_quant_store<Cfg::FMT, Cfg::GTAB>(w[j], (c & 3) == 0, m < M && n < qld,
+                                                  m * q_row_bytes + ((Cfg::FMT == FMT_MXFP8) ? n : n / 2),
+                                                  m * (qld / 32) + n / 32, q_rs, qs_rs, gtab);
+          }
+        }
+      }
+    }
+  } else {
+    block_sync();
+    const bool vec = ((N & 3) == 0);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = m0 + wm * WM + 32 * fm + r32;
+      if (m >= M) continue;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * WN + 32 * fn + 8 * q + 4 * g;
+          if (n >= N) continue;
+          const uint2 bb = bias4(n - n0);
+          float v[4];
+          v[0] = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb.x & 0xFFFFu);
+          v[1] = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb.x >> 16);
+          v[2] = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb.y & 0xFFFFu);
+          v[3] = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb.y >> 16);
+          const int64_t off = (int64_t)m * N + n;
+          if (out_f32_t) {
+            float* c = reinterpret_cast<float*>(Ct) + off;
+            if (vec && n + 3 < N) {
+              *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (n + j < N) c[j] = v[j];
+            }
+          } else {
+            uint16_t* c = reinterpret_cast<uint16_t*>(Ct) + off;
+            if (vec && n + 3 < N) {
+              *reinterpret_cast<uint2*>(c) = make_uint2(pack_bf16x2(v[0], v[1]),
+                                                        pack_bf16x2(v[2], v[3]));
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (n + j < N) c[j] = (uint16_t)f32_to_bf16_rne(v[j]);
+            }
+          }
+        }
+    }
+  }
+}
+
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_t* __restrict__ A,
                                                           const uint8_t* __restrict__ As,
@@ -556,120 +686,10 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
       for (int i = (int)threadIdx.x; i < BN; i += Cfg::NT)
         reinterpret_cast<uint16_t*>(lds_bias)[i] = (bias != nullptr && n0 + i < N) ? bias[n0 + i] : (uint16_t)0;
     }
-    auto bias4 = [&](int nl) -> uint2 { return *reinterpret_cast<const uint2*>(lds_bias + 2 * nl); };
-    if (staged) {
-      uint8_t* stg = lds + ((gs - 1) & 1) * Cfg::STAGE;   // buffer of the stage just consumed
-#pragma unroll
-      for (int h = 0; h < Cfg::WAVES_M; ++h) {
-        block_sync();                        // previous readers of the buffer are done
-        if (wm == h) {
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) {
-            uint2 bb[4];                     // bias of this lane's columns of fragment column fn
-#pragma unroll
-            for (int q = 0; q < 4; ++q) bb[q] = bias4(wn * WN + 32 * fn + 8 * q + 4 * g);
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-              const int lr = 32 * fm + r32;
-              uint32_t P[4][2];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const float v0 = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb[q].x & 0xFFFFu);
-                const float v1 = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb[q].x >> 16);
-                const float v2 = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb[q].y & 0xFFFFu);
-                const float v3 = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb[q].y >> 16);
-                P[q][0] = pack_bf16x2(v0, v1);
-                P[q][1] = pack_bf16x2(v2, v3);
-              }
-#pragma unroll
-              for (int p = 0; p < 2; ++p) {
-                // the two lanes holding adjacent 4-column runs of a row swap
-                // halves across the wave: lane g = 0 ends with columns
-                // 16p .. 16p + 7 of the fragment, lane g = 1 with 16p + 8 .. + 15
-                const auto s0 = __builtin_amdgcn_permlane32_swap(P[2 * p][0], P[2 * p + 1][0], false, false);
-                const auto s1 = __builtin_amdgcn_permlane32_swap(P[2 * p][1], P[2 * p + 1][1], false, false);
-                const int chunk = (wn * WN + 32 * fn + 16 * p + 8 * g) >> 3;
-                *reinterpret_cast<uint4*>(stg + lr * (BN * 2) + ((chunk ^ (lr & (CPR - 1))) * 16)) =
-                    make_uint4(s0[0], s1[0], s0[1], s1[1]);
-              }
-            }
-          }
-        }
-        block_sync();
-        // LDS reads in batches of up to 4, each batch ahead of its stores
-        constexpr int E = Cfg::EPI_STORES;
-        constexpr int BATCH = E % 4 == 0 ? 4 : E % 3 == 0 ? 3 : E % 2 == 0 ? 2 : 1;
-        static_assert(Cfg::EPI_STORES % BATCH == 0, "store batches");
-#pragma unroll
-        for (int j0 = 0; j0 < Cfg::EPI_STORES; j0 += BATCH) {
-          uint4 w[BATCH];
-#pragma unroll
-          for (int j = 0; j < BATCH; ++j) {
-            const int id = (int)threadIdx.x + (j0 + j) * Cfg::NT;
-            const int row = id / CPR, c = id % CPR;
-            w[j] = *reinterpret_cast<const uint4*>(stg + row * (BN * 2) + ((c ^ (row & (CPR - 1))) * 16));
-          }
-#pragma unroll
-          for (int j = 0; j < BATCH; ++j) {
-            const int id = (int)threadIdx.x + (j0 + j) * Cfg::NT;
-            const int row = id / CPR, c = id % CPR;
-            const int m = m0 + h * WM + row, n = n0 + 8 * c;
-            if constexpr (Cfg::EPI == 0) {
-              const int off = (m < M && n < N) ? (m * N + n) * 2 : (int)0x80000000u;
-              __builtin_amdgcn_raw_buffer_store_b128(v4u{w[j].x, w[j].y, w[j].z, w[j].w}, c_rs, off, 0, kStoreDeviceScope);
-            } else {
-              gelu_quant_store<Cfg::FMT, Cfg::GTAB>(w[j], (c & 3) == 0, m < M && n < qld,
-                                                    m * q_row_bytes + ((Cfg::FMT == FMT_MXFP8) ? n : n / 2),
-                                                    m * (qld / 32) + n / 32, q_rs, qs_rs,
-                                                    reinterpret_cast<const uint16_t*>(lds + Cfg::GTAB_OFF));
-            }
-          }
-        }
-      }
-    } else {
-      block_sync();
-      const bool vec = ((N & 3) == 0);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int m = m0 + wm * WM + 32 * fm + r32;
-        if (m >= M) continue;
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = n0 + wn * WN + 32 * fn + 8 * q + 4 * g;
-            if (n >= N) continue;
-            const uint2 bb = bias4(n - n0);
-            float v[4];
-            v[0] = acc[fm][fn][4 * q + 0] + bf16_to_f32(bb.x & 0xFFFFu);
-            v[1] = acc[fm][fn][4 * q + 1] + bf16_to_f32(bb.x >> 16);
-            v[2] = acc[fm][fn][4 * q + 2] + bf16_to_f32(bb.y & 0xFFFFu);
-            v[3] = acc[fm][fn][4 * q + 3] + bf16_to_f32(bb.y >> 16);
-            const int64_t off = (int64_t)m * N + n;
-            if (out_f32_t) {
-              float* c = reinterpret_cast<float*>(Ct) + off;
-              if (vec && n + 3 < N) {
-                *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
-              } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                  if (n + j < N) c[j] = v[j];
-              }
-            } else {
-              uint16_t* c = reinterpret_cast<uint16_t*>(Ct) + off;
-              if (vec && n + 3 < N) {
-                *reinterpret_cast<uint2*>(c) = make_uint2(pack_bf16x2(v[0], v[1]),
-                                                          pack_bf16x2(v[2], v[3]));
-              } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                  if (n + j < N) c[j] = (uint16_t)f32_to_bf16_rne(v[j]);
-              }
-            }
-          }
-      }
-      wait_vm<0>();                          // nothing but the next stage's copies stays in flight
-    }
+    mx_epilogue<Cfg>(acc, lds_bias, staged, M, N, m0, n0, wm, wn, g, r32, Ct, out_f32_t, c_rs, q_rs, qs_rs, qld,
+                     q_row_bytes, reinterpret_cast<const uint16_t*>(lds + Cfg::GTAB_OFF),
+                     [&](int lr) { return lds + ((gs - 1) & 1) * Cfg::STAGE + lr * (BN * 2); });
+    if (!staged) wait_vm<0>();               // nothing but the next stage's copies stays in flight
     ++ctc;
   }
   wait_vm<0>();                              // no copy into LDS outlives the workgroup
