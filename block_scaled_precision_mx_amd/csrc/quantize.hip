@@ -254,6 +254,56 @@ constexpr int kColTileR = 128;   // rows of X (the block axis) per tile
 constexpr int kColTileC = 64;    // columns of X per tile
 constexpr int kColLdsLd = kColTileC + 8;   // padded LDS row (elements), keeps 16-B alignment
 
+// Column-copy output of one 128 x 64 tile, staged through LDS so that the
+// stores are whole row segments: lane j of wave w hands in the codes of
+// output row c0 + j, elements r0 + 32 w .. + 31 (CB bytes: 32 for MXFP8, 16
+// for the fp4 formats) and their scale bytes (NVFP4: two, in the low 16 bits;
+// MX: one). After a barrier (every wave is done reading the tile) they go to
+// `stage` (the tile's own buffer) as rows of 4 CB bytes (+16 bytes of
+// padding, which keeps a wave's 16-byte writes on distinct banks) followed
+// by 64 rows of scale bytes; after a second barrier each output row is
+// stored as 16-byte chunks by adjacent lanes and its scale bytes by one lane
+// (one write request per row segment instead of one per lane and chunk).
+// Every thread of the workgroup must call it. Output rows at or past `cols`
+// are not stored.
+template <int FMT>
+__device__ __forceinline__ void col_tile_store(uint8_t* stage, int t, const uint32_t (&words)[8], uint32_t sbytes,
+                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad,
+                                               int r0, int c0, int cols) {
+  constexpr int CB = (FMT == FMT_MXFP8) ? 32 : 16;          // code bytes per lane
+  constexpr int ROW = 4 * CB;                                // code bytes per output row of the tile
+  constexpr int CS = ROW + 16;                               // staged row stride
+  constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
+  constexpr int NSB = 128 / BS;                              // scale bytes per output row of the tile
+  constexpr int SC_OFF = 64 * CS;
+  const int w = t / 64, j = t % 64;
+  __syncthreads();
+  uint8_t* dst = stage + j * CS + w * CB;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
+  if (CB == 32) *reinterpret_cast<uint4*>(dst + 16) = make_uint4(words[4], words[5], words[6], words[7]);
+  if (FMT == FMT_NVFP4) {
+    *reinterpret_cast<uint16_t*>(stage + SC_OFF + j * NSB + 2 * w) = (uint16_t)sbytes;
+  } else {
+    stage[SC_OFF + j * NSB + w] = (uint8_t)sbytes;
+  }
+  __syncthreads();
+  constexpr int RC = ROW / 16;                               // 16-byte chunks per output row
+  const int64_t out_row = (FMT == FMT_MXFP8) ? kpad : kpad / 2;
+  const int first = (FMT == FMT_MXFP8) ? r0 : r0 / 2;        // byte offset of the tile in an output row
+#pragma unroll
+  for (int q = t; q < 64 * RC; q += 256) {
+    const int row = q / RC, k = q % RC;
+    if (c0 + row < cols)
+      *reinterpret_cast<uint4*>(codes + (int64_t)(c0 + row) * out_row + first + 16 * k) =
+          *reinterpret_cast<const uint4*>(stage + row * CS + 16 * k);
+  }
+  if (t < 64 && c0 + t < cols) {
+    uint8_t* sdst = scales + (int64_t)(c0 + t) * (kpad / BS) + r0 / BS;
+    if (NSB == 8) *reinterpret_cast<uint2*>(sdst) = *reinterpret_cast<const uint2*>(stage + SC_OFF + t * NSB);
+    else *reinterpret_cast<uint32_t*>(sdst) = *reinterpret_cast<const uint32_t*>(stage + SC_OFF + t * NSB);
+  }
+}
+
 // X [rows, cols] -> codes of X^T: [cols, kpad] with kpad = round_up(rows, 128).
 template <int FMT>
 __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
@@ -296,9 +346,9 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
     for (int p = 0; p < 4; ++p)
       *reinterpret_cast<uint4*>(&tile[(t / 8 + 32 * p) * kColLdsLd + (t % 8) * 8]) = v[p];
     __syncthreads();
-    // wave w owns tile rows 32w .. 32w+31; lane j owns column j
+    // wave w owns tile rows 32w .. 32w+31; lane j owns column j (output row
+    // c0 + j; lanes past `cols` encode zeros that are never stored)
     const int w = t / 64, j = t % 64;
-    const int oc = c0 + j;                    // output row (a column of X)
     float x[32];
     uint32_t m[2] = {0u, 0u};
 #pragma unroll
@@ -307,49 +357,35 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
       x[i] = bf16_to_f32(b);
       m[i / 16] = max(m[i / 16], b & 0x7FFFu);
     }
-    if (oc < cols) {
-      const int orow = r0 + 32 * w;           // first element index along the block axis
-      if (FMT == FMT_NVFP4) {
-        uint32_t packed[4];
+    uint32_t words[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t sbytes = 0u;
+    if (FMT == FMT_NVFP4) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          Nv4Thresholds th;
-          const uint32_t sb = block_scale<FMT>(m[h], s_t, th);
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) word |= nvfp4_encode(x[16 * h + 8 * q2 + i], th) << (4 * i);
-            packed[2 * h + q2] = word;
-          }
-          scales[(int64_t)oc * (kpad / 16) + orow / 16 + h] = (uint8_t)sb;
-        }
-        *reinterpret_cast<uint4*>(codes + (int64_t)oc * (kpad / 2) + orow / 2) =
-            make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      } else {
+      for (int h = 0; h < 2; ++h) {
         Nv4Thresholds th;
-        const uint32_t sb = block_scale<FMT>(max(m[0], m[1]), s_t, th);
-        if (FMT == FMT_MXFP8) {
-          uint32_t words[8];
+        const uint32_t sb = block_scale<FMT>(m[h], s_t, th);
 #pragma unroll
-          for (int q2 = 0; q2 < 8; ++q2) {
-            words[q2] = e4m3x4_scaled(x[4 * q2], x[4 * q2 + 1], x[4 * q2 + 2], x[4 * q2 + 3], sb);
-          }
-          uint4* dst = reinterpret_cast<uint4*>(codes + (int64_t)oc * kpad + orow);
-          dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
-          dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
-        } else {
-          uint32_t words[4];
+        for (int q2 = 0; q2 < 2; ++q2) {
+          uint32_t word = 0;
 #pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) {
-            words[q2] = e2m1x8_scaled(&x[8 * q2], sb);
-          }
-          *reinterpret_cast<uint4*>(codes + (int64_t)oc * (kpad / 2) + orow / 2) =
-              make_uint4(words[0], words[1], words[2], words[3]);
+          for (int i = 0; i < 8; ++i) word |= nvfp4_encode(x[16 * h + 8 * q2 + i], th) << (4 * i);
+          words[2 * h + q2] = word;
         }
-        scales[(int64_t)oc * (kpad / 32) + orow / 32] = (uint8_t)sb;
+        sbytes |= sb << (8 * h);
       }
+    } else {
+      Nv4Thresholds th;
+      const uint32_t sb = block_scale<FMT>(max(m[0], m[1]), s_t, th);
+      if (FMT == FMT_MXFP8) {
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2) words[q2] = e4m3x4_scaled(x[4 * q2], x[4 * q2 + 1], x[4 * q2 + 2], x[4 * q2 + 3], sb);
+      } else {
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) words[q2] = e2m1x8_scaled(&x[8 * q2], sb);
+      }
+      sbytes = sb;
     }
+    col_tile_store<FMT>(reinterpret_cast<uint8_t*>(tile), t, words, sbytes, codes, scales, kpad, r0, c0, cols);
     __syncthreads();
   }
 }
@@ -564,9 +600,10 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
     }
     __syncthreads();
 
-    // column copy, from LDS: wave w owns tile rows 32w .. 32w + 31, lane j column j
+    // column copy, from LDS: wave w owns tile rows 32w .. 32w + 31, lane j
+    // column j (output row c0 + j; lanes past `cols` encode zeros that are
+    // never stored)
     const int w = t / 64, j = t % 64;
-    const int oc = c0 + j;
     float x[32];
     uint32_t m2[2] = {0u, 0u};
 #pragma unroll
@@ -575,55 +612,41 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
       x[i] = bf16_to_f32(b);
       m2[i / 16] = max(m2[i / 16], b & 0x7FFFu);
     }
-    if (oc < cols) {
-      const int orow = r0 + 32 * w;
-      if (FMT == FMT_NVFP4) {
-        uint32_t packed[4];
+    uint32_t words[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t sbytes = 0u;
+    if (FMT == FMT_NVFP4) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          Nv4Thresholds th;
-          const uint32_t sb = block_scale<FMT>(m2[h], s_t, th);
-          [[maybe_unused]] float S32 = 0.0f;
-          if constexpr (SR) S32 = __fmul_rn((float)e4m3_value(sb), s_t);
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int k = 16 * h + 8 * q2 + i;
-              if constexpr (SR) word |= nvfp4_encode_sr(x[k], S32, draw[(32 * w + k) * kColTileC + j]) << (4 * i);
-              else word |= nvfp4_encode(x[k], th) << (4 * i);
-            }
-            packed[2 * h + q2] = word;
-          }
-          cscales[(int64_t)oc * (ckpad / 16) + orow / 16 + h] = (uint8_t)sb;
-        }
-        *reinterpret_cast<uint4*>(ccodes + (int64_t)oc * (ckpad / 2) + orow / 2) =
-            make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      } else {
+      for (int h = 0; h < 2; ++h) {
         Nv4Thresholds th;
-        const uint32_t sb = block_scale<FMT>(max(m2[0], m2[1]), s_t, th);
-        if (FMT == FMT_MXFP8) {
-          uint32_t words[8];
+        const uint32_t sb = block_scale<FMT>(m2[h], s_t, th);
+        [[maybe_unused]] float S32 = 0.0f;
+        if constexpr (SR) S32 = __fmul_rn((float)e4m3_value(sb), s_t);
 #pragma unroll
-          for (int q2 = 0; q2 < 8; ++q2) {
-            words[q2] = e4m3x4_scaled(x[4 * q2], x[4 * q2 + 1], x[4 * q2 + 2], x[4 * q2 + 3], sb);
-          }
-          uint4* dst = reinterpret_cast<uint4*>(ccodes + (int64_t)oc * ckpad + orow);
-          dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
-          dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
-        } else {
-          uint32_t words[4];
+        for (int q2 = 0; q2 < 2; ++q2) {
+          uint32_t word = 0;
 #pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) {
-            words[q2] = e2m1x8_scaled(&x[8 * q2], sb);
+          for (int i = 0; i < 8; ++i) {
+            const int k = 16 * h + 8 * q2 + i;
+            if constexpr (SR) word |= nvfp4_encode_sr(x[k], S32, draw[(32 * w + k) * kColTileC + j]) << (4 * i);
+            else word |= nvfp4_encode(x[k], th) << (4 * i);
           }
-          *reinterpret_cast<uint4*>(ccodes + (int64_t)oc * (ckpad / 2) + orow / 2) =
-              make_uint4(words[0], words[1], words[2], words[3]);
+          words[2 * h + q2] = word;
         }
-        cscales[(int64_t)oc * (ckpad / 32) + orow / 32] = (uint8_t)sb;
+        sbytes |= sb << (8 * h);
       }
+    } else {
+      Nv4Thresholds th;
+      const uint32_t sb = block_scale<FMT>(max(m2[0], m2[1]), s_t, th);
+      if (FMT == FMT_MXFP8) {
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2) words[q2] = e4m3x4_scaled(x[4 * q2], x[4 * q2 + 1], x[4 * q2 + 2], x[4 * q2 + 3], sb);
+      } else {
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) words[q2] = e2m1x8_scaled(&x[8 * q2], sb);
+      }
+      sbytes = sb;
     }
+    col_tile_store<FMT>(reinterpret_cast<uint8_t*>(tile), t, words, sbytes, ccodes, cscales, ckpad, r0, c0, cols);
     __syncthreads();
   }
   if (FMT == FMT_NVFP4 && delayed) {          // this tensor's amax, for the next call

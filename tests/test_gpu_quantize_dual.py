@@ -82,6 +82,33 @@ def test_dual_nvfp4_delayed_scale(amax_prev, headroom):
     compare_dual(bits, "nvfp4", amax_prev, headroom)
 
 
+def every_block_amax(seed):
+    """One 16-element block per finite bf16 magnitude (0 .. 0x7F7F): element
+    0 is the magnitude itself (the block amax, sign alternating), the other 15
+    are seeded values of no larger magnitude, 8 blocks to a 128-element row."""
+    rng = np.random.default_rng(seed)
+    amax = np.arange(0, 0x7F80, dtype=np.uint32)
+    n = amax.size
+    rest = (rng.integers(0, 1 << 16, size=(n, 15), dtype=np.uint32) & 0x7FFF) % (amax[:, None] + 1)
+    rest |= rng.integers(0, 2, size=(n, 15), dtype=np.uint32) << 15
+    blocks = np.concatenate([(amax | ((np.arange(n, dtype=np.uint32) & 1) << 15))[:, None], rest], axis=1)
+    pad = (-n) % 8
+    blocks = np.concatenate([blocks, np.zeros((pad, 16), dtype=np.uint32)])
+    return blocks.astype(np.uint16).reshape(-1, 128)
+
+
+@pytest.mark.parametrize("amax_prev,headroom", [(3.5, 32.0), (1.0e-38, 1.0), (1.0e-30, 3.0), (3.0e38, 1.0),
+                                                (2.0e-8, 0.75), (0.0, 32.0)])
+def test_dual_nvfp4_every_block_amax(amax_prev, headroom):
+    """The NVFP4 block scale byte and element codes of every finite bf16
+    magnitude as a block amax, under delayed tensor scales from zero and
+    fp32-subnormal up to about 10^35: both copies byte for byte against the
+    oracle (the row copy holds the 16-element blocks as built; the column
+    copy re-blocks them down the columns)."""
+    bits = every_block_amax(seed=int(headroom * 1000) % 9973)
+    compare_dual(bits, "nvfp4", amax_prev, headroom)
+
+
 def test_dual_nvfp4_headroom_one_equals_plain_quantize():
     bits = W.np_gelu_activation((257, 333), seed=32)
     x = to_device_bf16(bits)
