@@ -35,7 +35,10 @@ SPLIT_FULL = [
     (300, 260, 7000, "nvfp4", "bf16", True),
     (3072, 1024, 11235, "mxfp8", "bf16", False),   # the large tile, split
     (3072, 1024, 11235, "nvfp4", "bf16", False),
+    (4096, 1024, 11235, "mxfp8", "bf16", False),   # fc1's and fc2's weight gradients, every output
+    (1024, 4096, 11235, "mxfp8", "bf16", False),
 ]
+_ORACLE = {}   # (M, N, K, fmt, bias) -> (inputs, quantized operands, reference): shared by both workspace sizes
 # the weight-gradient GEMMs of the training workloads, with the benchmark's
 # workspace: (workload, GEMM label)
 WGRAD = [(name, s.label) for name in ("vitl16_mxfp8_block_train", "vitl16_p3_block_train", "vitl16_nvfp4_fc1fc2_train",
@@ -71,8 +74,8 @@ def run_ws(a, b, fmt, bias_bits, out_dtype, ws_bytes, a_axis="row", b_axis="row"
     return f64_of(out)
 
 
-def check_every_output(got, qa, qb, bias_bits, out_dtype):
-    c, s = G.gemm_ref(qa, qb, bias_bits)
+def check_every_output(got, qa, qb, bias_bits, out_dtype, ref=None):
+    c, s = G.gemm_ref(qa, qb, bias_bits) if ref is None else ref
     ok = G.accept(got, c, s, out_dtype)
     if qa.fmt == "mxfp8" and not ok.all():
         r, q = np.nonzero(~ok)
@@ -82,8 +85,8 @@ def check_every_output(got, qa, qb, bias_bits, out_dtype):
     assert bad.size == 0, f"{len(bad)} outside the bound, e.g. {[(tuple(i), got[tuple(i)], c[tuple(i)]) for i in bad[:3]]}"
 
 
-@pytest.mark.parametrize("m,n,k,fmt,out_dtype,with_bias", SPLIT_FULL)
 @pytest.mark.parametrize("ws_part", ["full", "half"])
+@pytest.mark.parametrize("m,n,k,fmt,out_dtype,with_bias", SPLIT_FULL)
 def test_gemm_ws_every_output(m, n, k, fmt, out_dtype, with_bias, ws_part):
     need = api.gemm_workspace_bytes(m, n, k, fmt)
     assert need > 0, "the case must split K"
@@ -92,11 +95,17 @@ def test_gemm_ws_every_output(m, n, k, fmt, out_dtype, with_bias, ws_part):
     log(f"gemm_ws plan={plan} m={m} n={n} k={k} fmt={fmt} out={out_dtype} ws={ws}")
     if ws_part == "full":
         assert "+splitk" in plan
-    a = W.np_activation((m, k), seed=m + k)
-    b = W.np_normal((n, k), seed=n + k, std=W.W_STD)
-    bias = W.np_normal((n,), seed=n, std=W.BIAS_STD) if with_bias else None
+    key = (m, n, k, fmt, with_bias)
+    if key not in _ORACLE:
+        a = W.np_activation((m, k), seed=m + k)
+        b = W.np_normal((n, k), seed=n + k, std=W.W_STD)
+        bias = W.np_normal((n,), seed=n, std=W.BIAS_STD) if with_bias else None
+        qa, qb = Q.quantize(a, fmt), Q.quantize(b, fmt)
+        _ORACLE.clear()
+        _ORACLE[key] = (a, b, bias, qa, qb, G.gemm_ref(qa, qb, bias))
+    a, b, bias, qa, qb, ref = _ORACLE[key]
     got = run_ws(a, b, fmt, bias, out_dtype, ws)
-    check_every_output(got, Q.quantize(a, fmt), Q.quantize(b, fmt), bias, out_dtype)
+    check_every_output(got, qa, qb, bias, out_dtype, ref)
 
 
 @pytest.mark.parametrize("name,label", WGRAD)
