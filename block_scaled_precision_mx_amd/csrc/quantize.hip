@@ -139,17 +139,114 @@ __device__ __forceinline__ uint32_t block_scale(uint32_t amax_bits, float s_t, N
   return (uint32_t)(e + 127);
 }
 
-// Encode 8 values with scale byte sb; packed codes in the low 64 (fp8) or
-// 32 (fp4) bits.
+// ------------------------------------------------------------ NVFP4 encode
+//
+// The NVFP4 element code is the E2M1 rounding (nearest, ties to the even
+// code, saturating at 6) of the real quotient |x| / S with S = E4M3(byte) *
+// s_t, sign copied. The threshold form (nvfp4_thresholds / nvfp4_encode)
+// compares |x| with the fp32 ceilings of the seven midpoints times S: seven
+// compares per element and fp64 work per block. The fast form below gets the
+// same codes with gfx950's scaled E2M1 conversion, which at scale 2^0 rounds
+// an fp32 value to nearest even, saturates at 6 and keeps the sign: it
+// converts x * r_lo and x * r_hi, where r_lo < 1 / S < r_hi bracket the
+// reciprocal within 2^-19 (relative). The two products then bracket the
+// quotient and the conversion is monotone, so two equal codes are the
+// quotient's code; they differ only when a midpoint lies within about 2^-19
+// of the quotient (an exact tie or a near one), and those elements take the
+// threshold form. Both forms compute the same function; the fast one needs
+// a finite block amax and an s_t for which S and 1 / S stay normal fp32.
+//
+// Error budget of the bracket: S32 = fp32(S) (2^-24), v_rcp_f32 (1 ulp,
+// 2^-23), r_lo / r_hi rounded (2^-24) and the product rounded (2^-24): under
+// 2^-21.5 in all, well inside the 2^-19 offsets.
+
+struct Nv4Tensor {
+  float s_t;
+  float inv6;      // fp32(1 / (6 s_t)) when `fast`
+  bool fast;       // s_t in [2^-96, 2^96] (false for 0, inf, NaN)
+};
+
+__device__ __forceinline__ Nv4Tensor nv4_tensor(float s_t) {
+  Nv4Tensor t;
+  t.s_t = s_t;
+  t.fast = s_t >= 0x1p-96f && s_t <= 0x1p96f;
+  t.inv6 = t.fast ? (float)(1.0 / (6.0 * (double)s_t)) : 0.0f;
+  return t;
+}
+
+// E4M3 byte (RNE, saturating at 448) of a q >= 0 known through qf, an fp32
+// value within 2^-22 (relative) of it. False when qf is too close to a
+// rounding midpoint for its rounding to be the rounding of q.
+__device__ __forceinline__ bool e4m3_from_near(float qf, uint32_t& b) {
+  if (qf >= 448.0f) {                   // q > 447.9: 448 (the midpoint below it is 432)
+    b = 0x7Eu;
+    return true;
+  }
+  if (qf >= 0x1p-6f) {                  // normal E4M3: keep 3 of the 23 fraction bits
+    const uint32_t u = __float_as_uint(qf);
+    const uint32_t low = u & 0xFFFFFu;  // the midpoint is low == 0x80000
+    if (low - 0x7FFF0u < 0x21u) return false;
+    b = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+    return true;
+  }
+  const float t = qf * 512.0f;          // subnormal E4M3: multiples of 2^-9 (t < 8, exact)
+  const float fl = floorf(t);
+  const float fr = t - fl;
+  if (fabsf(fr - 0.5f) < 0x1p-16f) return false;
+  b = (uint32_t)fl + (fr > 0.5f ? 1u : 0u);
+  return true;
+}
+
+struct Nv4Block {
+  uint32_t sb;     // E4M3 scale byte
+  bool fast;       // the bracket below is valid
+  float r_lo, r_hi;
+};
+
+// Block scale byte of q = amax / (6 s_t) and the reciprocal bracket of S.
+__device__ __forceinline__ Nv4Block nv4_block(uint32_t amax_bits, const Nv4Tensor& T) {
+  Nv4Block B;
+  const bool finite = amax_bits < 0x7F80u;
+  uint32_t b = 0u;
+  if (!(T.fast && finite && e4m3_from_near(bf16_to_f32(amax_bits) * T.inv6, b))) {
+    const double q = (T.s_t == 0.0f) ? 0.0 : (double)bf16_to_f32(amax_bits) / (6.0 * (double)T.s_t);
+    b = e4m3_encode_pos_f64(q);
+  }
+  B.sb = b;
+  B.fast = T.fast && finite;
+  const float r = b ? __builtin_amdgcn_rcpf((float)e4m3_value(b) * T.s_t) : 0.0f;   // S = 0: codes are signs
+  B.r_lo = r * (1.0f - 0x1p-19f);
+  B.r_hi = r * (1.0f + 0x1p-19f);
+  return B;
+}
+
+// 8 NVFP4 codes (nibble i = x[i]) of one block's elements.
+__device__ __forceinline__ uint32_t nv4_encode8(const float (&x)[8], const Nv4Block& B, const Nv4Tensor& T) {
+  const float one = 1.0f;               // scale operand 2^0
+  uint32_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0] * B.r_lo, x[1] * B.r_lo, one, 0);
+  uint32_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0] * B.r_hi, x[1] * B.r_hi, one, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[2] * B.r_lo, x[3] * B.r_lo, one, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[2] * B.r_hi, x[3] * B.r_hi, one, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[4] * B.r_lo, x[5] * B.r_lo, one, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[4] * B.r_hi, x[5] * B.r_hi, one, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[6] * B.r_lo, x[7] * B.r_lo, one, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[6] * B.r_hi, x[7] * B.r_hi, one, 3);
+  if (B.fast && lo == hi) return lo;
+  const Nv4Thresholds th = nvfp4_thresholds(e4m3_value(B.sb) * (double)T.s_t);
+  uint32_t word = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) word |= nvfp4_encode(x[i], th) << (4 * i);
+  return word;
+}
+
+// Encode 8 values with MX scale byte sb; packed codes in the low 64 (fp8) or
+// 32 (fp4) bits. (NVFP4 goes through nv4_encode8.)
 template <int FMT>
-__device__ __forceinline__ uint64_t encode8(const float (&x)[8], uint32_t sb, const Nv4Thresholds& th) {
+__device__ __forceinline__ uint64_t encode8(const float (&x)[8], uint32_t sb, const Nv4Thresholds&) {
+  static_assert(FMT != FMT_NVFP4, "NVFP4 elements are encoded by nv4_encode8");
   if (FMT == FMT_MXFP8)
     return (uint64_t)e4m3x4_scaled(x[0], x[1], x[2], x[3], sb) | ((uint64_t)e4m3x4_scaled(x[4], x[5], x[6], x[7], sb) << 32);
-  if (FMT == FMT_MXFP4) return e2m1x8_scaled(x, sb);
-  uint64_t out = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) out |= (uint64_t)nvfp4_encode(x[i], th) << (4 * i);
-  return out;
+  return e2m1x8_scaled(x, sb);
 }
 
 // ------------------------------------------------------------ row quantizer
@@ -176,6 +273,7 @@ __device__ __forceinline__ void quant_rows(const uint16_t* __restrict__ src, int
                                                   // are adjacent, aligned and in one row
   const int total = rows * tpr;
   const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
+  [[maybe_unused]] const Nv4Tensor nt = nv4_tensor(s_t);
   for (int tid = first_tid; tid < total; tid += stride) {
     const int r = tid / tpr;
     const int j = tid - r * tpr;
@@ -208,9 +306,17 @@ __device__ __forceinline__ void quant_rows(const uint16_t* __restrict__ src, int
       // block amax across the adjacent lanes of this block
 #pragma unroll
       for (int off = 1; off < LANES_PER_BLOCK; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-      Nv4Thresholds th;
-      const uint32_t sb = block_scale<FMT>(m, s_t, th);
-      const uint64_t packed = encode8<FMT>(x, sb, th);
+      uint32_t sb;
+      uint64_t packed;
+      if constexpr (FMT == FMT_NVFP4) {
+        const Nv4Block B = nv4_block(m, nt);
+        sb = B.sb;
+        packed = nv4_encode8(x, B, nt);
+      } else {
+        Nv4Thresholds th;
+        sb = block_scale<FMT>(m, s_t, th);
+        packed = encode8<FMT>(x, sb, th);
+      }
       if (FMT == FMT_MXFP8) {
         *reinterpret_cast<uint2*>(codes + (int64_t)r * kpad + c) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
       } else {
@@ -320,6 +426,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
     s_t = nvfp4_tensor_scale(tr->amax_bits);
     if (blockIdx.x == 0 && t == 0) tr->s_t = s_t;
   }
+  [[maybe_unused]] const Nv4Tensor nt = nv4_tensor(s_t);
   for (int tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
     const int tr_ = tile_id / tiles_c;
     const int tc = tile_id - tr_ * tiles_c;
@@ -362,16 +469,10 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
     if (FMT == FMT_NVFP4) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        Nv4Thresholds th;
-        const uint32_t sb = block_scale<FMT>(m[h], s_t, th);
+        const Nv4Block B = nv4_block(m[h], nt);
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) word |= nvfp4_encode(x[16 * h + 8 * q2 + i], th) << (4 * i);
-          words[2 * h + q2] = word;
-        }
-        sbytes |= sb << (8 * h);
+        for (int q2 = 0; q2 < 2; ++q2) words[2 * h + q2] = nv4_encode8(reinterpret_cast<const float(&)[8]>(x[16 * h + 8 * q2]), B, nt);
+        sbytes |= B.sb << (8 * h);
       }
     } else {
       Nv4Thresholds th;
@@ -429,13 +530,25 @@ __global__ void nv_dual_init_kernel(uint8_t* rgap, int rgap_bytes, NvTrailer* rt
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC 2011): ten rounds of the four-word round function,
 // the key bumped by the Weyl constants between rounds.
+// 128-bit product m * c as (hi, lo), from four 32 x 32 -> 64 multiply-adds
+// (V_MAD_U64_U32); no partial sum overflows 64 bits.
+__device__ __forceinline__ void mul_64x64(uint64_t m, uint64_t c, uint64_t& hi, uint64_t& lo) {
+  const uint32_t m0 = (uint32_t)m, m1 = (uint32_t)(m >> 32), c0 = (uint32_t)c, c1 = (uint32_t)(c >> 32);
+  const uint64_t p00 = (uint64_t)m0 * c0;
+  const uint64_t p01 = (uint64_t)m0 * c1 + (p00 >> 32);
+  const uint64_t p10 = (uint64_t)m1 * c0 + (uint32_t)p01;
+  hi = (uint64_t)m1 * c1 + (p01 >> 32) + (p10 >> 32);
+  lo = (p10 << 32) | (uint32_t)p00;
+}
+
 __device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
   constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
-    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    uint64_t hi0, lo0, hi1, lo1;
+    mul_64x64(M0, c[0], hi0, lo0);
+    mul_64x64(M1, c[2], hi1, lo1);
     const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
     c[0] = n0;
     c[1] = lo1;
@@ -462,26 +575,18 @@ __device__ __forceinline__ void sr_draws8(uint64_t q, uint64_t k0, uint64_t k1, 
 // E2M1 magnitude code of y >= 0 rounded stochastically with draw u: between
 // the grid neighbours lo <= y < hi, hi iff u < ceil(frac * 2^32), frac =
 // (y - lo) / (hi - lo) (exact); y >= 6 saturates.
+// Without branches: the grid spacing is 2^(e - 1) with e = clamp(floor(log2
+// y), 0, 2), so s = y / spacing is exact, floor(s) + 2e is the code of lo and
+// s - floor(s) the exact fraction.
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) {
-  if (!(y < 6.0f)) return 7u;
-  uint32_t lo;
-  float glo, inv_span;
-  if (y < 2.0f) {
-    lo = (uint32_t)(y * 2.0f);             // 0, 0.5, 1, 1.5: floor of 2y
-    glo = (float)lo * 0.5f;
-    inv_span = 2.0f;
-  } else if (y < 4.0f) {
-    lo = y < 3.0f ? 4u : 5u;               // 2, 3
-    glo = y < 3.0f ? 2.0f : 3.0f;
-    inv_span = 1.0f;
-  } else {
-    lo = 6u;                               // 4 (next: 6)
-    glo = 4.0f;
-    inv_span = 0.5f;
-  }
-  const float frac = (y - glo) * inv_span;                 // exact
+  const int E = (int)(__float_as_uint(y) >> 23) - 127;     // y >= 0
+  const int e = min(max(E, 0), 2);
+  const float s = y * __uint_as_float((uint32_t)(128 - e) << 23);   // y * 2^(1 - e), exact
+  const float f = floorf(s);
+  const float frac = s - f;                                // exact
   const uint32_t T = (uint32_t)ceilf(frac * 4294967296.0f); // < 2^32 - 255: exact
-  return u < T ? lo + 1u : lo;
+  const uint32_t code = (uint32_t)f + 2u * (uint32_t)e + (u < T ? 1u : 0u);
+  return y < 6.0f ? code : 7u;                             // 6 and above (inf, NaN too): 6
 }
 
 // NVFP4 code of x with scale S32 = fp32(dec(byte) * s_t), rounded
@@ -526,6 +631,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
       }
     }
   }
+  [[maybe_unused]] const Nv4Tensor nt = nv4_tensor(s_t);
   uint32_t own_max = 0u;                      // largest |x| bits this thread saw (delayed NVFP4)
   for (int slot = blockIdx.x; slot < ntiles; slot += gridDim.x) {
     const int tile_id = xcd_tile(slot, ntiles);
@@ -569,10 +675,10 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
       own_max = max(own_max, m);
 #pragma unroll
       for (int off = 1; off < LANES_PER_BLOCK; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-      Nv4Thresholds th;
-      const uint32_t sb = block_scale<FMT>(m, s_t, th);
+      uint32_t sb;
       uint64_t packed;
       if constexpr (SR) {
+        sb = nv4_block(m, nt).sb;
         // draws of elements (r, c .. c + 7): one Philox block when the
         // element index r * cols + c is a multiple of 8 (cols % 8 == 0 is a
         // precondition); tile padding never reaches a code (its x is 0)
@@ -586,7 +692,13 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < 8; ++i) word |= nvfp4_encode_sr(x[i], S32, d[i]) << (4 * i);
         packed = word;
+      } else if constexpr (FMT == FMT_NVFP4) {
+        const Nv4Block B = nv4_block(m, nt);
+        sb = B.sb;
+        packed = nv4_encode8(x, B, nt);
       } else {
+        Nv4Thresholds th;
+        sb = block_scale<FMT>(m, s_t, th);
         packed = encode8<FMT>(x, sb, th);
       }
       if (r < rows) {
@@ -617,22 +729,25 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
     if (FMT == FMT_NVFP4) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        Nv4Thresholds th;
-        const uint32_t sb = block_scale<FMT>(m2[h], s_t, th);
-        [[maybe_unused]] float S32 = 0.0f;
-        if constexpr (SR) S32 = __fmul_rn((float)e4m3_value(sb), s_t);
+        const Nv4Block B = nv4_block(m2[h], nt);
+        if constexpr (SR) {
+          const float S32 = __fmul_rn((float)e4m3_value(B.sb), s_t);
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          uint32_t word = 0;
+          for (int q2 = 0; q2 < 2; ++q2) {
+            uint32_t word = 0;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int k = 16 * h + 8 * q2 + i;
-            if constexpr (SR) word |= nvfp4_encode_sr(x[k], S32, draw[(32 * w + k) * kColTileC + j]) << (4 * i);
-            else word |= nvfp4_encode(x[k], th) << (4 * i);
+            for (int i = 0; i < 8; ++i) {
+              const int k = 16 * h + 8 * q2 + i;
+              word |= nvfp4_encode_sr(x[k], S32, draw[(32 * w + k) * kColTileC + j]) << (4 * i);
+            }
+            words[2 * h + q2] = word;
           }
-          words[2 * h + q2] = word;
+        } else {
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2)
+            words[2 * h + q2] = nv4_encode8(reinterpret_cast<const float(&)[8]>(x[16 * h + 8 * q2]), B, nt);
         }
-        sbytes |= sb << (8 * h);
+        sbytes |= B.sb << (8 * h);
       }
     } else {
       Nv4Thresholds th;

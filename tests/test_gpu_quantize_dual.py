@@ -10,6 +10,7 @@ import torch
 
 from block_scaled_precision_mx_amd import api
 from block_scaled_precision_mx_amd import workloads as W
+from oracle import formats as F
 from oracle import quantize as Q
 from gpu_util import bytes_of, guarded_quantized, log, to_device_bf16
 from test_gpu_quantize import special
@@ -107,6 +108,62 @@ def test_dual_nvfp4_every_block_amax(amax_prev, headroom):
     copy re-blocks them down the columns)."""
     bits = every_block_amax(seed=int(headroom * 1000) % 9973)
     compare_dual(bits, "nvfp4", amax_prev, headroom)
+
+
+E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def near_midpoint_tiles(width_tiles: int = 4) -> np.ndarray:
+    """16 x 16 tiles stacked down and across, so that every row block and
+    every column block of 16 holds its tile's amax (on the tile's
+    diagonal). Tile i has amax 6 (block scale byte 1.0 at s_t near 1) or
+    6 x an E4M3 rounding midpoint (the block scale rounds up or down by a
+    hair); its other entries are the E2M1 midpoints times the E4M3 values
+    around amax / 6, both signs, and their bf16 neighbours. At s_t = 1 +
+    delta the quotients x / S then sit within about delta of E2M1 midpoints,
+    and the block scale quotients within delta of E4M3 midpoints."""
+    amaxes = [6.0] + [(51 + 6 * k) / 8 for k in range(8)] + [(51 + 6 * k) / 16 for k in range(0, 8, 2)] + [6.0 * 2 ** -5, 6.0 * 2 ** 4]
+    tiles = []
+    for a in amaxes:
+        q = a / 6.0
+        e = np.floor(np.log2(q))
+        k = np.floor(q / 2.0 ** e * 8) - 8                   # E4M3 values (8 + k) 2^(e-3) and (9 + k) 2^(e-3)
+        vals = [m * (8 + k + d) * 2.0 ** (e - 3) for m in E2M1_MIDPOINTS for d in (0, 1)]
+        vals += [-v for v in vals]
+        exact = W.to_bf16_bits(np.array(vals))
+        assert np.array_equal(F.bf16_to_f64(exact), np.array(vals)), "tile values must be bf16-exact"
+        body = np.concatenate([exact, exact + 1, exact - 1]).astype(np.uint16)
+        for t in range(width_tiles):
+            tile = np.zeros((16, 16), dtype=np.uint16)
+            off = [(r, c) for r in range(16) for c in range(16) if r != c]
+            for n, (r, c) in enumerate(off):
+                tile[r, c] = body[(n + 7 * t) % len(body)]
+            np.fill_diagonal(tile, W.to_bf16_bits(np.array([a]))[0])
+            tiles.append(tile)
+    rows = [np.concatenate(tiles[i:i + width_tiles], axis=1) for i in range(0, len(tiles), width_tiles)]
+    return np.concatenate(rows, axis=0)
+
+
+# s_t = fp32(A / 2688) for A = 2688 + j 2^-12 (fp32-exact): s_t - 1 runs from
+# 0 through about +-2^-23 .. 2^-15
+NEAR_MIDPOINT_J = [-300, -40, -7, -3, -1, 0, 1, 2, 5, 33, 257]
+
+
+@pytest.mark.parametrize("j", NEAR_MIDPOINT_J)
+def test_dual_nvfp4_near_midpoints(j):
+    """Element quotients and block-scale quotients at and within 2^-23 ..
+    2^-15 of their rounding midpoints (ties, and near ties on both sides):
+    both copies byte for byte against the oracle's exact rounding."""
+    amax_prev = 2688.0 + j * 2.0 ** -12
+    assert float(np.float32(amax_prev)) == amax_prev
+    compare_dual(near_midpoint_tiles(), "nvfp4", amax_prev, 1.0)
+
+
+@pytest.mark.parametrize("j", [-7, 0, 1, 33])
+def test_dual_sr_near_midpoints(j):
+    """Stochastic rounding of the same tiles: block scales next to E4M3
+    midpoints, quotients on and next to E2M1 grid points and midpoints."""
+    compare_dual_sr(near_midpoint_tiles(), SR_SEED, 2688.0 + j * 2.0 ** -12, 1.0)
 
 
 def test_dual_nvfp4_headroom_one_equals_plain_quantize():
