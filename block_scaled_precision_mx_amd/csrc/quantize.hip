@@ -27,24 +27,29 @@
 #include "mx_device.h"
 #include "mx_launch.h"
 
+#include <algorithm>
+#include <mutex>
+#include <utility>
+#include <vector>
+
 namespace mx {
+
+// Output buffers are written with raw buffer stores: a lane with nothing to
+// store gives an offset past the end (kDropped), which the buffer's range
+// check discards. The stores are then unconditional, so the compiler knows
+// how many are in flight and can wait for a tile's prefetched loads without
+// waiting for the stores issued after them.
+constexpr uint32_t kDropped = 0x80000000u;   // outputs are < 2 GiB
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes, 0x00020000);
+}
 
 // 16-byte streaming load (the source is read once).
 __device__ __forceinline__ uint4 load16_stream(const void* p) {
   typedef unsigned v4 __attribute__((ext_vector_type(4)));
   const v4 v = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// Tile of workgroup slot `id` when the grid holds one workgroup per tile:
-// workgroups are dealt to the 8 XCDs round-robin, so tiles are renumbered to
-// give each XCD a contiguous range. Neighbouring tiles along a row then share
-// an L2, which matters where each writes half of a 128-byte line (the row copy
-// of a 64-column tile). With fewer workgroups than tiles, the identity.
-__device__ __forceinline__ int xcd_tile(int id, int ntiles) {
-  if ((int)gridDim.x != ntiles) return id;
-  const int q = ntiles / 8, r = ntiles % 8, xcd = id % 8, local = id / 8;
-  return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
 }
 
 struct NvTrailer {
@@ -361,171 +366,71 @@ constexpr int kColTileC = 64;    // columns of X per tile
 constexpr int kColLdsLd = kColTileC + 8;   // padded LDS row (elements), keeps 16-B alignment
 
 // Column-copy output of one 128 x 64 tile, staged through LDS so that the
-// stores are whole row segments: lane j of wave w hands in the codes of
-// output row c0 + j, elements r0 + 32 w .. + 31 (CB bytes: 32 for MXFP8, 16
-// for the fp4 formats) and their scale bytes (NVFP4: two, in the low 16 bits;
-// MX: one). After a barrier (every wave is done reading the tile) they go to
-// `stage` (the tile's own buffer) as rows of 4 CB bytes (+16 bytes of
-// padding, which keeps a wave's 16-byte writes on distinct banks) followed
-// by 64 rows of scale bytes; after a second barrier each output row is
-// stored as 16-byte chunks by adjacent lanes and its scale bytes by one lane
-// (one write request per row segment instead of one per lane and chunk).
-// Every thread of the workgroup must call it. Output rows at or past `cols`
-// are not stored.
+// stores are whole row segments. col_stage_write: lane j of wave w hands in
+// the codes of output row c0 + j, elements r0 + 32 w .. + 31 (CB bytes: 32
+// for MXFP8, 16 for the fp4 formats) and their scale bytes (NVFP4: two, in
+// the low 16 bits; MX: one); they go to `stage` as rows of 4 CB bytes (+16
+// bytes of padding, which keeps a wave's 16-byte writes on distinct banks)
+// followed by 64 rows of scale bytes. col_stage_flush, after a barrier:
+// each output row is stored as 16-byte chunks by adjacent lanes and its
+// scale bytes by one lane (one write request per row segment instead of one
+// per lane and chunk); output rows at or past `cols` are dropped. Every
+// thread of the workgroup calls both.
 template <int FMT>
-__device__ __forceinline__ void col_tile_store(uint8_t* stage, int t, const uint32_t (&words)[8], uint32_t sbytes,
-                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad,
-                                               int r0, int c0, int cols) {
-  constexpr int CB = (FMT == FMT_MXFP8) ? 32 : 16;          // code bytes per lane
-  constexpr int ROW = 4 * CB;                                // code bytes per output row of the tile
-  constexpr int CS = ROW + 16;                               // staged row stride
-  constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
-  constexpr int NSB = 128 / BS;                              // scale bytes per output row of the tile
-  constexpr int SC_OFF = 64 * CS;
+struct ColStage {
+  static constexpr int CB = (FMT == FMT_MXFP8) ? 32 : 16;   // code bytes per lane
+  static constexpr int ROW = 4 * CB;                         // code bytes per output row of the tile
+  static constexpr int CS = ROW + 16;                        // staged row stride
+  static constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
+  static constexpr int NSB = 128 / BS;                       // scale bytes per output row of the tile
+  static constexpr int SC_OFF = 64 * CS;
+  static constexpr int BYTES = SC_OFF + 64 * NSB;
+};
+
+template <int FMT>
+__device__ __forceinline__ void col_stage_write(uint8_t* stage, int t, const uint32_t (&words)[8], uint32_t sbytes) {
+  using C = ColStage<FMT>;
   const int w = t / 64, j = t % 64;
-  __syncthreads();
-  uint8_t* dst = stage + j * CS + w * CB;
+  uint8_t* dst = stage + j * C::CS + w * C::CB;
   *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
-  if (CB == 32) *reinterpret_cast<uint4*>(dst + 16) = make_uint4(words[4], words[5], words[6], words[7]);
+  if (C::CB == 32) *reinterpret_cast<uint4*>(dst + 16) = make_uint4(words[4], words[5], words[6], words[7]);
   if (FMT == FMT_NVFP4) {
-    *reinterpret_cast<uint16_t*>(stage + SC_OFF + j * NSB + 2 * w) = (uint16_t)sbytes;
+    *reinterpret_cast<uint16_t*>(stage + C::SC_OFF + j * C::NSB + 2 * w) = (uint16_t)sbytes;
   } else {
-    stage[SC_OFF + j * NSB + w] = (uint8_t)sbytes;
+    stage[C::SC_OFF + j * C::NSB + w] = (uint8_t)sbytes;
   }
-  __syncthreads();
-  constexpr int RC = ROW / 16;                               // 16-byte chunks per output row
-  const int64_t out_row = (FMT == FMT_MXFP8) ? kpad : kpad / 2;
+}
+
+template <int FMT>
+__device__ __forceinline__ void col_stage_flush(const uint8_t* stage, int t, __amdgpu_buffer_rsrc_t codes,
+                                                __amdgpu_buffer_rsrc_t scales, int kpad, int r0, int c0, int cols) {
+  using C = ColStage<FMT>;
+  constexpr int RC = C::ROW / 16;                            // 16-byte chunks per output row
+  static_assert((64 * RC) % 256 == 0, "every thread stores the same number of chunks");
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  const int out_row = (FMT == FMT_MXFP8) ? kpad : kpad / 2;
   const int first = (FMT == FMT_MXFP8) ? r0 : r0 / 2;        // byte offset of the tile in an output row
 #pragma unroll
   for (int q = t; q < 64 * RC; q += 256) {
     const int row = q / RC, k = q % RC;
-    if (c0 + row < cols)
-      *reinterpret_cast<uint4*>(codes + (int64_t)(c0 + row) * out_row + first + 16 * k) =
-          *reinterpret_cast<const uint4*>(stage + row * CS + 16 * k);
+    const uint4 c = *reinterpret_cast<const uint4*>(stage + row * C::CS + 16 * k);
+    const uint32_t off = c0 + row < cols ? (uint32_t)((c0 + row) * out_row + first + 16 * k) : kDropped;
+    __builtin_amdgcn_raw_buffer_store_b128(v4u{c.x, c.y, c.z, c.w}, codes, off, 0, 0);
   }
-  if (t < 64 && c0 + t < cols) {
-    uint8_t* sdst = scales + (int64_t)(c0 + t) * (kpad / BS) + r0 / BS;
-    if (NSB == 8) *reinterpret_cast<uint2*>(sdst) = *reinterpret_cast<const uint2*>(stage + SC_OFF + t * NSB);
-    else *reinterpret_cast<uint32_t*>(sdst) = *reinterpret_cast<const uint32_t*>(stage + SC_OFF + t * NSB);
-  }
-}
-
-// X [rows, cols] -> codes of X^T: [cols, kpad] with kpad = round_up(rows, 128).
-template <int FMT>
-__global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
-                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                        int kpad, NvTrailer* tr) {
-  __shared__ __align__(16) uint16_t tile[kColTileR * kColLdsLd];
-  const int tiles_c = (cols + kColTileC - 1) / kColTileC;
-  const int tiles_r = kpad / kColTileR;
-  const int ntiles = tiles_c * tiles_r;
-  const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
-  const int t = threadIdx.x;
-  float s_t = 0.0f;
-  if (FMT == FMT_NVFP4) {
-    s_t = nvfp4_tensor_scale(tr->amax_bits);
-    if (blockIdx.x == 0 && t == 0) tr->s_t = s_t;
-  }
-  [[maybe_unused]] const Nv4Tensor nt = nv4_tensor(s_t);
-  for (int tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
-    const int tr_ = tile_id / tiles_c;
-    const int tc = tile_id - tr_ * tiles_c;
-    const int r0 = tr_ * kColTileR, c0 = tc * kColTileC;
-    // stage: 128 rows x 64 cols; thread t loads 8 columns of rows t/8 + 32 p
-    uint4 v[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = r0 + t / 8 + 32 * p, c = c0 + (t % 8) * 8;
-      v[p] = make_uint4(0u, 0u, 0u, 0u);
-      if (r < rows) {
-        const uint16_t* q = src + (int64_t)r * ld + c;
-        if (vec_ok && c + 8 <= cols) {
-          v[p] = load16_stream(q);
-        } else {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};
-          for (int i = 0; i < 8; ++i)
-            if (c + i < cols) w[i / 2] |= (uint32_t)q[i] << (16 * (i % 2));
-          v[p] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      *reinterpret_cast<uint4*>(&tile[(t / 8 + 32 * p) * kColLdsLd + (t % 8) * 8]) = v[p];
-    __syncthreads();
-    // wave w owns tile rows 32w .. 32w+31; lane j owns column j (output row
-    // c0 + j; lanes past `cols` encode zeros that are never stored)
-    const int w = t / 64, j = t % 64;
-    float x[32];
-    uint32_t m[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t b = tile[(32 * w + i) * kColLdsLd + j];
-      x[i] = bf16_to_f32(b);
-      m[i / 16] = max(m[i / 16], b & 0x7FFFu);
-    }
-    uint32_t words[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    uint32_t sbytes = 0u;
-    if (FMT == FMT_NVFP4) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const Nv4Block B = nv4_block(m[h], nt);
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) words[2 * h + q2] = nv4_encode8(reinterpret_cast<const float(&)[8]>(x[16 * h + 8 * q2]), B, nt);
-        sbytes |= B.sb << (8 * h);
-      }
-    } else {
-      Nv4Thresholds th;
-      const uint32_t sb = block_scale<FMT>(max(m[0], m[1]), s_t, th);
-      if (FMT == FMT_MXFP8) {
-#pragma unroll
-        for (int q2 = 0; q2 < 8; ++q2) words[q2] = e4m3x4_scaled(x[4 * q2], x[4 * q2 + 1], x[4 * q2 + 2], x[4 * q2 + 3], sb);
-      } else {
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) words[q2] = e2m1x8_scaled(&x[8 * q2], sb);
-      }
-      sbytes = sb;
-    }
-    col_tile_store<FMT>(reinterpret_cast<uint8_t*>(tile), t, words, sbytes, codes, scales, kpad, r0, c0, cols);
-    __syncthreads();
+  // scale bytes: row t of the tile, by the first wave (the others drop theirs)
+  const int srow = t % 64;
+  const uint32_t soff = (t < 64 && c0 + srow < cols) ? (uint32_t)((c0 + srow) * (kpad / C::BS) + r0 / C::BS) : kDropped;
+  if (C::NSB == 8) {
+    const uint2 sv = *reinterpret_cast<const uint2*>(stage + C::SC_OFF + srow * C::NSB);
+    __builtin_amdgcn_raw_buffer_store_b64(v2u{sv.x, sv.y}, scales, soff, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(stage + C::SC_OFF + srow * C::NSB), scales,
+                                          soff, 0, 0);
   }
 }
 
-// ------------------------------------------------------------ fused row + col
-
-// README section 5.5: the weight-gradient GEMM needs each operand twice,
-// quantized along its rows and along its columns (stored transposed); one
-// kernel reads X once and writes both copies. A 128 x 64 tile is loaded as
-// in quant_col_kernel: thread t holds 8 consecutive elements of rows
-// t / 8 + 32 p, which the 4 (MX) or 2 (NVFP4) adjacent lanes of a row block
-// quantize straight from registers into the row copy, while the tile goes
-// through LDS for the column copy. The tiles cover round_up(cols, 128)
-// columns so that the row copy's padding is written too, and round_up(rows,
-// 128) rows for the column copy's.
-//
-// NVFP4 tensor scale: either from this tensor's amax (reduced first into the
-// row copy's trailer, as mx_quantize does), or delayed (README section 5.5):
-// set before this kernel from an earlier amax times a headroom, in which case
-// this kernel reduces the tensor's own amax into both trailers on the side
-// (one atomic max per workgroup), for the next call.
-
-// Trailers of both copies and the padding before them; with `delayed`,
-// s_t = fp32(fp64(headroom * *amax_prev) / 2688), read before anything is
-// written (amax_prev may be the amax field of either trailer).
-__global__ void nv_dual_init_kernel(uint8_t* rgap, int rgap_bytes, NvTrailer* rtr, uint8_t* cgap, int cgap_bytes,
-                                    NvTrailer* ctr, const float* amax_prev, float headroom, int delayed) {
-  const int t = threadIdx.x;
-  if (t == 0) {
-    float s_t = 0.0f;
-    if (delayed) s_t = (float)(((double)headroom * (double)*amax_prev) / 2688.0);
-    rtr->s_t = s_t;
-    ctr->s_t = s_t;
-    rtr->amax_bits = ctr->amax_bits = 0u;
-    rtr->pad[0] = rtr->pad[1] = ctr->pad[0] = ctr->pad[1] = 0u;
-  }
-  if (t < rgap_bytes) rgap[t] = 0;
-  if (t < cgap_bytes) cgap[t] = 0;
-}
+// ------------------------------------------------------------ stochastic rounding
 
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC 2011): ten rounds of the four-word round function,
@@ -598,20 +503,301 @@ __device__ __forceinline__ uint32_t nvfp4_encode_sr(float x, float S32, uint32_t
   return sign | e2m1_sr(y, u);
 }
 
-template <int FMT, bool SR = false>
+// Tile walk of a persistent grid (gridDim.x a multiple of 8). Workgroups are
+// dealt to the 8 XCDs round-robin, so workgroup b runs on XCD b % 8; each XCD
+// takes a contiguous range of tile numbers and its workgroups interleave over
+// it (number start + b / 8 + i * gridDim.x / 8). A workgroup walks several
+// tiles and loads the next one while it encodes the current one: with one
+// tile per workgroup, loads were only in flight between encodes, too few
+// bytes to cover HBM latency.
+struct TileWalk {
+  int first, step, end;
+};
+
+__device__ __forceinline__ TileWalk tile_walk(int ntiles) {
+  const int x = (int)blockIdx.x % 8, nb = (int)gridDim.x / 8;
+  const int q = ntiles / 8, r = ntiles % 8;
+  const int start = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+  return {start + (int)blockIdx.x / 8, nb, start + q + (x < r ? 1 : 0)};
+}
+
+// Tile (row, column) of tile number n: super-rows of 8 tile rows, numbered
+// down each column of tiles, then across. Tiles that share output lines then
+// get numbers close together (one XCD, the same step of the walk): the column
+// copy's scale bytes of 8 tiles down a column fill one 64-byte segment, and
+// its codes of 2 tiles one 128-byte line; the row copy's codes of 4 tiles
+// across fill a line (scale bytes: 16). Lines written in parts by different
+// L2s, or evicted between parts, cost extra partial writes to HBM.
+__device__ __forceinline__ void tile_coords(int n, int tiles_r, int tiles_c, int& r0, int& c0) {
+  const int band = n / (8 * tiles_c);
+  const int h = min(8, tiles_r - 8 * band);
+  const int rem = n - band * 8 * tiles_c;
+  const int tc = rem / h;
+  r0 = (8 * band + rem - tc * h) * kColTileR;
+  c0 = tc * kColTileC;
+}
+
+// Thread t's share of the 128 x 64 tile at (r0, c0): 8 columns of rows
+// t / 8 + 32 p (16-byte loads), zeros outside X.
+__device__ __forceinline__ void load_tile(uint4 (&v)[4], const uint16_t* __restrict__ src, int rows, int cols, int ld,
+                                          bool vec_ok, int r0, int c0, int t) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = r0 + t / 8 + 32 * p, c = c0 + (t % 8) * 8;
+    v[p] = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rows && c < cols) {
+      const uint16_t* q = src + (int64_t)r * ld + c;
+      if (vec_ok && c + 8 <= cols) {
+        v[p] = load16_stream(q);
+      } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int i = 0; i < 8; ++i)
+          if (c + i < cols) w[i / 2] |= (uint32_t)q[i] << (16 * (i % 2));
+        v[p] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void stage_tile(uint16_t* tile, const uint4 (&v)[4], int t) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) *reinterpret_cast<uint4*>(&tile[(t / 8 + 32 * p) * kColLdsLd + (t % 8) * 8]) = v[p];
+}
+
+// Elements 8g .. 8g + 7 of a lane's column, from the packed bf16 pairs.
+__device__ __forceinline__ void unpack8(const uint32_t (&h)[16], int g, float (&x)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(h[4 * g + k] << 16);
+    x[2 * k + 1] = __uint_as_float(h[4 * g + k] & 0xFFFF0000u);
+  }
+}
+
+// Column pass of a staged tile: wave w owns tile rows 32 w .. 32 w + 31, lane
+// j column j (output row c0 + j; lanes past `cols` encode zeros that are
+// never stored). The 32 values are kept as 16 packed bf16 pairs: block amax
+// first, then the codes 8 at a time. NVFP4: two 16-row blocks, their scale
+// bytes in the low 16 bits of sbytes; stochastic rounding takes element k's
+// draw from draw[(32 w + k) * 64 + j]. MX: one 32-row block.
+template <int FMT, bool SR>
+__device__ __forceinline__ void col_encode(const uint16_t* tile, const uint32_t* draw, int w, int j,
+                                           const Nv4Tensor& nt, uint32_t (&words)[8], uint32_t& sbytes) {
+  uint32_t h[16];
+  uint32_t m2[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t lo = tile[(32 * w + 2 * i) * kColLdsLd + j];
+    const uint32_t hi = tile[(32 * w + 2 * i + 1) * kColLdsLd + j];
+    h[i] = lo | (hi << 16);
+    m2[i / 8] = max(m2[i / 8], max(lo & 0x7FFFu, hi & 0x7FFFu));
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) words[q] = 0u;
+  sbytes = 0u;
+  if constexpr (FMT == FMT_NVFP4) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const Nv4Block B = nv4_block(m2[hb], nt);
+      [[maybe_unused]] float S32 = 0.0f;
+      if constexpr (SR) S32 = __fmul_rn((float)e4m3_value(B.sb), nt.s_t);
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        float x[8];
+        unpack8(h, 2 * hb + q2, x);
+        if constexpr (SR) {
+          uint32_t word = 0u;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            word |= nvfp4_encode_sr(x[i], S32, draw[(32 * w + 16 * hb + 8 * q2 + i) * kColTileC + j]) << (4 * i);
+          words[2 * hb + q2] = word;
+        } else {
+          words[2 * hb + q2] = nv4_encode8(x, B, nt);
+        }
+      }
+      sbytes |= B.sb << (8 * hb);
+    }
+  } else {
+    Nv4Thresholds th;
+    const uint32_t sb = block_scale<FMT>(max(m2[0], m2[1]), 0.0f, th);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float x[8];
+      unpack8(h, g, x);
+      if (FMT == FMT_MXFP8) {
+        words[2 * g] = e4m3x4_scaled(x[0], x[1], x[2], x[3], sb);
+        words[2 * g + 1] = e4m3x4_scaled(x[4], x[5], x[6], x[7], sb);
+      } else {
+        words[g] = e2m1x8_scaled(x, sb);
+      }
+    }
+    sbytes = sb;
+  }
+}
+
+// X [rows, cols] -> codes of X^T: [cols, kpad] with kpad = round_up(rows, 128).
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
+                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                        int kpad, NvTrailer* tr) {
+  __shared__ __align__(16) uint16_t tile[kColTileR * kColLdsLd];
+  uint8_t* const stage = reinterpret_cast<uint8_t*>(tile);   // the staged output reuses the tile
+  static_assert(ColStage<FMT>::BYTES <= (int)sizeof(tile), "staged output fits in the tile buffer");
+  const int tiles_c = (cols + kColTileC - 1) / kColTileC;
+  const int tiles_r = kpad / kColTileR;
+  const int ntiles = tiles_c * tiles_r;
+  const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
+  const int t = threadIdx.x;
+  float s_t = 0.0f;
+  if (FMT == FMT_NVFP4) {
+    s_t = nvfp4_tensor_scale(tr->amax_bits);
+    if (blockIdx.x == 0 && t == 0) tr->s_t = s_t;
+  }
+  [[maybe_unused]] const Nv4Tensor nt = nv4_tensor(s_t);
+  constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
+  const __amdgpu_buffer_rsrc_t c_rs = out_rsrc(codes, (int64_t)cols * (FMT == FMT_MXFP8 ? kpad : kpad / 2));
+  const __amdgpu_buffer_rsrc_t s_rs = out_rsrc(scales, (int64_t)cols * (kpad / BS));
+  // one tile per workgroup when the grid covers the tiles (the launch does);
+  // many workgroups resident per CU keep the loads in flight
+  const TileWalk tw = tile_walk(ntiles);
+  for (int n = tw.first; n < tw.end; n += tw.step) {
+    int r0, c0;
+    tile_coords(n, tiles_r, tiles_c, r0, c0);
+    uint4 v[4];
+    load_tile(v, src, rows, cols, ld, vec_ok, r0, c0, t);
+    stage_tile(tile, v, t);
+    __syncthreads();                          // tile staged
+    uint32_t words[8], sbytes;
+    col_encode<FMT, false>(tile, nullptr, t / 64, t % 64, nt, words, sbytes);
+    __syncthreads();                          // tile read
+    col_stage_write<FMT>(stage, t, words, sbytes);
+    __syncthreads();                          // output staged
+    col_stage_flush<FMT>(stage, t, c_rs, s_rs, kpad, r0, c0, cols);
+    __syncthreads();                          // staged output read
+  }
+}
+
+// ------------------------------------------------------------ fused row + col
+
+// README section 5.5: the weight-gradient GEMM needs each operand twice,
+// quantized along its rows and along its columns (stored transposed); one
+// kernel reads X once and writes both copies. A 128 x 64 tile is loaded as
+// in quant_col_kernel: thread t holds 8 consecutive elements of rows
+// t / 8 + 32 p, which the 4 (MX) or 2 (NVFP4) adjacent lanes of a row block
+// quantize straight from registers into the row copy, while the tile goes
+// through LDS for the column copy. The tiles cover round_up(cols, 128)
+// columns so that the row copy's padding is written too, and round_up(rows,
+// 128) rows for the column copy's.
+//
+// NVFP4 tensor scale: either from this tensor's amax (reduced first into the
+// row copy's trailer, as mx_quantize does), or delayed (README section 5.5):
+// set before this kernel from an earlier amax times a headroom, in which case
+// this kernel reduces the tensor's own amax into both trailers on the side
+// (one atomic max per workgroup), for the next call.
+
+// Trailers of both copies and the padding before them; with `delayed`,
+// s_t = fp32(fp64(headroom * *amax_prev) / 2688), read before anything is
+// written (amax_prev may be the amax field of either trailer).
+__global__ void nv_dual_init_kernel(uint8_t* rgap, int rgap_bytes, NvTrailer* rtr, uint8_t* cgap, int cgap_bytes,
+                                    NvTrailer* ctr, const float* amax_prev, float headroom, int delayed) {
+  const int t = threadIdx.x;
+  if (t == 0) {
+    float s_t = 0.0f;
+    if (delayed) s_t = (float)(((double)headroom * (double)*amax_prev) / 2688.0);
+    rtr->s_t = s_t;
+    ctr->s_t = s_t;
+    rtr->amax_bits = ctr->amax_bits = 0u;
+    rtr->pad[0] = rtr->pad[1] = ctr->pad[0] = ctr->pad[1] = 0u;
+  }
+  if (t < rgap_bytes) rgap[t] = 0;
+  if (t < cgap_bytes) cgap[t] = 0;
+}
+
+// Row copy of 8 consecutive elements of tile row t / 8 + 32 p (thread t;
+// the lanes of a row block are adjacent): block amax across the lanes, scale
+// byte, codes, stores (dropped past the last row). Stochastic rounding draws
+// the 8 elements' numbers here and leaves them in `draw` for the column copy.
+template <int FMT, bool SR>
+__device__ __forceinline__ void row_encode_store(const uint4 vv, int p, int t, int r0, int c0, int rows, int cols,
+                                                 int rkpad, const Nv4Tensor& nt, uint32_t* draw, uint64_t seed0,
+                                                 uint64_t seed1, __amdgpu_buffer_rsrc_t rc_rs,
+                                                 __amdgpu_buffer_rsrc_t rs_rs, uint32_t& own_max) {
+  constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
+  constexpr int LANES_PER_BLOCK = BS / 8;
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  const int r = r0 + t / 8 + 32 * p, c = c0 + (t % 8) * 8;
+  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+  float x[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t b = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+    x[i] = bf16_to_f32(b);
+    m = max(m, b & 0x7FFFu);
+  }
+  own_max = max(own_max, m);
+#pragma unroll
+  for (int off = 1; off < LANES_PER_BLOCK; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  uint32_t sb;
+  uint64_t packed;
+  if constexpr (SR) {
+    sb = nv4_block(m, nt).sb;
+    // draws of elements (r, c .. c + 7): one Philox block when the element
+    // index r * cols + c is a multiple of 8 (cols % 8 == 0 is a
+    // precondition); tile padding never reaches a code (its x is 0)
+    uint32_t d[8];
+    sr_draws8(((uint64_t)r * (uint64_t)cols + (uint64_t)c) >> 3, seed0, seed1, d);
+    *reinterpret_cast<uint4*>(&draw[(t / 8 + 32 * p) * kColTileC + (t % 8) * 8]) = make_uint4(d[0], d[1], d[2], d[3]);
+    *reinterpret_cast<uint4*>(&draw[(t / 8 + 32 * p) * kColTileC + (t % 8) * 8 + 4]) = make_uint4(d[4], d[5], d[6], d[7]);
+    const float S32 = __fmul_rn((float)e4m3_value(sb), nt.s_t);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= nvfp4_encode_sr(x[i], S32, d[i]) << (4 * i);
+    packed = word;
+  } else if constexpr (FMT == FMT_NVFP4) {
+    const Nv4Block B = nv4_block(m, nt);
+    sb = B.sb;
+    packed = nv4_encode8(x, B, nt);
+  } else {
+    Nv4Thresholds th;
+    sb = block_scale<FMT>(m, 0.0f, th);
+    packed = encode8<FMT>(x, sb, th);
+  }
+  if (FMT == FMT_MXFP8) {
+    const uint32_t off = r < rows ? (uint32_t)(r * rkpad + c) : kDropped;
+    __builtin_amdgcn_raw_buffer_store_b64(v2u{(uint32_t)packed, (uint32_t)(packed >> 32)}, rc_rs, off, 0, 0);
+  } else {
+    const uint32_t off = r < rows ? (uint32_t)(r * (rkpad / 2) + c / 2) : kDropped;
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)packed, rc_rs, off, 0, 0);
+  }
+  const uint32_t soff = (r < rows && ((t % 8) % LANES_PER_BLOCK) == 0) ? (uint32_t)(r * (rkpad / BS) + c / BS) : kDropped;
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rs_rs, soff, 0, 0);
+}
+
+// WALK: a persistent grid walks the tiles, loading the next one while it
+// encodes the current one (the staged column output gets a buffer of its
+// own: it is stored while the next tile is already staged); pays off where
+// encoding is long (NVFP4). Otherwise one tile per workgroup, the many
+// resident workgroups keeping loads in flight, and the output staged in the
+// tile buffer.
+template <int FMT, bool SR, bool WALK>
 __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
                                                          uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
                                                          int rkpad, uint8_t* __restrict__ ccodes,
                                                          uint8_t* __restrict__ cscales, int ckpad, NvTrailer* rtr,
-                                                         NvTrailer* ctr, int delayed, uint64_t seed0 = 0,
-                                                         uint64_t seed1 = 0) {
+                                                         NvTrailer* ctr, int delayed, uint64_t seed0, uint64_t seed1) {
   constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
-  constexpr int LANES_PER_BLOCK = BS / 8;
   static_assert(!SR || FMT == FMT_NVFP4, "stochastic rounding is an NVFP4 option");
   __shared__ __align__(16) uint16_t tile[kColTileR * kColLdsLd];
   // stochastic rounding: the draw of every element of the tile, written by
-  // the row pass and read by the column pass (one draw per element of X)
-  __shared__ __align__(16) uint32_t draw[SR ? kColTileR * kColTileC : 4];
+  // the row pass and read by the column pass (one draw per element of X).
+  // WALK: the staged column output, which shares the draws' space (it is
+  // written after the column pass has read them and stored before the next
+  // row pass writes them).
+  constexpr int kDrawWords = kColTileR * kColTileC, kStageWords = (ColStage<FMT>::BYTES + 3) / 4;
+  __shared__ __align__(16) uint32_t draw[SR ? kDrawWords : (WALK ? kStageWords : 4)];
+  uint8_t* const stage = WALK ? reinterpret_cast<uint8_t*>(draw) : reinterpret_cast<uint8_t*>(tile);
+  static_assert(ColStage<FMT>::BYTES <= (int)sizeof(tile) && (!WALK || kStageWords * 4 <= (int)sizeof(draw)),
+                "staged output fits");
   __shared__ uint32_t wave_max[4];
   const int tiles_c = rkpad / kColTileC;
   const int tiles_r = ckpad / kColTileR;
@@ -632,137 +818,67 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
     }
   }
   [[maybe_unused]] const Nv4Tensor nt = nv4_tensor(s_t);
+  const __amdgpu_buffer_rsrc_t rc_rs = out_rsrc(rcodes, (int64_t)rows * (FMT == FMT_MXFP8 ? rkpad : rkpad / 2));
+  const __amdgpu_buffer_rsrc_t rs_rs = out_rsrc(rscales, (int64_t)rows * (rkpad / BS));
+  const __amdgpu_buffer_rsrc_t cc_rs = out_rsrc(ccodes, (int64_t)cols * (FMT == FMT_MXFP8 ? ckpad : ckpad / 2));
+  const __amdgpu_buffer_rsrc_t cs_rs = out_rsrc(cscales, (int64_t)cols * (ckpad / BS));
   uint32_t own_max = 0u;                      // largest |x| bits this thread saw (delayed NVFP4)
-  for (int slot = blockIdx.x; slot < ntiles; slot += gridDim.x) {
-    const int tile_id = xcd_tile(slot, ntiles);
-    const int tr_ = tile_id / tiles_c;
-    const int tc = tile_id - tr_ * tiles_c;
-    const int r0 = tr_ * kColTileR, c0 = tc * kColTileC;
+  const TileWalk tw = tile_walk(ntiles);
+  if constexpr (WALK) {
     uint4 v[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = r0 + t / 8 + 32 * p, c = c0 + (t % 8) * 8;
-      v[p] = make_uint4(0u, 0u, 0u, 0u);
-      if (r < rows && c < cols) {
-        const uint16_t* q = src + (int64_t)r * ld + c;
-        if (vec_ok && c + 8 <= cols) {
-          v[p] = load16_stream(q);
-        } else {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};
-          for (int i = 0; i < 8; ++i)
-            if (c + i < cols) w[i / 2] |= (uint32_t)q[i] << (16 * (i % 2));
-          v[p] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
+    int nr0 = 0, nc0 = 0;                     // the tile in v
+    if (tw.first < tw.end) {
+      tile_coords(tw.first, tiles_r, tiles_c, nr0, nc0);
+      load_tile(v, src, rows, cols, ld, vec_ok, nr0, nc0, t);
     }
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      *reinterpret_cast<uint4*>(&tile[(t / 8 + 32 * p) * kColLdsLd + (t % 8) * 8]) = v[p];
-
-    // row copy, from registers: the lanes of a row block are adjacent
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = r0 + t / 8 + 32 * p, c = c0 + (t % 8) * 8;
-      const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
-      float x[8];
-      uint32_t m = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t b = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
-        x[i] = bf16_to_f32(b);
-        m = max(m, b & 0x7FFFu);
+    // Per tile: stage it, store the previous tile's staged column output,
+    // load the next tile, then encode both copies (the row copy's stores go
+    // out during the encode). The loop head waits for every memory operation
+    // in flight (loads and stores share one counter), which were then all
+    // issued an encode earlier.
+    int pr0 = -1, pc0 = 0;
+    for (int n = tw.first; n < tw.end; n += tw.step) {
+      const int r0 = nr0, c0 = nc0;
+      stage_tile(tile, v, t);
+      if (pr0 >= 0) col_stage_flush<FMT>(stage, t, cc_rs, cs_rs, ckpad, pr0, pc0, cols);
+      if (n + tw.step < tw.end) {
+        tile_coords(n + tw.step, tiles_r, tiles_c, nr0, nc0);
+        load_tile(v, src, rows, cols, ld, vec_ok, nr0, nc0, t);
       }
-      own_max = max(own_max, m);
+      __syncthreads();                        // tile staged; staged output read
 #pragma unroll
-      for (int off = 1; off < LANES_PER_BLOCK; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-      uint32_t sb;
-      uint64_t packed;
-      if constexpr (SR) {
-        sb = nv4_block(m, nt).sb;
-        // draws of elements (r, c .. c + 7): one Philox block when the
-        // element index r * cols + c is a multiple of 8 (cols % 8 == 0 is a
-        // precondition); tile padding never reaches a code (its x is 0)
-        uint32_t d[8];
-        sr_draws8(((uint64_t)r * (uint64_t)cols + (uint64_t)c) >> 3, seed0, seed1, d);
-        *reinterpret_cast<uint4*>(&draw[(t / 8 + 32 * p) * kColTileC + (t % 8) * 8]) = make_uint4(d[0], d[1], d[2], d[3]);
-        *reinterpret_cast<uint4*>(&draw[(t / 8 + 32 * p) * kColTileC + (t % 8) * 8 + 4]) =
-            make_uint4(d[4], d[5], d[6], d[7]);
-        const float S32 = __fmul_rn((float)e4m3_value(sb), s_t);
-        uint32_t word = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) word |= nvfp4_encode_sr(x[i], S32, d[i]) << (4 * i);
-        packed = word;
-      } else if constexpr (FMT == FMT_NVFP4) {
-        const Nv4Block B = nv4_block(m, nt);
-        sb = B.sb;
-        packed = nv4_encode8(x, B, nt);
-      } else {
-        Nv4Thresholds th;
-        sb = block_scale<FMT>(m, s_t, th);
-        packed = encode8<FMT>(x, sb, th);
-      }
-      if (r < rows) {
-        if (FMT == FMT_MXFP8) {
-          *reinterpret_cast<uint2*>(rcodes + (int64_t)r * rkpad + c) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
-        } else {
-          *reinterpret_cast<uint32_t*>(rcodes + (int64_t)r * (rkpad / 2) + c / 2) = (uint32_t)packed;
-        }
-        if (((t % 8) % LANES_PER_BLOCK) == 0) rscales[(int64_t)r * (rkpad / BS) + c / BS] = (uint8_t)sb;
-      }
+      for (int p = 0; p < 4; ++p)
+        row_encode_store<FMT, SR>(*reinterpret_cast<const uint4*>(&tile[(t / 8 + 32 * p) * kColLdsLd + (t % 8) * 8]), p, t,
+                                  r0, c0, rows, cols, rkpad, nt, draw, seed0, seed1, rc_rs, rs_rs, own_max);
+      if constexpr (SR) __syncthreads();     // draws written before the column pass reads them
+      uint32_t words[8], sbytes;
+      col_encode<FMT, SR>(tile, draw, t / 64, t % 64, nt, words, sbytes);
+      if constexpr (SR) __syncthreads();     // draws read before the staged output overwrites them
+      col_stage_write<FMT>(stage, t, words, sbytes);
+      __syncthreads();                        // output staged; tile read
+      pr0 = r0;
+      pc0 = c0;
     }
-    __syncthreads();
-
-    // column copy, from LDS: wave w owns tile rows 32w .. 32w + 31, lane j
-    // column j (output row c0 + j; lanes past `cols` encode zeros that are
-    // never stored)
-    const int w = t / 64, j = t % 64;
-    float x[32];
-    uint32_t m2[2] = {0u, 0u};
+    if (pr0 >= 0) col_stage_flush<FMT>(stage, t, cc_rs, cs_rs, ckpad, pr0, pc0, cols);
+  } else {
+    for (int n = tw.first; n < tw.end; n += tw.step) {
+      int r0, c0;
+      tile_coords(n, tiles_r, tiles_c, r0, c0);
+      uint4 v[4];
+      load_tile(v, src, rows, cols, ld, vec_ok, r0, c0, t);
+      stage_tile(tile, v, t);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t b = tile[(32 * w + i) * kColLdsLd + j];
-      x[i] = bf16_to_f32(b);
-      m2[i / 16] = max(m2[i / 16], b & 0x7FFFu);
+      for (int p = 0; p < 4; ++p)
+        row_encode_store<FMT, SR>(v[p], p, t, r0, c0, rows, cols, rkpad, nt, draw, seed0, seed1, rc_rs, rs_rs, own_max);
+      __syncthreads();                        // tile staged (and draws written)
+      uint32_t words[8], sbytes;
+      col_encode<FMT, SR>(tile, draw, t / 64, t % 64, nt, words, sbytes);
+      __syncthreads();                        // tile read
+      col_stage_write<FMT>(stage, t, words, sbytes);
+      __syncthreads();                        // output staged
+      col_stage_flush<FMT>(stage, t, cc_rs, cs_rs, ckpad, r0, c0, cols);
+      __syncthreads();                        // staged output read
     }
-    uint32_t words[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    uint32_t sbytes = 0u;
-    if (FMT == FMT_NVFP4) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const Nv4Block B = nv4_block(m2[h], nt);
-        if constexpr (SR) {
-          const float S32 = __fmul_rn((float)e4m3_value(B.sb), s_t);
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int k = 16 * h + 8 * q2 + i;
-              word |= nvfp4_encode_sr(x[k], S32, draw[(32 * w + k) * kColTileC + j]) << (4 * i);
-            }
-            words[2 * h + q2] = word;
-          }
-        } else {
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2)
-            words[2 * h + q2] = nv4_encode8(reinterpret_cast<const float(&)[8]>(x[16 * h + 8 * q2]), B, nt);
-        }
-        sbytes |= B.sb << (8 * h);
-      }
-    } else {
-      Nv4Thresholds th;
-      const uint32_t sb = block_scale<FMT>(max(m2[0], m2[1]), s_t, th);
-      if (FMT == FMT_MXFP8) {
-#pragma unroll
-        for (int q2 = 0; q2 < 8; ++q2) words[q2] = e4m3x4_scaled(x[4 * q2], x[4 * q2 + 1], x[4 * q2 + 2], x[4 * q2 + 3], sb);
-      } else {
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) words[q2] = e2m1x8_scaled(&x[8 * q2], sb);
-      }
-      sbytes = sb;
-    }
-    col_tile_store<FMT>(reinterpret_cast<uint8_t*>(tile), t, words, sbytes, ccodes, cscales, ckpad, r0, c0, cols);
-    __syncthreads();
   }
   if (FMT == FMT_NVFP4 && delayed) {          // this tensor's amax, for the next call
 #pragma unroll
@@ -780,6 +896,37 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
 }
 
 // ------------------------------------------------------------ launchers
+
+// Resident workgroups of 256 threads of `kernel` on the current device
+// (occupancy x CUs), cached per kernel and device.
+static int resident_wgs(const void* kernel) {
+  static std::mutex mu;
+  static std::vector<std::pair<std::pair<const void*, int>, int>> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : cache)
+    if (e.first.first == kernel && e.first.second == dev) return e.second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 8;
+  cache.push_back({{kernel, dev}, per_cu * cus});
+  return per_cu * cus;
+}
+
+// Grid of a tile-walking kernel (tile_walk): at most one resident round of
+// workgroups, no more than the tiles need, and a multiple of 8 so that each
+// XCD gets the same share; every workgroup of an XCD walks the same number
+// of tiles, give or take one.
+static int walk_grid(int64_t ntiles, const void* kernel) {
+  const int64_t per_xcd = std::max<int64_t>(1, resident_wgs(kernel) / 8);
+  const int64_t tiles_xcd = std::max<int64_t>(1, (ntiles + 7) / 8);
+  const int64_t rounds = (tiles_xcd + per_xcd - 1) / per_xcd;
+  return (int)(8 * ((tiles_xcd + rounds - 1) / rounds));
+}
+
+// One workgroup per tile, rounded up to a multiple of 8 (tile_walk).
+static int one_tile_grid(int64_t ntiles) { return (int)(8 * std::max<int64_t>(1, (ntiles + 7) / 8)); }
 
 static int grid_for(int64_t work_items, int per_block, int cap) {
   int64_t g = (work_items + per_block - 1) / per_block;
@@ -823,11 +970,22 @@ hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int6
       launch_row<kRowGroupsSmall>(src, ir, ic, ild, codes, scales, ikp, tr, R, fmt, stream);
   } else {
     const int64_t ntiles = ((cols + kColTileC - 1) / kColTileC) * (kpad / kColTileR);
-    const int g = grid_for(ntiles, 1, 1 << 20);
     switch (fmt) {
-      case FMT_MXFP8: quant_col_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
-      case FMT_MXFP4: quant_col_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
-      default:        quant_col_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
+      case FMT_MXFP8: {
+        const int g = one_tile_grid(ntiles);
+        quant_col_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr);
+        break;
+      }
+      case FMT_MXFP4: {
+        const int g = one_tile_grid(ntiles);
+        quant_col_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr);
+        break;
+      }
+      default: {
+        const int g = one_tile_grid(ntiles);
+        quant_col_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr);
+        break;
+      }
     }
   }
   return hipGetLastError();
@@ -1080,23 +1238,26 @@ hipError_t launch_quantize_dual(const uint16_t* src, int64_t rows, int64_t cols,
     }
   }
   const int64_t ntiles = (rkpad / kColTileC) * (ckpad / kColTileR);
-  const int g = grid_for(ntiles, 1, 1 << 20);
+  const int g = one_tile_grid(ntiles);
+  const int rk = (int)rkpad, ck = (int)ckpad;
   switch (fmt) {
     case FMT_MXFP8:
-      quant_dual_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, (int)rkpad, ccodes, cscales,
-                                                          (int)ckpad, rtr, ctr, delayed);
+      quant_dual_kernel<FMT_MXFP8, false, false><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, rk, ccodes,
+                                                                        cscales, ck, rtr, ctr, delayed, 0, 0);
       break;
     case FMT_MXFP4:
-      quant_dual_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, (int)rkpad, ccodes, cscales,
-                                                          (int)ckpad, rtr, ctr, delayed);
+      quant_dual_kernel<FMT_MXFP4, false, false><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, rk, ccodes,
+                                                                        cscales, ck, rtr, ctr, delayed, 0, 0);
       break;
     default:
-      if (sr)
-        quant_dual_kernel<FMT_NVFP4, true><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, (int)rkpad, ccodes,
-                                                                  cscales, (int)ckpad, rtr, ctr, delayed, seed0, seed1);
-      else
-        quant_dual_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, (int)rkpad, ccodes,
-                                                            cscales, (int)ckpad, rtr, ctr, delayed);
+      if (sr) {
+        quant_dual_kernel<FMT_NVFP4, true, false><<<g, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, rk, ccodes,
+                                                                         cscales, ck, rtr, ctr, delayed, seed0, seed1);
+      } else {
+        const int gw = walk_grid(ntiles, reinterpret_cast<const void*>(&quant_dual_kernel<FMT_NVFP4, false, true>));
+        quant_dual_kernel<FMT_NVFP4, false, true><<<gw, 256, 0, stream>>>(src, ir, ic, ild, rcodes, rscales, rk, ccodes,
+                                                                          cscales, ck, rtr, ctr, delayed, 0, 0);
+      }
       break;
   }
   return hipGetLastError();
