@@ -157,9 +157,10 @@ __device__ __forceinline__ uint32_t block_scale(uint32_t amax_bits, float s_t, N
 // reciprocal within 2^-19 (relative). The two products then bracket the
 // quotient and the conversion is monotone, so two equal codes are the
 // quotient's code; they differ only when a midpoint lies within about 2^-19
-// of the quotient (an exact tie or a near one), and those elements take the
-// threshold form. Both forms compute the same function; the fast one needs
-// a finite block amax and an s_t for which S and 1 / S stay normal fp32.
+// of the quotient (an exact tie or a near one), and then by one step, which
+// an exact fp64 comparison with that midpoint settles. Both forms compute the
+// same function; the fast one needs a finite block amax and an s_t for which
+// S and 1 / S stay normal fp32.
 //
 // Error budget of the bracket: S32 = fp32(S) (2^-24), v_rcp_f32 (1 ulp,
 // 2^-23), r_lo / r_hi rounded (2^-24) and the product rounded (2^-24): under
@@ -236,7 +237,27 @@ __device__ __forceinline__ uint32_t nv4_encode8(const float (&x)[8], const Nv4Bl
   hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[4] * B.r_hi, x[5] * B.r_hi, one, 2);
   lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[6] * B.r_lo, x[7] * B.r_lo, one, 3);
   hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[6] * B.r_hi, x[7] * B.r_hi, one, 3);
-  if (B.fast && lo == hi) return lo;
+  if (B.fast) {
+    if (lo == hi) return lo;
+    // Elements whose bracket straddles a midpoint (ties are common: with s_t
+    // from a bf16 amax the quotients are ratios of short integers): their
+    // two codes are c and c + 1 around the midpoint m_c, and the code is c +
+    // 1 when |x| > m_c S, or |x| == m_c S with c odd (ties to even). In fp64
+    // both sides are exact (m_c S has at most 33 significant bits).
+    const double S = e4m3_value(B.sb) * (double)T.s_t;
+    const uint32_t diff = lo ^ hi;
+    uint32_t word = lo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((diff >> (4 * i)) & 0xFu) {
+        const uint32_t c = (lo >> (4 * i)) & 7u;
+        const double m = c < 4u ? 0.25 + 0.5 * (double)c : (c == 6u ? 5.0 : (double)c - 1.5);
+        const double a = fabs((double)x[i]), t = m * S;
+        if (a > t || (a == t && (c & 1u))) word += 1u << (4 * i);   // c <= 6: the sign bit is untouched
+      }
+    }
+    return word;
+  }
   const Nv4Thresholds th = nvfp4_thresholds(e4m3_value(B.sb) * (double)T.s_t);
   uint32_t word = 0u;
 #pragma unroll
