@@ -283,11 +283,13 @@ def build_block_train(bt, dev):
     wgrad). FINAL (one format): each of X, W and dY is dual-quantized once
     (X and W when the forward pass uses them, dY in the backward pass). P3
     (MXFP8 forward, NVFP4 backward): X and W are row-quantized in MXFP8 for
-    fprop (one batch launch) and quantized again along the other axis in
-    NVFP4 for the backward GEMMs; dY gets both NVFP4 copies, stochastically
-    rounded, from one read."""
+    fprop (one batch launch, which also reduces their amax) and quantized
+    again along the other axis in NVFP4 for the backward GEMMs, with the
+    tensor scale from that amax (no amax pass); dY gets both NVFP4 copies,
+    stochastically rounded, from one read."""
     from block_scaled_precision_mx_amd import api
     from block_scaled_precision_mx_amd import workloads as W
+    from block_scaled_precision_mx_amd._lib import AMAX_WORDS
 
     import torch
     specs = iter(workload_gemms(bt.name))
@@ -310,21 +312,30 @@ def build_block_train(bt, dev):
                 w_row, w_col = _quant_dual(ops, f"quant_{lin.name}_w_rowcol", w, ff, dev)
             else:
                 x_row, w_row = _empty_q(bt.m, lin.k, ff, "row", dev), _empty_q(lin.n, lin.k, ff, "row", dev)
-                ops.append(Op("quant", lambda x=x, w=w, qa=x_row, qw=w_row:
-                              api.mx_quantize_batch([x, w], ff, out=[qa, qw]), f"quant_{lin.name}_x_w",
+                # NVFP4 backward copies take X's and W's amax from this launch
+                amax_xw = torch.empty(2 * AMAX_WORDS, dtype=torch.float32, device=dev) if bf == "nvfp4" else None
+                ops.append(Op("quant", lambda x=x, w=w, qa=x_row, qw=w_row, a=amax_xw:
+                              api.mx_quantize_batch([x, w], ff, out=[qa, qw], amax=a), f"quant_{lin.name}_x_w",
                               nbytes=QUANT_BYTES[ff] * (x.numel() + w.numel())))
                 x_col, w_col = None, None
             _gemm_op(ops, next(specs), x_row, w_row, bias, dev, ws)
-            saved.append((lin, x, w, dy, x_col, w_col))
-        for lin, x, w, dy, x_col, w_col in reversed(saved):  # backward
+            saved.append((lin, x, w, dy, x_col, w_col, amax_xw if ff != bf else None))
+        for lin, x, w, dy, x_col, w_col, amax_xw in reversed(saved):  # backward
             if x_col is None:
                 # the backward format's copies along the token / output axis
                 x_col, w_col = _empty_q(bt.m, lin.k, bf, "col", dev), _empty_q(lin.n, lin.k, bf, "col", dev)
-                amax = 2.0 if bf == "nvfp4" else 0.0
-                ops.append(Op("quant", lambda x=x, q=x_col: api.mx_quantize(x, bf, "col", q.codes, q.scales),
-                              f"quant_{lin.name}_x_col", nbytes=(QUANT_BYTES[bf] + amax) * x.numel()))
-                ops.append(Op("quant", lambda w=w, q=w_col: api.mx_quantize(w, bf, "col", q.codes, q.scales),
-                              f"quant_{lin.name}_w_col", nbytes=(QUANT_BYTES[bf] + amax) * w.numel()))
+                if amax_xw is not None:
+                    ops.append(Op("quant", lambda x=x, q=x_col, a=amax_xw[:AMAX_WORDS]:
+                                  api.mx_quantize_amax(x, bf, "col", a, q.codes, q.scales),
+                                  f"quant_{lin.name}_x_col", nbytes=QUANT_BYTES[bf] * x.numel()))
+                    ops.append(Op("quant", lambda w=w, q=w_col, a=amax_xw[AMAX_WORDS:]:
+                                  api.mx_quantize_amax(w, bf, "col", a, q.codes, q.scales),
+                                  f"quant_{lin.name}_w_col", nbytes=QUANT_BYTES[bf] * w.numel()))
+                else:
+                    ops.append(Op("quant", lambda x=x, q=x_col: api.mx_quantize(x, bf, "col", q.codes, q.scales),
+                                  f"quant_{lin.name}_x_col", nbytes=QUANT_BYTES[bf] * x.numel()))
+                    ops.append(Op("quant", lambda w=w, q=w_col: api.mx_quantize(w, bf, "col", q.codes, q.scales),
+                                  f"quant_{lin.name}_w_col", nbytes=QUANT_BYTES[bf] * w.numel()))
             dy_row, dy_col = _quant_dual(ops, f"quant_{lin.name}_dy_rowcol", dy, bf, dev, sr)
             _gemm_op(ops, next(specs), dy_row, w_col, None, dev, ws)   # dgrad: dX = dY W
             _gemm_op(ops, next(specs), dy_col, x_col, None, dev, ws)   # wgrad: dW = dY^T X

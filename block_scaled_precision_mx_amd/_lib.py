@@ -16,6 +16,8 @@ class QuantItem(ctypes.Structure):
 
 
 QUANT_BATCH_MAX = 32   # MX_QUANT_BATCH_MAX
+AMAX_WORDS = 256        # MX_AMAX_WORDS
+AMAX_MAX_WORDS = 256    # MX_AMAX_MAX_WORDS
 SCRATCH_BYTES = 64 << 20   # MX_SCRATCH_BYTES
 
 # every symbol include/mx.h declares, with (restype, argtypes)
@@ -27,6 +29,9 @@ SIGNATURES = {
     "mx_quantize": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
                                _c.c_int, _c.c_int, _c.c_void_p]),
     "mx_quantize_batch": (_c.c_int, [_c.POINTER(QuantItem), _c.c_int, _c.c_int, _c.c_void_p]),
+    "mx_quantize_batch_amax": (_c.c_int, [_c.POINTER(QuantItem), _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p]),
+    "mx_quantize_amax": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
+                                    _c.c_int, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p]),
     "mx_layernorm_quantize": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
                                          _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
     "mx_quantize_dual": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,

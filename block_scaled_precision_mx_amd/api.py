@@ -103,13 +103,19 @@ def mx_quantize(x: torch.Tensor, fmt: str, axis: str = "row", codes: torch.Tenso
 
 
 def mx_quantize_batch(xs: list[torch.Tensor], fmt: str, out: list[Quantized] | None = None,
-                      stream=None) -> list[Quantized]:
+                      stream=None, amax: torch.Tensor | None = None) -> list[Quantized]:
     """Row quantization of several 2-D bf16 device tensors in one launch
     (MXFP8 / MXFP4; at most QUANT_BATCH_MAX tensors per call). `out` reuses
-    the buffers of an earlier call's result."""
-    from ._lib import QUANT_BATCH_MAX, QuantItem
+    the buffers of an earlier call's result. With `amax` (a float32 device
+    tensor of len(xs) * AMAX_WORDS elements) the call is
+    mx_quantize_batch_amax: each tensor's amax is also reduced, tensor i into
+    amax[i * AMAX_WORDS:(i + 1) * AMAX_WORDS], for mx_quantize_amax."""
+    from ._lib import AMAX_WORDS, QUANT_BATCH_MAX, QuantItem
     if not 1 <= len(xs) <= QUANT_BATCH_MAX:
         raise ValueError(f"between 1 and {QUANT_BATCH_MAX} tensors per call")
+    if amax is not None and (amax.dtype != torch.float32 or not amax.is_cuda or not amax.is_contiguous()
+                             or amax.numel() < len(xs) * AMAX_WORDS):
+        raise ValueError(f"amax must be a contiguous float32 device tensor of {len(xs) * AMAX_WORDS} elements")
     items = (QuantItem * len(xs))()
     result = []
     for i, x in enumerate(xs):
@@ -128,8 +134,39 @@ def mx_quantize_batch(xs: list[torch.Tensor], fmt: str, out: list[Quantized] | N
                 raise ValueError("out buffers are too small")
         items[i] = QuantItem(x.data_ptr(), rows, cols, _ld(x), q.codes.data_ptr(), q.scales.data_ptr())
         result.append(Quantized(q.codes, q.scales, fmt, rows, cols))
-    _check(lib().mx_quantize_batch(items, len(xs), FMT[fmt], _stream(stream)))
+    if amax is None:
+        _check(lib().mx_quantize_batch(items, len(xs), FMT[fmt], _stream(stream)))
+    else:
+        _check(lib().mx_quantize_batch_amax(items, len(xs), FMT[fmt], amax.data_ptr(), _stream(stream)))
     return result
+
+
+def mx_quantize_amax(x: torch.Tensor, fmt: str, axis: str, amax: torch.Tensor, codes: torch.Tensor | None = None,
+                     scales: torch.Tensor | None = None, stream=None) -> Quantized:
+    """mx_quantize (NVFP4) with the tensor amax given: the largest magnitude
+    among the elements of `amax` (a contiguous float32 device tensor of 1 ..
+    AMAX_MAX_WORDS elements, e.g. one tensor's slice of mx_quantize_batch's
+    `amax`)."""
+    from ._lib import AMAX_MAX_WORDS
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D bfloat16 device tensor")
+    if x.stride(1) != 1 and x.shape[1] > 1:
+        raise ValueError("x must have unit stride along its last dimension")
+    if amax.dtype != torch.float32 or not amax.is_cuda or not amax.is_contiguous() or \
+            not 1 <= amax.numel() <= AMAX_MAX_WORDS:
+        raise ValueError(f"amax must be a contiguous float32 device tensor of 1 .. {AMAX_MAX_WORDS} elements")
+    rows, cols = x.shape
+    nc, ns = codes_bytes(rows, cols, fmt, axis), scales_bytes(rows, cols, fmt, axis)
+    if codes is None:
+        codes = torch.empty(nc, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(ns, dtype=torch.uint8, device=x.device)
+    if codes.numel() < nc or scales.numel() < ns:
+        raise ValueError("codes / scales buffers are too small")
+    _check(lib().mx_quantize_amax(x.data_ptr(), rows, cols, _ld(x), codes.data_ptr(), scales.data_ptr(),
+                                  FMT[fmt], AXIS[axis], amax.data_ptr(), amax.numel(), _stream(stream)))
+    stored_rows, length = (rows, cols) if axis == "row" else (cols, rows)
+    return Quantized(codes, scales, fmt, stored_rows, length)
 
 
 def mx_layernorm_quantize(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, eps: float, fmt: str,

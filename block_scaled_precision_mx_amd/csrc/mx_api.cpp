@@ -69,29 +69,51 @@ size_t mx_scales_bytes(int64_t rows, int64_t cols, mx_fmt fmt, mx_axis axis) {
   return (size_t)scales_total(R, k_pad(L), fmt);
 }
 
-mx_status mx_quantize(const void* src, int64_t rows, int64_t cols, int64_t ld, void* codes, void* scales,
-                      mx_fmt fmt, mx_axis axis, void* hip_stream) {
-  if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown format %d", (int)fmt);
-  if (!valid_axis(axis)) return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown axis %d", (int)axis);
-  if (rows < 1 || cols < 1) return fail(MX_ERR_INVALID_ARG, "mx_quantize: empty tensor (%lld x %lld)", (long long)rows, (long long)cols);
-  if (ld < cols) return fail(MX_ERR_INVALID_ARG, "mx_quantize: ld %lld < cols %lld", (long long)ld, (long long)cols);
-  if (!src || !codes || !scales) return fail(MX_ERR_INVALID_ARG, "mx_quantize: null pointer");
-  if (!aligned(src, 2)) return fail(MX_ERR_ALIGNMENT, "mx_quantize: src must be 2-byte aligned");
+// mx_quantize and mx_quantize_amax: `name` prefixes the messages; amax NULL
+// reduces the NVFP4 tensor amax from X.
+static mx_status quantize_impl(const char* name, const void* src, int64_t rows, int64_t cols, int64_t ld, void* codes,
+                               void* scales, mx_fmt fmt, mx_axis axis, const float* amax, int nslots,
+                               void* hip_stream) {
+  if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "%s: unknown format %d", name, (int)fmt);
+  if (!valid_axis(axis)) return fail(MX_ERR_INVALID_ARG, "%s: unknown axis %d", name, (int)axis);
+  if (rows < 1 || cols < 1) return fail(MX_ERR_INVALID_ARG, "%s: empty tensor (%lld x %lld)", name, (long long)rows, (long long)cols);
+  if (ld < cols) return fail(MX_ERR_INVALID_ARG, "%s: ld %lld < cols %lld", name, (long long)ld, (long long)cols);
+  if (!src || !codes || !scales) return fail(MX_ERR_INVALID_ARG, "%s: null pointer", name);
+  if (!aligned(src, 2)) return fail(MX_ERR_ALIGNMENT, "%s: src must be 2-byte aligned", name);
   if (!aligned(codes, 16) || !aligned(scales, 16))
-    return fail(MX_ERR_ALIGNMENT, "mx_quantize: codes and scales must be 16-byte aligned");
+    return fail(MX_ERR_ALIGNMENT, "%s: codes and scales must be 16-byte aligned", name);
   if (rows > kMaxCount || cols > kMaxCount)
-    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: rows and cols must be below 2^31 - 256");
+    return fail(MX_ERR_UNSUPPORTED, "%s: rows and cols must be below 2^31 - 256", name);
   const int64_t R = axis == MX_AXIS_ROW ? rows : cols, L = axis == MX_AXIS_ROW ? cols : rows;
   const int64_t kpad = k_pad(L);
   if (R * code_row_bytes(kpad, fmt) >= kMaxBytes || scales_total(R, kpad, fmt) >= kMaxBytes)
-    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: output larger than 2 GiB");
+    return fail(MX_ERR_UNSUPPORTED, "%s: output larger than 2 GiB", name);
   if (ld >= ((int64_t)1 << 31) || rows > ((int64_t)1 << 40) / ld)
-    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: input too large (ld must be below 2^31)");
+    return fail(MX_ERR_UNSUPPORTED, "%s: input too large (ld must be below 2^31)", name);
   hipError_t e = mx::launch_quantize(static_cast<const uint16_t*>(src), rows, cols, ld, static_cast<uint8_t*>(codes),
                                      static_cast<uint8_t*>(scales), (int)fmt, (int)axis,
+                                     reinterpret_cast<const uint32_t*>(amax), nslots,
                                      static_cast<hipStream_t>(hip_stream));
-  if (e != hipSuccess) return fail(MX_ERR_HIP, "mx_quantize: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(MX_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
   return MX_OK;
+}
+
+mx_status mx_quantize(const void* src, int64_t rows, int64_t cols, int64_t ld, void* codes, void* scales,
+                      mx_fmt fmt, mx_axis axis, void* hip_stream) {
+  return quantize_impl("mx_quantize", src, rows, cols, ld, codes, scales, fmt, axis, nullptr, 0, hip_stream);
+}
+
+mx_status mx_quantize_amax(const void* src, int64_t rows, int64_t cols, int64_t ld, void* codes, void* scales,
+                           mx_fmt fmt, mx_axis axis, const float* amax, int nslots, void* hip_stream) {
+  if (fmt != MX_FMT_NVFP4) {
+    if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "mx_quantize_amax: unknown format %d", (int)fmt);
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_amax: only NVFP4 has a tensor scale");
+  }
+  if (!amax) return fail(MX_ERR_INVALID_ARG, "mx_quantize_amax: null amax");
+  if (!aligned(amax, 4)) return fail(MX_ERR_ALIGNMENT, "mx_quantize_amax: amax must be 4-byte aligned");
+  if (nslots < 1 || nslots > MX_AMAX_MAX_WORDS)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_amax: nslots = %d outside [1, %d]", nslots, MX_AMAX_MAX_WORDS);
+  return quantize_impl("mx_quantize_amax", src, rows, cols, ld, codes, scales, fmt, axis, amax, nslots, hip_stream);
 }
 
 mx_status mx_layernorm_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, const void* gamma,
@@ -131,42 +153,56 @@ mx_status mx_layernorm_quantize(const void* x, int64_t rows, int64_t cols, int64
   return MX_OK;
 }
 
-mx_status mx_quantize_batch(const mx_quant_item* items, int n, mx_fmt fmt, void* hip_stream) {
+// mx_quantize_batch and mx_quantize_batch_amax (amax NULL: no reduction).
+static mx_status quantize_batch_impl(const char* name, const mx_quant_item* items, int n, mx_fmt fmt, float* amax,
+                                     void* hip_stream) {
   if (fmt != MX_FMT_MXFP8 && fmt != MX_FMT_MXFP4) {
     if (fmt == MX_FMT_NVFP4)
-      return fail(MX_ERR_UNSUPPORTED, "mx_quantize_batch: NVFP4 needs a tensor amax per item; use mx_quantize");
-    return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: unknown format %d", (int)fmt);
+      return fail(MX_ERR_UNSUPPORTED, "%s: NVFP4 needs a tensor amax per item; use mx_quantize", name);
+    return fail(MX_ERR_INVALID_ARG, "%s: unknown format %d", name, (int)fmt);
   }
-  if (!items) return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: null item array");
+  if (amax && !aligned(amax, 4)) return fail(MX_ERR_ALIGNMENT, "%s: amax must be 4-byte aligned", name);
+  if (!items) return fail(MX_ERR_INVALID_ARG, "%s: null item array", name);
   if (n < 1 || n > MX_QUANT_BATCH_MAX)
-    return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: n = %d outside [1, %d]", n, MX_QUANT_BATCH_MAX);
+    return fail(MX_ERR_INVALID_ARG, "%s: n = %d outside [1, %d]", name, n, MX_QUANT_BATCH_MAX);
   static_assert(MX_QUANT_BATCH_MAX == mx::kQuantBatchMax, "batch size of the header and the launcher");
   mx::QuantBatchItem q[MX_QUANT_BATCH_MAX];
   for (int i = 0; i < n; ++i) {
     const mx_quant_item& it = items[i];
     if (it.rows < 1 || it.cols < 1)
-      return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: item %d: empty tensor (%lld x %lld)", i, (long long)it.rows,
+      return fail(MX_ERR_INVALID_ARG, "%s: item %d: empty tensor (%lld x %lld)", name, i, (long long)it.rows,
                   (long long)it.cols);
     if (it.ld < it.cols)
-      return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: item %d: ld %lld < cols %lld", i, (long long)it.ld,
+      return fail(MX_ERR_INVALID_ARG, "%s: item %d: ld %lld < cols %lld", name, i, (long long)it.ld,
                   (long long)it.cols);
-    if (!it.src || !it.codes || !it.scales) return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch: item %d: null pointer", i);
-    if (!aligned(it.src, 2)) return fail(MX_ERR_ALIGNMENT, "mx_quantize_batch: item %d: src must be 2-byte aligned", i);
+    if (!it.src || !it.codes || !it.scales) return fail(MX_ERR_INVALID_ARG, "%s: item %d: null pointer", name, i);
+    if (!aligned(it.src, 2)) return fail(MX_ERR_ALIGNMENT, "%s: item %d: src must be 2-byte aligned", name, i);
     if (!aligned(it.codes, 16) || !aligned(it.scales, 16))
-      return fail(MX_ERR_ALIGNMENT, "mx_quantize_batch: item %d: codes and scales must be 16-byte aligned", i);
+      return fail(MX_ERR_ALIGNMENT, "%s: item %d: codes and scales must be 16-byte aligned", name, i);
     if (it.rows > kMaxCount || it.cols > kMaxCount)
-      return fail(MX_ERR_UNSUPPORTED, "mx_quantize_batch: item %d: rows and cols must be below 2^31 - 256", i);
+      return fail(MX_ERR_UNSUPPORTED, "%s: item %d: rows and cols must be below 2^31 - 256", name, i);
     const int64_t kpad = k_pad(it.cols);
     if (it.rows * code_row_bytes(kpad, fmt) >= kMaxBytes || scales_total(it.rows, kpad, fmt) >= kMaxBytes)
-      return fail(MX_ERR_UNSUPPORTED, "mx_quantize_batch: item %d: output larger than 2 GiB", i);
+      return fail(MX_ERR_UNSUPPORTED, "%s: item %d: output larger than 2 GiB", name, i);
     if (it.ld >= ((int64_t)1 << 31) || it.rows > (((int64_t)1 << 31) - 1) / it.ld)
-      return fail(MX_ERR_UNSUPPORTED, "mx_quantize_batch: item %d: input too large (rows * ld must be below 2^31)", i);
+      return fail(MX_ERR_UNSUPPORTED, "%s: item %d: input too large (rows * ld must be below 2^31)", name, i);
     q[i] = mx::QuantBatchItem{static_cast<const uint16_t*>(it.src), static_cast<uint8_t*>(it.codes),
-                              static_cast<uint8_t*>(it.scales), (int)it.rows, (int)it.cols, (int)it.ld, (int)kpad};
+                              static_cast<uint8_t*>(it.scales), (int)it.rows, (int)it.cols, (int)it.ld, (int)kpad,
+                              nullptr};
   }
-  hipError_t e = mx::launch_quantize_batch(q, n, (int)fmt, static_cast<hipStream_t>(hip_stream));
-  if (e != hipSuccess) return fail(MX_ERR_HIP, "mx_quantize_batch: launch failed: %s", hipGetErrorString(e));
+  hipError_t e = mx::launch_quantize_batch(q, n, (int)fmt, reinterpret_cast<uint32_t*>(amax),
+                                           static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(MX_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
   return MX_OK;
+}
+
+mx_status mx_quantize_batch(const mx_quant_item* items, int n, mx_fmt fmt, void* hip_stream) {
+  return quantize_batch_impl("mx_quantize_batch", items, n, fmt, nullptr, hip_stream);
+}
+
+mx_status mx_quantize_batch_amax(const mx_quant_item* items, int n, mx_fmt fmt, float* amax, void* hip_stream) {
+  if (!amax) return fail(MX_ERR_INVALID_ARG, "mx_quantize_batch_amax: null amax");
+  return quantize_batch_impl("mx_quantize_batch_amax", items, n, fmt, amax, hip_stream);
 }
 
 mx_status mx_quantize_dual(const void* src, int64_t rows, int64_t cols, int64_t ld, void* row_codes,

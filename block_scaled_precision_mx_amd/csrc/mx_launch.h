@@ -6,8 +6,15 @@
 
 namespace mx {
 
+// NVFP4: amax NULL -> the tensor amax is reduced first; else it is the
+// largest magnitude among the nslots fp32 words at amax (device).
 hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
-                           uint8_t* scales, int fmt, int axis, hipStream_t stream);
+                           uint8_t* scales, int fmt, int axis, const uint32_t* amax, int nslots, hipStream_t stream);
+
+// Amax accumulators of a batched quantization: kAmaxWords words per tensor,
+// of which the words kAmaxStride apart (one per 128-byte line) take partial
+// maxima; the others stay zero.
+constexpr int kAmaxWords = 256, kAmaxStride = 32, kAmaxLines = kAmaxWords / kAmaxStride;
 
 // One tensor of a batched row quantization (MX formats): its source, sizes,
 // outputs and K_pad = round_up(cols, 128).
@@ -16,6 +23,7 @@ struct QuantBatchItem {
   uint8_t* codes;
   uint8_t* scales;
   int rows, cols, ld, kpad;
+  uint32_t* amax;   // kAmaxWords accumulator words, or NULL (set by the launcher)
 };
 constexpr int kQuantBatchMax = 32;
 // Passed by value as the kernel argument (about 1.4 KB).
@@ -26,7 +34,9 @@ struct QuantBatch {
 };
 
 // Row quantization of n <= kQuantBatchMax MXFP8 / MXFP4 tensors in one launch.
-hipError_t launch_quantize_batch(const QuantBatchItem* items, int n, int fmt, hipStream_t stream);
+// amax non-NULL: n * kAmaxWords words, zeroed here, into which each item's
+// tensor amax is reduced (item i: words i * kAmaxWords ..).
+hipError_t launch_quantize_batch(const QuantBatchItem* items, int n, int fmt, uint32_t* amax, hipStream_t stream);
 
 // Both quantized copies (row, and column stored transposed) from one read.
 // NVFP4: amax_prev NULL -> tensor scale from this tensor; else delayed scale

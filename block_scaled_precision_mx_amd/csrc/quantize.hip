@@ -288,9 +288,9 @@ constexpr int64_t kRowSmallGroups = 1 << 20;
 // ... of the threads given to it (each thread: U groups of 8 elements of one
 // stored row).
 template <int FMT, int U>
-__device__ __forceinline__ void quant_rows(const uint16_t* __restrict__ src, int rows, int cols, int ld,
-                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad,
-                                           float s_t, int first_tid, int stride) {
+__device__ __forceinline__ uint32_t quant_rows(const uint16_t* __restrict__ src, int rows, int cols, int ld,
+                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad,
+                                               float s_t, int first_tid, int stride) {
   constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
   constexpr int LANES_PER_BLOCK = BS / 8;
   static_assert(U == 1 || U == 2 || U == 4, "kpad / 8 (a multiple of 16) / U must stay a multiple of 4");
@@ -300,6 +300,7 @@ __device__ __forceinline__ void quant_rows(const uint16_t* __restrict__ src, int
   const int total = rows * tpr;
   const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
   [[maybe_unused]] const Nv4Tensor nt = nv4_tensor(s_t);
+  uint32_t own_max = 0u;                          // largest |x| bits this thread saw
   for (int tid = first_tid; tid < total; tid += stride) {
     const int r = tid / tpr;
     const int j = tid - r * tpr;
@@ -329,6 +330,7 @@ __device__ __forceinline__ void quant_rows(const uint16_t* __restrict__ src, int
         x[i] = bf16_to_f32(b);
         m = max(m, b & 0x7FFFu);
       }
+      own_max = max(own_max, m);
       // block amax across the adjacent lanes of this block
 #pragma unroll
       for (int off = 1; off < LANES_PER_BLOCK; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
@@ -351,6 +353,7 @@ __device__ __forceinline__ void quant_rows(const uint16_t* __restrict__ src, int
       if ((j % LANES_PER_BLOCK) == 0) scales[(int64_t)r * (kpad / BS) + c / BS] = (uint8_t)sb;
     }
   }
+  return own_max;
 }
 
 template <int FMT, int U>
@@ -369,15 +372,56 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restri
 // Several MX tensors in one launch: workgroups first_wg[i] .. first_wg[i+1]-1
 // quantize item i (the search is over a handful of kernel-argument entries,
 // uniform per workgroup).
-template <int FMT>
+// AMAX: each item's tensor amax (bf16 magnitude bits, as fp32 bits) is also
+// reduced, one atomic max per workgroup into one of kAmaxLines words of the
+// item's accumulators, each on its own 128-byte line. Atomics on one line
+// are served one after another (about 9 ns each, measured): thousands of
+// workgroups on one line cost 50 us on an 11235 x 4096 tensor; spread over
+// lines, and finishing throughout the launch, they do not queue.
+template <int FMT, bool AMAX>
 __global__ __launch_bounds__(256) void quant_row_batch_kernel(const QuantBatch batch) {
+  __shared__ uint32_t wave_max[4];
   int i = 0;
   while (i + 1 < batch.n && (int)blockIdx.x >= batch.first_wg[i + 1]) ++i;
   const QuantBatchItem& it = batch.items[i];
   const int wg = (int)blockIdx.x - batch.first_wg[i];
   const int nwg = batch.first_wg[i + 1] - batch.first_wg[i];
-  quant_rows<FMT, kRowGroupsPerThread>(it.src, it.rows, it.cols, it.ld, it.codes, it.scales, it.kpad, 0.0f,
-                                      wg * 256 + (int)threadIdx.x, nwg * 256);
+  uint32_t m = quant_rows<FMT, kRowGroupsPerThread>(it.src, it.rows, it.cols, it.ld, it.codes, it.scales, it.kpad,
+                                                    0.0f, wg * 256 + (int)threadIdx.x, nwg * 256);
+  if constexpr (AMAX) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if ((t & 63) == 0) wave_max[t >> 6] = m;
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t b = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+      if (b != 0) atomicMax(&it.amax[(blockIdx.x % kAmaxLines) * kAmaxStride], b << 16);
+    }
+  }
+}
+
+// Zeroes n words (the amax accumulators of mx_quantize_batch_amax).
+__global__ void zero_words_kernel(uint32_t* w, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) w[i] = 0u;
+}
+
+// Trailer and gap of an NVFP4 quantization whose amax is given: the amax is
+// the largest magnitude among the nslots fp32 words (one wave of 64 lanes),
+// s_t derives from it as from a reduced amax.
+__global__ void nv_trailer_given_kernel(uint8_t* gap, int gap_bytes, NvTrailer* tr, const uint32_t* amax, int nslots) {
+  const int t = threadIdx.x;
+  if (t < gap_bytes) gap[t] = 0;
+  uint32_t b = 0u;
+  for (int i = t; i < nslots; i += 64) b = max(b, amax[i] & 0x7FFFFFFFu);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) b = max(b, (uint32_t)__shfl_xor((int)b, off));
+  if (t == 0) {
+    tr->amax_bits = b;
+    tr->s_t = nvfp4_tensor_scale(b);
+    tr->pad[0] = 0u;
+    tr->pad[1] = 0u;
+  }
 }
 
 // ------------------------------------------------------------ col quantizer
@@ -968,7 +1012,7 @@ static void launch_row(const uint16_t* src, int ir, int ic, int ild, uint8_t* co
 }
 
 hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
-                           uint8_t* scales, int fmt, int axis, hipStream_t stream) {
+                           uint8_t* scales, int fmt, int axis, const uint32_t* amax, int nslots, hipStream_t stream) {
   // The C ABI bounds every size so that element, group and byte counts fit
   // in 32 bits (outputs < 2 GiB, input < 2^40 bytes is checked per row).
   const int64_t R = axis == 0 ? rows : cols;        // stored rows
@@ -980,9 +1024,14 @@ hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int6
   if (fmt == FMT_NVFP4) {
     const int64_t nscale = R * (kpad / bs);
     tr = reinterpret_cast<NvTrailer*>(scales + round_up(nscale, 16));
-    nv_trailer_init_kernel<<<1, 64, 0, stream>>>(scales + nscale, (int)(round_up(nscale, 16) - nscale), tr);
-    const int gpr = (int)((cols + 7) / 8);
-    amax_kernel<<<grid_for(rows * gpr, 256 * kAmaxUnroll, 512), 256, 0, stream>>>(src, ir, ic, ild, gpr, tr);
+    if (amax) {
+      nv_trailer_given_kernel<<<1, 64, 0, stream>>>(scales + nscale, (int)(round_up(nscale, 16) - nscale), tr, amax,
+                                                     nslots);
+    } else {
+      nv_trailer_init_kernel<<<1, 64, 0, stream>>>(scales + nscale, (int)(round_up(nscale, 16) - nscale), tr);
+      const int gpr = (int)((cols + 7) / 8);
+      amax_kernel<<<grid_for(rows * gpr, 256 * kAmaxUnroll, 512), 256, 0, stream>>>(src, ir, ic, ild, gpr, tr);
+    }
   }
   if (axis == 0) {
     if (R * (kpad / 8) >= kRowSmallGroups)
@@ -1012,19 +1061,26 @@ hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int6
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_batch(const QuantBatchItem* items, int n, int fmt, hipStream_t stream) {
+hipError_t launch_quantize_batch(const QuantBatchItem* items, int n, int fmt, uint32_t* amax, hipStream_t stream) {
   QuantBatch batch{};
   batch.n = n;
   int64_t wg = 0;
   for (int i = 0; i < n; ++i) {
     batch.items[i] = items[i];
+    batch.items[i].amax = amax ? amax + (int64_t)i * kAmaxWords : nullptr;
     batch.first_wg[i] = (int)wg;
     const int64_t threads = (int64_t)items[i].rows * (items[i].kpad / 8 / kRowGroupsPerThread);
     wg += grid_for(threads, 256, 1 << 16);
   }
   batch.first_wg[n] = (int)wg;
-  if (fmt == FMT_MXFP8) quant_row_batch_kernel<FMT_MXFP8><<<(int)wg, 256, 0, stream>>>(batch);
-  else quant_row_batch_kernel<FMT_MXFP4><<<(int)wg, 256, 0, stream>>>(batch);
+  if (amax) {
+    zero_words_kernel<<<1, 256, 0, stream>>>(amax, n * kAmaxWords);
+    if (fmt == FMT_MXFP8) quant_row_batch_kernel<FMT_MXFP8, true><<<(int)wg, 256, 0, stream>>>(batch);
+    else quant_row_batch_kernel<FMT_MXFP4, true><<<(int)wg, 256, 0, stream>>>(batch);
+  } else {
+    if (fmt == FMT_MXFP8) quant_row_batch_kernel<FMT_MXFP8, false><<<(int)wg, 256, 0, stream>>>(batch);
+    else quant_row_batch_kernel<FMT_MXFP4, false><<<(int)wg, 256, 0, stream>>>(batch);
+  }
   return hipGetLastError();
 }
 

@@ -207,6 +207,44 @@ typedef struct {
  * item. Outputs of different items must not overlap. */
 mx_status mx_quantize_batch(const mx_quant_item* items, int n, mx_fmt fmt, void* hip_stream);
 
+/* Words per tensor of the amax accumulators of mx_quantize_batch_amax, and
+ * the most words mx_quantize_amax reduces. */
+#define MX_AMAX_WORDS 256
+#define MX_AMAX_MAX_WORDS 256
+
+/* mx_quantize_batch that also reduces each item's tensor amax (the largest
+ * |x|, as the fp32 bit pattern of the bf16 magnitude). README section 5.3:
+ * the P3 recipe quantizes activations and weights in MXFP8 for the forward
+ * GEMMs and again in NVFP4 for the backward ones, whose tensor scale needs
+ * the tensor amax (section 2); the forward quantization reads every element
+ * anyway, so a later mx_quantize_amax of the same tensor needs no amax pass.
+ *   amax: device array of n * MX_AMAX_WORDS fp32 words, 4-byte aligned,
+ *     owned by the caller. The call zeroes it, then item i's amax is the
+ *     largest of words i * MX_AMAX_WORDS .. (i + 1) * MX_AMAX_WORDS - 1
+ *     (partial maxima, spread over words on separate cache lines so that
+ *     the reductions of many workgroups do not queue on one); pass those
+ *     words to mx_quantize_amax. Stream-ordered like the codes.
+ * Codes and scales are byte for byte those of mx_quantize_batch; other
+ * arguments, errors (also: amax NULL or misaligned) and memory rules as for
+ * mx_quantize_batch; amax must not overlap an output. */
+mx_status mx_quantize_batch_amax(const mx_quant_item* items, int n, mx_fmt fmt, float* amax, void* hip_stream);
+
+/* mx_quantize with the NVFP4 tensor amax given instead of reduced from X
+ * (README sections 5.3 and 5.5: the backward copy of a tensor whose amax
+ * the forward quantization found). amax: device pointer to nslots fp32
+ * words, nslots in [1, MX_AMAX_MAX_WORDS], 4-byte aligned; the tensor amax
+ * is the largest magnitude among them (e.g. the MX_AMAX_WORDS words of an
+ * item of mx_quantize_batch_amax, or, with nslots 1, the amax field of a
+ * scales trailer). s_t = fp32 RNE of fp64(amax) / 2688 as mx_quantize derives
+ * it, blocks whose amax exceeds 2688 s_t saturate, and the trailer gets
+ * {s_t, the given amax}. With X's own amax the bytes are mx_quantize's.
+ * fmt must be MX_FMT_NVFP4 (MX_ERR_UNSUPPORTED otherwise: the MX formats
+ * have no tensor scale); other arguments, errors and memory rules as for
+ * mx_quantize; amax must not overlap an output. */
+mx_status mx_quantize_amax(const void* src, int64_t rows, int64_t cols, int64_t ld,
+                           void* codes, void* scales, mx_fmt fmt, mx_axis axis,
+                           const float* amax, int nslots, void* hip_stream);
+
 /* C = A * B^T (+ bias) from quantized operands (README section 4.3 GEMMs,
  * section 5.5 TN layout). A / As: codes and scales of an M-row operand,
  * B / Bs: of an N-row operand, both of logical length K. bias: bf16[N] or

@@ -8,10 +8,11 @@
 
 namespace mx {
 
-hipError_t launch_quantize(const uint16_t*, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, int, int, hipStream_t) {
+hipError_t launch_quantize(const uint16_t*, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, int, int, const uint32_t*,
+                           int, hipStream_t) {
   return hipSuccess;
 }
-hipError_t launch_quantize_batch(const QuantBatchItem*, int, int, hipStream_t) { return hipSuccess; }
+hipError_t launch_quantize_batch(const QuantBatchItem*, int, int, uint32_t*, hipStream_t) { return hipSuccess; }
 hipError_t launch_layernorm_quantize(const float*, int64_t, int64_t, int64_t, const float*, const float*, float,
                                      uint8_t*, uint8_t*, int, hipStream_t) {
   return hipSuccess;

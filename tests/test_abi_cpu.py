@@ -149,6 +149,39 @@ def test_quantize_batch_null_items(L):
     assert "null item array" in L.mx_last_error().decode()
 
 
+@pytest.mark.parametrize("specs,n,fmt,amax,status,msg", [
+    ((GOOD,), 1, 1, None, 1, "null amax"),
+    ((GOOD,), 1, 1, ALIGNED + 2, 3, "amax must be 4-byte"),
+    ((GOOD,), 1, 3, ALIGNED, 2, "NVFP4"),
+    ((GOOD,), 0, 1, ALIGNED, 1, "outside [1, 32]"),
+    ((GOOD, (ALIGNED, 0, 4, 4, ALIGNED, ALIGNED)), 2, 2, ALIGNED, 1, "item 1: empty"),
+])
+def test_quantize_batch_amax_validation(L, specs, n, fmt, amax, status, msg):
+    """mx_quantize_batch_amax checks its accumulator pointer and every item as
+    mx_quantize_batch does, and names itself in the message."""
+    assert L.mx_quantize_batch_amax(_items(*specs), n, fmt, amax, None) == status
+    err = L.mx_last_error().decode()
+    assert msg in err and err.startswith("mx_quantize_batch_amax")
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, 1, 0, ALIGNED, 8), 2, "only NVFP4"),
+    ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, 7, 0, ALIGNED, 8), 1, "unknown format"),
+    ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, 3, 0, None, 8), 1, "null amax"),
+    ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, 3, 0, ALIGNED + 2, 8), 3, "amax must be 4-byte"),
+    ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, 3, 0, ALIGNED, 0), 1, "nslots = 0"),
+    ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, 3, 0, ALIGNED, 257), 1, "nslots = 257"),
+    ((ALIGNED, 4, 4, 4, ALIGNED, ALIGNED, 3, 3, ALIGNED, 8), 1, "unknown axis"),
+    ((ALIGNED, 4, 8, 4, ALIGNED, ALIGNED, 3, 1, ALIGNED, 8), 1, "ld"),
+    ((ALIGNED, 4, 4, 4, ALIGNED + 8, ALIGNED, 3, 1, ALIGNED, 8), 3, "16-byte"),
+    ((ALIGNED, 3_000_000_000, 1, 1, ALIGNED, ALIGNED, 3, 1, ALIGNED, 1), 2, "below 2^31"),
+])
+def test_quantize_amax_validation(L, args, status, msg):
+    assert L.mx_quantize_amax(*args, None) == status
+    err = L.mx_last_error().decode()
+    assert msg in err and err.startswith("mx_quantize_amax")
+
+
 @pytest.mark.parametrize("args,status,msg", [
     ((ALIGNED, 4, 8, 8) + (ALIGNED,) * 4 + (1, None, 32.0), 2, "NVFP4 only"),
     ((ALIGNED, 4, 8, 8) + (ALIGNED,) * 4 + (9, None, 32.0), 1, "unknown format"),
