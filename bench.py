@@ -512,8 +512,7 @@ def cpu_baseline(workload_name, fmt):
 # headers it includes); their hash ties a counter summary to one build
 _CSRC = "block_scaled_precision_mx_amd/csrc/"
 _DEVICE_HEADERS = [_CSRC + "gemm_common.h", _CSRC + "mx_device.h"]
-KERNEL_SOURCES = {"gemm_mx_kernel": [_CSRC + "gemm_mx.hip"] + _DEVICE_HEADERS,
-                  "gemm_nv_kernel": [_CSRC + "gemm_nv.hip"] + _DEVICE_HEADERS}
+KERNEL_SOURCES = {"gemm_mx_kernel": [_CSRC + "gemm_mx.hip"] + _DEVICE_HEADERS}
 
 
 def source_sha256(kernel):

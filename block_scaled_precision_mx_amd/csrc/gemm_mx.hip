@@ -1,5 +1,7 @@
-// MXFP8 / MXFP4 GEMM on CDNA4's scaled matrix cores:
-//   C[M, N] = sum_k (a_k 2^ea)(b_k 2^eb) (+ bias[n]),  fp32 accumulate.
+// MXFP8 / MXFP4 GEMM on CDNA4's scaled matrix cores, and NVFP4 on its fp16
+// matrix cores:
+//   C[M, N] = sum_k (a_k 2^ea)(b_k 2^eb) (+ bias[n]),  fp32 accumulate
+//   (NVFP4: s_tA s_tB sum_k (a_k dA)(b_k dB) (+ bias[n])).
 //
 // lightly-train README "DINOv3 + EoMT on RTX 5090": section 2 (MXFP8 = E4M3
 // + UE8M0 per 1x32, MXFP4 = E2M1 + UE8M0 per 1x32), section 4.3 (qkv / proj
@@ -10,6 +12,19 @@
 // E8M0 scale bytes of both operands directly, so no dequantization happens
 // outside the matrix core. (The 16x16x128 form runs FP4 at only the FP8 rate
 // on this chip; the 32x32x64 form runs FP4 at twice the FP8 rate.)
+//
+// NVFP4 (section 2: E2M1 + E4M3 per 1x16 + an fp32 scale per tensor;
+// sections 5.3-5.5 use it for training's dgrad / wgrad GEMMs) runs on the
+// same data path: its codes are staged exactly like MXFP4's, its scale bytes
+// (one per 16 K) like MX scales, but an E4M3 scale is no power of two, so the
+// scaled instructions cannot take it. Each wave instead folds the scale into
+// its fp4 fragments, exactly, as fp16 (an E2M1 value times an E4M3 scale has
+// at most 6 significant bits and lies in [2^-10, 2688], inside fp16's normal
+// range; the product of two such values has at most 12 bits, exact in the
+// fp32 accumulator) and runs V_MFMA_F32_32X32X16_F16 (fp16 operand: lane l
+// holds row l % 32, K 8 (l / 32) .. + 7, measured on gfx950). s_tA s_tB
+// multiplies the fp32 sums before the epilogue. This path's roof is the fp16
+// matrix rate, and the conversions are VALU work beside it.
 //
 // Operand layout inside the instruction (measured on gfx950), lane l,
 // r = l % 32, g = l / 32:
@@ -76,8 +91,10 @@ struct MxCfg {
   static constexpr int RB = 128;                              // code bytes per row per stage
   static constexpr int CH = RB / 16;                          // 16-byte chunks per row
   static constexpr int KS = (FMT == FMT_MXFP8) ? RB : 2 * RB; // K elements per stage
-  static constexpr int SUB = KS / 64;                         // 32x32x64 sub-steps per stage
-  static constexpr int SPC = 512 / KS;                        // stages per scale chunk
+  static constexpr int SUB = KS / 64;                         // 64-K sub-steps per stage
+  // K elements per scale byte: MX blocks of 32, NVFP4 blocks of 16
+  static constexpr int BSZ = (FMT == FMT_NVFP4) ? 16 : 32;
+  static constexpr int SPC = 16 * BSZ / KS;                   // stages per 16-byte scale chunk
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int STAGE = (BM + BN) * RB;                 // code bytes per stage
@@ -92,6 +109,11 @@ struct MxCfg {
   static constexpr int SCALE_COPIES = (BM + BN) / 64;         // 1-KB copies per scale chunk
   static constexpr int SCALE_DMA = (SCALE_COPIES + NW - 1) / NW;  // per wave (some may be idle)
   static constexpr int MFMA_FMT = (FMT == FMT_MXFP8) ? 0 : 4;  // E4M3 / E2M1 operand selector
+  // NVFP4: the software-pipelined stage where a SIMD runs one wave (no other
+  // wave's conversions to fill its matrix instructions' shadow), with
+  // NV_VALU VALU instructions scheduled after each fp16 matrix instruction
+  static constexpr bool NV_PIPED = NW * OCC == 4;
+  static constexpr int NV_VALU = 6;
   static constexpr int CPR = BN / 8;                          // 16-byte bf16 chunks per C row
   static constexpr int EPI_STORES = WM * CPR / NT;            // stores per thread per epilogue pass
   // stores per thread per tile: one per 16-byte chunk of C, or a code store
@@ -183,6 +205,176 @@ __device__ __forceinline__ void mma_stage(v16f (&acc)[Cfg::FM][Cfg::FN], const u
     if (t + 1 < SUB) {
 #pragma unroll
       for (int f = 0; f < FN; ++f) b_cur[f] = b_nxt[f];
+    }
+  }
+}
+
+// NVFP4 (E2M1 codes with an E4M3 scale per 16 elements): the E4M3 scale is
+// not a power of two, so the scaled matrix instructions cannot take it;
+// instead each wave dequantizes its fp4 fragments, read from the stage as
+// for MXFP4, exactly to fp16 (nv_dequant8: an element times its scale has at
+// most 6 significant bits within fp16's normal range) and runs
+// V_MFMA_F32_32X32X16_F16. The fp4 fragment of sub-step t holds K 64t + 32g
+// .. + 31 of its row (dword k: K 64t + 32g + 8k ..), so its 4 dwords feed 4
+// fp16 instructions: instruction k pairs, in A and B alike, K 64t + 8k + i
+// (lanes g = 0) and 64t + 32 + 8k + i (lanes g = 1), i < 8; over k = 0..3
+// that is every K of the sub-step once. The scale of K 64t + 32g + 8k is
+// byte 4t + 2g + k / 2 of the row's 16 scale bytes of the stage.
+
+// E4M3 byte j (0 or 1) of the 16-bit value in the low half of `s`, placed as
+// fp16 bits into both halves: 2^-8 times its value (the exponent rebiased by
+// 8, E4M3 subnormals as fp16 subnormals); the factor 2^8 is carried by the
+// element conversion.
+template <int J>
+__device__ __forceinline__ uint32_t nv_scale_h2(uint32_t s) {
+  constexpr uint32_t sel = 0x0C000C00u | (J << 16) | J;
+  return __builtin_amdgcn_perm(0u, s & 0x7F7F7F7Fu, sel) << 7;
+}
+
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
+
+// 8 E2M1 codes (element j in nibble j) times an fp16 scale pair -> 8 fp16:
+// the hardware conversion at scale operand 2^8 (only its exponent is used),
+// then one packed multiply per pair.
+__device__ __forceinline__ v8h_t nv_dequant8(uint32_t x, uint32_t scale_h2) {
+  const v2h_t s = __builtin_bit_cast(v2h_t, scale_h2);
+  const v2h_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 0) * s;
+  const v2h_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 1) * s;
+  const v2h_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 2) * s;
+  const v2h_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 3) * s;
+  return v8h_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Dequantized fragment: 4 x 8 fp16 from the fp4 fragment `f` (first 4
+// dwords) with the scale bytes of its two blocks in the low 16 bits of `s`.
+__device__ __forceinline__ void nv_dequant_frag(const v8i& f, uint32_t s, v8h_t (&out)[4]) {
+  const uint32_t s0 = nv_scale_h2<0>(s), s1 = nv_scale_h2<1>(s);
+  out[0] = nv_dequant8((uint32_t)f[0], s0);
+  out[1] = nv_dequant8((uint32_t)f[1], s0);
+  out[2] = nv_dequant8((uint32_t)f[2], s1);
+  out[3] = nv_dequant8((uint32_t)f[3], s1);
+}
+
+// This lane's two scale bytes of sub-step t for tile row `row` (in the low
+// 16 bits): bytes 4t + 2g, 4t + 2g + 1 of the row's 16 bytes of the stage.
+template <class Cfg>
+__device__ __forceinline__ uint32_t nv_substep_scales(const uint8_t* sc, int row, int t, int g) {
+  return *reinterpret_cast<const uint32_t*>(sc + row * 16 + 4 * t) >> (16 * g);
+}
+
+template <class Cfg, class AfterBlock>
+__device__ __forceinline__ void nv_mma_stage(v16f (&acc)[Cfg::FM][Cfg::FN], const uint8_t* st, const uint8_t* sc,
+                                             int g, int ra, int rb, AfterBlock&& after_block) {
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, SUB = Cfg::SUB;
+  v8i b_cur[FN], b_nxt[FN], a_cur, a_nxt;
+#pragma unroll
+  for (int f = 0; f < FN; ++f) b_cur[f] = load_frag<Cfg>(st, Cfg::BM + rb + 32 * f, 0, g);
+  a_cur = load_frag<Cfg>(st, ra, 0, g);
+#pragma unroll
+  for (int t = 0; t < SUB; ++t) {
+    v8h_t bd[FN][4];
+#pragma unroll
+    for (int f = 0; f < FN; ++f) nv_dequant_frag(b_cur[f], nv_substep_scales<Cfg>(sc, Cfg::BM + rb + 32 * f, t, g), bd[f]);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (fm + 1 < FM) a_nxt = load_frag<Cfg>(st, ra + 32 * (fm + 1), t, g);
+      else if (t + 1 < SUB) a_nxt = load_frag<Cfg>(st, ra, t + 1, g);
+      if (fm == 0 && t + 1 < SUB) {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) b_nxt[f] = load_frag<Cfg>(st, Cfg::BM + rb + 32 * f, t + 1, g);
+      }
+      v8h_t ad[4];
+      nv_dequant_frag(a_cur, nv_substep_scales<Cfg>(sc, ra + 32 * fm, t, g), ad);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bd[fn][k], ad[k], acc[fm][fn], 0, 0, 0);
+      after_block(t * FM + fm);
+      if (fm + 1 < FM || t + 1 < SUB) a_cur = a_nxt;
+    }
+    if (t + 1 < SUB) {
+#pragma unroll
+      for (int f = 0; f < FN; ++f) b_cur[f] = b_nxt[f];
+    }
+  }
+}
+
+// The same stage, software-pipelined: the 4 FN fp16 instructions of block
+// (t, fm) use A dequantized during the previous block and B dequantized
+// during sub-step t - 1, so the conversions that run beside them (the next
+// block's A fragment and a share of sub-step t + 1's B fragments) do not
+// feed them, and the schedule alternates one matrix instruction with a few
+// conversions. B's raw fragments for t + 1 are read from LDS at block
+// (t, 0) and converted in the blocks fm >= 1 (all of them at fm = 0 when
+// FM = 1); A's raw fragment is read two blocks ahead.
+template <class Cfg, class AfterBlock>
+__device__ __forceinline__ void nv_mma_stage_piped(v16f (&acc)[Cfg::FM][Cfg::FN], const uint8_t* st,
+                                                   const uint8_t* sc, int g, int ra, int rb,
+                                                   AfterBlock&& after_block) {
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, SUB = Cfg::SUB, NB = SUB * FM;
+  auto a_frag = [&](int b) { return load_frag<Cfg>(st, ra + 32 * (b % FM), b / FM, g); };
+  auto a_scales = [&](int b) { return nv_substep_scales<Cfg>(sc, ra + 32 * (b % FM), b / FM, g); };
+  auto b_scales = [&](int f, int t) { return nv_substep_scales<Cfg>(sc, Cfg::BM + rb + 32 * f, t, g); };
+  auto b_block = [](int f) { return FM > 1 ? 1 + f * (FM - 1) / FN : 0; };   // block fm that converts B frag f
+  v8i b_raw[FN], a_raw1, a_raw2;
+  uint32_t b_sc[FN], a_sc1, a_sc2;
+  v8h_t bd[FN][4], bdn[FN][4], ad[4], adn[4];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    b_raw[f] = load_frag<Cfg>(st, Cfg::BM + rb + 32 * f, 0, g);
+    b_sc[f] = b_scales(f, 0);
+  }
+  const v8i a_raw0 = a_frag(0);
+  const uint32_t a_sc0 = a_scales(0);
+  if (NB > 1) {
+    a_raw1 = a_frag(1);
+    a_sc1 = a_scales(1);
+  }
+#pragma unroll
+  for (int f = 0; f < FN; ++f) nv_dequant_frag(b_raw[f], b_sc[f], bd[f]);
+  nv_dequant_frag(a_raw0, a_sc0, ad);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int t = b / FM, fm = b % FM;
+    if (b + 2 < NB) {
+      a_raw2 = a_frag(b + 2);
+      a_sc2 = a_scales(b + 2);
+    }
+    if (fm == 0 && t + 1 < SUB) {
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        b_raw[f] = load_frag<Cfg>(st, Cfg::BM + rb + 32 * f, t + 1, g);
+        b_sc[f] = b_scales(f, t + 1);
+      }
+    }
+    if (b + 1 < NB) nv_dequant_frag(a_raw1, a_sc1, adn);
+    if (t + 1 < SUB) {
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+        if (b_block(f) == fm) nv_dequant_frag(b_raw[f], b_sc[f], bdn[f]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bd[fn][k], ad[k], acc[fm][fn], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * FN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one matrix instruction
+      __builtin_amdgcn_sched_group_barrier(0x002, Cfg::NV_VALU, 0);  // then a few VALU
+    }
+    after_block(b);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ad[k] = adn[k];
+    a_raw1 = a_raw2;
+    a_sc1 = a_sc2;
+    if (fm == FM - 1 && t + 1 < SUB) {
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) bd[f][k] = bdn[f][k];
     }
   }
 }
@@ -465,7 +657,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int row_bytes = (Cfg::FMT == FMT_MXFP8) ? kpad : kpad / 2;
-  const int srow = kpad / 32;               // scale bytes per row
+  const int srow = kpad / Cfg::BSZ;         // scale bytes per row
   // stages per tile; with fp4 a stage holds 256 elements while K_pad is a
   // multiple of 128, so the last stage may hold only its first 64 bytes
   const int nk = (kpad + Cfg::KS - 1) / Cfg::KS;
@@ -622,6 +814,12 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   };
 
   const int ra = wm * WM + r32, rb = wn * WN + r32;     // this lane's fragment-0 rows in the tile
+  // NVFP4: s_tA s_tB, the fp32 words at the start of the scale buffers'
+  // trailers (16-byte aligned after the scale bytes)
+  [[maybe_unused]] float tensor_scale = 1.0f;
+  if constexpr (Cfg::FMT == FMT_NVFP4)
+    tensor_scale = *reinterpret_cast<const float*>(As + (((int64_t)M * srow + 15) & ~(int64_t)15)) *
+                   *reinterpret_cast<const float*>(Bs + (((int64_t)N * srow + 15) & ~(int64_t)15));
 
   // the GELU table; the first stage barrier orders it before every reader
   if constexpr (Cfg::GTAB) fill_gelu_table(reinterpret_cast<uint16_t*>(lds + Cfg::GTAB_OFF), (int)threadIdx.x, Cfg::NT);
@@ -663,19 +861,32 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
       if (Cfg::SPREAD) open_copy_stage();
       else if (lt < tiles) issue_next();
       if (ks == k0 || ks % Cfg::SPC == 0) slot = gc++ & 1;   // a new scale chunk (as on the copy side)
-      mma_stage<Cfg>(acc, lds + (gs & 1) * Cfg::STAGE, lds + 2 * Cfg::STAGE + slot * Cfg::SCHUNK, ks % Cfg::SPC, g,
-                     ra, rb, [&](int blk) {
-                       constexpr int BLOCKS = Cfg::SUB * FM;
-                       if (Cfg::SPREAD) {
+      auto after_block = [&](int blk) {
+        constexpr int BLOCKS = Cfg::SUB * FM;
+        if (Cfg::SPREAD) {
 #pragma unroll
-                         for (int j = 0; j < Cfg::CODE_DMA; ++j)
-                           if (j * BLOCKS / Cfg::CODE_DMA == blk) issue_code(j);
-                       }
-                     });
+          for (int j = 0; j < Cfg::CODE_DMA; ++j)
+            if (j * BLOCKS / Cfg::CODE_DMA == blk) issue_code(j);
+        }
+      };
+      const uint8_t* const st_codes = lds + (gs & 1) * Cfg::STAGE;
+      const uint8_t* const st_scales = lds + 2 * Cfg::STAGE + slot * Cfg::SCHUNK;
+      if constexpr (Cfg::FMT == FMT_NVFP4 && Cfg::NV_PIPED)
+        nv_mma_stage_piped<Cfg>(acc, st_codes, st_scales, g, ra, rb, after_block);
+      else if constexpr (Cfg::FMT == FMT_NVFP4)
+        nv_mma_stage<Cfg>(acc, st_codes, st_scales, g, ra, rb, after_block);
+      else
+        mma_stage<Cfg>(acc, st_codes, st_scales, ks % Cfg::SPC, g, ra, rb, after_block);
       if (Cfg::SPREAD) close_copy_stage();
       ++gs;
     }
 
+    if constexpr (Cfg::FMT == FMT_NVFP4) {   // the two tensor scales, from the scale buffers' trailers
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] *= tensor_scale;
+    }
     // epilogue: register 4q + v of acc[fm][fn] is C[m][n + v] with
     // m = m0 + wm WM + 32 fm + r32, n = n0 + wn WN + 32 fn + 8 q + 4 g.
     // The tile's bias sits in bias slot ctc & 1 (copied with the tile's first
@@ -729,6 +940,22 @@ static hipError_t run_mx_q(const uint8_t* A, const uint8_t* As, const uint8_t* B
   gemm_mx_kernel<Cfg><<<grid, Cfg::NT, 0, stream>>>(A, As, B, Bs, qcodes, (int)M, (int)N, (int)kpad, bias, 0, tiles_m,
                                                     tiles_n, qcodes, qscales, (int)round_up(N, kAlignK), 1, nullptr);
   return hipGetLastError();
+}
+
+// NVFP4 through the MX kernel's data path (fp4 stages, dequantized per
+// wave to fp16): 128x128 tiles (4 waves of 64x64, two workgroups per CU) or
+// 192x256 (4 waves of 96x128, one wave per SIMD, so the pipelined stage).
+// Four waves of 96x128 convert 7 fragments per 48 matrix instructions where
+// eight of 96x64 convert 5 per 24, and the conversions are this path's VALU
+// limit.
+hipError_t run_gemm_nvfp4_mx(bool small, int splits, const uint8_t* A, const uint8_t* As, const uint8_t* B,
+                             const uint8_t* Bs, void* C, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
+                             int out_f32, float* ws, hipStream_t stream) {
+  if (small)
+    return run_mx<MxCfg<FMT_NVFP4, 128, 128, 2, 2, 2, true>>(A, As, B, Bs, C, M, N, K, bias, out_f32, splits, ws,
+                                                               stream);
+  return run_mx<MxCfg<FMT_NVFP4, 192, 256, 2, 2, 1, true>>(A, As, B, Bs, C, M, N, K, bias, out_f32, splits, ws,
+                                                             stream);
 }
 
 enum MxTile { TILE_128x128 = 0, TILE_192x256 = 1, TILE_256x256 = 2 };

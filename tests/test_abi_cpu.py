@@ -266,10 +266,10 @@ def test_gemm_plan_names(L):
     assert L.mx_gemm_plan(256, 768, 768, 1).decode() == "gemm_mx_kernel<mxfp8, 128x128>"
     # NVFP4: weight-gradient shapes (few output tiles) take 128x128; the
     # token-major shapes keep the large tiles.
-    assert L.mx_gemm_plan(4096, 1024, 11235, 3).decode() == "gemm_nv_kernel<nvfp4, 128x128>"
-    assert L.mx_gemm_plan(1024, 4096, 11235, 3).decode() == "gemm_nv_kernel<nvfp4, 128x128>"
-    assert L.mx_gemm_plan(11235, 4096, 1024, 3).decode() == "gemm_nv_kernel<nvfp4, 192x256>"
-    assert L.mx_gemm_plan(4160, 4096, 384, 3).decode() == "gemm_nv_kernel<nvfp4, 192x256>"
+    assert L.mx_gemm_plan(4096, 1024, 11235, 3).decode() == "gemm_mx_kernel<nvfp4, 128x128>"
+    assert L.mx_gemm_plan(1024, 4096, 11235, 3).decode() == "gemm_mx_kernel<nvfp4, 128x128>"
+    assert L.mx_gemm_plan(11235, 4096, 1024, 3).decode() == "gemm_mx_kernel<nvfp4, 192x256>"
+    assert L.mx_gemm_plan(4160, 4096, 384, 3).decode() == "gemm_mx_kernel<nvfp4, 192x256>"
     assert L.mx_gemm_plan(0, 4, 4, 1) is None
     assert L.mx_gemm_plan(4, 4, 4, 9) is None
 
