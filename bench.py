@@ -380,13 +380,18 @@ def build(name, dev):
 
 # ------------------------------------------------------------------ timing
 
+# host time allowed per launch while a replay's launches are enqueued
+LEAD_US_PER_LAUNCH = 40.0
+
+
 def measure(sets, steps, warmup, stream):
     """ms per step over `steps` timed steps (step s runs input set
     s % len(sets)), then the average duration of every launch, per label:
     each replay runs all launches of one label (every block's, every set's,
     each on its own tensors as in the step) back to back between one pair of
     HIP events on the stream the kernels run on, so that the events' own
-    overhead is spread over many launches; `steps` replays are averaged.
+    overhead is spread over many launches, after a spin that lets the host
+    enqueue them all first; `steps` replays are averaged.
     Returns (ms per step, [(op, average ms)] for the ops of every set)."""
     import torch
 
@@ -411,9 +416,22 @@ def measure(sets, steps, warmup, stream):
         for op in ops:
             groups.setdefault(op.label, []).append(op)
     per_label = {lab: 0.0 for lab in groups}
+    # the spin kernel counts the counter its clock read uses; its rate, once
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(1_000_000)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    spin_per_us = 1.0e6 / max(e0.elapsed_time(e1) * 1.0e3, 1.0)
     for _ in range(steps):
         ev = {lab: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for lab in groups}
         for lab, ops in groups.items():
+            # a spin on the stream ahead of the start event keeps the GPU busy
+            # while the host enqueues the label's launches, so the events time
+            # the kernels back to back and not the host's launch rate (a short
+            # kernel after a synchronization would otherwise wait for each
+            # launch)
+            torch.cuda._sleep(int(spin_per_us * LEAD_US_PER_LAUNCH * len(ops)))
             ev[lab][0].record(stream)
             for op in ops:
                 op.fn()
