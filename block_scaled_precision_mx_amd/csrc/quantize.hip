@@ -72,6 +72,44 @@ __global__ void nv_trailer_init_kernel(uint8_t* gap, int gap_bytes, NvTrailer* t
   }
 }
 
+// An NVFP4 quantization whose amax is given (mx_quantize_amax): the amax is
+// the largest magnitude among `nslots` fp32 words. Every wave reduces the
+// words itself (a few loads from L2, no synchronization), s_t derives from
+// the result as from a reduced amax, and workgroup 0 writes the trailer and
+// zeroes the padding before it, so no separate launch precedes the encode.
+struct NvGiven {
+  const uint32_t* words;   // nullptr: the amax is in the trailer already
+  int nslots;
+  uint8_t* gap;
+  int gap_bytes;
+};
+
+__device__ __forceinline__ uint32_t nv_given_amax(const NvGiven& gv, NvTrailer* tr) {
+  const int t = threadIdx.x;
+  uint32_t b = 0u;
+  for (int i = t & 63; i < gv.nslots; i += 64) b = max(b, gv.words[i] & 0x7FFFFFFFu);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) b = max(b, (uint32_t)__shfl_xor((int)b, off));
+  if (blockIdx.x == 0) {
+    if (t < gv.gap_bytes) gv.gap[t] = 0;
+    if (t == 0) {
+      tr->amax_bits = b;
+      tr->pad[0] = 0u;
+      tr->pad[1] = 0u;
+    }
+  }
+  return b;
+}
+
+// The tensor scale an NVFP4 encode uses: from the given words, or from the
+// amax already reduced into the trailer; workgroup 0 records it there.
+__device__ __forceinline__ float nv_kernel_s_t(const NvGiven& gv, NvTrailer* tr) {
+  const uint32_t b = gv.words != nullptr ? nv_given_amax(gv, tr) : tr->amax_bits;
+  const float s_t = nvfp4_tensor_scale(b);
+  if (blockIdx.x == 0 && threadIdx.x == 0) tr->s_t = s_t;
+  return s_t;
+}
+
 // Largest |x| of X [rows, cols]: 8-element groups, gpr per row. A grid of
 // about one workgroup per CU walks the tensor with 4 loads in flight per
 // thread; waves reduce through LDS and each workgroup issues one atomic
@@ -359,12 +397,9 @@ __device__ __forceinline__ uint32_t quant_rows(const uint16_t* __restrict__ src,
 template <int FMT, int U>
 __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                        int kpad, NvTrailer* tr) {
+                                                        int kpad, NvTrailer* tr, NvGiven gv) {
   float s_t = 0.0f;
-  if (FMT == FMT_NVFP4) {
-    s_t = nvfp4_tensor_scale(tr->amax_bits);
-    if (blockIdx.x == 0 && threadIdx.x == 0) tr->s_t = s_t;
-  }
+  if (FMT == FMT_NVFP4) s_t = nv_kernel_s_t(gv, tr);
   quant_rows<FMT, U>(src, rows, cols, ld, codes, scales, kpad, s_t, blockIdx.x * blockDim.x + threadIdx.x,
                   gridDim.x * blockDim.x);
 }
@@ -404,24 +439,6 @@ __global__ __launch_bounds__(256) void quant_row_batch_kernel(const QuantBatch b
 // Zeroes n words (the amax accumulators of mx_quantize_batch_amax).
 __global__ void zero_words_kernel(uint32_t* w, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) w[i] = 0u;
-}
-
-// Trailer and gap of an NVFP4 quantization whose amax is given: the amax is
-// the largest magnitude among the nslots fp32 words (one wave of 64 lanes),
-// s_t derives from it as from a reduced amax.
-__global__ void nv_trailer_given_kernel(uint8_t* gap, int gap_bytes, NvTrailer* tr, const uint32_t* amax, int nslots) {
-  const int t = threadIdx.x;
-  if (t < gap_bytes) gap[t] = 0;
-  uint32_t b = 0u;
-  for (int i = t; i < nslots; i += 64) b = max(b, amax[i] & 0x7FFFFFFFu);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) b = max(b, (uint32_t)__shfl_xor((int)b, off));
-  if (t == 0) {
-    tr->amax_bits = b;
-    tr->s_t = nvfp4_tensor_scale(b);
-    tr->pad[0] = 0u;
-    tr->pad[1] = 0u;
-  }
 }
 
 // ------------------------------------------------------------ col quantizer
@@ -703,7 +720,7 @@ __device__ __forceinline__ void col_encode(const uint16_t* tile, const uint32_t*
 template <int FMT>
 __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ src, int rows, int cols, int ld,
                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                        int kpad, NvTrailer* tr) {
+                                                        int kpad, NvTrailer* tr, NvGiven gv) {
   __shared__ __align__(16) uint16_t tile[kColTileR * kColLdsLd];
   uint8_t* const stage = reinterpret_cast<uint8_t*>(tile);   // the staged output reuses the tile
   static_assert(ColStage<FMT>::BYTES <= (int)sizeof(tile), "staged output fits in the tile buffer");
@@ -713,10 +730,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
   const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
   const int t = threadIdx.x;
   float s_t = 0.0f;
-  if (FMT == FMT_NVFP4) {
-    s_t = nvfp4_tensor_scale(tr->amax_bits);
-    if (blockIdx.x == 0 && t == 0) tr->s_t = s_t;
-  }
+  if (FMT == FMT_NVFP4) s_t = nv_kernel_s_t(gv, tr);
   [[maybe_unused]] const Nv4Tensor nt = nv4_tensor(s_t);
   constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
   const __amdgpu_buffer_rsrc_t c_rs = out_rsrc(codes, (int64_t)cols * (FMT == FMT_MXFP8 ? kpad : kpad / 2));
@@ -1002,12 +1016,18 @@ static int grid_for(int64_t work_items, int per_block, int cap) {
 
 template <int U>
 static void launch_row(const uint16_t* src, int ir, int ic, int ild, uint8_t* codes, uint8_t* scales, int ikp,
-                       NvTrailer* tr, int64_t R, int fmt, hipStream_t stream) {
+                       NvTrailer* tr, NvGiven gv, int64_t R, int fmt, hipStream_t stream) {
   const int g = grid_for(R * (ikp / 8 / U), 256, 1 << 20);
   switch (fmt) {
-    case FMT_MXFP8: quant_row_kernel<FMT_MXFP8, U><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
-    case FMT_MXFP4: quant_row_kernel<FMT_MXFP4, U><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
-    default:        quant_row_kernel<FMT_NVFP4, U><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr); break;
+    case FMT_MXFP8:
+      quant_row_kernel<FMT_MXFP8, U><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr, gv);
+      break;
+    case FMT_MXFP4:
+      quant_row_kernel<FMT_MXFP4, U><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr, gv);
+      break;
+    default:
+      quant_row_kernel<FMT_NVFP4, U><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr, gv);
+      break;
   }
 }
 
@@ -1021,12 +1041,12 @@ hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int6
   const int bs = fmt == FMT_NVFP4 ? 16 : 32;
   const int ir = (int)rows, ic = (int)cols, ild = (int)ld, ikp = (int)kpad;
   NvTrailer* tr = nullptr;
+  NvGiven gv{nullptr, 0, nullptr, 0};
   if (fmt == FMT_NVFP4) {
     const int64_t nscale = R * (kpad / bs);
     tr = reinterpret_cast<NvTrailer*>(scales + round_up(nscale, 16));
     if (amax) {
-      nv_trailer_given_kernel<<<1, 64, 0, stream>>>(scales + nscale, (int)(round_up(nscale, 16) - nscale), tr, amax,
-                                                     nslots);
+      gv = NvGiven{amax, nslots, scales + nscale, (int)(round_up(nscale, 16) - nscale)};   // the encode derives s_t
     } else {
       nv_trailer_init_kernel<<<1, 64, 0, stream>>>(scales + nscale, (int)(round_up(nscale, 16) - nscale), tr);
       const int gpr = (int)((cols + 7) / 8);
@@ -1035,25 +1055,25 @@ hipError_t launch_quantize(const uint16_t* src, int64_t rows, int64_t cols, int6
   }
   if (axis == 0) {
     if (R * (kpad / 8) >= kRowSmallGroups)
-      launch_row<kRowGroupsPerThread>(src, ir, ic, ild, codes, scales, ikp, tr, R, fmt, stream);
+      launch_row<kRowGroupsPerThread>(src, ir, ic, ild, codes, scales, ikp, tr, gv, R, fmt, stream);
     else
-      launch_row<kRowGroupsSmall>(src, ir, ic, ild, codes, scales, ikp, tr, R, fmt, stream);
+      launch_row<kRowGroupsSmall>(src, ir, ic, ild, codes, scales, ikp, tr, gv, R, fmt, stream);
   } else {
     const int64_t ntiles = ((cols + kColTileC - 1) / kColTileC) * (kpad / kColTileR);
     switch (fmt) {
       case FMT_MXFP8: {
         const int g = one_tile_grid(ntiles);
-        quant_col_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr);
+        quant_col_kernel<FMT_MXFP8><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr, gv);
         break;
       }
       case FMT_MXFP4: {
         const int g = one_tile_grid(ntiles);
-        quant_col_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr);
+        quant_col_kernel<FMT_MXFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr, gv);
         break;
       }
       default: {
         const int g = one_tile_grid(ntiles);
-        quant_col_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr);
+        quant_col_kernel<FMT_NVFP4><<<g, 256, 0, stream>>>(src, ir, ic, ild, codes, scales, ikp, tr, gv);
         break;
       }
     }
