@@ -73,10 +73,12 @@ __global__ void nv_trailer_init_kernel(uint8_t* gap, int gap_bytes, NvTrailer* t
 }
 
 // An NVFP4 quantization whose amax is given (mx_quantize_amax): the amax is
-// the largest magnitude among `nslots` fp32 words. Every wave reduces the
-// words itself (a few loads from L2, no synchronization), s_t derives from
-// the result as from a reduced amax, and workgroup 0 writes the trailer and
-// zeroes the padding before it, so no separate launch precedes the encode.
+// the largest magnitude among `nslots` (<= 256) fp32 words. Each workgroup
+// reduces them itself, one word per thread of its 4 waves, then a wave max
+// and a max over the waves through LDS; s_t derives from the result as from
+// a reduced amax, and workgroup 0 writes the trailer and zeroes the padding
+// before it, so no separate launch precedes the encode. Called by every
+// thread of a 256-thread workgroup in uniform control flow.
 struct NvGiven {
   const uint32_t* words;   // nullptr: the amax is in the trailer already
   int nslots;
@@ -85,11 +87,14 @@ struct NvGiven {
 };
 
 __device__ __forceinline__ uint32_t nv_given_amax(const NvGiven& gv, NvTrailer* tr) {
+  __shared__ uint32_t wave_max[4];
   const int t = threadIdx.x;
-  uint32_t b = 0u;
-  for (int i = t & 63; i < gv.nslots; i += 64) b = max(b, gv.words[i] & 0x7FFFFFFFu);
+  uint32_t b = t < gv.nslots ? gv.words[t] & 0x7FFFFFFFu : 0u;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) b = max(b, (uint32_t)__shfl_xor((int)b, off));
+  if ((t & 63) == 0) wave_max[t >> 6] = b;
+  __syncthreads();
+  b = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
   if (blockIdx.x == 0) {
     if (t < gv.gap_bytes) gv.gap[t] = 0;
     if (t == 0) {
@@ -729,9 +734,10 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
   const int ntiles = tiles_c * tiles_r;
   const bool vec_ok = (ld % 8) == 0 && ((uintptr_t)src % 16) == 0;
   const int t = threadIdx.x;
-  float s_t = 0.0f;
-  if (FMT == FMT_NVFP4) s_t = nv_kernel_s_t(gv, tr);
-  [[maybe_unused]] const Nv4Tensor nt = nv4_tensor(s_t);
+  // NVFP4: s_t is read once, after the first tile's loads are issued, so
+  // that its loads and theirs are in flight together
+  [[maybe_unused]] Nv4Tensor nt = nv4_tensor(0.0f);
+  bool nt_ready = FMT != FMT_NVFP4;
   constexpr int BS = (FMT == FMT_NVFP4) ? 16 : 32;
   const __amdgpu_buffer_rsrc_t c_rs = out_rsrc(codes, (int64_t)cols * (FMT == FMT_MXFP8 ? kpad : kpad / 2));
   const __amdgpu_buffer_rsrc_t s_rs = out_rsrc(scales, (int64_t)cols * (kpad / BS));
@@ -743,6 +749,10 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
     tile_coords(n, tiles_r, tiles_c, r0, c0);
     uint4 v[4];
     load_tile(v, src, rows, cols, ld, vec_ok, r0, c0, t);
+    if (!nt_ready) {                          // uniform: the walk is per workgroup
+      nt = nv4_tensor(nv_kernel_s_t(gv, tr));
+      nt_ready = true;
+    }
     stage_tile(tile, v, t);
     __syncthreads();                          // tile staged
     uint32_t words[8], sbytes;
@@ -753,6 +763,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
     col_stage_flush<FMT>(stage, t, c_rs, s_rs, kpad, r0, c0, cols);
     __syncthreads();                          // staged output read
   }
+  if (!nt_ready) nv_kernel_s_t(gv, tr);       // a workgroup without tiles still records the trailer
 }
 
 // ------------------------------------------------------------ fused row + col
