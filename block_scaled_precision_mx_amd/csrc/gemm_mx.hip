@@ -301,7 +301,7 @@ __device__ __forceinline__ void nv_mma_stage(v16f (&acc)[Cfg::FM][Cfg::FN], cons
   }
 }
 
-// The same stage, software-pipelined: the 4 FN fp16 instructions of block
+// The same stage, software-pipelined: the 4 * FN fp16 instructions of block
 // (t, fm) use A dequantized during the previous block and B dequantized
 // during sub-step t - 1, so the conversions that run beside them (the next
 // block's A fragment and a share of sub-step t + 1's B fragments) do not
@@ -332,12 +332,24 @@ __device__ __forceinline__ void nv_mma_stage_piped(v16f (&acc)[Cfg::FM][Cfg::FN]
     a_raw1 = a_frag(1);
     a_sc1 = a_scales(1);
   }
-#pragma unroll
-  for (int f = 0; f < FN; ++f) nv_dequant_frag(b_raw[f], b_sc[f], bd[f]);
+  // before the first instruction only B fragment 0 and A are converted; the
+  // other B fragments of sub-step 0 are converted beside block 0's
+  // instructions, which run fragment by fragment (each accumulator still
+  // takes its 4 instructions in K order)
+  nv_dequant_frag(b_raw[0], b_sc[0], bd[0]);
   nv_dequant_frag(a_raw0, a_sc0, ad);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int t = b / FM, fm = b % FM;
+    if (b == 0) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        if (fn + 1 < FN) nv_dequant_frag(b_raw[fn + 1], b_sc[fn + 1], bd[fn + 1]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          acc[0][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bd[fn][k], ad[k], acc[0][fn], 0, 0, 0);
+      }
+    }
     if (b + 2 < NB) {
       a_raw2 = a_frag(b + 2);
       a_sc2 = a_scales(b + 2);
@@ -355,11 +367,13 @@ __device__ __forceinline__ void nv_mma_stage_piped(v16f (&acc)[Cfg::FM][Cfg::FN]
       for (int f = 0; f < FN; ++f)
         if (b_block(f) == fm) nv_dequant_frag(b_raw[f], b_sc[f], bdn[f]);
     }
+    if (b > 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bd[fn][k], ad[k], acc[fm][fn], 0, 0, 0);
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bd[fn][k], ad[k], acc[fm][fn], 0, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < 4 * FN; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one matrix instruction
