@@ -12,7 +12,6 @@
 #include <algorithm>
 #include <cstdio>
 #include <mutex>
-#include <type_traits>
 
 namespace mx {
 
@@ -36,11 +35,12 @@ static bool nv_small_tiles(int64_t M, int64_t N) {
   return cost(128, 128, 2) < cost(192, 256, 1);
 }
 
-// Estimated time of a plan (us): rounds x stages per item x stage time (a
-// 64-K stage of one workgroup with every CU busy, measured on MI355X on the
-// training shapes; two 128x128 workgroups sharing a CU split its throughput,
-// the dequantization being VALU and LDS work), plus the split-K partials
-// (about 3 us + 0.25 us per MB, measured).
+// Estimated time of a plan (us): rounds x 64-K steps per item x the time of
+// one 64-K step of one workgroup with every CU busy (measured on MI355X on
+// the training shapes: about 1.7 us for 192x256, 0.7 us for 128x128, whose
+// two workgroups per CU split the CU's throughput, the dequantization being
+// VALU work), plus the split-K partials (about 3 us + 0.25 us per MB,
+// measured). The kernel stages 256 K at a time; the model counts in 64 K.
 static double nv_plan_us(int64_t M, int64_t N, int64_t K, NvPlan p) {
   const int64_t nk = round_up(K, kAlignK) / 64;
   const int bm = p.small ? 128 : 192, bn = p.small ? 128 : 256, occ = p.small ? 2 : 1;
