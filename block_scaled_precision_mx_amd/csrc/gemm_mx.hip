@@ -957,16 +957,20 @@ static hipError_t run_mx_q(const uint8_t* A, const uint8_t* As, const uint8_t* B
 }
 
 // NVFP4 through the MX kernel's data path (fp4 stages, dequantized per
-// wave to fp16): 128x128 tiles (4 waves of 64x64, two workgroups per CU) or
-// 192x256 (4 waves of 96x128, one wave per SIMD, so the pipelined stage).
-// Four waves of 96x128 convert 7 fragments per 48 matrix instructions where
-// eight of 96x64 convert 5 per 24, and the conversions are this path's VALU
-// limit.
-hipError_t run_gemm_nvfp4_mx(bool small, int splits, const uint8_t* A, const uint8_t* As, const uint8_t* B,
+// wave to fp16). Tiles: 192x256 (4 waves of 96x128, one wave per SIMD, so
+// the pipelined stage), 128x128 (4 waves of 64x64, two workgroups per CU)
+// or 128x256 (4 waves of 64x128, one workgroup per CU, pipelined; the
+// split weight gradients). Four waves of 96x128 convert 7 fragments per 48
+// matrix instructions where eight of 96x64 convert 5 per 24, and the
+// conversions are this path's VALU limit.
+hipError_t run_gemm_nvfp4_mx(int tile, int splits, const uint8_t* A, const uint8_t* As, const uint8_t* B,
                              const uint8_t* Bs, void* C, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
                              int out_f32, float* ws, hipStream_t stream) {
-  if (small)
+  if (tile == NV_TILE_128x128)
     return run_mx<MxCfg<FMT_NVFP4, 128, 128, 2, 2, 2, true>>(A, As, B, Bs, C, M, N, K, bias, out_f32, splits, ws,
+                                                               stream);
+  if (tile == NV_TILE_128x256)
+    return run_mx<MxCfg<FMT_NVFP4, 128, 256, 2, 2, 1, true>>(A, As, B, Bs, C, M, N, K, bias, out_f32, splits, ws,
                                                                stream);
   return run_mx<MxCfg<FMT_NVFP4, 192, 256, 2, 2, 1, true>>(A, As, B, Bs, C, M, N, K, bias, out_f32, splits, ws,
                                                              stream);

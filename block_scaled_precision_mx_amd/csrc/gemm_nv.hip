@@ -16,9 +16,22 @@
 namespace mx {
 
 struct NvPlan {
-  bool small;                                // 128x128 (two workgroups per CU) instead of 192x256
+  int tile;                                  // NvTile
   int splits;
 };
+
+struct NvTileShape {
+  int bm, bn, occ;                           // rows, columns, workgroups per CU
+  double step_us;                            // one 64-K step of one workgroup, every CU busy (see nv_plan_us)
+};
+
+static NvTileShape nv_tile_shape(int tile) {
+  switch (tile) {
+    case NV_TILE_128x128: return {128, 128, 2, 0.73};
+    case NV_TILE_128x256: return {128, 256, 1, 1.12};
+    default:              return {192, 256, 1, 1.7};
+  }
+}
 
 // Tile shape with the least work per CU lost to a partly filled last round:
 // rounds of resident workgroups x tile area x workgroups per CU. 128x128 (4
@@ -26,48 +39,52 @@ struct NvPlan {
 // gradient shapes (4096 x 1024 outputs, K = tokens), where 192x256 tiles
 // leave most CUs idle; on ties the larger tiles win (less dequantization
 // and LDS traffic per output).
-static bool nv_small_tiles(int64_t M, int64_t N) {
+static int nv_unsplit_tile(int64_t M, int64_t N) {
   auto cost = [&](int bm, int bn, int occ) {
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const int64_t slots = std::max(8, occ * cu_count() / 8 * 8);
     return (double)((tiles + slots - 1) / slots) * bm * bn * occ;
   };
-  return cost(128, 128, 2) < cost(192, 256, 1);
+  return cost(128, 128, 2) < cost(192, 256, 1) ? NV_TILE_128x128 : NV_TILE_192x256;
 }
 
 // Estimated time of a plan (us): rounds x 64-K steps per item x the time of
 // one 64-K step of one workgroup with every CU busy (measured on MI355X on
-// the training shapes: about 1.7 us for 192x256, 0.7 us for 128x128, whose
-// two workgroups per CU split the CU's throughput, the dequantization being
-// VALU work), plus the split-K partials (about 3 us + 0.25 us per MB,
-// measured). The kernel stages 256 K at a time; the model counts in 64 K.
+// the training shapes: about 1.7 us for 192x256, 1.1 us for 128x256, 0.7 us
+// for 128x128, whose two workgroups per CU split the CU's throughput, the
+// dequantization being VALU work), plus the split-K partials (about 3 us +
+// 0.25 us per MB, measured). The kernel stages 256 K at a time; the model
+// counts in 64 K.
 static double nv_plan_us(int64_t M, int64_t N, int64_t K, NvPlan p) {
+  const NvTileShape t = nv_tile_shape(p.tile);
   const int64_t nk = round_up(K, kAlignK) / 64;
-  const int bm = p.small ? 128 : 192, bn = p.small ? 128 : 256, occ = p.small ? 2 : 1;
   const int64_t cus = cu_count();
-  const int64_t items = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * p.splits;
-  const int64_t rounds = (items + occ * cus - 1) / (occ * cus);
-  const double stage = p.small ? 0.73 * (items > cus ? 2.0 : 1.0) : 1.7;
-  double t = (double)rounds * (double)(2 * ((nk / 2 + p.splits - 1) / p.splits)) * stage;
-  if (p.splits > 1) t += 3.0 + 0.25 * (double)(p.splits * 4) * (double)(M * N) / 1.0e6;
-  return t;
+  const int64_t items = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn) * p.splits;
+  const int64_t rounds = (items + t.occ * cus - 1) / (t.occ * cus);
+  const double step = t.occ == 2 && items > cus ? 2.0 * t.step_us : t.step_us;
+  double us = (double)rounds * (double)(2 * ((nk / 2 + p.splits - 1) / p.splits)) * step;
+  if (p.splits > 1) us += 3.0 + 0.25 * (double)(p.splits * 4) * (double)(M * N) / 1.0e6;
+  return us;
 }
 
 // As for the MX GEMM: a split plan only if the workspace holds its partials
-// and the estimate beats the unsplit plan by 5%.
+// and the estimate beats the unsplit plan by 5%. Split plans may also take
+// 128x256 tiles (4 waves of 64x128): with one workgroup per CU and fewer
+// conversions per matrix instruction than 128x128, they fill the chip on
+// the 4096 x 1024 weight gradients with two splits.
 static NvPlan nv_choose_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes) {
-  NvPlan best{nv_small_tiles(M, N), 1};
+  NvPlan best{nv_unsplit_tile(M, N), 1};
   if (ws_bytes < 2 * M * N * 4) return best;
   double best_us = nv_plan_us(M, N, K, best);
   const int64_t pairs = round_up(K, kAlignK) / 128;
-  for (bool small : {false, true}) {
-    const int bm = small ? 128 : 192, bn = small ? 128 : 256, occ = small ? 2 : 1;
-    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-    for (int s = 2; s <= 16 && tiles * s <= occ * cu_count() && pairs >= 2 * s && s * M * N * 4 <= ws_bytes; ++s) {
-      const double us = nv_plan_us(M, N, K, NvPlan{small, s});
+  for (int tile : {NV_TILE_192x256, NV_TILE_128x128, NV_TILE_128x256}) {
+    const NvTileShape t = nv_tile_shape(tile);
+    const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    for (int s = 2; s <= 16 && tiles * s <= t.occ * cu_count() && pairs >= 2 * s && s * M * N * 4 <= ws_bytes; ++s) {
+      const double us = nv_plan_us(M, N, K, NvPlan{tile, s});
       if (us < 0.95 * best_us) {
         best_us = us;
-        best = NvPlan{small, s};
+        best = NvPlan{tile, s};
       }
     }
   }
@@ -80,22 +97,23 @@ int64_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 const char* plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, int64_t ws_bytes) {
-  static const char* names[2] = {"gemm_mx_kernel<nvfp4, 192x256>", "gemm_mx_kernel<nvfp4, 128x128>"};
-  static char split_names[2][17][48];
+  static const char* names[3] = {"gemm_mx_kernel<nvfp4, 192x256>", "gemm_mx_kernel<nvfp4, 128x128>",
+                                 "gemm_mx_kernel<nvfp4, 128x256>"};
+  static char split_names[3][17][48];
   static std::once_flag once;
   std::call_once(once, [] {
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 3; ++t)
       for (int sp = 2; sp <= 16; ++sp) snprintf(split_names[t][sp], 48, "%s+splitk%d", names[t], sp);
   });
   const NvPlan p = nv_choose_plan(M, N, K, ws_bytes);
-  return p.splits > 1 ? split_names[p.small][p.splits] : names[p.small];
+  return p.splits > 1 ? split_names[p.tile][p.splits] : names[p.tile];
 }
 
 hipError_t launch_gemm_nvfp4(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
                              int64_t M, int64_t N, int64_t K, const uint16_t* bias, int out_f32, float* ws,
                              int64_t ws_bytes, hipStream_t stream) {
   const NvPlan p = nv_choose_plan(M, N, K, ws != nullptr ? ws_bytes : 0);
-  return run_gemm_nvfp4_mx(p.small, p.splits, A, As, B, Bs, C, M, N, K, bias, out_f32, ws, stream);
+  return run_gemm_nvfp4_mx(p.tile, p.splits, A, As, B, Bs, C, M, N, K, bias, out_f32, ws, stream);
 }
 
 }  // namespace mx

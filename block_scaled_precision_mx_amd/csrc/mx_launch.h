@@ -60,8 +60,9 @@ hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B,
                           void* C, int64_t M, int64_t N, int64_t K, int fmt, const uint16_t* bias,
                           int out_f32, float* ws, int64_t ws_bytes, hipStream_t stream);
 
-// NVFP4 GEMM on the MX kernel's data path (128x128 or 192x256 tiles).
-hipError_t run_gemm_nvfp4_mx(bool small, int splits, const uint8_t* A, const uint8_t* As, const uint8_t* B,
+// NVFP4 GEMM on the MX kernel's data path, in one of its tile shapes.
+enum NvTile { NV_TILE_192x256 = 0, NV_TILE_128x128 = 1, NV_TILE_128x256 = 2 };
+hipError_t run_gemm_nvfp4_mx(int tile, int splits, const uint8_t* A, const uint8_t* As, const uint8_t* B,
                              const uint8_t* Bs, void* C, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
                              int out_f32, float* ws, hipStream_t stream);
 

@@ -37,6 +37,8 @@ SPLIT_FULL = [
     (3072, 1024, 11235, "nvfp4", "bf16", False),
     (4096, 1024, 11235, "mxfp8", "bf16", False),   # fc1's and fc2's weight gradients, every output
     (1024, 4096, 11235, "mxfp8", "bf16", False),
+    (4096, 1024, 11235, "nvfp4", "bf16", False),   # NVFP4: 128x256 tiles, 2 splits (half: 128x128 unsplit)
+    (1024, 4096, 11235, "nvfp4", "bf16", True),
 ]
 _ORACLE = {}   # (M, N, K, fmt, bias) -> (inputs, quantized operands, reference): shared by both workspace sizes
 # the weight-gradient GEMMs of the training workloads, with the benchmark's
