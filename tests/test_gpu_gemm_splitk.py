@@ -39,6 +39,8 @@ SPLIT_FULL = [
     (1024, 4096, 11235, "mxfp8", "bf16", False),
     (4096, 1024, 11235, "nvfp4", "bf16", False),   # NVFP4: 128x256 tiles, 2 splits (half: 128x128 unsplit)
     (1024, 4096, 11235, "nvfp4", "bf16", True),
+    (1000, 770, 9000, "nvfp4", "f32", True),       # 128x256 in 8 ragged splits, ragged M and N (half: 128x128)
+    (1234, 2050, 9999, "nvfp4", "bf16", False),    # 192x256 in 4 splits (half: 128x256 in 2)
 ]
 _ORACLE = {}   # (M, N, K, fmt, bias) -> (inputs, quantized operands, reference): shared by both workspace sizes
 # the weight-gradient GEMMs of the training workloads, with the benchmark's
