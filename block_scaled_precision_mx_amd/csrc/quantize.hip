@@ -581,13 +581,24 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) {
   return y < 6.0f ? code : 7u;                             // 6 and above (inf, NaN too): 6
 }
 
-// NVFP4 code of x with scale S32 = fp32(dec(byte) * s_t), rounded
-// stochastically with draw u: y = fp32(|x| / S32), sign copied from x.
-__device__ __forceinline__ uint32_t nvfp4_encode_sr(float x, float S32, uint32_t u) {
+// fp64 reciprocal of a block's S32 = fp32(dec(byte) * s_t) for
+// nvfp4_encode_sr (0 when S32 is not positive).
+__device__ __forceinline__ double sr_inv_scale(float S32) { return S32 > 0.0f ? 1.0 / (double)S32 : 0.0; }
+
+// NVFP4 code of x with scale S32 > 0, rounded stochastically with draw u:
+// y = fp32(|x| / S32), the correctly rounded quotient, sign copied from x
+// (S32 = 0: a zero code). y comes from fp64 instead of an fp32 division:
+// |x| (a bf16 value, at most 8 significant bits) over S32 (24 bits) is never
+// an fp32 rounding midpoint and lies at least 2^-25 ulp from every one (the
+// difference |x| - m S32 for a midpoint m is a nonzero multiple of
+// ulp(m) S32 / 2^25 or coarser), while |x| * RN64(1 / S32) in fp64 is within
+// 2^-52 of the quotient (relative; also for fp32-subnormal results, whose
+// midpoints are as far apart in ulps). Rounding that product to fp32 is
+// therefore the rounding of the quotient itself.
+__device__ __forceinline__ uint32_t nvfp4_encode_sr(float x, double inv_S, uint32_t u) {
   const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
-  if (!(S32 > 0.0f)) return sign;
-  const float y = __fdiv_rn(fabsf(x), S32);
-  return sign | e2m1_sr(y, u);
+  const float y = (float)((double)fabsf(x) * inv_S);
+  return sign | (inv_S > 0.0 ? e2m1_sr(y, u) : 0u);
 }
 
 // Tile walk of a persistent grid (gridDim.x a multiple of 8). Workgroups are
@@ -685,8 +696,8 @@ __device__ __forceinline__ void col_encode(const uint16_t* tile, const uint32_t*
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const Nv4Block B = nv4_block(m2[hb], nt);
-      [[maybe_unused]] float S32 = 0.0f;
-      if constexpr (SR) S32 = __fmul_rn((float)e4m3_value(B.sb), nt.s_t);
+      [[maybe_unused]] double inv_S = 0.0;
+      if constexpr (SR) inv_S = sr_inv_scale(__fmul_rn((float)e4m3_value(B.sb), nt.s_t));
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         float x[8];
@@ -695,7 +706,7 @@ __device__ __forceinline__ void col_encode(const uint16_t* tile, const uint32_t*
           uint32_t word = 0u;
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            word |= nvfp4_encode_sr(x[i], S32, draw[(32 * w + 16 * hb + 8 * q2 + i) * kColTileC + j]) << (4 * i);
+            word |= nvfp4_encode_sr(x[i], inv_S, draw[(32 * w + 16 * hb + 8 * q2 + i) * kColTileC + j]) << (4 * i);
           words[2 * hb + q2] = word;
         } else {
           words[2 * hb + q2] = nv4_encode8(x, B, nt);
@@ -838,10 +849,10 @@ __device__ __forceinline__ void row_encode_store(const uint4 vv, int p, int t, i
     sr_draws8(((uint64_t)r * (uint64_t)cols + (uint64_t)c) >> 3, seed0, seed1, d);
     *reinterpret_cast<uint4*>(&draw[(t / 8 + 32 * p) * kColTileC + (t % 8) * 8]) = make_uint4(d[0], d[1], d[2], d[3]);
     *reinterpret_cast<uint4*>(&draw[(t / 8 + 32 * p) * kColTileC + (t % 8) * 8 + 4]) = make_uint4(d[4], d[5], d[6], d[7]);
-    const float S32 = __fmul_rn((float)e4m3_value(sb), nt.s_t);
+    const double inv_S = sr_inv_scale(__fmul_rn((float)e4m3_value(sb), nt.s_t));
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) word |= nvfp4_encode_sr(x[i], S32, d[i]) << (4 * i);
+    for (int i = 0; i < 8; ++i) word |= nvfp4_encode_sr(x[i], inv_S, d[i]) << (4 * i);
     packed = word;
   } else if constexpr (FMT == FMT_NVFP4) {
     const Nv4Block B = nv4_block(m, nt);
