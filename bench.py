@@ -380,7 +380,8 @@ def build(name, dev):
 
 # ------------------------------------------------------------------ timing
 
-# host time allowed per launch while a replay's launches are enqueued
+# host time allowed per launch while a replay's launches are enqueued, before
+# the first replay has measured it
 LEAD_US_PER_LAUNCH = 40.0
 
 
@@ -391,7 +392,8 @@ def measure(sets, steps, warmup, stream):
     each on its own tensors as in the step) back to back between one pair of
     HIP events on the stream the kernels run on, so that the events' own
     overhead is spread over many launches, after a spin that lets the host
-    enqueue them all first; `steps` replays are averaged.
+    enqueue them all first (sized from the host time a first, untimed
+    replay took); `steps` replays are averaged.
     Returns (ms per step, [(op, average ms)] for the ops of every set)."""
     import torch
 
@@ -423,22 +425,27 @@ def measure(sets, steps, warmup, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     spin_per_us = 1.0e6 / max(e0.elapsed_time(e1) * 1.0e3, 1.0)
-    for _ in range(steps):
+    # host microseconds per launch of each label, as the last replay took them
+    host_us = {lab: LEAD_US_PER_LAUNCH for lab in groups}
+    for rep in range(steps + 1):                # replay 0 only measures the host side
         ev = {lab: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for lab in groups}
         for lab, ops in groups.items():
             # a spin on the stream ahead of the start event keeps the GPU busy
-            # while the host enqueues the label's launches, so the events time
-            # the kernels back to back and not the host's launch rate (a short
-            # kernel after a synchronization would otherwise wait for each
-            # launch)
-            torch.cuda._sleep(int(spin_per_us * LEAD_US_PER_LAUNCH * len(ops)))
+            # while the host enqueues the label's launches (1.5 times the time
+            # the host took last time), so the events time the kernels back to
+            # back and not the host's launch rate (a short kernel after a
+            # synchronization would otherwise wait for each launch)
+            torch.cuda._sleep(int(spin_per_us * 1.5 * host_us[lab] * len(ops)))
             ev[lab][0].record(stream)
+            h0 = time.perf_counter()
             for op in ops:
                 op.fn()
+            host_us[lab] = max(LEAD_US_PER_LAUNCH, (time.perf_counter() - h0) * 1.0e6 / len(ops))
             ev[lab][1].record(stream)
         torch.cuda.synchronize()
-        for lab, ops in groups.items():
-            per_label[lab] += ev[lab][0].elapsed_time(ev[lab][1]) / len(ops)
+        if rep > 0:
+            for lab, ops in groups.items():
+                per_label[lab] += ev[lab][0].elapsed_time(ev[lab][1]) / len(ops)
     timed = [(op, per_label[op.label] / steps) for ops in sets for op in ops]
     return ms_per_step, timed, len(sets)
 
