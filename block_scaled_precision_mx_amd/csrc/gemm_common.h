@@ -39,6 +39,14 @@ __device__ __forceinline__ void dma16(v4u rs, uint32_t lds_addr, uint32_t voff, 
                : "=&s"(saved) : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
 }
 
+// One wave-wide 4-byte-per-lane copy global -> LDS, used only to touch a
+// line so that the L2 holds it when the stage copy that reads it comes.
+__device__ __forceinline__ void dma4(v4u rs, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
+}
+
 // Wait until at most N vector memory operations of this wave are in flight
 // (they complete in issue order). Issued through the builtin so the
 // compiler's own wait bookkeeping sees it too.
