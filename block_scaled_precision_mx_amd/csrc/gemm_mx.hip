@@ -675,7 +675,7 @@ __device__ __forceinline__ void mx_epilogue(const v16f (&acc)[Cfg::FM][Cfg::FN],
 // stores per fragment row, FM WN / 16 = EPI_TOTAL in all. Only this wave
 // touches its area, so no workgroup barrier is needed; the LDS returns a
 // wave's reads and writes in order.
-template <class Cfg>
+template <class Cfg, int POLICY>
 __device__ __forceinline__ void mx_epilogue_wave(const v16f (&acc)[Cfg::FM][Cfg::FN], const uint8_t* lds_bias,
                                                  int M, int N, int m0, int n0, int wm, int wn, int g, int r32,
                                                  int lane, __amdgpu_buffer_rsrc_t c_rs, uint8_t* wst) {
@@ -719,7 +719,7 @@ __device__ __forceinline__ void mx_epilogue_wave(const v16f (&acc)[Cfg::FM][Cfg:
       const uint4 w = *reinterpret_cast<const uint4*>(wst + row * (2 * WN) + ((c ^ (row & (CW - 1))) * 16));
       const int m = m0 + wm * WM + 32 * fm + row, n = n0 + wn * WN + 8 * c;
       const int off = (m < M && n < N) ? (m * N + n) * 2 : (int)0x80000000u;
-      __builtin_amdgcn_raw_buffer_store_b128(v4u{w.x, w.y, w.z, w.w}, c_rs, off, 0, kStoreDeviceScope);
+      __builtin_amdgcn_raw_buffer_store_b128(v4u{w.x, w.y, w.z, w.w}, c_rs, off, 0, POLICY);
     }
   }
 }
@@ -1030,7 +1030,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
         if (!Cfg::WAVE_OWN || !bias_dma) block_sync();
         uint8_t* const area =
             (Cfg::WAVE_OWN ? lds + Cfg::WAREA_OFF : lds + ((gs - 1) & 1) * Cfg::STAGE) + wave * Cfg::WAREA;
-        mx_epilogue_wave<Cfg>(acc, lds_bias, M, N, m0, n0, wm, wn, g, r32, lane, c_rs, area);
+        // tiles before a workgroup's last one: streaming stores as well
+        if (ct + (int)gridDim.x < tiles)
+          mx_epilogue_wave<Cfg, kStoreStreamDeviceScope>(acc, lds_bias, M, N, m0, n0, wm, wn, g, r32, lane, c_rs, area);
+        else
+          mx_epilogue_wave<Cfg, kStoreDeviceScope>(acc, lds_bias, M, N, m0, n0, wm, wn, g, r32, lane, c_rs, area);
         wave_done = true;
       }
     }
