@@ -261,6 +261,9 @@ def test_last_error_is_per_thread(L):
 def test_gemm_plan_names(L):
     assert L.mx_gemm_plan(11235, 4096, 1024, 1).decode() == "gemm_mx_kernel<mxfp8, 256x256>"
     assert L.mx_gemm_plan(11235, 3072, 1024, 1).decode() == "gemm_mx_kernel<mxfp8, 192x256>"
+    # at least 32 K-stages of 128 (fp8): the L2-prefetching variant of the tile
+    assert L.mx_gemm_plan(11235, 1024, 4096, 1).decode() == "gemm_mx_kernel<mxfp8, 192x256, l2pf>"
+    assert L.mx_gemm_plan(11235, 1024, 3968, 1).decode() == "gemm_mx_kernel<mxfp8, 192x256>"
     assert L.mx_gemm_plan(11235, 1024, 4096, 2).decode() == "gemm_mx_kernel<mxfp4, 192x256>"
     assert L.mx_gemm_plan(11235, 4096, 1024, 2).decode() == "gemm_mx_kernel<mxfp4, 192x256>"
     assert L.mx_gemm_plan(256, 768, 768, 1).decode() == "gemm_mx_kernel<mxfp8, 128x128>"

@@ -68,3 +68,23 @@ def test_workload_gemm_lists():
         assert all(s.fmt == bt.fwd_fmt for s in first[:4]) and all(s.fmt == bt.bwd_fmt for s in first[4:])
         # wgrad contracts over the tokens
         assert all(s.k == bt.m for s in first if s.label.endswith("wgrad"))
+
+
+def test_kernel_families_aggregate():
+    """The roofline's kernel: a format's tile configurations summed (flops
+    over time), each family priced against its own matrix-core peak."""
+    kernels = {
+        "gemm_mx_kernel<mxfp8, 192x256>": {"launches_per_step": 2, "ms_per_step": 0.1, "flops_per_launch_avg": 5e10},
+        "gemm_mx_kernel<mxfp8, 192x256, l2pf>": {"launches_per_step": 1, "ms_per_step": 0.05,
+                                                 "flops_per_launch_avg": 9e10},
+        "gemm_mx_kernel<nvfp4, 128x256>+splitk2": {"launches_per_step": 1, "ms_per_step": 0.2,
+                                                   "flops_per_launch_avg": 9e10},
+    }
+    fam = bench.kernel_families(kernels)
+    f8 = fam["gemm_mx_kernel<mxfp8>"]
+    assert f8["launches_per_step"] == 3 and abs(f8["ms_per_step"] - 0.15) < 1e-12
+    assert abs(f8["flops_per_launch_avg"] - (2 * 5e10 + 9e10) / 3) < 1.0
+    assert abs(f8["avg_launch_us"] - 50.0) < 1e-9
+    assert f8["configurations"] == ["gemm_mx_kernel<mxfp8, 192x256, l2pf>", "gemm_mx_kernel<mxfp8, 192x256>"]
+    assert fam["gemm_mx_kernel<nvfp4>"]["launches_per_step"] == 1
+    assert set(bench.FAMILY_PEAK) >= set(fam)
