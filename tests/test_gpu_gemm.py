@@ -54,6 +54,8 @@ MANY_TILES = [
     (4160, 4096, 384, "nvfp4", "bf16", "192x256"),
     (2048, 8192, 256, "nvfp4", "bf16", "128x128"),   # every slot walks 2 tiles
     (4160, 4096, 4200, "mxfp8", "bf16", "192x256, l2pf"),   # >= 32 stages: L2 prefetch, ragged M and K
+    (4160, 4040, 384, "mxfp8", "bf16", "192x256"),   # N % 64 != 0: per-wave 128-byte row segments cut at N
+    (4160, 4040, 384, "nvfp4", "bf16", "192x256"),   # per-wave 256-byte row segments cut at N
 ]
 # forward linears of the stacks at full size, sampled outputs: (workload, linear)
 FULL_SIZE_FWD = [(wl, lin) for wl in ("vitl16_mxfp8_fwd_stack", "vitl16_mxfp4_fwd_stack", "vitb16_mxfp8_fwd_stack")
