@@ -429,14 +429,18 @@ def measure(sets, steps, warmup, stream):
     spin_per_us = 1.0e6 / max(e0.elapsed_time(e1) * 1.0e3, 1.0)
     # host microseconds per launch of each label, as the last replay took them
     host_us = {lab: LEAD_US_PER_LAUNCH for lab in groups}
+    # the replays run back to back with no synchronization between them (a
+    # GPU left idle by one runs the next replay's first labels slower: the
+    # first two labels after a synchronization measured up to 2.5x their
+    # kernels' own time in the trace); the events are read at the end
+    events = []
     for rep in range(steps + 1):                # replay 0 only measures the host side
         ev = {lab: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for lab in groups}
         for lab, ops in groups.items():
             # a spin on the stream ahead of the start event keeps the GPU busy
             # while the host enqueues the label's launches (1.5 times the time
             # the host took last time), so the events time the kernels back to
-            # back and not the host's launch rate (a short kernel after a
-            # synchronization would otherwise wait for each launch)
+            # back and not the host's launch rate
             torch.cuda._sleep(int(spin_per_us * 1.5 * host_us[lab] * len(ops)))
             ev[lab][0].record(stream)
             h0 = time.perf_counter()
@@ -444,10 +448,12 @@ def measure(sets, steps, warmup, stream):
                 op.fn()
             host_us[lab] = max(LEAD_US_PER_LAUNCH, (time.perf_counter() - h0) * 1.0e6 / len(ops))
             ev[lab][1].record(stream)
-        torch.cuda.synchronize()
         if rep > 0:
-            for lab, ops in groups.items():
-                per_label[lab] += ev[lab][0].elapsed_time(ev[lab][1]) / len(ops)
+            events.append(ev)
+    torch.cuda.synchronize()
+    for ev in events:
+        for lab, ops in groups.items():
+            per_label[lab] += ev[lab][0].elapsed_time(ev[lab][1]) / len(ops)
     timed = [(op, per_label[op.label] / steps) for ops in sets for op in ops]
     return ms_per_step, timed, len(sets)
 
