@@ -881,8 +881,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_mx_kernel(const uint8_
   // stage waits allow PF_OPS of them in flight. It pays only where the
   // operands miss the L2 at every stage of long tiles (measured: MXFP8 fc2,
   // K = 4096, 8% faster; 1-3% slower on the K = 1024 shapes and on MXFP4).
-  // the prefetch reads B rows in wave 1, A rows in the other waves (the
-  // components go through readfirstlane so that they stay scalar)
+  // Wave 1's copy reads B, the others' A; the buffer resource goes through
+  // readfirstlane so that the compiler keeps it in scalar registers.
   v4u pf_rs = a_rs;
   if constexpr (Cfg::PF) {
     const v4u r = wave == 1 ? b_rs : a_rs;
