@@ -26,8 +26,10 @@ within LN_REL * B_i of the exact value, where
 
 covering the fp32 rounding of the row sums (the mean's error scales with
 the row's magnitude, the centred value's with |x_i - mu|), of the reciprocal
-square root and of the final multiply-adds, with a factor of about 4 to
-spare for rows up to 4096 long. Each element then has an interval of
+square root and of the final multiply-adds. A row sum of C fp32 terms taken
+as C / 64 sequential terms per lane and then a 64-lane tree carries at most
+about (C / 64 + 6) 2^-24 of the sum of magnitudes: a factor of about 4 to
+spare at 4096 columns and about 2 at 8192, the widest row the kernel takes. Each element then has an interval of
 possible bf16 values, and check_rows accepts an output iff some choice
 inside the intervals explains every scale byte and code (fused.check_intervals).
 """

@@ -62,11 +62,11 @@ def check(x, g, b, eps, fmt, rows=None, **kw):
 
 @pytest.mark.parametrize("fmt", MX)
 @pytest.mark.parametrize("rc", [(1, 32), (3, 100), (37, 1000), (64, 1024), (130, 768), (17, 2000), (6, 1536),
-                                (9, 4096), (5, 4000)])
+                                (9, 4096), (5, 4000), (7, 6000), (3, 8192)])
 def test_layernorm_quantize_shapes(fmt, rc):
     """Widths up to 512, 1024 and 2048 take the register-resident kernel with
     one, two and four 512-column chunks per row; wider rows the three-pass
-    kernel."""
+    kernel, up to the C ABI's 8192 columns."""
     r, c = rc
     x = residual(r, c, seed=r * 7 + c)
     g, b = params(c, seed=c)
